@@ -1,0 +1,222 @@
+/*
+ * scape.h - C ABI of libscape, the SCAPE per-worker optimizer step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * SCAPE is the sparse-communication distributed optimizer of "SCAPE: Accurate
+ * and Efficient LLM Training with Extreme Sparse Communication" (Zheng, Chen,
+ * Xie, Zhang; arXiv 2607.01678).  Citations below name the page and section:
+ *   [abs]   shd-paper.top page, English abstract;
+ *   [TS-n]  gist.science "Technical Summary: SCAPE - Accurate and Efficient
+ *           LLM Training with Extreme Sparse Communication", section n.
+ * The pages print no formula; where they leave a step open the library takes
+ * one explicit reading, stated at the entry point that uses it.
+ *
+ * Conventions for every entry point:
+ *   - Return value: SCAPE_OK (0) or a negative SCAPE_ERR_* code.  Nothing
+ *     throws.  scape_last_error() gives a text for the calling thread's last
+ *     failure.  Arguments are validated on the host before anything is
+ *     enqueued; on a validation error nothing is launched and no output is
+ *     touched.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *     enqueued asynchronously on it; no call synchronizes the host, except
+ *     scape_init/scape_destroy/scape_profile_read as noted.
+ *   - Pointers named "device" point to device memory the caller owns; they
+ *     must be 16-byte aligned unless stated otherwise.  Pointer arrays
+ *     (`r`, `g`, `sparse_bufs`) are host arrays of W device pointers.
+ *   - A context must not be used on two streams at once; separate contexts
+ *     are independent.
+ *
+ * Layout (one flat buffer for all parameter tensors): tensor l starts at
+ * element offset layer_offset[l], a multiple of 64, and the flat length n_pad
+ * is a multiple of 64 (elements between tensors are padding and are never
+ * read or written by the step).  A mask over the flat buffer is stored as
+ *   bits[n_pad/64]           element j is bit (j % 64) of word j/64, LSB first;
+ *   idx[k_total]             the set positions in ascending order (uint32);
+ *   block_prefix[n_pad/64+1] number of set bits in words 0..w-1.
+ * Masks use one bit per element, the packed single-bit format of the Memory
+ * Optimization paragraph of [TS-2].
+ */
+#ifndef SCAPE_H
+#define SCAPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SCAPE_VERSION_MAJOR 1
+#define SCAPE_VERSION_MINOR 0
+
+#define SCAPE_OK 0
+#define SCAPE_ERR_INVALID_ARG (-1) /* null pointer, bad enum, out-of-range scalar     */
+#define SCAPE_ERR_SHAPE (-2)       /* sizes that do not fit the layout or the limits  */
+#define SCAPE_ERR_ALIGN (-3)       /* a device pointer is not aligned as required     */
+#define SCAPE_ERR_OOM (-4)         /* device allocation failed or would exceed limits */
+#define SCAPE_ERR_HIP (-5)         /* a HIP call failed; text in scape_last_error()   */
+#define SCAPE_ERR_STATE (-6)       /* call not valid in the context's current state   */
+
+#define SCAPE_MAX_WORKERS 32
+
+typedef struct scape_ctx scape_ctx;
+
+/* Problem description.  All fields are read at scape_init and copied. */
+typedef struct scape_config {
+    int32_t num_layers;         /* L >= 1 parameter tensors ("layers")               */
+    const int64_t* layer_numel; /* host array [L], each >= 0, sum of padded sizes
+                                   below 2^31 elements                               */
+    int32_t workers;            /* W, 1..SCAPE_MAX_WORKERS simulated workers         */
+    int32_t owner_shards;       /* P, 1..W ownership shards; 0 means W               */
+    float beta1, beta2;         /* AdamS moment coefficients, each in [0, 1)         */
+    float lr, eps, weight_decay;
+    uint32_t keep_num, keep_den;/* kept fraction (1 - sparsity) = keep_num/keep_den,
+                                   0 <= keep_num <= keep_den, keep_den >= 1          */
+} scape_config;
+
+/* A mask in the layout above; all three arrays are caller-owned device memory
+ * (bits 8-byte aligned, idx and block_prefix 4-byte aligned). */
+typedef struct scape_mask {
+    uint64_t* bits;
+    uint32_t* idx;
+    uint32_t* block_prefix;
+} scape_mask;
+
+/* Library version. */
+int scape_version(int32_t* major, int32_t* minor);
+
+/* Text of the calling thread's last failure ("" if none).  The pointer stays
+ * valid until the thread's next failing call. */
+const char* scape_last_error(void);
+
+/*
+ * Host-only layout query (no GPU needed).  Kept count per layer:
+ * k_l = ceil(n_l * keep_num / keep_den) (the pages evaluate 90% and 99%
+ * sparsity, [abs]; rounding up keeps at least one element of a non-empty
+ * layer).  Owner of layer l under P shards: the shard of an even split of
+ * [0, n_pad) into P parts that holds the layer midpoint, capped at P-1 - the
+ * layer-aligned ownership of Partitioned Mask Synchronization [TS-2].
+ * Outputs may be NULL; layer_offset/layer_k/layer_owner have L entries.
+ * Errors: INVALID_ARG / SHAPE for a config scape_init would reject.
+ */
+int scape_layout(const scape_config* cfg, int64_t* n_pad, int64_t* k_total, int64_t* layer_offset,
+                 int64_t* layer_k, int32_t* layer_owner);
+
+/* Host-only: owner shard of every layer for an arbitrary shard count P >= 1
+ * (owner[L]).  Used to pick the layers of one worker's mask build. */
+int scape_owner_map(const scape_config* cfg, int32_t num_shards, int32_t* owner);
+
+/*
+ * Create a context: validates the config, builds the layout and tile tables,
+ * and allocates the context's own device workspaces (histograms, per-layer
+ * selection state, candidate records, scan partials, statistic buffer) on the
+ * current HIP device.  Synchronizes the device once (table upload).
+ * Errors: INVALID_ARG, SHAPE, OOM, HIP.  *out is set only on success.
+ */
+int scape_init(const scape_config* cfg, scape_ctx** out);
+
+/* Free a context and its workspaces (synchronizes the device).  NULL is OK. */
+int scape_destroy(scape_ctx* ctx);
+
+/*
+ * One SCAPE step on W simulated workers, all resident on this GPU.
+ *
+ * Per element j (in any tensor l, with mo = m[j] before the step):
+ *   a_i  = r_i[j] + float(g_i[j])                 error feedback: the residual
+ *                                                 keeps unsent gradient mass
+ *                                                 ([TS-1] Problem Statement;
+ *                                                 [TS-2] Key Design Insights)
+ *   mt_i = beta1*mo + (1-beta1)*a_i               AdamS first-moment candidate
+ *   r_i[j] = (j in M_t) ? 0 : a_i
+ *   key[j] = bit pattern of |mt_owner(l)|         first-moment statistic of the
+ *                                                 layer's owner ([abs])
+ * At the positions of M_t (`cur`), in ascending order q = 0..|M_t|-1:
+ *   sparse_bufs[i][q] = mt_i                      worker i's sparse buffer: the
+ *                                                 payload one collective carries
+ *   bbar = ((mt_0 + mt_1) + ... + mt_{W-1}) / W   the synchronized buffer
+ *   g_hat = (bbar - beta1*mo) / (1-beta1)         averaged gradient and residual
+ *                                                 recovered from bbar alone
+ *                                                 ([TS-2] Single-Buffer Second-
+ *                                                 Moment Reconstruction)
+ *   v[j] = beta2*mo^2 + (1-beta2)*g_hat^2         AdamS normaliser (reading: no
+ *                                                 bias correction)
+ *   m[j] = bbar
+ *   x[j] = x[j] - lr*(bbar/(sqrt(v[j]) + eps) + weight_decay*x[j])
+ * Off M_t, x, m and v are unchanged.  Then M_{t+1} (`next`): per layer, the
+ * k_l positions with the largest key, ties to the lower position ([TS-2]
+ * Partitioned Mask Synchronization), written as bits, idx and block_prefix.
+ * M_{t+1} is for the next call: the caller passes it as `cur` then ([TS-2]
+ * Delayed Mask Usage).  The first step normally passes an all-zero mask.
+ * Every floating-point operation is IEEE fp32, round to nearest even, in the
+ * order written, with no fused multiply-add.
+ *
+ * Arguments (device, n_pad elements unless stated):
+ *   x, m, v       fp32 state, updated in place;
+ *   r[W]          fp32 residual of each worker, updated in place;
+ *   g[W]          bfloat16 gradient bits (uint16) of each worker, read only;
+ *   cur           M_t, read only, as written by scape_step/scape_mask_build/
+ *                 scape_mask_index (bits, idx, block_prefix consistent);
+ *                 positions beyond the first k_total set bits are treated as
+ *                 unmasked;
+ *   next          M_{t+1}, written; must not alias `cur`;
+ *   sparse_bufs[W] fp32 device arrays of k_total entries, written (4-byte
+ *                 alignment suffices);
+ *   key_out       uint32 statistic array (n_pad), written; NULL uses the
+ *                 context's own buffer.
+ * Errors: INVALID_ARG, ALIGN, STATE (next aliases cur), HIP.
+ */
+int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
+               const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+               void* stream);
+
+/*
+ * Mask build alone, from first-moment statistics mtilde (fp32, n_pad): per
+ * layer, the k_l positions with the largest |mtilde| (bit pattern order),
+ * ties to the lower position ([TS-2] Partitioned Mask Synchronization).
+ *   num_shards <= 0 or shard < 0: every layer; writes out->bits (all words),
+ *     out->idx and out->block_prefix.
+ *   otherwise: only the layers whose owner under num_shards shards is
+ *     `shard` (the one worker's share); writes only the words of those
+ *     layers in out->bits; idx and block_prefix are not touched (may be NULL)
+ *     - after all shards are gathered, scape_mask_index builds them.
+ * Errors: INVALID_ARG, ALIGN, HIP.
+ */
+int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, int32_t shard,
+                     const scape_mask* out, void* stream);
+
+/* idx and block_prefix of a mask from its bits (all n_pad/64 words).  At most
+ * k_total positions are stored in idx; block_prefix counts every set bit.
+ * Errors: INVALID_ARG, ALIGN, HIP. */
+int scape_mask_index(scape_ctx* ctx, const scape_mask* mask, void* stream);
+
+/* Pack n bytes (nonzero = set) into ceil(n/64) words, LSB first; bits past n
+ * are zero.  Unpack writes n bytes of 0/1.  pred needs no alignment, bits
+ * 8-byte alignment.  n >= 0 (n = 0 enqueues nothing).  Errors: INVALID_ARG,
+ * ALIGN, SHAPE (n >= 2^37), HIP. */
+int scape_pack(const uint8_t* pred, int64_t n, uint64_t* bits, void* stream);
+int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream);
+
+/* out[q] = ((bufs[0][q] + bufs[1][q]) + ... + bufs[W-1][q]) / W for q < k:
+ * the mean of the W sparse buffers summed in worker order, the one-GPU
+ * stand-in for the all-reduce of [TS-2] Single-Buffer Second-Moment
+ * Reconstruction.  bufs is a host array of W device pointers (4-byte
+ * aligned); 1 <= W <= 32; k >= 0.  Errors: INVALID_ARG, ALIGN, SHAPE, HIP. */
+int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream);
+
+/* Optional per-phase timing of scape_step with HIP events recorded on the
+ * step's stream.  Phases: */
+#define SCAPE_PHASE_EF_COMPACT 0    /* error feedback, candidates, compaction, statistic */
+#define SCAPE_PHASE_REDUCE_UPDATE 1 /* W-way reduction, reconstruction, v/m/x update     */
+#define SCAPE_PHASE_MASK_SELECT 2   /* per-layer top-k into bits                        */
+#define SCAPE_PHASE_MASK_INDEX 3    /* idx and block_prefix of the new mask             */
+#define SCAPE_PHASE_COUNT 4
+/* enable != 0 starts recording (clearing earlier records); 0 stops. */
+int scape_profile_enable(scape_ctx* ctx, int32_t enable);
+/* Waits for the recorded events and returns, per phase, the summed
+ * milliseconds (ms[SCAPE_PHASE_COUNT]) and the number of steps recorded. */
+int scape_profile_read(scape_ctx* ctx, double* ms, int64_t* steps);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCAPE_H */

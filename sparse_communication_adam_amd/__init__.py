@@ -1,0 +1,16 @@
+"""SCAPE per-worker optimizer step on AMD Instinct MI355X (gfx950).
+
+The data-parallel hot path of SCAPE ("SCAPE: Accurate and Efficient LLM
+Training with Extreme Sparse Communication") as hand-written HIP kernels
+behind a C ABI (include/scape.h, libscape.so); this package is the Python
+binding with the same entry-point names.
+"""
+from ._scape import (  # noqa: F401
+    LIB_PATH, PHASES, Context, Layout, Mask, ScapeConfig, ScapeError, alloc_mask, lib, scape_destroy, scape_init,
+    scape_last_error, scape_layout, scape_mask_build, scape_mask_index, scape_owner_map, scape_pack,
+    scape_profile_enable, scape_profile_read, scape_reduce_sparse, scape_step, scape_unpack, scape_version)
+
+
+def build(verbose: bool = False) -> str:
+    from .build import build as _build
+    return _build(verbose)

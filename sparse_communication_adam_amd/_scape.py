@@ -1,0 +1,317 @@
+"""ctypes binding of libscape (include/scape.h), same names as the C ABI.
+
+Argument marshalling only: every step of the SCAPE path runs in the HIP
+kernels of libscape.so.  Device arrays are torch tensors (PyTorch supplies
+device memory and streams); host arrays are Python sequences.  If the
+library is not built, every call raises - there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libscape.so")
+
+SCAPE_OK = 0
+SCAPE_ERR_INVALID_ARG = -1
+SCAPE_ERR_SHAPE = -2
+SCAPE_ERR_ALIGN = -3
+SCAPE_ERR_OOM = -4
+SCAPE_ERR_HIP = -5
+SCAPE_ERR_STATE = -6
+SCAPE_MAX_WORKERS = 32
+PHASES = ("ef_compact", "reduce_update", "mask_select", "mask_index")
+
+_ERR_NAMES = {-1: "INVALID_ARG", -2: "SHAPE", -3: "ALIGN", -4: "OOM", -5: "HIP", -6: "STATE"}
+
+_lib = None
+
+
+class ScapeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"SCAPE_ERR_{_ERR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("layer_numel", ctypes.POINTER(ctypes.c_int64)),
+                ("workers", ctypes.c_int32), ("owner_shards", ctypes.c_int32), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("lr", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("keep_num", ctypes.c_uint32), ("keep_den", ctypes.c_uint32)]
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("block_prefix", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        cfgp, maskp = ctypes.POINTER(_Config), ctypes.POINTER(_Mask)
+        sig = {
+            "scape_version": [vp, vp],
+            "scape_layout": [cfgp, vp, vp, vp, vp, vp],
+            "scape_owner_map": [cfgp, i32, vp],
+            "scape_init": [cfgp, ctypes.POINTER(vp)],
+            "scape_destroy": [vp],
+            "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
+            "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
+            "scape_mask_index": [vp, maskp, vp],
+            "scape_pack": [vp, i64, vp, vp],
+            "scape_unpack": [vp, i64, vp, vp],
+            "scape_reduce_sparse": [vp, i32, i64, vp, vp],
+            "scape_profile_enable": [vp, i32],
+            "scape_profile_read": [vp, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.scape_last_error.argtypes = []
+        L.scape_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def scape_last_error() -> str:
+    return lib().scape_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != SCAPE_OK:
+        raise ScapeError(rc, scape_last_error())
+
+
+# ----------------------------------------------------------------------------
+# configuration and layout
+
+
+@dataclass
+class ScapeConfig:
+    layer_numel: Sequence[int]
+    workers: int
+    keep_num: int
+    keep_den: int
+    owner_shards: int = 0
+    beta1: float = 0.9
+    beta2: float = 0.95
+    lr: float = 1e-3
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+    def _c(self):
+        arr = (ctypes.c_int64 * max(len(self.layer_numel), 1))(*[int(n) for n in self.layer_numel])
+        c = _Config(len(self.layer_numel), arr, self.workers, self.owner_shards, self.beta1, self.beta2, self.lr,
+                    self.eps, self.weight_decay, self.keep_num, self.keep_den)
+        c._keep = arr  # keep the array alive with the struct
+        return c
+
+
+@dataclass
+class Layout:
+    n_pad: int
+    k_total: int
+    layer_offset: list
+    layer_k: list
+    layer_owner: list
+
+    @property
+    def n_words(self) -> int:
+        return self.n_pad // 64
+
+
+def scape_version():
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().scape_version(ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def scape_layout(cfg: ScapeConfig) -> Layout:
+    c = cfg._c()
+    L = len(cfg.layer_numel)
+    n_pad, k_total = ctypes.c_int64(), ctypes.c_int64()
+    off = (ctypes.c_int64 * max(L, 1))()
+    kk = (ctypes.c_int64 * max(L, 1))()
+    own = (ctypes.c_int32 * max(L, 1))()
+    _check(lib().scape_layout(ctypes.byref(c), ctypes.byref(n_pad), ctypes.byref(k_total), off, kk, own))
+    return Layout(n_pad.value, k_total.value, list(off)[:L], list(kk)[:L], list(own)[:L])
+
+
+def scape_owner_map(cfg: ScapeConfig, num_shards: int) -> list:
+    c = cfg._c()
+    L = len(cfg.layer_numel)
+    own = (ctypes.c_int32 * max(L, 1))()
+    _check(lib().scape_owner_map(ctypes.byref(c), num_shards, own))
+    return list(own)[:L]
+
+
+# ----------------------------------------------------------------------------
+# device marshalling
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, numel: Optional[int], name: str) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _ptr_array(ptrs) -> ctypes.Array:
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+
+
+class Mask:
+    """A mask in the library layout, backed by three device tensors."""
+
+    def __init__(self, bits, idx, block_prefix):
+        self.bits, self.idx, self.block_prefix = bits, idx, block_prefix
+
+    def _c(self) -> _Mask:
+        import torch
+        ints = (torch.int64,)
+        b = _dev(self.bits, ints, None, "mask.bits")
+        i = _dev(self.idx, (torch.int32,), None, "mask.idx") if self.idx is not None else None
+        p = _dev(self.block_prefix, (torch.int32,), None, "mask.block_prefix") if self.block_prefix is not None else None
+        return _Mask(b, i, p)
+
+    def clear(self):
+        self.bits.zero_()
+        self.idx.zero_()
+        self.block_prefix.zero_()
+
+
+def alloc_mask(layout: Layout, device="cuda") -> Mask:
+    """An all-zero mask sized for `layout` (bits int64, idx/block_prefix int32)."""
+    import torch
+    return Mask(torch.zeros(layout.n_words, dtype=torch.int64, device=device),
+                torch.zeros(max(layout.k_total, 1), dtype=torch.int32, device=device),
+                torch.zeros(layout.n_words + 1, dtype=torch.int32, device=device))
+
+
+# ----------------------------------------------------------------------------
+# context and entry points
+
+
+class Context:
+    def __init__(self, cfg: ScapeConfig):
+        self.cfg = cfg
+        self.layout = scape_layout(cfg)
+        h = ctypes.c_void_p()
+        c = cfg._c()
+        _check(lib().scape_init(ctypes.byref(c), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ScapeError(SCAPE_ERR_STATE, "context destroyed")
+        return self._h
+
+    def destroy(self):
+        if self._h is not None:
+            _check(lib().scape_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def scape_init(cfg: ScapeConfig) -> Context:
+    return Context(cfg)
+
+
+def scape_destroy(ctx: Context) -> None:
+    ctx.destroy()
+
+
+def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next: Mask, sparse_bufs: Sequence,
+               key_out=None, stream=None) -> None:
+    import torch
+    n, W, k = ctx.layout.n_pad, ctx.cfg.workers, ctx.layout.k_total
+    if len(r) != W or len(g) != W or len(sparse_bufs) != W:
+        raise ValueError(f"r, g and sparse_bufs need {W} entries each")
+    xp = _dev(x, torch.float32, n, "x")
+    mp = _dev(m, torch.float32, n, "m")
+    vp = _dev(v, torch.float32, n, "v")
+    rp = _ptr_array([_dev(t, torch.float32, n, f"r[{i}]") for i, t in enumerate(r)])
+    gp = _ptr_array([_dev(t, (torch.int16, torch.bfloat16, torch.uint16), n, f"g[{i}]") for i, t in enumerate(g)])
+    bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
+    kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
+    c, nx = cur._c(), next._c()
+    _check(lib().scape_step(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
+                            _stream(stream)))
+
+
+def scape_mask_build(ctx: Context, mtilde, out: Mask, num_shards: int = 0, shard: int = -1, stream=None) -> None:
+    import torch
+    mp = _dev(mtilde, torch.float32, ctx.layout.n_pad, "mtilde")
+    o = out._c()
+    _check(lib().scape_mask_build(ctx.handle, mp, num_shards, shard, ctypes.byref(o), _stream(stream)))
+
+
+def scape_mask_index(ctx: Context, mask: Mask, stream=None) -> None:
+    c = mask._c()
+    _check(lib().scape_mask_index(ctx.handle, ctypes.byref(c), _stream(stream)))
+
+
+def scape_pack(pred, bits, n: Optional[int] = None, stream=None) -> None:
+    import torch
+    n = pred.numel() if n is None else n
+    pp = _dev(pred, (torch.uint8, torch.bool), n, "pred")
+    bp = _dev(bits, torch.int64, (n + 63) // 64, "bits")
+    _check(lib().scape_pack(pp, n, bp, _stream(stream)))
+
+
+def scape_unpack(bits, pred, n: Optional[int] = None, stream=None) -> None:
+    import torch
+    n = pred.numel() if n is None else n
+    bp = _dev(bits, torch.int64, (n + 63) // 64, "bits")
+    pp = _dev(pred, (torch.uint8, torch.bool), n, "pred")
+    _check(lib().scape_unpack(bp, n, pp, _stream(stream)))
+
+
+def scape_reduce_sparse(bufs: Sequence, out, k: Optional[int] = None, stream=None) -> None:
+    import torch
+    k = out.numel() if k is None else k
+    ptrs = _ptr_array([_dev(b, torch.float32, k, f"bufs[{i}]") for i, b in enumerate(bufs)])
+    op = _dev(out, torch.float32, k, "out")
+    _check(lib().scape_reduce_sparse(ptrs, len(bufs), k, op, _stream(stream)))
+
+
+def scape_profile_enable(ctx: Context, enable: bool = True) -> None:
+    _check(lib().scape_profile_enable(ctx.handle, 1 if enable else 0))
+
+
+def scape_profile_read(ctx: Context):
+    """(dict phase -> summed ms, steps recorded)."""
+    ms = (ctypes.c_double * 4)()
+    steps = ctypes.c_int64()
+    _check(lib().scape_profile_read(ctx.handle, ms, ctypes.byref(steps)))
+    return dict(zip(PHASES, list(ms))), steps.value

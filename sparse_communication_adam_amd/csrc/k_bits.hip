@@ -1,0 +1,156 @@
+// k_bits.hip - 1-bit mask kernels for gfx950: pack, unpack, and the index of
+// a mask (ascending positions and the per-word prefix of set bits).
+//
+// Masks are one bit per element, LSB first in 64-bit words: the packed
+// single-bit format of the Memory Optimization paragraph of the gist.science
+// Technical Summary, s.2.  On wave64 hardware one word is one wave: a ballot
+// over the 64 lanes packs a word, and a masked lane's rank inside its word is
+// one mbcnt.
+//
+// The index is built in three passes over the bits (N/8 bytes each):
+// per-workgroup popcounts, one scan of those partial sums, then an emit pass
+// that writes block_prefix for every word and, one wave per word, the set
+// positions into idx with contiguous stores.
+#include "scape_device.h"
+
+namespace scape {
+
+constexpr int kWordsPerThread = kIndexWordsPerBlock / kBlock;  // 8
+
+__global__ __launch_bounds__(kBlock) void k_index_count(const uint64_t* __restrict__ bits, uint32_t n_words,
+                                                        uint32_t* __restrict__ block_sums) {
+    __shared__ uint32_t scratch[kWaves];
+    const uint32_t w0 = blockIdx.x * kIndexWordsPerBlock + threadIdx.x * kWordsPerThread;
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < kWordsPerThread; ++e)
+        if (w0 + e < n_words) c += (uint32_t)__popcll(bits[w0 + e]);
+    uint32_t total = 0;
+    block_exclusive_scan(c, scratch, &total);
+    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums) {
+    const uint32_t nb = (n_words + kIndexWordsPerBlock - 1) / kIndexWordsPerBlock;
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_index_count, dim3(nb), dim3(kBlock), 0, s, bits, n_words, block_sums);
+    return hipGetLastError();
+}
+
+// Exclusive scan of n_blocks partial sums in place; the total goes to
+// block_sums[n_blocks].  One workgroup of 1024 threads, each owning a run.
+__global__ __launch_bounds__(1024) void k_index_scan(uint32_t* __restrict__ block_sums, uint32_t n_blocks) {
+    __shared__ uint32_t sc[1024];
+    const uint32_t per = (n_blocks + 1023) / 1024;
+    const uint32_t a = threadIdx.x * per;
+    const uint32_t b = min(a + per, n_blocks);
+    uint32_t c = 0;
+    for (uint32_t i = a; i < b; ++i) c += block_sums[i];
+    sc[threadIdx.x] = c;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        uint32_t t = threadIdx.x >= (unsigned)d ? sc[threadIdx.x - d] : 0u;
+        __syncthreads();
+        sc[threadIdx.x] += t;
+        __syncthreads();
+    }
+    uint32_t off = sc[threadIdx.x] - c;
+    for (uint32_t i = a; i < b; ++i) {
+        const uint32_t v = block_sums[i];
+        block_sums[i] = off;
+        off += v;
+    }
+    if (threadIdx.x == 1023) block_sums[n_blocks] = sc[1023];
+}
+
+hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blocks) {
+    hipLaunchKernelGGL(k_index_scan, dim3(1), dim3(1024), 0, s, block_sums, n_blocks);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kBlock) void k_index_emit(const uint64_t* __restrict__ bits, uint32_t n_words,
+                                                       const uint32_t* __restrict__ block_offs,
+                                                       uint32_t* __restrict__ idx, uint32_t k_cap,
+                                                       uint32_t* __restrict__ prefix) {
+    __shared__ uint32_t scratch[kWaves];
+    __shared__ uint64_t s_words[kIndexWordsPerBlock];
+    __shared__ uint32_t s_pref[kIndexWordsPerBlock];
+    const uint32_t wb = blockIdx.x * kIndexWordsPerBlock;
+    const uint32_t lw0 = threadIdx.x * kWordsPerThread;
+    uint64_t w[kWordsPerThread];
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < kWordsPerThread; ++e) {
+        const uint32_t wi = wb + lw0 + e;
+        w[e] = wi < n_words ? bits[wi] : 0ull;
+        c += (uint32_t)__popcll(w[e]);
+    }
+    uint32_t run = block_offs[blockIdx.x] + block_exclusive_scan(c, scratch, nullptr);
+#pragma unroll
+    for (int e = 0; e < kWordsPerThread; ++e) {
+        const uint32_t wi = wb + lw0 + e;
+        s_words[lw0 + e] = w[e];
+        s_pref[lw0 + e] = run;
+        if (wi < n_words) prefix[wi] = run;
+        run += (uint32_t)__popcll(w[e]);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) prefix[n_words] = block_offs[gridDim.x];
+    __syncthreads();
+    // one wave per word: lane l emits position 64*word + l if its bit is set
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    for (uint32_t lw = wave; lw < (uint32_t)kIndexWordsPerBlock; lw += kWaves) {
+        const uint64_t word = s_words[lw];
+        if (word == 0ull) continue;
+        if ((word >> lane) & 1ull) {
+            const uint32_t r = s_pref[lw] + lanes_below(word);
+            if (r < k_cap) idx[r] = (wb + lw) * 64u + lane;
+        }
+    }
+}
+
+hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,
+                             uint32_t* idx, uint32_t k_cap, uint32_t* prefix) {
+    const uint32_t nb = (n_words + kIndexWordsPerBlock - 1) / kIndexWordsPerBlock;
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_index_emit, dim3(nb), dim3(kBlock), 0, s, bits, n_words, block_offs, idx, k_cap, prefix);
+    return hipGetLastError();
+}
+
+// Pack: one wave per word, lane l tests element 64*word + l.
+__global__ __launch_bounds__(kBlock) void k_pack(const uint8_t* __restrict__ pred, uint64_t n, uint64_t n_words,
+                                                 uint64_t* __restrict__ bits) {
+    const uint32_t lane = lane_id();
+    const uint64_t waves = (uint64_t)gridDim.x * kWaves;
+    for (uint64_t w = (uint64_t)blockIdx.x * kWaves + threadIdx.x / 64; w < n_words; w += waves) {
+        const uint64_t j = w * 64 + lane;
+        const bool p = j < n && pred[j] != 0;
+        const uint64_t word = __ballot(p);
+        if (lane == 0) bits[w] = word;
+    }
+}
+
+hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits) {
+    if (n <= 0) return hipSuccess;
+    const uint64_t nw = ((uint64_t)n + 63) / 64;
+    uint64_t blocks = (nw + kWaves - 1) / kWaves;
+    if (blocks > 16384u) blocks = 16384u;
+    hipLaunchKernelGGL(k_pack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, pred, (uint64_t)n, nw, bits);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kBlock) void k_unpack(const uint64_t* __restrict__ bits, uint64_t n,
+                                                   uint8_t* __restrict__ pred) {
+    for (uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += (uint64_t)gridDim.x * kBlock)
+        pred[j] = (uint8_t)((bits[j >> 6] >> (j & 63)) & 1ull);
+}
+
+hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred) {
+    if (n <= 0) return hipSuccess;
+    uint64_t blocks = ((uint64_t)n + kBlock - 1) / kBlock;
+    if (blocks > 16384u) blocks = 16384u;
+    hipLaunchKernelGGL(k_unpack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, bits, (uint64_t)n, pred);
+    return hipGetLastError();
+}
+
+}  // namespace scape

@@ -1,0 +1,532 @@
+// scape_api.cpp - host side of libscape: argument validation, the flat
+// layout, tile tables, device workspaces, and the launch sequence of each
+// entry point declared in include/scape.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "scape_internal.h"
+
+using namespace scape;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SCAPE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+#define SCAPE_HIP(call, what)                      \
+    do {                                           \
+        hipError_t e_ = (call);                    \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxFlat = int64_t(1) << 31;  // positions are uint32 and j*64 stays below 2^32
+
+struct HostLayout {
+    int32_t L = 0;
+    std::vector<int64_t> n, off, k;
+    int64_t n_pad = 0, k_total = 0;
+};
+
+int validate_config(const scape_config* cfg) {
+    if (!cfg) return fail(SCAPE_ERR_INVALID_ARG, "config is NULL");
+    if (cfg->num_layers < 1) return fail(SCAPE_ERR_SHAPE, "num_layers must be >= 1 (got %d)", cfg->num_layers);
+    if (!cfg->layer_numel) return fail(SCAPE_ERR_INVALID_ARG, "layer_numel is NULL");
+    if (cfg->workers < 1 || cfg->workers > SCAPE_MAX_WORKERS)
+        return fail(SCAPE_ERR_INVALID_ARG, "workers must be in 1..%d (got %d)", SCAPE_MAX_WORKERS, cfg->workers);
+    if (cfg->owner_shards < 0 || cfg->owner_shards > cfg->workers)
+        return fail(SCAPE_ERR_INVALID_ARG, "owner_shards must be in 0..workers (got %d)", cfg->owner_shards);
+    if (cfg->keep_den < 1 || cfg->keep_num > cfg->keep_den)
+        return fail(SCAPE_ERR_INVALID_ARG, "keep must satisfy 0 <= keep_num <= keep_den, keep_den >= 1 (got %u/%u)",
+                    cfg->keep_num, cfg->keep_den);
+    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f) || !(cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f))
+        return fail(SCAPE_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+    if (!(cfg->lr == cfg->lr) || !(cfg->eps == cfg->eps) || !(cfg->weight_decay == cfg->weight_decay))
+        return fail(SCAPE_ERR_INVALID_ARG, "lr, eps and weight_decay must not be NaN");
+    int64_t cur = 0;
+    for (int32_t l = 0; l < cfg->num_layers; ++l) {
+        const int64_t n = cfg->layer_numel[l];
+        if (n < 0) return fail(SCAPE_ERR_SHAPE, "layer %d has negative size %lld", l, (long long)n);
+        if (n >= kMaxFlat) return fail(SCAPE_ERR_SHAPE, "layer %d is too large (%lld)", l, (long long)n);
+        cur += (n + 63) / 64 * 64;
+        if (cur >= kMaxFlat)
+            return fail(SCAPE_ERR_SHAPE, "padded total exceeds 2^31 - 1 elements at layer %d", l);
+    }
+    return SCAPE_OK;
+}
+
+int64_t kept_count(int64_t n, uint32_t num, uint32_t den) {
+    // n < 2^31 and num < 2^32: the product fits in 64 bits
+    return (int64_t)(((uint64_t)n * num + den - 1) / den);
+}
+
+void build_layout(const scape_config* cfg, HostLayout* h) {
+    h->L = cfg->num_layers;
+    h->n.assign(cfg->layer_numel, cfg->layer_numel + h->L);
+    h->off.resize(h->L);
+    h->k.resize(h->L);
+    int64_t cur = 0, kt = 0;
+    for (int32_t l = 0; l < h->L; ++l) {
+        h->off[l] = cur;
+        cur += (h->n[l] + 63) / 64 * 64;
+        h->k[l] = kept_count(h->n[l], cfg->keep_num, cfg->keep_den);
+        if (h->k[l] > h->n[l]) h->k[l] = h->n[l];
+        kt += h->k[l];
+    }
+    h->n_pad = cur;
+    h->k_total = kt;
+}
+
+// Shard of an even split of [0, n_pad) into P parts holding the layer
+// midpoint off + n/2, i.e. floor(P * (2*off + n) / (2*n_pad)), capped.
+void owner_map(const HostLayout& h, int32_t P, int32_t* owner) {
+    for (int32_t l = 0; l < h.L; ++l) {
+        if (h.n_pad == 0) {
+            owner[l] = 0;
+            continue;
+        }
+        const uint64_t num = (uint64_t)P * (uint64_t)(2 * h.off[l] + h.n[l]);
+        int64_t s = (int64_t)(num / (uint64_t)(2 * h.n_pad));
+        owner[l] = (int32_t)(s > P - 1 ? P - 1 : s);
+    }
+}
+
+struct ProfSlot {
+    hipEvent_t ev[SCAPE_PHASE_COUNT + 1];
+    bool pending;
+};
+
+constexpr int kProfSlots = 64;
+
+}  // namespace
+
+struct scape_ctx {
+    int device = 0;
+    scape_config cfg{};
+    HostLayout lay;
+    int32_t P = 1;
+    std::vector<int32_t> owner;
+    std::vector<TileDesc> tiles;
+    std::vector<uint32_t> layer_tile0;  // first tile of each layer (L+1 entries)
+    uint32_t n_words = 0;
+    uint32_t n_index_blocks = 0;
+    uint32_t cand_cap = 0;
+    // device workspaces
+    LayerDesc* d_layers = nullptr;
+    TileDesc* d_tiles = nullptr;
+    uint32_t* d_hist = nullptr;
+    SelState* d_sel = nullptr;
+    uint32_t* d_cand_fill = nullptr;
+    uint32_t* d_totals = nullptr;
+    uint64_t* d_cand = nullptr;
+    uint32_t* d_key = nullptr;
+    uint32_t* d_block_sums = nullptr;
+    // profiling
+    bool prof_on = false;
+    ProfSlot prof[kProfSlots]{};
+    bool prof_events = false;
+    int prof_next = 0;
+    double prof_ms[SCAPE_PHASE_COUNT] = {0, 0, 0, 0};
+    int64_t prof_steps = 0;
+};
+
+namespace {
+
+void free_ctx(scape_ctx* c) {
+    hipFree(c->d_layers);
+    hipFree(c->d_tiles);
+    hipFree(c->d_hist);
+    hipFree(c->d_sel);
+    hipFree(c->d_cand_fill);
+    hipFree(c->d_totals);
+    hipFree(c->d_cand);
+    hipFree(c->d_key);
+    hipFree(c->d_block_sums);
+    if (c->prof_events)
+        for (auto& s : c->prof)
+            for (auto& e : s.ev) hipEventDestroy(e);
+    delete c;
+}
+
+template <typename T>
+int dev_alloc(T** p, size_t count, const char* what) {
+    const size_t bytes = count * sizeof(T) > 0 ? count * sizeof(T) : 16;
+    hipError_t e = hipMalloc((void**)p, bytes);
+    if (e == hipErrorOutOfMemory) return fail(SCAPE_ERR_OOM, "out of device memory allocating %s (%zu bytes)", what, bytes);
+    if (e != hipSuccess) return hip_fail(e, what);
+    return SCAPE_OK;
+}
+
+int check_device(const scape_ctx* ctx) {
+    int dev = -1;
+    SCAPE_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev != ctx->device)
+        return fail(SCAPE_ERR_STATE, "context was created on device %d but device %d is current", ctx->device, dev);
+    return SCAPE_OK;
+}
+
+int check_mask(const scape_mask* m, bool need_index, const char* name) {
+    if (!m) return fail(SCAPE_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!m->bits) return fail(SCAPE_ERR_INVALID_ARG, "%s->bits is NULL", name);
+    if (!aligned(m->bits, 8)) return fail(SCAPE_ERR_ALIGN, "%s->bits must be 8-byte aligned", name);
+    if (need_index) {
+        if (!m->idx || !m->block_prefix) return fail(SCAPE_ERR_INVALID_ARG, "%s->idx/block_prefix is NULL", name);
+        if (!aligned(m->idx, 4) || !aligned(m->block_prefix, 4))
+            return fail(SCAPE_ERR_ALIGN, "%s->idx/block_prefix must be 4-byte aligned", name);
+    }
+    return SCAPE_OK;
+}
+
+// Record the event that closes `phase` (0..COUNT-1) or opens the step (-1).
+void prof_mark(scape_ctx* c, int slot, int point, hipStream_t s) {
+    if (slot >= 0) hipEventRecord(c->prof[slot].ev[point], s);
+}
+
+void prof_collect(scape_ctx* c, int slot) {
+    ProfSlot& p = c->prof[slot];
+    if (!p.pending) return;
+    hipEventSynchronize(p.ev[SCAPE_PHASE_COUNT]);
+    for (int i = 0; i < SCAPE_PHASE_COUNT; ++i) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, p.ev[i], p.ev[i + 1]) == hipSuccess) c->prof_ms[i] += ms;
+    }
+    c->prof_steps += 1;
+    p.pending = false;
+}
+
+int prof_begin(scape_ctx* c) {
+    if (!c->prof_on) return -1;
+    const int slot = c->prof_next;
+    c->prof_next = (c->prof_next + 1) % kProfSlots;
+    prof_collect(c, slot);  // the ring wrapped: fold the old record first
+    c->prof[slot].pending = true;
+    return slot;
+}
+
+// Mask selection over layers [la, la+nl) and tiles [ta, tb), keys in d_key,
+// bits into `bits`.
+int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint32_t* key, uint64_t* bits,
+               hipStream_t s) {
+    SCAPE_HIP(launch_select_first(s, la, nl, c->d_layers, c->d_hist, c->d_sel), "select_first");
+    SCAPE_HIP(launch_cand_scan(s, la, nl, c->cand_cap, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
+    SCAPE_HIP(launch_filter(s, c->d_tiles + ta, tb - ta, c->d_layers, c->d_sel, key, bits, c->d_cand_fill,
+                            c->d_cand),
+              "filter");
+    for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
+        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_cand_fill, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+        SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
+    }
+    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals, c->d_cand, bits), "cand_mark");
+    return SCAPE_OK;
+}
+
+int run_index(scape_ctx* c, const scape_mask* mk, hipStream_t s) {
+    SCAPE_HIP(launch_index_count(s, mk->bits, c->n_words, c->d_block_sums), "index_count");
+    SCAPE_HIP(launch_index_scan(s, c->d_block_sums, c->n_index_blocks), "index_scan");
+    SCAPE_HIP(launch_index_emit(s, mk->bits, c->n_words, c->d_block_sums, mk->idx, (uint32_t)c->lay.k_total,
+                                mk->block_prefix),
+              "index_emit");
+    return SCAPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int scape_version(int32_t* major, int32_t* minor) {
+    if (!major || !minor) return fail(SCAPE_ERR_INVALID_ARG, "NULL output");
+    *major = SCAPE_VERSION_MAJOR;
+    *minor = SCAPE_VERSION_MINOR;
+    return SCAPE_OK;
+}
+
+const char* scape_last_error(void) { return g_last_error.c_str(); }
+
+int scape_layout(const scape_config* cfg, int64_t* n_pad, int64_t* k_total, int64_t* layer_offset, int64_t* layer_k,
+                 int32_t* layer_owner) {
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    HostLayout h;
+    build_layout(cfg, &h);
+    if (n_pad) *n_pad = h.n_pad;
+    if (k_total) *k_total = h.k_total;
+    for (int32_t l = 0; l < h.L; ++l) {
+        if (layer_offset) layer_offset[l] = h.off[l];
+        if (layer_k) layer_k[l] = h.k[l];
+    }
+    if (layer_owner) owner_map(h, cfg->owner_shards ? cfg->owner_shards : cfg->workers, layer_owner);
+    return SCAPE_OK;
+}
+
+int scape_owner_map(const scape_config* cfg, int32_t num_shards, int32_t* owner) {
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    if (num_shards < 1) return fail(SCAPE_ERR_INVALID_ARG, "num_shards must be >= 1 (got %d)", num_shards);
+    if (!owner) return fail(SCAPE_ERR_INVALID_ARG, "owner is NULL");
+    HostLayout h;
+    build_layout(cfg, &h);
+    owner_map(h, num_shards, owner);
+    return SCAPE_OK;
+}
+
+int scape_init(const scape_config* cfg, scape_ctx** out) {
+    if (!out) return fail(SCAPE_ERR_INVALID_ARG, "out is NULL");
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    scape_ctx* c = new scape_ctx();
+    c->cfg = *cfg;
+    c->cfg.layer_numel = nullptr;
+    build_layout(cfg, &c->lay);
+    c->P = cfg->owner_shards ? cfg->owner_shards : cfg->workers;
+    c->owner.resize(c->lay.L);
+    owner_map(c->lay, c->P, c->owner.data());
+    c->n_words = (uint32_t)(c->lay.n_pad / 64);
+    c->n_index_blocks = (c->n_words + kIndexWordsPerBlock - 1) / kIndexWordsPerBlock;
+    c->cand_cap = (uint32_t)c->lay.n_pad;
+
+    std::vector<LayerDesc> ld(c->lay.L);
+    c->layer_tile0.assign(c->lay.L + 1, 0);
+    for (int32_t l = 0; l < c->lay.L; ++l) {
+        ld[l].off = (uint32_t)c->lay.off[l];
+        ld[l].n = (uint32_t)c->lay.n[l];
+        ld[l].k = (uint32_t)c->lay.k[l];
+        ld[l].owner = c->owner[l];
+        c->layer_tile0[l] = (uint32_t)c->tiles.size();
+        const uint32_t w0 = (uint32_t)(c->lay.off[l] / 64);
+        const uint32_t w1 = (uint32_t)((c->lay.off[l] + c->lay.n[l] + 63) / 64);
+        for (uint32_t w = w0; w < w1; w += kTileWords) {
+            TileDesc t;
+            t.layer = l;
+            t.w0 = w;
+            t.w1 = w + kTileWords < w1 ? w + kTileWords : w1;
+            t.pad = 0;
+            c->tiles.push_back(t);
+        }
+    }
+    c->layer_tile0[c->lay.L] = (uint32_t)c->tiles.size();
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        free_ctx(c);
+        return hip_fail(e, "hipGetDevice");
+    }
+    c->device = dev;
+    const size_t L = (size_t)c->lay.L;
+    if ((rc = dev_alloc(&c->d_layers, L, "layer table")) || (rc = dev_alloc(&c->d_tiles, c->tiles.size(), "tile table")) ||
+        (rc = dev_alloc(&c->d_hist, L * kHistBins, "histograms")) || (rc = dev_alloc(&c->d_sel, L, "selection state")) ||
+        (rc = dev_alloc(&c->d_cand_fill, L, "candidate counters")) || (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
+        (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
+        (rc = dev_alloc(&c->d_key, (size_t)c->lay.n_pad, "statistic keys")) ||
+        (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums"))) {
+        free_ctx(c);
+        return rc;
+    }
+    e = hipMemcpy(c->d_layers, ld.data(), L * sizeof(LayerDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !c->tiles.empty())
+        e = hipMemcpy(c->d_tiles, c->tiles.data(), c->tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(c->d_hist, 0, L * kHistBins * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(c->d_sel, 0, L * sizeof(SelState));
+    if (e == hipSuccess) e = hipMemset(c->d_totals, 0, 4 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_ctx(c);
+        return hip_fail(e, "uploading context tables");
+    }
+    *out = c;
+    return SCAPE_OK;
+}
+
+int scape_destroy(scape_ctx* ctx) {
+    if (!ctx) return SCAPE_OK;
+    hipDeviceSynchronize();
+    free_ctx(ctx);
+    return SCAPE_OK;
+}
+
+int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
+               const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+               void* stream) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
+        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    if (!r || !g || !sparse_bufs) return fail(SCAPE_ERR_INVALID_ARG, "r, g and sparse_bufs must not be NULL");
+    const int W = ctx->cfg.workers;
+    for (int i = 0; i < W; ++i) {
+        if (!r[i] || !g[i]) return fail(SCAPE_ERR_INVALID_ARG, "r[%d] or g[%d] is NULL", i, i);
+        if (!aligned(r[i], 16) || !aligned(g[i], 16))
+            return fail(SCAPE_ERR_ALIGN, "r[%d] and g[%d] must be 16-byte aligned", i, i);
+        if (ctx->lay.k_total > 0) {
+            if (!sparse_bufs[i]) return fail(SCAPE_ERR_INVALID_ARG, "sparse_bufs[%d] is NULL", i);
+            if (!aligned(sparse_bufs[i], 4)) return fail(SCAPE_ERR_ALIGN, "sparse_bufs[%d] must be 4-byte aligned", i);
+        }
+    }
+    if (key_out && !aligned(key_out, 16)) return fail(SCAPE_ERR_ALIGN, "key_out must be 16-byte aligned");
+    int rc;
+    if ((rc = check_mask(cur, true, "cur")) || (rc = check_mask(next, true, "next"))) return rc;
+    if (cur->bits == next->bits || cur->idx == next->idx || cur->block_prefix == next->block_prefix)
+        return fail(SCAPE_ERR_STATE, "next must not alias cur (the mask built now is used at the next step)");
+    if ((rc = check_device(ctx))) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    WorkerPtrs wp{};
+    for (int i = 0; i < W; ++i) {
+        wp.r[i] = r[i];
+        wp.g[i] = g[i];
+        wp.b[i] = ctx->lay.k_total > 0 ? sparse_bufs[i] : nullptr;
+    }
+    StepScalars sc;
+    sc.beta1 = ctx->cfg.beta1;
+    sc.beta2 = ctx->cfg.beta2;
+    sc.c1 = 1.0f - ctx->cfg.beta1;
+    sc.c2 = 1.0f - ctx->cfg.beta2;
+    sc.lr = ctx->cfg.lr;
+    sc.eps = ctx->cfg.eps;
+    sc.wd = ctx->cfg.weight_decay;
+    sc.W = W;
+    uint32_t* key = key_out ? key_out : ctx->d_key;
+    const uint32_t k_cap = (uint32_t)ctx->lay.k_total;
+    const uint32_t n_tiles = (uint32_t)ctx->tiles.size();
+    const int32_t L = ctx->lay.L;
+
+    const int slot = prof_begin(ctx);
+    prof_mark(ctx, slot, 0, s);
+    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
+    SCAPE_HIP(launch_ef_compact(s, ctx->d_tiles, n_tiles, ctx->d_layers, wp, sc, m, cur->bits, cur->block_prefix,
+                                k_cap, key, ctx->d_hist),
+              "ef_compact");
+    prof_mark(ctx, slot, 1, s);
+    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->n_words,
+                                   (uint32_t)ctx->lay.n_pad, k_cap),
+              "reduce_update");
+    prof_mark(ctx, slot, 2, s);
+    if ((rc = run_select(ctx, 0, L, 0, n_tiles, key, next->bits, s))) return rc;
+    prof_mark(ctx, slot, 3, s);
+    if ((rc = run_index(ctx, next, s))) return rc;
+    prof_mark(ctx, slot, 4, s);
+    return SCAPE_OK;
+}
+
+int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, int32_t shard, const scape_mask* out,
+                     void* stream) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!mtilde) return fail(SCAPE_ERR_INVALID_ARG, "mtilde is NULL");
+    if (!aligned(mtilde, 16)) return fail(SCAPE_ERR_ALIGN, "mtilde must be 16-byte aligned");
+    const bool all = num_shards <= 0 || shard < 0;
+    if (!all && shard >= num_shards)
+        return fail(SCAPE_ERR_INVALID_ARG, "shard %d out of range for %d shards", shard, num_shards);
+    int rc;
+    if ((rc = check_mask(out, all, "out"))) return rc;
+    if ((rc = check_device(ctx))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t la = 0, lb = ctx->lay.L;  // layer range [la, lb)
+    if (!all) {
+        std::vector<int32_t> own(ctx->lay.L);
+        owner_map(ctx->lay, num_shards, own.data());
+        la = ctx->lay.L;
+        lb = ctx->lay.L;
+        for (int32_t l = 0; l < ctx->lay.L; ++l)
+            if (own[l] == shard) {
+                if (la == ctx->lay.L) la = l;
+                lb = l + 1;
+            }
+        if (la >= lb) return SCAPE_OK;  // the shard owns no layer
+    }
+    const uint32_t ta = ctx->layer_tile0[la], tb = ctx->layer_tile0[lb];
+    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist + (size_t)la * kHistBins, (uint64_t)(lb - la) * kHistBins, 0u), "fill");
+    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_tiles + ta, tb - ta, ctx->d_layers, mtilde, ctx->d_key, ctx->d_hist),
+              "keys");
+    if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key, out->bits, s))) return rc;
+    if (all && (rc = run_index(ctx, out, s))) return rc;
+    return SCAPE_OK;
+}
+
+int scape_mask_index(scape_ctx* ctx, const scape_mask* mask, void* stream) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    int rc;
+    if ((rc = check_mask(mask, true, "mask"))) return rc;
+    if ((rc = check_device(ctx))) return rc;
+    return run_index(ctx, mask, (hipStream_t)stream);
+}
+
+int scape_pack(const uint8_t* pred, int64_t n, uint64_t* bits, void* stream) {
+    if (n < 0) return fail(SCAPE_ERR_INVALID_ARG, "n must be >= 0");
+    if (n >= (int64_t(1) << 37)) return fail(SCAPE_ERR_SHAPE, "n too large");
+    if (n == 0) return SCAPE_OK;
+    if (!pred || !bits) return fail(SCAPE_ERR_INVALID_ARG, "pred and bits must not be NULL");
+    if (!aligned(bits, 8)) return fail(SCAPE_ERR_ALIGN, "bits must be 8-byte aligned");
+    SCAPE_HIP(launch_pack((hipStream_t)stream, pred, n, bits), "pack");
+    return SCAPE_OK;
+}
+
+int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream) {
+    if (n < 0) return fail(SCAPE_ERR_INVALID_ARG, "n must be >= 0");
+    if (n >= (int64_t(1) << 37)) return fail(SCAPE_ERR_SHAPE, "n too large");
+    if (n == 0) return SCAPE_OK;
+    if (!pred || !bits) return fail(SCAPE_ERR_INVALID_ARG, "pred and bits must not be NULL");
+    if (!aligned(bits, 8)) return fail(SCAPE_ERR_ALIGN, "bits must be 8-byte aligned");
+    SCAPE_HIP(launch_unpack((hipStream_t)stream, bits, n, pred), "unpack");
+    return SCAPE_OK;
+}
+
+int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream) {
+    if (W < 1 || W > SCAPE_MAX_WORKERS) return fail(SCAPE_ERR_INVALID_ARG, "W must be in 1..%d", SCAPE_MAX_WORKERS);
+    if (k < 0) return fail(SCAPE_ERR_INVALID_ARG, "k must be >= 0");
+    if (k >= kMaxFlat * 4) return fail(SCAPE_ERR_SHAPE, "k too large");
+    if (k == 0) return SCAPE_OK;
+    if (!bufs || !out) return fail(SCAPE_ERR_INVALID_ARG, "bufs and out must not be NULL");
+    for (int i = 0; i < W; ++i) {
+        if (!bufs[i]) return fail(SCAPE_ERR_INVALID_ARG, "bufs[%d] is NULL", i);
+        if (!aligned(bufs[i], 4)) return fail(SCAPE_ERR_ALIGN, "bufs[%d] must be 4-byte aligned", i);
+    }
+    if (!aligned(out, 4)) return fail(SCAPE_ERR_ALIGN, "out must be 4-byte aligned");
+    SCAPE_HIP(launch_reduce_sparse((hipStream_t)stream, bufs, W, k, out), "reduce_sparse");
+    return SCAPE_OK;
+}
+
+int scape_profile_enable(scape_ctx* ctx, int32_t enable) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (enable && !ctx->prof_events) {
+        for (auto& s : ctx->prof)
+            for (auto& e : s.ev) SCAPE_HIP(hipEventCreate(&e), "hipEventCreate");
+        ctx->prof_events = true;
+    }
+    if (enable) {
+        for (auto& s : ctx->prof) s.pending = false;
+        for (double& d : ctx->prof_ms) d = 0.0;
+        ctx->prof_steps = 0;
+        ctx->prof_next = 0;
+    }
+    ctx->prof_on = enable != 0;
+    return SCAPE_OK;
+}
+
+int scape_profile_read(scape_ctx* ctx, double* ms, int64_t* steps) {
+    if (!ctx || !ms || !steps) return fail(SCAPE_ERR_INVALID_ARG, "NULL argument");
+    for (int i = 0; i < kProfSlots; ++i) prof_collect(ctx, (ctx->prof_next + i) % kProfSlots);
+    for (int i = 0; i < SCAPE_PHASE_COUNT; ++i) ms[i] = ctx->prof_ms[i];
+    *steps = ctx->prof_steps;
+    return SCAPE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// scape_device.h - wave64 helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scape_internal.h"
+
+namespace scape {
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Bit pattern of |v| (sign cleared): the mask statistic's integer key.
+__device__ __forceinline__ uint32_t magnitude_key(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t t = __shfl_up(x, d, 64);
+        if (lane >= (uint32_t)d) x += t;
+    }
+    return x;
+}
+
+// Exclusive scan over a workgroup of kBlock threads.  `scratch` holds kWaves
+// entries of LDS.  Every thread of the block must call it.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    uint32_t inc = wave_inclusive_scan(v);
+    if (lane == 63) scratch[wave] = inc;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        uint32_t s = scratch[w];
+        if ((uint32_t)w < wave) off += s;
+        tot += s;
+    }
+    __syncthreads();
+    if (total) *total = tot;
+    return off + inc - v;
+}
+
+// Add one count per active lane with `take` set to lds_hist[bin].  When every
+// counting lane of the wave hits one bin (heavy ties), a single atomic adds
+// the whole wave's count.
+__device__ __forceinline__ void hist_add_wave(uint32_t* lds_hist, uint32_t bin, bool take) {
+    const uint64_t act = __ballot(take);
+    if (act == 0) return;
+    const uint32_t first = (uint32_t)__builtin_ctzll(act);
+    const uint32_t bin0 = __shfl(bin, (int)first, 64);
+    const uint64_t same = __ballot(take && bin == bin0);
+    if (same == act) {
+        if (lane_id() == first) atomicAdd(&lds_hist[bin0], (uint32_t)__popcll(act));
+    } else if (take) {
+        atomicAdd(&lds_hist[bin], 1u);
+    }
+}
+
+// Flush a workgroup's LDS histogram row into the global per-layer row.
+__device__ __forceinline__ void hist_flush(const uint32_t* lds_hist, uint32_t* row, int bins) {
+    for (int b = threadIdx.x; b < bins; b += kBlock) {
+        uint32_t c = lds_hist[b];
+        if (c) atomicAdd(&row[b], c);
+    }
+}
+
+}  // namespace scape

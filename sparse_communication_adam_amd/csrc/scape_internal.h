@@ -1,0 +1,117 @@
+// scape_internal.h - types shared by the host orchestration (scape_api.cpp)
+// and the gfx950 kernels (k_*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scape.h"
+
+namespace scape {
+
+// ---------------------------------------------------------------------------
+// Launch geometry.  A "tile" is a run of whole 64-element words inside one
+// layer; the elementwise and filter kernels give one tile to a workgroup.
+constexpr int kBlock = 256;             // threads per workgroup (4 waves of 64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kWordsPerWaveIter = 8;    // words a wave handles per loop trip
+constexpr int kTileWords = 512;         // 32768 elements per tile
+constexpr int kDigit1Bits = 11;         // first radix digit of the 31-bit key
+constexpr int kDigit1Bins = 1 << kDigit1Bits;
+constexpr int kHistBins = 2048;         // histogram row per layer (>= every digit's bins)
+constexpr int kIndexWordsPerBlock = 2048;  // words per workgroup in the index passes
+constexpr int kCandChunk = 8192;        // candidate records per virtual block
+
+struct TileDesc {
+    int32_t layer;
+    uint32_t w0;  // first word
+    uint32_t w1;  // one past the last word
+    uint32_t pad;
+};
+
+struct LayerDesc {
+    uint32_t off;    // first element (multiple of 64)
+    uint32_t n;      // elements
+    uint32_t k;      // kept count (<= n)
+    int32_t owner;   // worker whose candidate is the statistic
+};
+
+// Per-layer state of the radix selection.  The final rule for a layer is
+//   selected(j) = !none && (key > T || (key == T && jl <= J))
+// where jl is the layer-local position.
+enum SelPhase : uint32_t {
+    kPhaseDone = 0,
+    kPhaseKey2 = 1,   // key bits 19..10 pending
+    kPhaseKey3 = 2,   // key bits 9..0 pending
+    kPhasePos1 = 3,   // tie position bits 30..20 pending
+    kPhasePos2 = 4,   // tie position bits 19..10 pending
+    kPhasePos3 = 5,   // tie position bits 9..0 pending
+};
+
+struct SelState {
+    uint32_t phase;
+    uint32_t none;        // layer selects nothing (k == 0 or not built)
+    uint32_t all_bucket;  // whole first-digit bucket taken: no candidates
+    uint32_t d1;          // first-digit bucket of the threshold
+    uint32_t need;        // still to take among records matching the prefix
+    uint32_t kprefix;     // resolved high bits of T
+    uint32_t jprefix;     // resolved high bits of J
+    uint32_t T;
+    uint32_t J;
+    uint32_t cand_count;  // candidate records of this layer
+    uint32_t cand_off;    // first record of this layer
+    uint32_t vblk_off;    // first virtual candidate block of this layer
+};
+
+struct WorkerPtrs {
+    float* r[SCAPE_MAX_WORKERS];
+    const uint16_t* g[SCAPE_MAX_WORKERS];
+    float* b[SCAPE_MAX_WORKERS];
+};
+
+struct StepScalars {
+    float beta1, beta2, c1, c2, lr, eps, wd;
+    int32_t W;
+};
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (k_*.hip).  Each returns the hipError_t of the launch.
+
+// elementwise: error feedback, candidates, compaction, statistic, digit-1
+// histogram; then reduction + reconstruction + update.
+hipError_t launch_ef_compact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                             const WorkerPtrs& wp, const StepScalars& sc, const float* m, const uint64_t* cur_bits,
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, uint32_t* hist);
+hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
+                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, uint32_t n_words,
+                                uint32_t n_pad, uint32_t k_cap);
+hipError_t launch_keys_from_mtilde(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                                   const float* mtilde, uint32_t* key, uint32_t* hist);
+hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
+hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t value);
+
+// selection
+hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
+                               uint32_t* hist, SelState* st);
+hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, uint32_t cand_cap, SelState* st,
+                            uint32_t* cand_fill, uint32_t* totals);
+hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
+                         uint64_t* cand);
+hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
+                            const uint32_t* cand_fill, const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
+hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
+                              SelState* st);
+hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
+                            const SelState* st, const uint32_t* cand_fill, const uint32_t* totals,
+                            const uint64_t* cand, uint64_t* bits);
+
+// bits
+hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);
+hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blocks);
+hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,
+                             uint32_t* idx, uint32_t k_cap, uint32_t* prefix);
+hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits);
+hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred);
+
+}  // namespace scape

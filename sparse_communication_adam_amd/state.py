@@ -1,0 +1,56 @@
+"""Device state of one SCAPE optimizer instance and its step loop.
+
+Holds the fp32 master parameters x, moments m and v, the W residuals, the two
+mask slots and the W sparse buffers as torch tensors on one GPU, and calls
+``scape_step``.  The mask built at step t is used at step t+1 (Delayed Mask
+Usage, gist.science Technical Summary s.2): after each step the two mask
+slots swap roles.  The first step uses an all-zero mask.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+from ._scape import Context, Mask, ScapeConfig, alloc_mask, scape_step
+
+
+class ScapeState:
+    def __init__(self, cfg: ScapeConfig, device: str = "cuda", x=None):
+        import torch
+        self.cfg = cfg
+        self.ctx = Context(cfg)
+        self.layout = self.ctx.layout
+        n, W, k = self.layout.n_pad, cfg.workers, self.layout.k_total
+        f32 = dict(dtype=torch.float32, device=device)
+        self.x = torch.zeros(n, **f32) if x is None else x
+        self.m = torch.zeros(n, **f32)
+        self.v = torch.zeros(n, **f32)
+        self.r = [torch.zeros(n, **f32) for _ in range(W)]
+        self.sparse = [torch.zeros(max(k, 1), **f32) for _ in range(W)]
+        self.key = torch.zeros(n, dtype=torch.int32, device=device)
+        self.masks = [alloc_mask(self.layout, device), alloc_mask(self.layout, device)]
+        self._cur = 0
+        self.t = 0
+
+    @property
+    def cur_mask(self) -> Mask:
+        """The mask the next step applies (M_t)."""
+        return self.masks[self._cur]
+
+    @property
+    def next_mask(self) -> Mask:
+        return self.masks[1 - self._cur]
+
+    def step(self, grads: Sequence, stream=None, key_out: Optional[bool] = True) -> None:
+        """One step with the W workers' bfloat16 gradients (int16 views)."""
+        scape_step(self.ctx, self.x, self.m, self.v, self.r, grads, self.cur_mask, self.next_mask, self.sparse,
+                   self.key if key_out else None, stream)
+        self._cur = 1 - self._cur
+        self.t += 1
+
+    @property
+    def last_mask(self) -> Mask:
+        """The mask applied by the most recent step (M_t of step t)."""
+        return self.masks[1 - self._cur]
+
+    def destroy(self) -> None:
+        self.ctx.destroy()

@@ -24,7 +24,9 @@ from .configs import (ADVERSARIAL, GPT345M, LLAMA055, LLAMA175, SINGLE, WORKLOAD
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsynth.so")
+GPU_LIB_PATH = os.path.join(_HERE, "libsynth_gpu.so")
 _lib = None
+_gpu_lib = None
 
 
 def build(force: bool = True) -> str:
@@ -36,6 +38,33 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(LIB_PATH + ".tmp", LIB_PATH)
     return LIB_PATH
+
+
+def build_gpu(force: bool = True) -> str:
+    """Compile the GPU twin of the generator (hipcc, gfx950)."""
+    import subprocess
+    if force or not os.path.exists(GPU_LIB_PATH):
+        cmd = ["/opt/rocm/bin/hipcc", "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+               "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", os.path.join(_HERE, "synth_gen.hip"), "-o", GPU_LIB_PATH + ".tmp"]
+        subprocess.run(cmd, check=True, capture_output=True)
+        os.replace(GPU_LIB_PATH + ".tmp", GPU_LIB_PATH)
+    return GPU_LIB_PATH
+
+
+def gpu_lib():
+    global _gpu_lib
+    if _gpu_lib is None:
+        if not os.path.exists(GPU_LIB_PATH):
+            raise RuntimeError(f"{GPU_LIB_PATH} is not built (synth.build_gpu())")
+        L = ctypes.CDLL(GPU_LIB_PATH)
+        u32, u64, f32, i32, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+        L.synth_gpu_grad_bf16.argtypes = [u32, u32, u32, u32, i32, f32, i32, u64, u64, vp, vp]
+        L.synth_gpu_grad_bf16.restype = i32
+        L.synth_gpu_param_f32.argtypes = [u32, u32, f32, u64, u64, vp, vp]
+        L.synth_gpu_param_f32.restype = i32
+        _gpu_lib = L
+    return _gpu_lib
 
 
 def lib():
@@ -53,7 +82,7 @@ def lib():
         L.synth_normal_scale.restype = f32
         L.synth_tensor_sigma.argtypes = [u32, u32]
         L.synth_tensor_sigma.restype = f64
-        L.synth_grad_bf16.argtypes = [u32, u32, u32, u32, i32, f32, f64, i32, u64, u64, vp]
+        L.synth_grad_bf16.argtypes = [u32, u32, u32, u32, i32, f32, i32, u64, u64, vp]
         L.synth_grad_bf16.restype = None
         L.synth_param_f32.argtypes = [u32, u32, f32, u64, u64, vp]
         L.synth_param_f32.restype = None
@@ -91,13 +120,17 @@ def grad_tensor(wl: Workload, step: int, worker: int, tensor: int, e0: int = 0,
     assert out.dtype == np.uint16 and out.size >= n and out.flags.c_contiguous
     if n == 0:
         return out
-    if wl.grad_kind == "student2":
-        kind, scale, t_scale = 1, 0.0, float(wl.t_scale)
-    else:
-        kind, scale, t_scale = 0, lib().synth_normal_scale(tensor_sigma(wl, tensor)), 0.0
-    lib().synth_grad_bf16(wl.seed, tensor, step, worker, kind, scale, t_scale,
+    kind, scale = grad_recipe(wl, tensor)
+    lib().synth_grad_bf16(wl.seed, tensor, step, worker, kind, scale,
                           1 if wl.quantised(tensor) else 0, e0, n, out.ctypes.data)
     return out
+
+
+def grad_recipe(wl: Workload, tensor: int):
+    """(kind, fp32 scale) of a tensor's gradient: kind 0 normal, 1 Student-t(2)."""
+    if wl.grad_kind == "student2":
+        return 1, float(np.float32(wl.t_scale))
+    return 0, float(lib().synth_normal_scale(tensor_sigma(wl, tensor)))
 
 
 def param_tensor(wl: Workload, tensor: int, out: Optional[np.ndarray] = None) -> np.ndarray:
@@ -145,3 +178,44 @@ def uniform_u32(seed: int, purpose: int, n: int, tensor: int = 0, step: int = 0,
     if n:
         lib().synth_u32(seed, purpose, tensor, step, worker, 0, n, out.ctypes.data)
     return out
+
+
+# ----------------------------------------------------------------------------
+# GPU twin: the same numbers written straight into device tensors
+
+
+def _gpu_stream(stream):
+    import torch
+    return (stream or torch.cuda.current_stream()).cuda_stream
+
+
+def grads_flat_gpu(wl: Workload, offsets: Sequence[int], out, step: int, worker: int,
+                   tensors: Optional[Sequence[int]] = None, stream=None) -> None:
+    """Fill a device tensor (int16/uint16/bfloat16 view, n_pad long) with one
+    worker's gradient for one step, bit-identical to ``grads_flat``.  Padding
+    is left as it is."""
+    if tensors is None:
+        tensors = range(len(wl.tensors))
+    base = out.data_ptr()
+    st = _gpu_stream(stream)
+    for off, t in zip(offsets, tensors):
+        n = wl.tensors[t].numel
+        kind, scale = grad_recipe(wl, t)
+        rc = gpu_lib().synth_gpu_grad_bf16(wl.seed, t, step, worker, kind, scale, 1 if wl.quantised(t) else 0,
+                                           0, n, base + 2 * int(off), st)
+        if rc:
+            raise RuntimeError(f"synth_gpu_grad_bf16 failed: hipError {rc}")
+
+
+def params_flat_gpu(wl: Workload, offsets: Sequence[int], out, tensors: Optional[Sequence[int]] = None,
+                    stream=None) -> None:
+    if tensors is None:
+        tensors = range(len(wl.tensors))
+    base = out.data_ptr()
+    st = _gpu_stream(stream)
+    scale = lib().synth_normal_scale(wl.param_sigma)
+    for off, t in zip(offsets, tensors):
+        n = wl.tensors[t].numel
+        rc = gpu_lib().synth_gpu_param_f32(wl.seed, t, scale, 0, n, base + 4 * int(off), st)
+        if rc:
+            raise RuntimeError(f"synth_gpu_param_f32 failed: hipError {rc}")

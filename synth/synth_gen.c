@@ -15,14 +15,18 @@
  * even, so the output bits are a pure function of the counter):
  *   normal   : Irwin-Hall sum of the eight 16-bit halves of one Philox call,
  *              centred and scaled to unit variance (support +-4.9 sigma).
- *   student2 : Student-t with two degrees of freedom by exact inversion of
- *              its CDF, t = (2u-1)/sqrt(2u(1-u)).
+ *   student2 : Student-t with two degrees of freedom by inversion of its
+ *              CDF, t = (2u-1)/sqrt(2u(1-u)), in fp32 with u on a 2^-24 grid
+ *              (u = (2*(w>>9)+1) * 2^-24, so 2u-1 and 1-u are exact).
  *   quantised: a value v snapped to Delta*clamp(rne(v/Delta), -8, 7) with
  *              Delta = 2^-12, i.e. 16 levels, all exact in bfloat16.
  * Gradients are rounded to bfloat16 (round to nearest even) from fp32.
  *
  * Built with gcc -O2 -fopenmp -ffp-contract=off; elements are independent,
- * so the OpenMP split does not change any output bit.
+ * so the OpenMP split does not change any output bit.  synth_gen.hip is the
+ * same generator for the GPU; both use only integer operations and
+ * correctly rounded fp32 operations (add, multiply, divide, sqrt, rint), so
+ * they agree bit for bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -100,28 +104,26 @@ static inline float quantise16(float v) {
     return q * delta;
 }
 
+static inline float student2(uint32_t w) {
+    const float u = (float)(2u * (w >> 9) + 1u) * (1.0f / 16777216.0f);
+    return (2.0f * u - 1.0f) / sqrtf(2.0f * u * (1.0f - u));
+}
+
 /*
  * Gradient values for elements [e0, e0+n) of one tensor, as bfloat16 bits.
  * kind 0: normal with fp32 scale `scale` (from synth_normal_scale(sigma)).
- * kind 1: Student-t(2) times `t_scale`.
+ * kind 1: Student-t(2) times `scale`.
  * quantise != 0 snaps the fp32 value to the 16-level grid before rounding.
  */
 void synth_grad_bf16(uint32_t seed, uint32_t tensor, uint32_t step, uint32_t worker, int kind,
-                     float scale, double t_scale, int quantise, uint64_t e0, uint64_t n,
-                     uint16_t* out) {
+                     float scale, int quantise, uint64_t e0, uint64_t n, uint16_t* out) {
     const uint32_t key[2] = {seed, PURPOSE_GRAD};
 #pragma omp parallel for schedule(static, 65536)
     for (int64_t i = 0; i < (int64_t)n; ++i) {
         uint32_t ctr[4] = {(uint32_t)(e0 + (uint64_t)i), tensor, step, worker}, w[4];
         synth_philox4x32_10(ctr, key, w);
-        float v;
-        if (kind == 0) {
-            v = irwin_hall8(w) * scale;
-        } else {
-            double u = ((double)w[0] + 0.5) * (1.0 / 4294967296.0);
-            double t = (2.0 * u - 1.0) / sqrt(2.0 * u * (1.0 - u));
-            v = (float)(t_scale * t);
-        }
+        const float v0 = kind == 0 ? irwin_hall8(w) : student2(w[0]);
+        float v = v0 * scale;
         if (quantise) v = quantise16(v);
         out[i] = f32_to_bf16_rne(v);
     }
