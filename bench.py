@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the fused SCAPE optimizer step on one MI355X.
+
+One step = one scape_step call: the whole hot path (error feedback into W
+residuals, first-moment candidates, compaction of the current mask's
+positions into W sparse buffers, the W-way reduction, single-buffer
+reconstruction and the v/m/x update, per-layer top-k of the next mask, its
+packed bits and index) over one batch of synthetic gradients that is already
+resident in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is parameters per second (N / step time).
+`roofline` is the dominant kernel (the dense pass, SCAPE_PHASE_EF_COMPACT)
+timed with HIP events on the step's stream: algorithmic bytes per launch
+divided by its mean duration, against the 8 TB/s HBM peak.  `cpu_baseline`
+is the oracle (plain single-threaded C) timed on this host on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused SCAPE step: params/sec and achieved HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "llama-1.75b"
+# oracle sample per workload: a contiguous run of tensors (one transformer block
+# or its equivalent), timed on the host for one step with a built mask
+CPU_SAMPLE = {
+    "single-1024x1024": [0],
+    "gpt-345m": list(range(2, 14)),
+    "llama-0.55b": list(range(1, 7)),
+    "llama-1.75b": list(range(1, 7)),
+    "adversarial-ties": list(range(1, 18)),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(N: int, W: int, ksum: int):
+    """Algorithmic bytes of one step and of its dense pass."""
+    dense = N * (10 * W + 8.125) + 4 * W * ksum
+    step = N * (10 * W + 12.25) + ksum * (8 * W + 28)
+    return dense, step
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("k_elementwise.hip", "scape_device.h", "scape_internal.h"):
+        with open(os.path.join(ROOT, "sparse_communication_adam_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per dense-pass launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"ef_compact_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel source hash:\s*`?([0-9a-f]+)", text)
+    val = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(wl, steps_needed: int = 2):
+    import numpy as np
+    import oracle
+    import synth
+    tensors = CPU_SAMPLE[wl.name]
+    full = oracle.layout(wl.layer_sizes, wl.keep_num, wl.keep_den, wl.P or wl.W)
+    lay = oracle.sub_layout(full, tensors)
+    hp = oracle.Hyper(wl.beta1, wl.beta2, wl.lr, wl.eps, wl.weight_decay)
+    st = oracle.State.zeros(lay.n_pad, wl.W, synth.params_flat(wl, lay.off, lay.n_pad, tensors))
+    cur = np.zeros(lay.n_words, np.uint64)
+    times = []
+    for t in range(1, steps_needed + 1):
+        gs = [synth.grads_flat(wl, lay.off, lay.n_pad, t, i, tensors) for i in range(wl.W)]
+        t0 = time.perf_counter()
+        out = oracle.step(lay, hp, st, gs, cur)
+        times.append(time.perf_counter() - t0)
+        cur = out.next_words
+        log(f"cpu baseline step {t}: {times[-1]:.2f} s on {int(lay.sizes.sum())} params")
+    n = int(lay.sizes.sum())
+    names = [wl.tensors[t].name for t in tensors]
+    return {"value": n / times[-1], "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(tensors)} tensors ({names[0]}..{names[-1]}, {n} params, W={wl.W}) of {wl.name}; "
+                      f"step {steps_needed} timed (mask built by step {steps_needed - 1}); single-threaded C oracle",
+            "seconds": times[-1]}
+
+
+def copy_bandwidth(nbytes: int = 4 << 30) -> float:
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 10
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(CPU_SAMPLE))
+    ap.add_argument("--grad-sets", type=int, default=2, help="distinct gradient batches cycled over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    from sparse_communication_adam_amd.state import ScapeState
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sc.lib()
+    wl = synth.WORKLOADS[args.workload]
+    cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
+                         owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
+                         weight_decay=wl.weight_decay)
+    log(f"workload {wl.name}: {len(wl.tensors)} tensors, N={wl.numel}, W={wl.W}, keep={wl.keep_num}/{wl.keep_den}")
+    state = ScapeState(cfg)
+    lay = state.layout
+    N, W, ksum = wl.numel, wl.W, lay.k_total
+    synth.params_flat_gpu(wl, lay.layer_offset, state.x)
+    sets = []
+    for s in range(args.grad_sets):
+        gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(W)]
+        for i, g in enumerate(gs):
+            synth.grads_flat_gpu(wl, lay.layer_offset, g, s + 1, i)
+        sets.append(gs)
+    torch.cuda.synchronize()
+    log(f"state and {args.grad_sets} gradient batches resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    for s in range(args.warmup):
+        state.step(sets[s % len(sets)])
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warmup steps done")
+
+    sc.scape_profile_enable(state.ctx, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        state.step(sets[(args.warmup + s) % len(sets)])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phase_ms, nrec = sc.scape_profile_read(state.ctx)
+    sc.scape_profile_enable(state.ctx, False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"{args.steps} timed steps: {ms:.3f} ms/step; phases " +
+        ", ".join(f"{k} {v / nrec:.3f} ms" for k, v in phase_ms.items()))
+
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("calibration copy of 1 GiB done")
+
+    dense_b, step_b = alg_bytes(N, W, ksum)
+    ef_ms = phase_ms["ef_compact"] / nrec
+    ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
+    step_gbps = step_b / (ms * 1e-3) / 1e9
+    traffic = counter_traffic(wl.name)
+    state.destroy()
+    del sets, state
+    torch.cuda.empty_cache()
+    copy_gbps = copy_bandwidth()
+    log(f"device copy: {copy_gbps:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": N / (ms * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "params": N, "tensors": len(wl.tensors), "workers": W,
+                   "keep": f"{wl.keep_num}/{wl.keep_den}", "kept_total": ksum, "grad_dtype": "bf16",
+                   "gradient_batches": args.grad_sets},
+        "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
+        "device_copy_GBps": copy_gbps,
+        "roofline": {"kernel": "scape_k_ef_compact (dense pass)", "bound": "hbm", "achieved": ef_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
+                     "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

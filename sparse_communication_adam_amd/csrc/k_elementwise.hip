@@ -26,12 +26,102 @@
 
 namespace scape {
 
+// Workers are processed in chunks of up to kWorkerChunk; within a chunk every
+// load is issued before any store, so a wave keeps E words x chunk x (fp32 r,
+// bf16 g) in flight.  WT > 0 fixes the worker count at compile time.
+constexpr int kWorkerChunk = 4;
+
+// One wave-iteration of the dense pass over words [w0, w0+E).  GUARD = false
+// is the interior case (all E words inside the tile and the layer), with no
+// per-element predicate; GUARD = true handles a layer's last, partial words.
+// Lane addresses are one 64-bit base per array plus compile-time offsets of
+// 64 elements per word.
+template <int WT, bool GUARD>
+__device__ __forceinline__ void ef_iteration(uint32_t w0, uint32_t w1, uint32_t lend, int owner, int W,
+                                             const WorkerPtrs& wp, float b1, float c1, const float* __restrict__ m,
+                                             const uint64_t* __restrict__ cur_bits,
+                                             const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
+                                             uint32_t* __restrict__ key, uint32_t* h) {
+    constexpr int E = kWordsPerWaveIter;
+    const uint32_t lane = lane_id();
+    const size_t j0 = (size_t)w0 * 64u + lane;
+    uint64_t word[E];
+    uint32_t pre[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t wc = GUARD ? min(w0 + e, w1 - 1) : w0 + e;
+        word[e] = cur_bits[wc];
+        pre[e] = cur_prefix[wc];
+    }
+    bool inl[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) inl[e] = GUARD ? (w0 + e < w1) && (j0 + 64u * e < lend) : true;
+    float bm[E];
+    const float* mp = m + j0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) bm[e] = inl[e] ? mp[64 * e] : 0.0f;
+    uint32_t rank[E], kk[E];
+    bool msk[E];
+    uint64_t any = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        bm[e] = b1 * bm[e];
+        rank[e] = pre[e] + lanes_below(word[e]);
+        msk[e] = inl[e] && ((word[e] >> lane) & 1ull) && rank[e] < k_cap;
+        kk[e] = 0;
+        any |= word[e];
+    }
+    for (int i0 = 0; i0 < W; i0 += kWorkerChunk) {
+        float rv[kWorkerChunk][E];
+        uint16_t gv[kWorkerChunk][E];
+#pragma unroll
+        for (int c = 0; c < kWorkerChunk; ++c) {
+            if (i0 + c >= W) break;
+            const float* rp = wp.r[i0 + c] + j0;
+            const uint16_t* gp = wp.g[i0 + c] + j0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                rv[c][e] = inl[e] ? rp[64 * e] : 0.0f;
+                gv[c][e] = inl[e] ? gp[64 * e] : (uint16_t)0;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kWorkerChunk; ++c) {
+            const int i = i0 + c;
+            if (i >= W) break;
+            float* rp = wp.r[i] + j0;
+            float mt[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float a = rv[c][e] + bf16_bits_to_f32(gv[c][e]);
+                mt[e] = bm[e] + c1 * a;
+                if (i == owner) kk[e] = magnitude_key(mt[e]);
+                if (inl[e]) rp[64 * e] = msk[e] ? 0.0f : a;
+            }
+            if (any) {  // wave-uniform: most iterations of a sparse mask skip this
+                float* __restrict__ b = wp.b[i];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (msk[e]) b[rank[e]] = mt[e];
+            }
+        }
+    }
+    uint32_t* kp = key + j0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (inl[e]) kp[64 * e] = kk[e];
+        hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
+    }
+}
+
+template <int WT>
 __global__ __launch_bounds__(kBlock) void k_ef_compact(const TileDesc* __restrict__ tiles,
                                                        const LayerDesc* __restrict__ layers, WorkerPtrs wp,
                                                        StepScalars sc, const float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
                                                        uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
+    constexpr int E = kWordsPerWaveIter;
     __shared__ uint32_t h[kDigit1Bins];
     for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
     __syncthreads();
@@ -39,59 +129,17 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const TileDesc* __restric
     const TileDesc t = tiles[blockIdx.x];
     const LayerDesc L = layers[t.layer];
     const uint32_t lend = L.off + L.n;
-    const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
-    const int owner = L.owner;
-    const int W = sc.W;
-    const float b1 = sc.beta1, c1 = sc.c1;
-
-    for (uint32_t w0 = t.w0 + wave * kWordsPerWaveIter; w0 < t.w1; w0 += kWaves * kWordsPerWaveIter) {
-        uint32_t j[kWordsPerWaveIter], rank[kWordsPerWaveIter], kk[kWordsPerWaveIter];
-        bool inl[kWordsPerWaveIter], msk[kWordsPerWaveIter];
-        float bm[kWordsPerWaveIter];
-#pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
-            const uint32_t wi = w0 + e;
-            const bool valid = wi < t.w1;
-            j[e] = wi * 64u + lane;
-            inl[e] = valid && j[e] < lend;
-            const uint64_t word = valid ? cur_bits[wi] : 0ull;
-            const float mo = inl[e] ? m[j[e]] : 0.0f;
-            bm[e] = b1 * mo;
-            msk[e] = false;
-            rank[e] = 0;
-            if (word != 0ull) {
-                rank[e] = cur_prefix[wi] + lanes_below(word);
-                msk[e] = inl[e] && ((word >> lane) & 1ull) && rank[e] < k_cap;
-            }
-            kk[e] = 0;
-        }
-        for (int i = 0; i < W; ++i) {
-            float* __restrict__ r = wp.r[i];
-            const uint16_t* __restrict__ g = wp.g[i];
-            float* __restrict__ b = wp.b[i];
-            float rv[kWordsPerWaveIter];
-            uint16_t gv[kWordsPerWaveIter];
-#pragma unroll
-            for (int e = 0; e < kWordsPerWaveIter; ++e) {
-                rv[e] = inl[e] ? r[j[e]] : 0.0f;
-                gv[e] = inl[e] ? g[j[e]] : (uint16_t)0;
-            }
-#pragma unroll
-            for (int e = 0; e < kWordsPerWaveIter; ++e) {
-                if (!inl[e]) continue;
-                const float a = rv[e] + bf16_bits_to_f32(gv[e]);
-                const float mt = bm[e] + c1 * a;
-                if (i == owner) kk[e] = magnitude_key(mt);
-                r[j[e]] = msk[e] ? 0.0f : a;
-                if (msk[e]) b[rank[e]] = mt;
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
-            if (inl[e]) key[j[e]] = kk[e];
-            hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
-        }
+    const int W = WT > 0 ? WT : sc.W;
+    // words [t.w0, full_end) lie wholly inside the layer
+    const uint32_t full_end = min(t.w1, lend / 64u);
+    for (uint32_t w0 = t.w0 + wave * E; w0 < t.w1; w0 += kWaves * E) {
+        if (w0 + E <= full_end)
+            ef_iteration<WT, false>(w0, t.w1, lend, L.owner, W, wp, sc.beta1, sc.c1, m, cur_bits, cur_prefix, k_cap,
+                                    key, h);
+        else
+            ef_iteration<WT, true>(w0, t.w1, lend, L.owner, W, wp, sc.beta1, sc.c1, m, cur_bits, cur_prefix, k_cap,
+                                   key, h);
     }
     __syncthreads();
     hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
@@ -101,8 +149,24 @@ hipError_t launch_ef_compact(hipStream_t s, const TileDesc* tiles, uint32_t n_ti
                              const WorkerPtrs& wp, const StepScalars& sc, const float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, uint32_t* hist) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_ef_compact, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, wp, sc, m, cur_bits,
-                       cur_prefix, k_cap, key, hist);
+#define SCAPE_EF_CASE(WV)                                                                                       \
+    case WV:                                                                                                    \
+        hipLaunchKernelGGL(k_ef_compact<WV>, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, wp, sc, m, cur_bits, \
+                           cur_prefix, k_cap, key, hist);                                                       \
+        break;
+    switch (sc.W) {
+        SCAPE_EF_CASE(1)
+        SCAPE_EF_CASE(2)
+        SCAPE_EF_CASE(3)
+        SCAPE_EF_CASE(4)
+        SCAPE_EF_CASE(8)
+        SCAPE_EF_CASE(16)
+        SCAPE_EF_CASE(32)
+        default:
+            hipLaunchKernelGGL(k_ef_compact<0>, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, wp, sc, m, cur_bits,
+                               cur_prefix, k_cap, key, hist);
+    }
+#undef SCAPE_EF_CASE
     return hipGetLastError();
 }
 

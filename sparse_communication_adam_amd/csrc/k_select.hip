@@ -167,11 +167,39 @@ hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, uin
     return hipGetLastError();
 }
 
+// Candidate records are staged in LDS and copied out in bulk: one global
+// atomic per flush (normally one per tile) reserves the slots, instead of one
+// per word - per-word atomics on a single per-layer counter serialize.
+constexpr int kFilterWords = 8;                                 // words per wave per trip
+constexpr int kFilterTrip = kWaves * kFilterWords * 64;        // elements per workgroup trip
+constexpr int kStage = 2 * kFilterTrip;                         // LDS records (32 KB)
+
+__device__ __forceinline__ void filter_flush(uint32_t* s_n, uint32_t* s_base, const uint64_t* s_rec,
+                                             uint32_t* cand_fill, int layer, const SelState& S,
+                                             uint64_t* __restrict__ cand) {
+    __syncthreads();
+    const uint32_t n = *s_n;
+    if (n) {
+        if (threadIdx.x == 0) *s_base = atomicAdd(&cand_fill[layer], n);
+        __syncthreads();
+        const uint32_t base = *s_base;
+        for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
+            const uint32_t slot = base + i;
+            if (slot < S.cand_count) cand[(size_t)S.cand_off + slot] = s_rec[i];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) *s_n = 0;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
                                                    const LayerDesc* __restrict__ layers,
                                                    const SelState* __restrict__ st, const uint32_t* __restrict__ key,
                                                    uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
                                                    uint64_t* __restrict__ cand) {
+    __shared__ uint64_t s_rec[kStage];
+    __shared__ uint32_t s_n, s_base;
     const TileDesc t = tiles[blockIdx.x];
     const LayerDesc L = layers[t.layer];
     const SelState S = st[t.layer];
@@ -181,16 +209,20 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
     const uint32_t d1 = S.d1;
     const bool none = S.none != 0;
     const bool whole = S.all_bucket != 0;
-    for (uint32_t w0 = t.w0 + wave * kWordsPerWaveIter; w0 < t.w1; w0 += kWaves * kWordsPerWaveIter) {
-        uint32_t kv[kWordsPerWaveIter];
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    // workgroup-uniform trips so that every thread reaches the barriers
+    for (uint32_t wb = t.w0; wb < t.w1; wb += kWaves * kFilterWords) {
+        const uint32_t w0 = wb + wave * kFilterWords;
+        uint32_t kv[kFilterWords];
 #pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
+        for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
             kv[e] = (w0 + e < t.w1 && jj < lend) ? key[jj] : 0u;
         }
         uint64_t mine = 0;
 #pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
+        for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
             const bool inl = (w0 + e < t.w1) && jj < lend && !none;
             const uint32_t d = kv[e] >> (31 - kDigit1Bits);
@@ -201,15 +233,16 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
             const uint64_t cb = __ballot(cnd);
             if (cb) {
                 uint32_t base = 0;
-                if (lane == 0) base = atomicAdd(&cand_fill[t.layer], (uint32_t)__popcll(cb));
+                if (lane == 0) base = atomicAdd(&s_n, (uint32_t)__popcll(cb));
                 base = __shfl(base, 0, 64);
-                const uint32_t slot = base + lanes_below(cb);
-                if (cnd && slot < S.cand_count)
-                    cand[(size_t)S.cand_off + slot] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
+                if (cnd) s_rec[base + lanes_below(cb)] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
             }
         }
-        if (lane < (uint32_t)kWordsPerWaveIter && w0 + lane < t.w1) bits[w0 + lane] = mine;
+        if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) bits[w0 + lane] = mine;
+        __syncthreads();
+        if (s_n > (uint32_t)(kStage - kFilterTrip)) filter_flush(&s_n, &s_base, s_rec, cand_fill, t.layer, S, cand);
     }
+    filter_flush(&s_n, &s_base, s_rec, cand_fill, t.layer, S, cand);
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,

@@ -410,8 +410,8 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
     const int32_t L = ctx->lay.L;
 
     const int slot = prof_begin(ctx);
-    prof_mark(ctx, slot, 0, s);
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
+    prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
     SCAPE_HIP(launch_ef_compact(s, ctx->d_tiles, n_tiles, ctx->d_layers, wp, sc, m, cur->bits, cur->block_prefix,
                                 k_cap, key, ctx->d_hist),
               "ef_compact");

@@ -14,8 +14,14 @@ namespace scape {
 // layer; the elementwise and filter kernels give one tile to a workgroup.
 constexpr int kBlock = 256;             // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kWordsPerWaveIter = 8;    // words a wave handles per loop trip
-constexpr int kTileWords = 512;         // 32768 elements per tile
+#ifndef SCAPE_EF_WORDS
+#define SCAPE_EF_WORDS 8
+#endif
+constexpr int kWordsPerWaveIter = SCAPE_EF_WORDS;  // words a wave handles per loop trip
+#ifndef SCAPE_TILE_WORDS
+#define SCAPE_TILE_WORDS 512
+#endif
+constexpr int kTileWords = SCAPE_TILE_WORDS;  // words per tile (512 words = 32768 elements)
 constexpr int kDigit1Bits = 11;         // first radix digit of the 31-bit key
 constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kHistBins = 2048;         // histogram row per layer (>= every digit's bins)
