@@ -26,133 +26,66 @@
 
 namespace scape {
 
-// Workers are processed in chunks of up to kWorkerChunk; within a chunk every
-// load is issued before any store, so a wave keeps E words x chunk x (fp32 r,
-// bf16 g) in flight.  WT > 0 fixes the worker count at compile time.
-constexpr int kWorkerChunk = 4;
-
-// One wave-iteration of the dense pass over words [w0, w0+E).  GUARD = false
-// is the interior case (all E words inside the tile and the layer), with no
-// per-element predicate; GUARD = true handles a layer's last, partial words.
-// Lane addresses are one 64-bit base per array plus compile-time offsets of
-// 64 elements per word.
-template <int WT, bool GUARD>
-__device__ __forceinline__ void ef_iteration(uint32_t w0, uint32_t w1, uint32_t lend, int owner, int W,
-                                             const WorkerPtrs& wp, float b1, float c1, const float* __restrict__ m,
-                                             const uint64_t* __restrict__ cur_bits,
-                                             const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
-                                             uint32_t* __restrict__ key, uint32_t* h) {
-    constexpr int E = kWordsPerWaveIter;
-    const uint32_t lane = lane_id();
-    const size_t j0 = (size_t)w0 * 64u + lane;
-    uint64_t word[E];
-    uint32_t pre[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t wc = GUARD ? min(w0 + e, w1 - 1) : w0 + e;
-        word[e] = cur_bits[wc];
-        pre[e] = cur_prefix[wc];
-    }
-    bool inl[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) inl[e] = GUARD ? (w0 + e < w1) && (j0 + 64u * e < lend) : true;
-    float bm[E];
-    const float* mp = m + j0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) bm[e] = inl[e] ? mp[64 * e] : 0.0f;
-    uint32_t rank[E], kk[E];
-    bool msk[E];
-    uint64_t any = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        bm[e] = b1 * bm[e];
-        rank[e] = pre[e] + lanes_below(word[e]);
-        msk[e] = inl[e] && ((word[e] >> lane) & 1ull) && rank[e] < k_cap;
-        kk[e] = 0;
-        any |= word[e];
-    }
-    for (int i0 = 0; i0 < W; i0 += kWorkerChunk) {
-        float rv[kWorkerChunk][E];
-        uint16_t gv[kWorkerChunk][E];
-#pragma unroll
-        for (int c = 0; c < kWorkerChunk; ++c) {
-            if (i0 + c >= W) break;
-            const float* rp = wp.r[i0 + c] + j0;
-            const uint16_t* gp = wp.g[i0 + c] + j0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                rv[c][e] = inl[e] ? rp[64 * e] : 0.0f;
-                gv[c][e] = inl[e] ? gp[64 * e] : (uint16_t)0;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kWorkerChunk; ++c) {
-            const int i = i0 + c;
-            if (i >= W) break;
-            float* rp = wp.r[i] + j0;
-            float mt[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float a = rv[c][e] + bf16_bits_to_f32(gv[c][e]);
-                mt[e] = bm[e] + c1 * a;
-                if (i == owner) kk[e] = magnitude_key(mt[e]);
-                if (inl[e]) rp[64 * e] = msk[e] ? 0.0f : a;
-            }
-            if (any) {  // wave-uniform: most iterations of a sparse mask skip this
-                float* __restrict__ b = wp.b[i];
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (msk[e]) b[rank[e]] = mt[e];
-            }
-        }
-    }
-    uint32_t* kp = key + j0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if (inl[e]) kp[64 * e] = kk[e];
-        hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
-    }
-}
-
+// Dense pass, one-shot layout: a wave handles one 64-element word and
+// exits; a workgroup is 4 consecutive words.  Work is dispatched in address
+// order, so the words in flight at any time are a compact window of every
+// array; on MI355X that sustains a higher HBM rate than long-lived
+// workgroups streaming separate tiles or striding over the grid.  Per word, a
+// 16-bit descriptor gives the owner worker (bits 8..13) and the number of
+// elements of the word inside its layer (bits 0..6, 1..64; 0 = padding).
+// Every worker's loads are issued before any store.
 template <int WT>
-__global__ __launch_bounds__(kBlock) void k_ef_compact(const TileDesc* __restrict__ tiles,
-                                                       const LayerDesc* __restrict__ layers, WorkerPtrs wp,
-                                                       StepScalars sc, const float* __restrict__ m,
+__global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
+                                                       WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
-                                                       uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
-    constexpr int E = kWordsPerWaveIter;
-    __shared__ uint32_t h[kDigit1Bins];
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
-    __syncthreads();
-
-    const TileDesc t = tiles[blockIdx.x];
-    const LayerDesc L = layers[t.layer];
-    const uint32_t lend = L.off + L.n;
-    const uint32_t wave = threadIdx.x / 64;
+                                                       uint32_t* __restrict__ key) {
+    constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
+    const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
+    if (w >= n_words) return;
+    const uint32_t lane = lane_id();
+    const uint32_t info = word_info[w];
+    const uint64_t word = cur_bits[w];
+    const uint32_t pre = cur_prefix[w];
+    const uint32_t count = info & 127u;
+    const int owner = (int)((info >> 8) & 63u);
     const int W = WT > 0 ? WT : sc.W;
-    // words [t.w0, full_end) lie wholly inside the layer
-    const uint32_t full_end = min(t.w1, lend / 64u);
-    for (uint32_t w0 = t.w0 + wave * E; w0 < t.w1; w0 += kWaves * E) {
-        if (w0 + E <= full_end)
-            ef_iteration<WT, false>(w0, t.w1, lend, L.owner, W, wp, sc.beta1, sc.c1, m, cur_bits, cur_prefix, k_cap,
-                                    key, h);
-        else
-            ef_iteration<WT, true>(w0, t.w1, lend, L.owner, W, wp, sc.beta1, sc.c1, m, cur_bits, cur_prefix, k_cap,
-                                   key, h);
+    if (lane >= count) return;  // padding lanes of a layer's last word
+    const size_t j = (size_t)w * 64u + lane;
+    const float mo = m[j];
+    float rv[WMAX];
+    uint16_t gv[WMAX];
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+        if (i >= W) break;
+        rv[i] = wp.r[i][j];
+        gv[i] = wp.g[i][j];
     }
-    __syncthreads();
-    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+    const uint32_t rank = pre + lanes_below(word);
+    const bool msk = ((word >> lane) & 1ull) && rank < k_cap;
+    const float bm = sc.beta1 * mo;
+    uint32_t kk = 0;
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+        if (i >= W) break;
+        const float a = rv[i] + bf16_bits_to_f32(gv[i]);
+        const float mt = bm + sc.c1 * a;
+        if (i == owner) kk = magnitude_key(mt);
+        wp.r[i][j] = msk ? 0.0f : a;
+        if (msk) wp.b[i][rank] = mt;
+    }
+    key[j] = kk;
 }
 
-hipError_t launch_ef_compact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                             const WorkerPtrs& wp, const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, uint32_t* hist) {
-    if (n_tiles == 0) return hipSuccess;
-#define SCAPE_EF_CASE(WV)                                                                                       \
-    case WV:                                                                                                    \
-        hipLaunchKernelGGL(k_ef_compact<WV>, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, wp, sc, m, cur_bits, \
-                           cur_prefix, k_cap, key, hist);                                                       \
+hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
+                             const StepScalars& sc, const float* m, const uint64_t* cur_bits,
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key) {
+    if (n_words == 0) return hipSuccess;
+    const dim3 grid((n_words + kWaves - 1) / kWaves);
+#define SCAPE_EF_CASE(WV)                                                                                 \
+    case WV:                                                                                              \
+        hipLaunchKernelGGL(k_ef_compact<WV>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
+                           cur_prefix, k_cap, key);                                                       \
         break;
     switch (sc.W) {
         SCAPE_EF_CASE(1)
@@ -163,10 +96,47 @@ hipError_t launch_ef_compact(hipStream_t s, const TileDesc* tiles, uint32_t n_ti
         SCAPE_EF_CASE(16)
         SCAPE_EF_CASE(32)
         default:
-            hipLaunchKernelGGL(k_ef_compact<0>, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, wp, sc, m, cur_bits,
-                               cur_prefix, k_cap, key, hist);
+            hipLaunchKernelGGL(k_ef_compact<0>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits,
+                               cur_prefix, k_cap, key);
     }
 #undef SCAPE_EF_CASE
+    return hipGetLastError();
+}
+
+// First-digit histogram of the statistic keys, per layer: LDS row per tile,
+// flushed once per tile (global atomics stay at a few hundred per tile).
+__global__ __launch_bounds__(kBlock) void k_key_hist(const TileDesc* __restrict__ tiles,
+                                                     const LayerDesc* __restrict__ layers,
+                                                     const uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
+    constexpr int E = kWordsPerWaveIter;
+    __shared__ uint32_t h[kDigit1Bins];
+    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+    __syncthreads();
+    const TileDesc t = tiles[blockIdx.x];
+    const LayerDesc L = layers[t.layer];
+    const uint32_t lend = L.off + L.n;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    for (uint32_t w0 = t.w0 + wave * E; w0 < t.w1; w0 += kWaves * E) {
+        uint32_t kk[E];
+        bool inl[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t jj = (w0 + e) * 64u + lane;
+            inl[e] = w0 + e < t.w1 && jj < lend;
+            kk[e] = inl[e] ? key[jj] : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
+    }
+    __syncthreads();
+    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+}
+
+hipError_t launch_key_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                           const uint32_t* key, uint32_t* hist) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_key_hist, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, key, hist);
     return hipGetLastError();
 }
 
@@ -208,46 +178,24 @@ hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepS
     return hipGetLastError();
 }
 
-// Statistic keys and the first-digit histogram from a given m-tilde (the
-// standalone mask build).
-__global__ __launch_bounds__(kBlock) void k_keys_from_mtilde(const TileDesc* __restrict__ tiles,
-                                                             const LayerDesc* __restrict__ layers,
-                                                             const float* __restrict__ mtilde,
-                                                             uint32_t* __restrict__ key,
-                                                             uint32_t* __restrict__ hist) {
-    __shared__ uint32_t h[kDigit1Bins];
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
-    __syncthreads();
-    const TileDesc t = tiles[blockIdx.x];
-    const LayerDesc L = layers[t.layer];
-    const uint32_t lend = L.off + L.n;
+// Statistic keys from a given m-tilde (the standalone mask build), one word
+// per wave, one-shot like the dense pass.
+__global__ __launch_bounds__(kBlock) void k_keys_from_mtilde(const uint16_t* __restrict__ word_info, uint32_t w_begin,
+                                                             uint32_t w_end, const float* __restrict__ mtilde,
+                                                             uint32_t* __restrict__ key) {
+    const uint32_t w = w_begin + blockIdx.x * kWaves + threadIdx.x / 64;
+    if (w >= w_end) return;
     const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
-    for (uint32_t w0 = t.w0 + wave * kWordsPerWaveIter; w0 < t.w1; w0 += kWaves * kWordsPerWaveIter) {
-        uint32_t kk[kWordsPerWaveIter];
-        bool inl[kWordsPerWaveIter];
-#pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
-            const uint32_t wi = w0 + e;
-            const uint32_t jj = wi * 64u + lane;
-            inl[e] = wi < t.w1 && jj < lend;
-            kk[e] = inl[e] ? magnitude_key(mtilde[jj]) : 0u;
-        }
-#pragma unroll
-        for (int e = 0; e < kWordsPerWaveIter; ++e) {
-            const uint32_t jj = (w0 + e) * 64u + lane;
-            if (inl[e]) key[jj] = kk[e];
-            hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
-        }
-    }
-    __syncthreads();
-    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+    if (lane >= (word_info[w] & 127u)) return;
+    const size_t j = (size_t)w * 64u + lane;
+    key[j] = magnitude_key(mtilde[j]);
 }
 
-hipError_t launch_keys_from_mtilde(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                                   const float* mtilde, uint32_t* key, uint32_t* hist) {
-    if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_keys_from_mtilde, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, mtilde, key, hist);
+hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
+                                   const float* mtilde, uint32_t* key) {
+    if (w_end <= w_begin) return hipSuccess;
+    hipLaunchKernelGGL(k_keys_from_mtilde, dim3((w_end - w_begin + kWaves - 1) / kWaves), dim3(kBlock), 0, s,
+                       word_info, w_begin, w_end, mtilde, key);
     return hipGetLastError();
 }
 

@@ -5,24 +5,32 @@
 // statistics: gist.science Technical Summary s.2, Partitioned Mask
 // Synchronization; the tie rule is the reading this library adopts).  That is
 // the top k of the 62-bit composite (key, ~position), found by radix
-// selection:
+// selection: first on the 11-bit digit d = bits 30..20 of the key, then on
+// the remaining key bits and, for ties, on the position.
 //
-//  1. The dense pass histograms the first 11-bit key digit (bits 30..20) per
-//     layer.  k_select_first walks the row from the top and picks the bucket
-//     holding the k-th element.  If the whole bucket is needed the layer is
-//     done; otherwise the bucket's elements are "candidates".
-//  2. k_filter reads every key once: keys above the bucket become mask bits
-//     (one wave ballot per 64-element word, written as whole words) and the
-//     bucket's elements are appended, as (key, layer position) records, to
-//     the layer's candidate region (wave-aggregated atomics; record order is
-//     irrelevant because the composite order is total).
-//  3. Up to five refinement passes over the candidate records only: key bits
-//     19..10, key bits 9..0, then, only if the exact threshold key T is tied
-//     beyond what is needed, position bits 30..20, 19..10, 9..0 from the
-//     smallest position upward.  Each pass is a histogram kernel (LDS row per
-//     virtual block, one layer per virtual block) and a per-layer select.
-//  4. k_cand_mark sets the bits of the selected candidates with 64-bit atomic
-//     ORs on the words the filter already wrote.
+//  1. k_sample_hist histograms d over a 1/16 sample of each layer's words
+//     (words picked by a hash of their index, so that no row or column
+//     structure aligns with the sample; layers of up to kFullSampleWords words
+//     are taken whole).  k_estimate turns the sample into a window [lo, hi] of
+//     buckets that holds the bucket of the k-th largest key unless the sample
+//     is off by more than kZ standard deviations; a wholly sampled layer gets
+//     its exact bucket.
+//  2. k_filter reads every key once: d > hi becomes a mask bit (one wave
+//     ballot per 64-element word, written as whole words, whose popcounts add
+//     up to the exact count above the window); lo <= d <= hi becomes a
+//     (key, layer position) record in the layer's own slice of the record
+//     buffer (staged per wave in LDS, one global atomic per flush).
+//  3. A first record pass histograms d of the records; with the count above
+//     the window, k_select_first finds the exact bucket d1 of the k-th key.  If
+//     d1 is outside the window (a sampling miss), k_hist_full and
+//     k_filter_exact redo that layer from all its keys, so the result is exact
+//     in every case.
+//  4. Up to five refinement passes over the records: key bits 19..10, key
+//     bits 9..0, then - only if the threshold key T is tied beyond what is
+//     needed - position bits 30..20, 19..10, 9..0 from the smallest position
+//     upward.  Each pass is a histogram kernel and a per-layer select.
+//  5. k_cand_mark sets the bits of the selected records with 64-bit atomic ORs
+//     on the words the filter wrote.
 //
 // Histogram rows are left zeroed by every select kernel, so a row is clean
 // for the next pass.
@@ -69,151 +77,169 @@ __device__ void find_bucket(uint32_t* h, int nbins, bool descending, uint32_t ne
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, const LayerDesc* __restrict__ layers,
-                                                         uint32_t* __restrict__ hist, SelState* __restrict__ st) {
-    __shared__ uint32_t scratch[kWaves];
-    __shared__ uint32_t s_bucket, s_before, s_count;
-    const int l = layer0 + blockIdx.x;
-    const uint32_t k = layers[l].k;
-    find_bucket(hist + (size_t)l * kHistBins, kDigit1Bins, true, k, &s_bucket, &s_before, &s_count, scratch);
-    if (threadIdx.x == 0) {
-        SelState S{};
-        S.J = 0xFFFFFFFFu;
-        if (k == 0 || s_bucket == kNone) {
-            S.none = 1;
-            S.phase = kPhaseDone;
-        } else {
-            const uint32_t need = k - s_before;
-            S.d1 = s_bucket;
-            S.kprefix = s_bucket;
-            S.need = need;
-            if (need == s_count) {  // the whole bucket is kept: key >= d1 << 20
-                S.all_bucket = 1;
-                S.phase = kPhaseDone;
-                S.T = s_bucket << (31 - kDigit1Bits);
-            } else {
-                S.phase = kPhaseKey2;
-                S.cand_count = s_count;
-            }
-        }
-        st[l] = S;
-    }
+
+
+constexpr uint32_t kSampleShift = 4;            // 1 word in 16
+constexpr uint32_t kFullSampleWords = 4096;     // layers up to 262144 elements are taken whole
+constexpr float kZ = 6.0f;                      // sampling margin in standard deviations
+
+enum SelMode : uint32_t { kModeWindow = 0, kModeFullHist = 2, kModeReclassify = 1 };
+
+__device__ __forceinline__ uint32_t word_hash(uint32_t w) {
+    uint32_t h = w * 0x9E3779B1u;
+    h ^= h >> 15;
+    h *= 0x85EBCA77u;
+    h ^= h >> 13;
+    return h;
 }
 
-hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                               uint32_t* hist, SelState* st) {
-    if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, layers, hist, st);
-    return hipGetLastError();
+// Is word w (of a layer with `lwords` words) in the layer's sample?
+__device__ __forceinline__ bool sampled(uint32_t w, uint32_t lwords) {
+    return lwords <= kFullSampleWords || (word_hash(w) & ((1u << kSampleShift) - 1)) == 0;
 }
 
-// Offsets of the layers' candidate regions and of their virtual blocks
-// (kCandChunk records each); clears the append counters.  One workgroup of
-// 1024 threads, each owning a contiguous run of layers.
-__global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_layers, uint32_t cand_cap,
-                                                    SelState* __restrict__ st, uint32_t* __restrict__ cand_fill,
-                                                    uint32_t* __restrict__ totals) {
-    __shared__ uint32_t sc[1024], sv[1024];
-    const int per = (n_layers + 1023) / 1024;
-    const int a = threadIdx.x * per;
-    const int b = min(a + per, n_layers);
-    uint32_t c = 0, v = 0;
-    for (int i = a; i < b; ++i) {
-        const uint32_t n = st[layer0 + i].cand_count;
-        c += n;
-        v += (n + kCandChunk - 1) / kCandChunk;
-    }
-    sc[threadIdx.x] = c;
-    sv[threadIdx.x] = v;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over 1024 entries
-    for (int d = 1; d < 1024; d <<= 1) {
-        uint32_t tc = 0, tv = 0;
-        if (threadIdx.x >= (unsigned)d) {
-            tc = sc[threadIdx.x - d];
-            tv = sv[threadIdx.x - d];
-        }
-        __syncthreads();
-        sc[threadIdx.x] += tc;
-        sv[threadIdx.x] += tv;
-        __syncthreads();
-    }
-    uint32_t oc = sc[threadIdx.x] - c, ov = sv[threadIdx.x] - v;
-    for (int i = a; i < b; ++i) {
-        SelState* S = &st[layer0 + i];
-        uint32_t n = S->cand_count;
-        // Counts come from the same keys the filter reads, so the regions fit
-        // the buffer (at most one record per element); clamp anyway so that no
-        // record is ever written or read past it.
-        if (oc >= cand_cap) n = 0;
-        else if (n > cand_cap - oc) n = cand_cap - oc;
-        S->cand_count = n;
-        S->cand_off = oc;
-        S->vblk_off = ov;
-        cand_fill[layer0 + i] = 0;
-        oc += n;
-        ov += (n + kCandChunk - 1) / kCandChunk;
-    }
-    if (threadIdx.x == 1023) {
-        totals[0] = sc[1023];
-        totals[1] = sv[1023];
-    }
-}
+// ---------------------------------------------------------------------------
+// 1. sample and window
 
-hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, uint32_t cand_cap, SelState* st,
-                            uint32_t* cand_fill, uint32_t* totals) {
-    if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, layer0, n_layers, cand_cap, st, cand_fill, totals);
-    return hipGetLastError();
-}
-
-// Candidate records are staged in LDS and copied out in bulk: one global
-// atomic per flush (normally one per tile) reserves the slots, instead of one
-// per word - per-word atomics on a single per-layer counter serialize.
-constexpr int kFilterWords = 8;                                 // words per wave per trip
-constexpr int kFilterTrip = kWaves * kFilterWords * 64;        // elements per workgroup trip
-constexpr int kStage = 2 * kFilterTrip;                         // LDS records (32 KB)
-
-__device__ __forceinline__ void filter_flush(uint32_t* s_n, uint32_t* s_base, const uint64_t* s_rec,
-                                             uint32_t* cand_fill, int layer, const SelState& S,
-                                             uint64_t* __restrict__ cand) {
-    __syncthreads();
-    const uint32_t n = *s_n;
-    if (n) {
-        if (threadIdx.x == 0) *s_base = atomicAdd(&cand_fill[layer], n);
-        __syncthreads();
-        const uint32_t base = *s_base;
-        for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
-            const uint32_t slot = base + i;
-            if (slot < S.cand_count) cand[(size_t)S.cand_off + slot] = s_rec[i];
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) *s_n = 0;
-    }
-    __syncthreads();
-}
-
-__global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
-                                                   const LayerDesc* __restrict__ layers,
-                                                   const SelState* __restrict__ st, const uint32_t* __restrict__ key,
-                                                   uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
-                                                   uint64_t* __restrict__ cand) {
-    __shared__ uint64_t s_rec[kStage];
-    __shared__ uint32_t s_n, s_base;
+__global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restrict__ tiles,
+                                                        const LayerDesc* __restrict__ layers,
+                                                        const uint32_t* __restrict__ key,
+                                                        uint32_t* __restrict__ hist,
+                                                        uint32_t* __restrict__ sample_words) {
+    __shared__ uint32_t h[kDigit1Bins];
+    __shared__ uint32_t s_words;
     const TileDesc t = tiles[blockIdx.x];
     const LayerDesc L = layers[t.layer];
-    const SelState S = st[t.layer];
+    if (L.k == 0) return;  // uniform: nothing to select in this layer
+    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+    if (threadIdx.x == 0) s_words = 0;
+    __syncthreads();
+    const uint32_t lwords = (L.n + 63) / 64;
     const uint32_t lend = L.off + L.n;
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
-    const uint32_t d1 = S.d1;
-    const bool none = S.none != 0;
-    const bool whole = S.all_bucket != 0;
-    if (threadIdx.x == 0) s_n = 0;
+    uint32_t nw = 0;
+    for (uint32_t w = t.w0 + wave; w < t.w1; w += kWaves) {
+        if (!sampled(w, lwords)) continue;  // wave-uniform
+        const uint32_t jj = w * 64u + lane;
+        const bool inl = jj < lend;
+        const uint32_t kv = inl ? key[jj] : 0u;
+        hist_add_wave(h, kv >> (31 - kDigit1Bits), inl);
+        nw += (uint32_t)__popcll(__ballot(inl));
+    }
+    if (lane == 0 && nw) atomicAdd(&s_words, nw);
     __syncthreads();
-    // workgroup-uniform trips so that every thread reaches the barriers
-    for (uint32_t wb = t.w0; wb < t.w1; wb += kWaves * kFilterWords) {
-        const uint32_t w0 = wb + wave * kFilterWords;
+    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+    if (threadIdx.x == 0 && s_words) atomicAdd(&sample_words[t.layer], s_words);
+}
+
+hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                              const uint32_t* key, uint32_t* hist, uint32_t* sample_count) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sample_hist, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, key, hist, sample_count);
+    return hipGetLastError();
+}
+
+// Window of buckets for each layer from its sample histogram (sample_count
+// keys of n).  With C(b) the sampled count at or above bucket b and
+// s = n / sample_count, the true count is about s*C(b) with standard
+// deviation about s*sqrt(C(b)); hi is the highest bucket whose count could
+// reach k and lo the highest bucket whose count surely does.  A layer taken
+// whole (s = 1) is exact: lo = hi = the bucket of the k-th key.
+__global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const LayerDesc* __restrict__ layers,
+                                                     uint32_t* __restrict__ hist,
+                                                     const uint32_t* __restrict__ sample_count,
+                                                     SelState* __restrict__ st) {
+    __shared__ uint32_t h[kDigit1Bins];
+    __shared__ uint32_t suffix[kDigit1Bins];
+    __shared__ uint32_t scratch[kWaves];
+    const int l = layer0 + blockIdx.x;
+    const LayerDesc L = layers[l];
+    uint32_t* row = hist + (size_t)l * kHistBins;
+    // per thread 8 bins from the top; suffix[b] = sampled count at or above b
+    constexpr int per = kDigit1Bins / kBlock;
+    uint32_t c[per], sum = 0;
+    for (int e = 0; e < per; ++e) {
+        const int b = kDigit1Bins - 1 - (threadIdx.x * per + e);
+        c[e] = row[b];
+        sum += c[e];
+    }
+    uint32_t run = block_exclusive_scan(sum, scratch, nullptr);
+    for (int e = 0; e < per; ++e) {
+        const int b = kDigit1Bins - 1 - (threadIdx.x * per + e);
+        run += c[e];
+        suffix[b] = run;
+        row[b] = 0;  // leave the row clean
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    SelState S{};
+    S.n_lo = 1;
+    S.n_hi = 0;  // empty window
+    const uint32_t m = sample_count[l];
+    if (L.k > 0 && m > 0) {
+        const bool exact = m >= L.n;
+        const float sc = exact ? 1.0f : (float)L.n / (float)m;
+        const float k = (float)L.k;
+        int hi = -1, lo = -1;
+        for (int b = kDigit1Bins - 1; b >= 0; --b) {
+            const float C = (float)suffix[b];
+            const float est = sc * C, dev = exact ? 0.0f : kZ * sc * sqrtf(C + 1.0f);
+            if (hi < 0 && est + dev >= k) hi = b;  // the k-th key may lie in b or below
+            if (est - dev >= k) {                   // the k-th key surely lies in b or above
+                lo = b;
+                break;
+            }
+        }
+        if (hi < 0) hi = 0;
+        if (lo < 0) lo = 0;
+        S.n_lo = (uint32_t)lo;
+        S.n_hi = (uint32_t)hi;
+    }
+    st[l] = S;
+}
+
+hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
+                           const uint32_t* sample_count, SelState* st) {
+    if (n_layers <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_estimate, dim3(n_layers), dim3(kBlock), 0, s, layer0, layers, hist, sample_count, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 2. the pass over every key
+
+constexpr int kFilterWords = 8;                 // words per wave per trip
+constexpr int kWaveStage = 1024;                // LDS records per wave (8 KB)
+
+// Flush a wave's staged records to the layer's slice (one atomic per flush).
+__device__ __forceinline__ void wave_flush(uint64_t* stage, uint32_t n, uint32_t* counter, const LayerDesc& L,
+                                           uint64_t* __restrict__ cand) {
+    if (n == 0) return;
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(counter, n);
+    base = __shfl(base, 0, 64);
+    for (uint32_t i = lane_id(); i < n; i += 64) {
+        const uint32_t slot = base + i;
+        if (slot < L.n) cand[(size_t)L.off + slot] = stage[i];
+    }
+}
+
+// Keys of a tile: digit d >= sel_from -> mask bit; cand_lo <= d <= cand_hi ->
+// record; `above` gets the number of bits set.  Every word of the tile is
+// written.  Each wave works alone: no workgroup barrier.
+__device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, uint32_t sel_from, uint32_t cand_lo,
+                                         uint32_t cand_hi, const uint32_t* __restrict__ key,
+                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
+                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+    __shared__ uint64_t s_rec[kWaves][kWaveStage];
+    const uint32_t lend = L.off + L.n;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    uint64_t* stage = s_rec[wave];
+    const bool records = cand_lo <= cand_hi;
+    uint32_t n_st = 0, n_above = 0;
+    for (uint32_t w0 = t.w0 + wave * kFilterWords; w0 < t.w1; w0 += kWaves * kFilterWords) {
         uint32_t kv[kFilterWords];
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
@@ -224,32 +250,228 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
-            const bool inl = (w0 + e < t.w1) && jj < lend && !none;
+            const bool inl = (w0 + e < t.w1) && jj < lend;
             const uint32_t d = kv[e] >> (31 - kDigit1Bits);
-            const bool sel = inl && (d > d1 || (whole && d == d1));
-            const bool cnd = inl && !whole && d == d1;
-            const uint64_t word = __ballot(sel);
+            const uint64_t word = __ballot(inl && d >= sel_from);
+            n_above += (uint32_t)__popcll(word);
             if (lane == (uint32_t)e) mine = word;
-            const uint64_t cb = __ballot(cnd);
-            if (cb) {
-                uint32_t base = 0;
-                if (lane == 0) base = atomicAdd(&s_n, (uint32_t)__popcll(cb));
-                base = __shfl(base, 0, 64);
-                if (cnd) s_rec[base + lanes_below(cb)] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
+            if (records) {
+                const bool cnd = inl && cand_lo <= d && d <= cand_hi;
+                const uint64_t cb = __ballot(cnd);
+                if (cb) {
+                    if (cnd) stage[n_st + lanes_below(cb)] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
+                    n_st += (uint32_t)__popcll(cb);
+                }
             }
         }
         if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) bits[w0 + lane] = mine;
-        __syncthreads();
-        if (s_n > (uint32_t)(kStage - kFilterTrip)) filter_flush(&s_n, &s_base, s_rec, cand_fill, t.layer, S, cand);
+        if (n_st > (uint32_t)(kWaveStage - kFilterWords * 64)) {  // room for one more trip
+            wave_flush(stage, n_st, &cand_fill[t.layer], L, cand);
+            n_st = 0;
+        }
     }
-    filter_flush(&s_n, &s_base, s_rec, cand_fill, t.layer, S, cand);
+    wave_flush(stage, n_st, &cand_fill[t.layer], L, cand);
+    if (lane == 0 && n_above) atomicAdd(&above[t.layer], n_above);
+}
+
+__global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
+                                                   const LayerDesc* __restrict__ layers,
+                                                   const SelState* __restrict__ st, const uint32_t* __restrict__ key,
+                                                   uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
+                                                   uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+    const TileDesc t = tiles[blockIdx.x];
+    const LayerDesc L = layers[t.layer];
+    const SelState S = st[t.layer];
+    const bool win = S.n_lo <= S.n_hi && L.k > 0;
+    // no window (nothing to select, or an empty sample): no bits, no records
+    key_pass(t, L, win ? S.n_hi + 1 : (uint32_t)kDigit1Bins, win ? S.n_lo : 1u, win ? S.n_hi : 0u, key, bits,
+             cand_fill, cand, above);
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
-                         uint64_t* cand) {
+                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill, uint64_t* cand,
+                         uint32_t* above) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, bits, cand_fill, cand);
+    hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, bits, cand_fill, cand,
+                       above);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 3. threshold bucket
+
+__device__ __forceinline__ void init_found(SelState& S, uint32_t k, uint32_t bucket, uint32_t before,
+                                           uint32_t count) {
+    const uint32_t need = k - before;
+    S.d1 = bucket;
+    S.kprefix = bucket;
+    S.need = need;
+    S.all_bucket = need == count;
+    S.J = 0xFFFFFFFFu;
+    if (S.all_bucket) {  // the whole bucket is kept: key >= d1 << 20
+        S.phase = kPhaseDone;
+        S.T = bucket << (31 - kDigit1Bits);
+    } else {
+        S.phase = kPhaseKey2;
+    }
+}
+
+// first_pass = true: hist holds the records' first digits and above[l] the
+// exact count above the window.  first_pass = false: only layers in
+// kModeFullHist, whose hist row now holds every key.
+__global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool first_pass,
+                                                         const LayerDesc* __restrict__ layers,
+                                                         uint32_t* __restrict__ hist, SelState* __restrict__ st,
+                                                         const uint32_t* __restrict__ above,
+                                                         uint32_t* __restrict__ cand_fill) {
+    __shared__ uint32_t scratch[kWaves];
+    __shared__ uint32_t s_bucket, s_before, s_count;
+    const int l = layer0 + blockIdx.x;
+    const SelState old = st[l];
+    if (!first_pass && old.mode != kModeFullHist) return;  // uniform
+    const uint32_t k = layers[l].k;
+    const uint32_t a = first_pass ? above[l] : 0u;
+    const bool win = old.n_lo <= old.n_hi;
+    // bucket search over the row, starting from the count above the window
+    const uint32_t need = (first_pass && a >= k) ? 0u : k - a;
+    find_bucket(hist + (size_t)l * kHistBins, kDigit1Bins, true, need, &s_bucket, &s_before, &s_count, scratch);
+    if (threadIdx.x != 0) return;
+    SelState S{};
+    S.n_lo = old.n_lo;
+    S.n_hi = old.n_hi;
+    S.vblk_off = old.vblk_off;
+    S.cand_off = old.cand_off;
+    S.cand_count = old.cand_count;
+    if (k == 0) {
+        S.none = 1;
+        S.phase = kPhaseDone;
+        S.J = 0xFFFFFFFFu;
+        S.mode = kModeWindow;
+    } else if (first_pass && (!win || a >= k || s_bucket == kNone)) {
+        // outside the window (or no window): count every key of the layer
+        S.mode = kModeFullHist;
+        S.none = 1;  // provisional; the second pass decides
+        S.phase = kPhaseDone;
+        cand_fill[l] = 0;
+    } else if (s_bucket == kNone) {  // cannot happen with a full row; select nothing rather than guess
+        S.none = 1;
+        S.phase = kPhaseDone;
+        S.mode = kModeReclassify;
+    } else {
+        init_found(S, k, s_bucket, s_before + a, s_count);
+        S.mode = first_pass ? kModeWindow : kModeReclassify;
+    }
+    st[l] = S;
+}
+
+hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
+                               const LayerDesc* layers, uint32_t* hist, SelState* st, const uint32_t* above,
+                               uint32_t* cand_fill) {
+    if (n_layers <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, first_pass, layers, hist, st, above,
+                       cand_fill);
+    return hipGetLastError();
+}
+
+// Full first-digit histogram of the layers in kModeFullHist.
+__global__ __launch_bounds__(kBlock) void k_hist_full(const TileDesc* __restrict__ tiles,
+                                                      const LayerDesc* __restrict__ layers,
+                                                      const SelState* __restrict__ st,
+                                                      const uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t h[kDigit1Bins];
+    const TileDesc t = tiles[blockIdx.x];
+    if (st[t.layer].mode != kModeFullHist) return;  // uniform
+    const LayerDesc L = layers[t.layer];
+    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+    __syncthreads();
+    const uint32_t lend = L.off + L.n;
+    const uint32_t lane = lane_id();
+    for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kWaves) {
+        const uint32_t jj = w * 64u + lane;
+        const bool inl = jj < lend;
+        hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
+    }
+    __syncthreads();
+    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+}
+
+hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                            const SelState* st, const uint32_t* key, uint32_t* hist) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_hist_full, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, hist);
+    return hipGetLastError();
+}
+
+// Reclassification (bits and records from the exact bucket) of the layers in
+// kModeReclassify.
+__global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restrict__ tiles,
+                                                         const LayerDesc* __restrict__ layers,
+                                                         const SelState* __restrict__ st,
+                                                         const uint32_t* __restrict__ key,
+                                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
+                                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+    const TileDesc t = tiles[blockIdx.x];
+    const SelState S = st[t.layer];
+    if (S.mode != kModeReclassify || S.none) return;  // uniform per workgroup
+    const LayerDesc L = layers[t.layer];
+    if (S.all_bucket)  // keys in the threshold bucket and above, no records
+        key_pass(t, L, S.d1, 1, 0, key, bits, cand_fill, cand, above);
+    else  // above the bucket: bits; in it: records
+        key_pass(t, L, S.d1 + 1, S.d1, S.d1, key, bits, cand_fill, cand, above);
+}
+
+hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                               const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
+                               uint64_t* cand, uint32_t* above) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_filter_exact, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, bits, cand_fill,
+                       cand, above);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 4. records
+
+// Virtual-block numbering of each layer's records [L.off, L.off + count),
+// kCandChunk records per block.  One workgroup of 1024 threads, each owning a
+// contiguous run of layers.
+__global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_layers,
+                                                    const LayerDesc* __restrict__ layers,
+                                                    SelState* __restrict__ st, const uint32_t* __restrict__ cand_fill,
+                                                    uint32_t* __restrict__ totals) {
+    __shared__ uint32_t sv[1024];
+    const int per = (n_layers + 1023) / 1024;
+    const int a = threadIdx.x * per;
+    const int b = min(a + per, n_layers);
+    uint32_t v = 0;
+    for (int i = a; i < b; ++i) {
+        const uint32_t n = min(cand_fill[layer0 + i], layers[layer0 + i].n);
+        v += (n + kCandChunk - 1) / kCandChunk;
+    }
+    sv[threadIdx.x] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const uint32_t t = threadIdx.x >= (unsigned)d ? sv[threadIdx.x - d] : 0u;
+        __syncthreads();
+        sv[threadIdx.x] += t;
+        __syncthreads();
+    }
+    uint32_t ov = sv[threadIdx.x] - v;
+    for (int i = a; i < b; ++i) {
+        const uint32_t n = min(cand_fill[layer0 + i], layers[layer0 + i].n);
+        SelState* S = &st[layer0 + i];
+        S->cand_count = n;
+        S->cand_off = layers[layer0 + i].off;
+        S->vblk_off = ov;
+        ov += (n + kCandChunk - 1) / kCandChunk;
+    }
+    if (threadIdx.x == 1023) totals[1] = sv[1023];
+}
+
+hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
+                            const uint32_t* cand_fill, uint32_t* totals) {
+    if (n_layers <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, layer0, n_layers, layers, st, cand_fill, totals);
     return hipGetLastError();
 }
 
@@ -267,31 +489,49 @@ __device__ int layer_of_vblock(const SelState* st, int32_t layer0, int32_t n_lay
     return layer0 + lo;
 }
 
-__device__ __forceinline__ int phase_bins(uint32_t phase) { return phase == kPhasePos1 ? 2048 : 1024; }
 
+__device__ __forceinline__ int phase_bins(uint32_t phase) {
+    return (phase == kPhasePos1 || phase == kPhaseKey1) ? 2048 : 1024;
+}
+
+// Record histogram for one phase.  Each workgroup takes a contiguous range of
+// virtual blocks and flushes its LDS row only when the layer changes.  Only
+// layers whose state is in `phase` take part; records are filtered by the
+// phase's prefix.
 __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t layer0, int32_t n_layers,
                                                       const SelState* __restrict__ st,
-                                                      const uint32_t* __restrict__ cand_fill,
                                                       const uint32_t* __restrict__ totals,
                                                       const uint64_t* __restrict__ cand,
                                                       uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[2048];
     __shared__ int s_layer;
     const uint32_t nv = totals[1];
+    const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
+    const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
     const int nb = phase_bins(phase);
-    for (uint32_t v = blockIdx.x; v < nv; v += gridDim.x) {
+    int cur = -1;
+    for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+    for (uint32_t v = v0; v < v1; ++v) {
         if (threadIdx.x == 0) s_layer = layer_of_vblock(st, layer0, n_layers, v);
         __syncthreads();
         const int l = s_layer;
         const SelState S = st[l];
         __syncthreads();
-        if (S.phase != phase) continue;  // uniform across the block
-        for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
-        __syncthreads();
+        const uint32_t sphase = phase == kPhaseKey1 ? (S.mode == kModeWindow && !S.none ? kPhaseKey1 : kPhaseDone)
+                                                    : S.phase;
+        if (sphase != phase) continue;  // uniform
+        if (l != cur) {
+            if (cur >= 0) {
+                hist_flush(h, hist + (size_t)cur * kHistBins, nb);
+                __syncthreads();
+                for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+            }
+            cur = l;
+            __syncthreads();
+        }
         const uint32_t chunk = v - S.vblk_off;
         const uint32_t p0 = S.cand_off + chunk * kCandChunk;
-        const uint32_t pend = S.cand_off + min(S.cand_count, cand_fill[l]);  // records actually written
-        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, pend);
+        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, S.cand_off + S.cand_count);
         for (uint32_t base = p0; base < p1; base += kBlock) {
             const uint32_t p = base + threadIdx.x;
             bool take = false;
@@ -300,7 +540,8 @@ __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t la
                 const uint64_t rec = cand[p];
                 const uint32_t kv = (uint32_t)(rec >> 32), jl = (uint32_t)rec;
                 switch (phase) {
-                    case kPhaseKey2: take = true; digit = (kv >> 10) & 1023u; break;
+                    case kPhaseKey1: take = true; digit = kv >> 20; break;
+                    case kPhaseKey2: take = (kv >> 20) == S.d1; digit = (kv >> 10) & 1023u; break;
                     case kPhaseKey3: take = (kv >> 10) == S.kprefix; digit = kv & 1023u; break;
                     case kPhasePos1: take = kv == S.T; digit = jl >> 20; break;
                     case kPhasePos2: take = kv == S.T && (jl >> 20) == S.jprefix; digit = (jl >> 10) & 1023u; break;
@@ -310,16 +551,17 @@ __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t la
             hist_add_wave(h, digit, take);
         }
         __syncthreads();
-        hist_flush(h, hist + (size_t)l * kHistBins, nb);
+    }
+    if (cur >= 0) {
         __syncthreads();
+        hist_flush(h, hist + (size_t)cur * kHistBins, nb);
     }
 }
 
 hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* cand_fill, const uint32_t* totals, const uint64_t* cand, uint32_t* hist) {
+                            const uint32_t* totals, const uint64_t* cand, uint32_t* hist) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_hist, dim3(1024), dim3(kBlock), 0, s, phase, layer0, n_layers, st, cand_fill, totals,
-                       cand, hist);
+    hipLaunchKernelGGL(k_cand_hist, dim3(1024), dim3(kBlock), 0, s, phase, layer0, n_layers, st, totals, cand, hist);
     return hipGetLastError();
 }
 
@@ -381,10 +623,10 @@ hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int
     return hipGetLastError();
 }
 
+
 __global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_layers,
                                                       const LayerDesc* __restrict__ layers,
                                                       const SelState* __restrict__ st,
-                                                      const uint32_t* __restrict__ cand_fill,
                                                       const uint32_t* __restrict__ totals,
                                                       const uint64_t* __restrict__ cand,
                                                       uint64_t* __restrict__ bits) {
@@ -397,12 +639,11 @@ __global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_
         const SelState S = st[l];
         const uint32_t off = layers[l].off;
         const uint32_t n = layers[l].n;
-        const uint32_t filled = cand_fill[l];
         __syncthreads();
-        if (S.none || S.all_bucket) continue;
+        if (S.none) continue;
         const uint32_t chunk = v - S.vblk_off;
         const uint32_t p0 = S.cand_off + chunk * kCandChunk;
-        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, S.cand_off + min(S.cand_count, filled));
+        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, S.cand_off + S.cand_count);
         for (uint32_t p = p0 + threadIdx.x; p < p1; p += kBlock) {
             const uint64_t rec = cand[p];
             const uint32_t kv = (uint32_t)(rec >> 32), jl = (uint32_t)rec;
@@ -415,11 +656,9 @@ __global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_
 }
 
 hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* cand_fill, const uint32_t* totals,
-                            const uint64_t* cand, uint64_t* bits) {
+                            const SelState* st, const uint32_t* totals, const uint64_t* cand, uint64_t* bits) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_mark, dim3(1024), dim3(kBlock), 0, s, layer0, n_layers, layers, st, cand_fill, totals,
-                       cand, bits);
+    hipLaunchKernelGGL(k_cand_mark, dim3(1024), dim3(kBlock), 0, s, layer0, n_layers, layers, st, totals, cand, bits);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // entry point declared in include/scape.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -140,6 +141,8 @@ struct scape_ctx {
     uint64_t* d_cand = nullptr;
     uint32_t* d_key = nullptr;
     uint32_t* d_block_sums = nullptr;
+    uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
+    uint32_t* d_counts = nullptr;     // per layer: sampled keys, keys above the window
     // profiling
     bool prof_on = false;
     ProfSlot prof[kProfSlots]{};
@@ -161,6 +164,8 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_cand);
     hipFree(c->d_key);
     hipFree(c->d_block_sums);
+    hipFree(c->d_word_info);
+    hipFree(c->d_counts);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -226,16 +231,34 @@ int prof_begin(scape_ctx* c) {
 // bits into `bits`.
 int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint32_t* key, uint64_t* bits,
                hipStream_t s) {
-    SCAPE_HIP(launch_select_first(s, la, nl, c->d_layers, c->d_hist, c->d_sel), "select_first");
-    SCAPE_HIP(launch_cand_scan(s, la, nl, c->cand_cap, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
-    SCAPE_HIP(launch_filter(s, c->d_tiles + ta, tb - ta, c->d_layers, c->d_sel, key, bits, c->d_cand_fill,
-                            c->d_cand),
+    const TileDesc* tiles = c->d_tiles + ta;
+    const uint32_t nt = tb - ta;
+    const uint32_t L = (uint32_t)c->lay.L;
+    uint32_t* sample_count = c->d_counts;
+    uint32_t* above = c->d_counts + L;
+    SCAPE_HIP(launch_fill_u32(s, c->d_cand_fill + la, (uint64_t)nl, 0u), "fill");
+    SCAPE_HIP(launch_fill_u32(s, sample_count + la, (uint64_t)nl, 0u), "fill");
+    SCAPE_HIP(launch_fill_u32(s, above + la, (uint64_t)nl, 0u), "fill");
+    SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
+    SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel), "estimate");
+    SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
               "filter");
+    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
+    SCAPE_HIP(launch_cand_hist(s, kPhaseKey1, la, nl, c->d_sel, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+    SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_hist, c->d_sel, above, c->d_cand_fill),
+              "select_first");
+    // sampling misses: full histogram, exact bucket, reclassification
+    SCAPE_HIP(launch_hist_full(s, tiles, nt, c->d_layers, c->d_sel, key, c->d_hist), "hist_full");
+    SCAPE_HIP(launch_select_first(s, la, nl, false, c->d_layers, c->d_hist, c->d_sel, above, c->d_cand_fill),
+              "select_first");
+    SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
+              "filter_exact");
+    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
-        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_cand_fill, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
-    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals, c->d_cand, bits), "cand_mark");
+    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_totals, c->d_cand, bits), "cand_mark");
     return SCAPE_OK;
 }
 
@@ -323,6 +346,14 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         }
     }
     c->layer_tile0[c->lay.L] = (uint32_t)c->tiles.size();
+    std::vector<uint16_t> winfo(c->n_words, 0);
+    for (int32_t l = 0; l < c->lay.L; ++l) {
+        const int64_t off = c->lay.off[l], n = c->lay.n[l];
+        for (int64_t w = off / 64; w < (off + n + 63) / 64; ++w) {
+            const int64_t inside = std::min<int64_t>(64, off + n - w * 64);
+            winfo[w] = (uint16_t)((c->owner[l] << 8) | inside);
+        }
+    }
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -337,13 +368,17 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_cand_fill, L, "candidate counters")) || (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
         (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
         (rc = dev_alloc(&c->d_key, (size_t)c->lay.n_pad, "statistic keys")) ||
-        (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums"))) {
+        (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
+        (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
+        (rc = dev_alloc(&c->d_counts, 2 * L, "per-layer counters"))) {
         free_ctx(c);
         return rc;
     }
     e = hipMemcpy(c->d_layers, ld.data(), L * sizeof(LayerDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess && !c->tiles.empty())
         e = hipMemcpy(c->d_tiles, c->tiles.data(), c->tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess && c->n_words)
+        e = hipMemcpy(c->d_word_info, winfo.data(), (size_t)c->n_words * sizeof(uint16_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(c->d_hist, 0, L * kHistBins * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(c->d_sel, 0, L * sizeof(SelState));
     if (e == hipSuccess) e = hipMemset(c->d_totals, 0, 4 * sizeof(uint32_t));
@@ -412,8 +447,8 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
     const int slot = prof_begin(ctx);
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
-    SCAPE_HIP(launch_ef_compact(s, ctx->d_tiles, n_tiles, ctx->d_layers, wp, sc, m, cur->bits, cur->block_prefix,
-                                k_cap, key, ctx->d_hist),
+    SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix, k_cap,
+                                key),
               "ef_compact");
     prof_mark(ctx, slot, 1, s);
     SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->n_words,
@@ -454,8 +489,10 @@ int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, in
     }
     const uint32_t ta = ctx->layer_tile0[la], tb = ctx->layer_tile0[lb];
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist + (size_t)la * kHistBins, (uint64_t)(lb - la) * kHistBins, 0u), "fill");
-    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_tiles + ta, tb - ta, ctx->d_layers, mtilde, ctx->d_key, ctx->d_hist),
-              "keys");
+    const uint32_t wa = (uint32_t)(ctx->lay.off[la] / 64), wb = ctx->layer_tile0[lb] > ctx->layer_tile0[la]
+                                                                 ? ctx->tiles[ctx->layer_tile0[lb] - 1].w1
+                                                                 : wa;
+    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, wa, wb, mtilde, ctx->d_key), "keys");
     if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key, out->bits, s))) return rc;
     if (all && (rc = run_index(ctx, out, s))) return rc;
     return SCAPE_OK;

@@ -46,6 +46,7 @@ struct LayerDesc {
 //   selected(j) = !none && (key > T || (key == T && jl <= J))
 // where jl is the layer-local position.
 enum SelPhase : uint32_t {
+    kPhaseKey1 = 6,   // first key digit of the records (threshold bucket) pending
     kPhaseDone = 0,
     kPhaseKey2 = 1,   // key bits 19..10 pending
     kPhaseKey3 = 2,   // key bits 9..0 pending
@@ -67,6 +68,9 @@ struct SelState {
     uint32_t cand_count;  // candidate records of this layer
     uint32_t cand_off;    // first record of this layer
     uint32_t vblk_off;    // first virtual candidate block of this layer
+    uint32_t n_lo, n_hi;  // first-digit window the filter made records for (n_lo > n_hi: none)
+    uint32_t mode;        // 0 decided by the window, 1 reclassified, 2 full histogram needed
+    uint32_t pad[3];
 };
 
 struct WorkerPtrs {
@@ -85,32 +89,41 @@ struct StepScalars {
 
 // elementwise: error feedback, candidates, compaction, statistic, digit-1
 // histogram; then reduction + reconstruction + update.
-hipError_t launch_ef_compact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                             const WorkerPtrs& wp, const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, uint32_t* hist);
+hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
+                             const StepScalars& sc, const float* m, const uint64_t* cur_bits,
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key);
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
                                 float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, uint32_t n_words,
                                 uint32_t n_pad, uint32_t k_cap);
-hipError_t launch_keys_from_mtilde(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                                   const float* mtilde, uint32_t* key, uint32_t* hist);
+hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
+                                   const float* mtilde, uint32_t* key);
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t value);
 
 // selection
-hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                               uint32_t* hist, SelState* st);
-hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, uint32_t cand_cap, SelState* st,
-                            uint32_t* cand_fill, uint32_t* totals);
+hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                              const uint32_t* key, uint32_t* hist, uint32_t* sample_count);
+hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
+                           const uint32_t* sample_count, SelState* st);
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
-                         uint64_t* cand);
+                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill, uint64_t* cand,
+                         uint32_t* above);
+hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
+                               const LayerDesc* layers, uint32_t* hist, SelState* st, const uint32_t* above,
+                               uint32_t* cand_fill);
+hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                            const SelState* st, const uint32_t* key, uint32_t* hist);
+hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
+                               const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
+                               uint64_t* cand, uint32_t* above);
+hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
+                            const uint32_t* cand_fill, uint32_t* totals);
 hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* cand_fill, const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
+                            const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
 hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* cand_fill, const uint32_t* totals,
-                            const uint64_t* cand, uint64_t* bits);
+                            const SelState* st, const uint32_t* totals, const uint64_t* cand, uint64_t* bits);
 
 // bits
 hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);
