@@ -15,6 +15,8 @@
 // Sparse pass (k_reduce_update): one lane per masked position: the W-way mean
 // of the sparse buffers in worker order, the reconstruction of the averaged
 // gradient from that one buffer, the AdamS normaliser, and the m/v/x update.
+// The dense pass leaves m of every masked position in a compacted stash, so
+// the sparse pass gathers only x.
 //
 // The operations follow the SCAPE step of "SCAPE: Accurate and Efficient LLM
 // Training with Extreme Sparse Communication" as stated in include/scape.h
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
                                                        WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
-                                                       uint32_t* __restrict__ key) {
+                                                       uint32_t* __restrict__ key, float* __restrict__ m_stash) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
     if (w >= n_words) return;
@@ -75,17 +77,20 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
         if (msk) wp.b[i][rank] = mt;
     }
     key[j] = kk;
+    // m before the step, compacted like the sparse buffers: the update pass
+    // reads it contiguously instead of gathering one cache line per position
+    if (msk) m_stash[rank] = mo;
 }
 
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key) {
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, float* m_stash) {
     if (n_words == 0) return hipSuccess;
     const dim3 grid((n_words + kWaves - 1) / kWaves);
 #define SCAPE_EF_CASE(WV)                                                                                 \
     case WV:                                                                                              \
         hipLaunchKernelGGL(k_ef_compact<WV>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
-                           cur_prefix, k_cap, key);                                                       \
+                           cur_prefix, k_cap, key, m_stash);                                              \
         break;
     switch (sc.W) {
         SCAPE_EF_CASE(1)
@@ -97,7 +102,7 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
         SCAPE_EF_CASE(32)
         default:
             hipLaunchKernelGGL(k_ef_compact<0>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits,
-                               cur_prefix, k_cap, key);
+                               cur_prefix, k_cap, key, m_stash);
     }
 #undef SCAPE_EF_CASE
     return hipGetLastError();
@@ -140,41 +145,83 @@ hipError_t launch_key_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tile
     return hipGetLastError();
 }
 
+// Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
+// by the workgroup size so that idx, the sparse buffers and the m stash are
+// read contiguously), every load issued before the arithmetic.
+constexpr int kUpdatePer = 4;
+
+template <int WT>
 __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepScalars sc, float* __restrict__ x,
                                                           float* __restrict__ m, float* __restrict__ v,
                                                           const uint32_t* __restrict__ idx,
-                                                          const uint32_t* __restrict__ prefix, uint32_t n_words,
+                                                          const uint32_t* __restrict__ prefix,
+                                                          const float* __restrict__ m_stash, uint32_t n_words,
                                                           uint32_t n_pad, uint32_t k_cap) {
+    constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     const uint32_t total = prefix[n_words];
     const uint32_t cnt = total < k_cap ? total : k_cap;
-    const int W = sc.W;
+    const int W = WT > 0 ? WT : sc.W;
     const float fW = (float)W;
-    for (uint32_t q = blockIdx.x * kBlock + threadIdx.x; q < cnt; q += gridDim.x * kBlock) {
-        const uint32_t jj = idx[q];
-        if (jj >= n_pad) continue;
-        float s = wp.b[0][q];
-        for (int i = 1; i < W; ++i) s = s + wp.b[i][q];
-        const float bb = s / fW;
-        const float mo = m[jj];
-        const float ghat = (bb - sc.beta1 * mo) / sc.c1;
-        const float vv = sc.beta2 * (mo * mo) + sc.c2 * (ghat * ghat);
-        v[jj] = vv;
-        m[jj] = bb;
-        const float xv = x[jj];
-        float u = bb / (sqrtf(vv) + sc.eps);
-        if (sc.wd != 0.0f) u = u + sc.wd * xv;
-        x[jj] = xv - sc.lr * u;
+    const uint32_t q0 = blockIdx.x * (kBlock * kUpdatePer) + threadIdx.x;
+    uint32_t jj[kUpdatePer];
+    float mo[kUpdatePer], xv[kUpdatePer], s[kUpdatePer];
+    bool ok[kUpdatePer];
+#pragma unroll
+    for (int u = 0; u < kUpdatePer; ++u) {
+        const uint32_t q = q0 + u * kBlock;
+        ok[u] = q < cnt;
+        jj[u] = ok[u] ? idx[q] : 0u;
+        ok[u] = ok[u] && jj[u] < n_pad;
+        mo[u] = ok[u] ? m_stash[q] : 0.0f;
+        xv[u] = ok[u] ? x[jj[u]] : 0.0f;
+        s[u] = ok[u] ? wp.b[0][q] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 1; i < WMAX; ++i) {
+        if (i >= W) break;
+#pragma unroll
+        for (int u = 0; u < kUpdatePer; ++u) {
+            const uint32_t q = q0 + u * kBlock;
+            if (ok[u]) s[u] = s[u] + wp.b[i][q];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUpdatePer; ++u) {
+        if (!ok[u]) continue;
+        const float bb = s[u] / fW;
+        const float ghat = (bb - sc.beta1 * mo[u]) / sc.c1;
+        const float vv = sc.beta2 * (mo[u] * mo[u]) + sc.c2 * (ghat * ghat);
+        v[jj[u]] = vv;
+        m[jj[u]] = bb;
+        float upd = bb / (sqrtf(vv) + sc.eps);
+        if (sc.wd != 0.0f) upd = upd + sc.wd * xv[u];
+        x[jj[u]] = xv[u] - sc.lr * upd;
     }
 }
 
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
-                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, uint32_t n_words,
-                                uint32_t n_pad, uint32_t k_cap) {
+                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
+                                uint32_t n_words, uint32_t n_pad, uint32_t k_cap) {
     if (k_cap == 0) return hipSuccess;
-    uint32_t blocks = (k_cap + kBlock - 1) / kBlock;
-    if (blocks > 16384u) blocks = 16384u;
-    hipLaunchKernelGGL(k_reduce_update, dim3(blocks), dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix,
-                       n_words, n_pad, k_cap);
+    const dim3 grid((k_cap + kBlock * kUpdatePer - 1) / (kBlock * kUpdatePer));
+#define SCAPE_RU_CASE(WV)                                                                                     \
+    case WV:                                                                                                  \
+        hipLaunchKernelGGL(k_reduce_update<WV>, grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix, \
+                           m_stash, n_words, n_pad, k_cap);                                                   \
+        break;
+    switch (sc.W) {
+        SCAPE_RU_CASE(1)
+        SCAPE_RU_CASE(2)
+        SCAPE_RU_CASE(3)
+        SCAPE_RU_CASE(4)
+        SCAPE_RU_CASE(8)
+        SCAPE_RU_CASE(16)
+        SCAPE_RU_CASE(32)
+        default:
+            hipLaunchKernelGGL(k_reduce_update<0>, grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix,
+                               m_stash, n_words, n_pad, k_cap);
+    }
+#undef SCAPE_RU_CASE
     return hipGetLastError();
 }
 

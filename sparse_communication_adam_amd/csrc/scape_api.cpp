@@ -143,6 +143,7 @@ struct scape_ctx {
     uint32_t* d_block_sums = nullptr;
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys, keys above the window
+    float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
     // profiling
     bool prof_on = false;
     ProfSlot prof[kProfSlots]{};
@@ -166,6 +167,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_block_sums);
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
+    hipFree(c->d_m_stash);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -370,7 +372,8 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_key, (size_t)c->lay.n_pad, "statistic keys")) ||
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
-        (rc = dev_alloc(&c->d_counts, 2 * L, "per-layer counters"))) {
+        (rc = dev_alloc(&c->d_counts, 2 * L, "per-layer counters")) ||
+        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash"))) {
         free_ctx(c);
         return rc;
     }
@@ -448,10 +451,10 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
     SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix, k_cap,
-                                key),
+                                key, ctx->d_m_stash),
               "ef_compact");
     prof_mark(ctx, slot, 1, s);
-    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->n_words,
+    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash, ctx->n_words,
                                    (uint32_t)ctx->lay.n_pad, k_cap),
               "reduce_update");
     prof_mark(ctx, slot, 2, s);

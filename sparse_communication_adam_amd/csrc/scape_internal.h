@@ -91,10 +91,10 @@ struct StepScalars {
 // histogram; then reduction + reconstruction + update.
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key);
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, float* m_stash);
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
-                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, uint32_t n_words,
-                                uint32_t n_pad, uint32_t k_cap);
+                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
+                                uint32_t n_words, uint32_t n_pad, uint32_t k_cap);
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
                                    const float* mtilde, uint32_t* key);
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
