@@ -9,22 +9,23 @@
 //
 // The index is built in three passes over the bits (N/8 bytes each):
 // per-workgroup popcounts, one scan of those partial sums, then an emit pass
-// that writes block_prefix for every word and, one wave per word, the set
-// positions into idx with contiguous stores.
+// that writes block_prefix for every word and the set positions into idx.
 #include "scape_device.h"
 
 namespace scape {
 
-constexpr int kWordsPerThread = kIndexWordsPerBlock / kBlock;  // 8
+constexpr int kWordsPerThread = kIndexWordsPerBlock / kBlock;  // 8, thread t owns words t, t+256, ...
 
 __global__ __launch_bounds__(kBlock) void k_index_count(const uint64_t* __restrict__ bits, uint32_t n_words,
                                                         uint32_t* __restrict__ block_sums) {
     __shared__ uint32_t scratch[kWaves];
-    const uint32_t w0 = blockIdx.x * kIndexWordsPerBlock + threadIdx.x * kWordsPerThread;
+    const uint32_t wb = blockIdx.x * kIndexWordsPerBlock;
     uint32_t c = 0;
 #pragma unroll
-    for (int e = 0; e < kWordsPerThread; ++e)
-        if (w0 + e < n_words) c += (uint32_t)__popcll(bits[w0 + e]);
+    for (int e = 0; e < kWordsPerThread; ++e) {
+        const uint32_t wi = wb + e * kBlock + threadIdx.x;
+        if (wi < n_words) c += (uint32_t)__popcll(bits[wi]);
+    }
     uint32_t total = 0;
     block_exclusive_scan(c, scratch, &total);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
@@ -68,45 +69,45 @@ hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blo
     return hipGetLastError();
 }
 
+// Thread t owns words wb + t + 256e (e < 8): reads and prefix writes are
+// contiguous across the workgroup.  The prefix runs in word order through 8
+// workgroup scans; each thread then writes the positions of its words' set
+// bits (a mask at 1% density has about 0.6 per word, so lanes rarely wait on
+// each other; a full mask costs 64 trips, as a wave per word would).
 __global__ __launch_bounds__(kBlock) void k_index_emit(const uint64_t* __restrict__ bits, uint32_t n_words,
                                                        const uint32_t* __restrict__ block_offs,
                                                        uint32_t* __restrict__ idx, uint32_t k_cap,
                                                        uint32_t* __restrict__ prefix) {
     __shared__ uint32_t scratch[kWaves];
-    __shared__ uint64_t s_words[kIndexWordsPerBlock];
-    __shared__ uint32_t s_pref[kIndexWordsPerBlock];
     const uint32_t wb = blockIdx.x * kIndexWordsPerBlock;
-    const uint32_t lw0 = threadIdx.x * kWordsPerThread;
     uint64_t w[kWordsPerThread];
-    uint32_t c = 0;
 #pragma unroll
     for (int e = 0; e < kWordsPerThread; ++e) {
-        const uint32_t wi = wb + lw0 + e;
+        const uint32_t wi = wb + e * kBlock + threadIdx.x;
         w[e] = wi < n_words ? bits[wi] : 0ull;
-        c += (uint32_t)__popcll(w[e]);
     }
-    uint32_t run = block_offs[blockIdx.x] + block_exclusive_scan(c, scratch, nullptr);
+    uint32_t run = block_offs[blockIdx.x];
+    uint32_t pre[kWordsPerThread];
 #pragma unroll
     for (int e = 0; e < kWordsPerThread; ++e) {
-        const uint32_t wi = wb + lw0 + e;
-        s_words[lw0 + e] = w[e];
-        s_pref[lw0 + e] = run;
-        if (wi < n_words) prefix[wi] = run;
-        run += (uint32_t)__popcll(w[e]);
+        uint32_t total = 0;
+        pre[e] = run + block_exclusive_scan((uint32_t)__popcll(w[e]), scratch, &total);
+        run += total;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) prefix[n_words] = block_offs[gridDim.x];
-    __syncthreads();
-    // one wave per word: lane l emits position 64*word + l if its bit is set
-    const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
-    for (uint32_t lw = wave; lw < (uint32_t)kIndexWordsPerBlock; lw += kWaves) {
-        const uint64_t word = s_words[lw];
-        if (word == 0ull) continue;
-        if ((word >> lane) & 1ull) {
-            const uint32_t r = s_pref[lw] + lanes_below(word);
-            if (r < k_cap) idx[r] = (wb + lw) * 64u + lane;
+#pragma unroll
+    for (int e = 0; e < kWordsPerThread; ++e) {
+        const uint32_t wi = wb + e * kBlock + threadIdx.x;
+        if (wi < n_words) prefix[wi] = pre[e];
+        uint64_t word = w[e];
+        uint32_t r = pre[e];
+        while (word) {
+            const uint32_t b = (uint32_t)__builtin_ctzll(word);
+            if (r < k_cap) idx[r] = wi * 64u + b;
+            ++r;
+            word &= word - 1;
         }
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0) prefix[n_words] = block_offs[gridDim.x];
 }
 
 hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,

@@ -93,50 +93,79 @@ __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
     return h;
 }
 
-// Is word w (of a layer with `lwords` words) in the layer's sample?
-__device__ __forceinline__ bool sampled(uint32_t w, uint32_t lwords) {
-    return lwords <= kFullSampleWords || (word_hash(w) & ((1u << kSampleShift) - 1)) == 0;
-}
-
 // ---------------------------------------------------------------------------
 // 1. sample and window
 
-__global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restrict__ tiles,
+constexpr int kSampleTiles = 8;  // tiles per workgroup in the sampling pass
+
+// In each aligned group of 16 words of a layer, the sampled word is the one at
+// offset hash(group) & 15; layers of up to kFullSampleWords words are taken
+// whole.  A workgroup walks kSampleTiles consecutive tiles and flushes its LDS
+// row when the layer changes.
+__global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                         const LayerDesc* __restrict__ layers,
                                                         const uint32_t* __restrict__ key,
                                                         uint32_t* __restrict__ hist,
                                                         uint32_t* __restrict__ sample_words) {
     __shared__ uint32_t h[kDigit1Bins];
-    __shared__ uint32_t s_words;
-    const TileDesc t = tiles[blockIdx.x];
-    const LayerDesc L = layers[t.layer];
-    if (L.k == 0) return;  // uniform: nothing to select in this layer
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
-    if (threadIdx.x == 0) s_words = 0;
-    __syncthreads();
-    const uint32_t lwords = (L.n + 63) / 64;
-    const uint32_t lend = L.off + L.n;
+    __shared__ uint32_t s_cnt;
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
-    uint32_t nw = 0;
-    for (uint32_t w = t.w0 + wave; w < t.w1; w += kWaves) {
-        if (!sampled(w, lwords)) continue;  // wave-uniform
-        const uint32_t jj = w * 64u + lane;
-        const bool inl = jj < lend;
-        const uint32_t kv = inl ? key[jj] : 0u;
-        hist_add_wave(h, kv >> (31 - kDigit1Bits), inl);
-        nw += (uint32_t)__popcll(__ballot(inl));
-    }
-    if (lane == 0 && nw) atomicAdd(&s_words, nw);
+    const uint32_t t0 = blockIdx.x * kSampleTiles, t1 = min(t0 + kSampleTiles, n_tiles);
+    int cur = -1;
+    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+    if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
-    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
-    if (threadIdx.x == 0 && s_words) atomicAdd(&sample_words[t.layer], s_words);
+    for (uint32_t ti = t0; ti < t1; ++ti) {
+        const TileDesc t = tiles[ti];
+        const LayerDesc L = layers[t.layer];
+        if (t.layer != cur) {  // uniform
+            if (cur >= 0) {
+                __syncthreads();
+                hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins);
+                if (threadIdx.x == 0 && s_cnt) atomicAdd(&sample_words[cur], s_cnt);
+                __syncthreads();
+                for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+                if (threadIdx.x == 0) s_cnt = 0;
+                __syncthreads();
+            }
+            cur = t.layer;
+        }
+        if (L.k == 0) continue;  // nothing to select: no sample
+        const uint32_t lw0 = L.off / 64u, lwords = (L.n + 63) / 64, lend = L.off + L.n;
+        uint32_t nw = 0;
+        if (lwords <= kFullSampleWords) {
+            for (uint32_t w = t.w0 + wave; w < t.w1; w += kWaves) {
+                const uint32_t jj = w * 64u + lane;
+                const bool inl = jj < lend;
+                hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
+                nw += (uint32_t)__popcll(__ballot(inl));
+            }
+        } else {
+            // groups of 16 words: tiles start on multiples of 16 words within the layer
+            const uint32_t g0 = (t.w0 - lw0) >> kSampleShift, g1 = (t.w1 - lw0 + 15) >> kSampleShift;
+            for (uint32_t g = g0 + wave; g < g1; g += kWaves) {
+                const uint32_t w = lw0 + (g << kSampleShift) + (word_hash(lw0 + (g << kSampleShift)) & 15u);
+                const uint32_t jj = w * 64u + lane;
+                const bool inl = w < t.w1 && jj < lend;
+                hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
+                nw += (uint32_t)__popcll(__ballot(inl));
+            }
+        }
+        if (lane == 0 && nw) atomicAdd(&s_cnt, nw);
+    }
+    if (cur >= 0) {
+        __syncthreads();
+        hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins);
+        if (threadIdx.x == 0 && s_cnt) atomicAdd(&sample_words[cur], s_cnt);
+    }
 }
 
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                               const uint32_t* key, uint32_t* hist, uint32_t* sample_count) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sample_hist, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, key, hist, sample_count);
+    hipLaunchKernelGGL(k_sample_hist, dim3((n_tiles + kSampleTiles - 1) / kSampleTiles), dim3(kBlock), 0, s, tiles,
+                       n_tiles, layers, key, hist, sample_count);
     return hipGetLastError();
 }
 
@@ -150,7 +179,6 @@ __global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const Layer
                                                      uint32_t* __restrict__ hist,
                                                      const uint32_t* __restrict__ sample_count,
                                                      SelState* __restrict__ st) {
-    __shared__ uint32_t h[kDigit1Bins];
     __shared__ uint32_t suffix[kDigit1Bins];
     __shared__ uint32_t scratch[kWaves];
     const int l = layer0 + blockIdx.x;
@@ -171,30 +199,39 @@ __global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const Layer
         suffix[b] = run;
         row[b] = 0;  // leave the row clean
     }
+    __shared__ int s_hi, s_lo;
+    if (threadIdx.x == 0) {
+        s_hi = -1;
+        s_lo = -1;
+    }
+    __syncthreads();
+    const uint32_t m = sample_count[l];
+    if (L.k > 0 && m > 0) {
+        // both conditions hold on a run of buckets from 0 upward (the counts
+        // at-or-above shrink as b grows), so each is "the largest b where it
+        // holds"
+        const bool exact = m >= L.n;
+        const float sc = exact ? 1.0f : (float)L.n / (float)m;
+        const float k = (float)L.k;
+        int my_hi = -1, my_lo = -1;
+        for (int e = 0; e < per; ++e) {
+            const int b = kDigit1Bins - 1 - (threadIdx.x * per + e);
+            const float C = (float)suffix[b];
+            const float est = sc * C, dev = exact ? 0.0f : kZ * sc * sqrtf(C + 1.0f);
+            if (est + dev >= k) my_hi = max(my_hi, b);  // the k-th key may lie in b or below
+            if (est - dev >= k) my_lo = max(my_lo, b);  // the k-th key surely lies in b or above
+        }
+        if (my_hi >= 0) atomicMax(&s_hi, my_hi);
+        if (my_lo >= 0) atomicMax(&s_lo, my_lo);
+    }
     __syncthreads();
     if (threadIdx.x != 0) return;
     SelState S{};
     S.n_lo = 1;
     S.n_hi = 0;  // empty window
-    const uint32_t m = sample_count[l];
     if (L.k > 0 && m > 0) {
-        const bool exact = m >= L.n;
-        const float sc = exact ? 1.0f : (float)L.n / (float)m;
-        const float k = (float)L.k;
-        int hi = -1, lo = -1;
-        for (int b = kDigit1Bins - 1; b >= 0; --b) {
-            const float C = (float)suffix[b];
-            const float est = sc * C, dev = exact ? 0.0f : kZ * sc * sqrtf(C + 1.0f);
-            if (hi < 0 && est + dev >= k) hi = b;  // the k-th key may lie in b or below
-            if (est - dev >= k) {                   // the k-th key surely lies in b or above
-                lo = b;
-                break;
-            }
-        }
-        if (hi < 0) hi = 0;
-        if (lo < 0) lo = 0;
-        S.n_lo = (uint32_t)lo;
-        S.n_hi = (uint32_t)hi;
+        S.n_hi = (uint32_t)max(s_hi, 0);
+        S.n_lo = (uint32_t)max(s_lo, 0);
     }
     st[l] = S;
 }
@@ -239,13 +276,22 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
     uint64_t* stage = s_rec[wave];
     const bool records = cand_lo <= cand_hi;
     uint32_t n_st = 0, n_above = 0;
-    for (uint32_t w0 = t.w0 + wave * kFilterWords; w0 < t.w1; w0 += kWaves * kFilterWords) {
-        uint32_t kv[kFilterWords];
+    constexpr uint32_t kStride = kWaves * kFilterWords;
+    // the next trip's keys are loaded before this trip is processed
+    uint32_t nxt[kFilterWords];
+    auto load_keys = [&](uint32_t w0, uint32_t* kv) {
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
             kv[e] = (w0 + e < t.w1 && jj < lend) ? key[jj] : 0u;
         }
+    };
+    load_keys(t.w0 + wave * kFilterWords, nxt);
+    for (uint32_t w0 = t.w0 + wave * kFilterWords; w0 < t.w1; w0 += kStride) {
+        uint32_t kv[kFilterWords];
+#pragma unroll
+        for (int e = 0; e < kFilterWords; ++e) kv[e] = nxt[e];
+        if (w0 + kStride < t.w1) load_keys(w0 + kStride, nxt);
         uint64_t mine = 0;
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
@@ -438,7 +484,7 @@ hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_
 __global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_layers,
                                                     const LayerDesc* __restrict__ layers,
                                                     SelState* __restrict__ st, const uint32_t* __restrict__ cand_fill,
-                                                    uint32_t* __restrict__ totals) {
+                                                    uint32_t* __restrict__ vblk_offs, uint32_t* __restrict__ totals) {
     __shared__ uint32_t sv[1024];
     const int per = (n_layers + 1023) / 1024;
     const int a = threadIdx.x * per;
@@ -463,32 +509,52 @@ __global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_la
         S->cand_count = n;
         S->cand_off = layers[layer0 + i].off;
         S->vblk_off = ov;
+        vblk_offs[i] = ov;
         ov += (n + kCandChunk - 1) / kCandChunk;
     }
     if (threadIdx.x == 1023) totals[1] = sv[1023];
 }
 
 hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
-                            const uint32_t* cand_fill, uint32_t* totals) {
+                            const uint32_t* cand_fill, uint32_t* vblk_offs, uint32_t* totals) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, layer0, n_layers, layers, st, cand_fill, totals);
+    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, layer0, n_layers, layers, st, cand_fill, vblk_offs,
+                       totals);
     return hipGetLastError();
 }
 
-// Layer of virtual candidate block v: the last layer l in [layer0, layer0+n)
-// with st[l].vblk_off <= v (offsets are non-decreasing; empty layers share
-// the next layer's offset, and the search skips them because their range is
-// empty).
-__device__ int layer_of_vblock(const SelState* st, int32_t layer0, int32_t n_layers, uint32_t v) {
-    int lo = 0, hi = n_layers - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (st[layer0 + mid].vblk_off <= v) lo = mid;
-        else hi = mid - 1;
+// Virtual record blocks -> layers.  vblk_offs[i] is the first virtual block
+// of layer layer0 + i (non-decreasing; a layer without records shares its
+// successor's offset).  A workgroup copies the offsets into LDS once and
+// searches there; the layer of block v is the last i with offs[i] <= v, which
+// skips record-less layers because their range is empty.
+constexpr int kLdsLayers = 4096;
+
+struct VblockMap {
+    const uint32_t* offs;  // LDS copy, or the global array when the layer count exceeds kLdsLayers
+    int n;
+    int layer0;
+};
+
+__device__ VblockMap load_vblock_map(uint32_t* s_offs, const uint32_t* __restrict__ vblk_offs, int32_t layer0,
+                                     int32_t n_layers) {
+    if (n_layers <= kLdsLayers) {
+        for (int i = threadIdx.x; i < n_layers; i += kBlock) s_offs[i] = vblk_offs[i];
+        __syncthreads();
+        return VblockMap{s_offs, n_layers, layer0};
     }
-    return layer0 + lo;
+    return VblockMap{vblk_offs, n_layers, layer0};
 }
 
+__device__ __forceinline__ int layer_of_vblock(const VblockMap& mp, uint32_t v) {
+    int lo = 0, hi = mp.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (mp.offs[mid] <= v) lo = mid;
+        else hi = mid - 1;
+    }
+    return mp.layer0 + lo;
+}
 
 __device__ __forceinline__ int phase_bins(uint32_t phase) {
     return (phase == kPhasePos1 || phase == kPhaseKey1) ? 2048 : 1024;
@@ -500,19 +566,22 @@ __device__ __forceinline__ int phase_bins(uint32_t phase) {
 // phase's prefix.
 __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t layer0, int32_t n_layers,
                                                       const SelState* __restrict__ st,
+                                                      const uint32_t* __restrict__ vblk_offs,
                                                       const uint32_t* __restrict__ totals,
                                                       const uint64_t* __restrict__ cand,
                                                       uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[2048];
+    __shared__ uint32_t s_offs[kLdsLayers];
     __shared__ int s_layer;
     const uint32_t nv = totals[1];
+    const VblockMap mp = load_vblock_map(s_offs, vblk_offs, layer0, n_layers);
     const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
     const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
     const int nb = phase_bins(phase);
     int cur = -1;
     for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
     for (uint32_t v = v0; v < v1; ++v) {
-        if (threadIdx.x == 0) s_layer = layer_of_vblock(st, layer0, n_layers, v);
+        if (threadIdx.x == 0) s_layer = layer_of_vblock(mp, v);
         __syncthreads();
         const int l = s_layer;
         const SelState S = st[l];
@@ -559,9 +628,10 @@ __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t la
 }
 
 hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* totals, const uint64_t* cand, uint32_t* hist) {
+                            const uint32_t* vblk_offs, const uint32_t* totals, const uint64_t* cand, uint32_t* hist) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_hist, dim3(1024), dim3(kBlock), 0, s, phase, layer0, n_layers, st, totals, cand, hist);
+    hipLaunchKernelGGL(k_cand_hist, dim3(1024), dim3(kBlock), 0, s, phase, layer0, n_layers, st, vblk_offs, totals,
+                       cand, hist);
     return hipGetLastError();
 }
 
@@ -627,13 +697,16 @@ hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int
 __global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_layers,
                                                       const LayerDesc* __restrict__ layers,
                                                       const SelState* __restrict__ st,
+                                                      const uint32_t* __restrict__ vblk_offs,
                                                       const uint32_t* __restrict__ totals,
                                                       const uint64_t* __restrict__ cand,
                                                       uint64_t* __restrict__ bits) {
+    __shared__ uint32_t s_offs[kLdsLayers];
     __shared__ int s_layer;
     const uint32_t nv = totals[1];
+    const VblockMap mp = load_vblock_map(s_offs, vblk_offs, layer0, n_layers);
     for (uint32_t v = blockIdx.x; v < nv; v += gridDim.x) {
-        if (threadIdx.x == 0) s_layer = layer_of_vblock(st, layer0, n_layers, v);
+        if (threadIdx.x == 0) s_layer = layer_of_vblock(mp, v);
         __syncthreads();
         const int l = s_layer;
         const SelState S = st[l];
@@ -656,9 +729,11 @@ __global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_
 }
 
 hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* totals, const uint64_t* cand, uint64_t* bits) {
+                            const SelState* st, const uint32_t* vblk_offs, const uint32_t* totals,
+                            const uint64_t* cand, uint64_t* bits) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_mark, dim3(1024), dim3(kBlock), 0, s, layer0, n_layers, layers, st, totals, cand, bits);
+    hipLaunchKernelGGL(k_cand_mark, dim3(1024), dim3(kBlock), 0, s, layer0, n_layers, layers, st, vblk_offs, totals,
+                       cand, bits);
     return hipGetLastError();
 }
 

@@ -144,6 +144,7 @@ struct scape_ctx {
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys, keys above the window
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
+    uint32_t* d_vblk_offs = nullptr;  // per layer: first virtual record block
     // profiling
     bool prof_on = false;
     ProfSlot prof[kProfSlots]{};
@@ -168,6 +169,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
     hipFree(c->d_m_stash);
+    hipFree(c->d_vblk_offs);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -245,8 +247,8 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel), "estimate");
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
               "filter");
-    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
-    SCAPE_HIP(launch_cand_hist(s, kPhaseKey1, la, nl, c->d_sel, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_vblk_offs + la, c->d_totals), "cand_scan");
+    SCAPE_HIP(launch_cand_hist(s, kPhaseKey1, la, nl, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
     SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_hist, c->d_sel, above, c->d_cand_fill),
               "select_first");
     // sampling misses: full histogram, exact bucket, reclassification
@@ -255,12 +257,12 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
               "select_first");
     SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
               "filter_exact");
-    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_totals), "cand_scan");
+    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_vblk_offs + la, c->d_totals), "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
-        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
-    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_totals, c->d_cand, bits), "cand_mark");
+    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, bits), "cand_mark");
     return SCAPE_OK;
 }
 
@@ -373,7 +375,8 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(&c->d_counts, 2 * L, "per-layer counters")) ||
-        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash"))) {
+        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
+        (rc = dev_alloc(&c->d_vblk_offs, L, "record block offsets"))) {
         free_ctx(c);
         return rc;
     }

@@ -117,13 +117,14 @@ hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_
                                const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
                                uint64_t* cand, uint32_t* above);
 hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
-                            const uint32_t* cand_fill, uint32_t* totals);
+                            const uint32_t* cand_fill, uint32_t* vblk_offs, uint32_t* totals);
 hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
+                            const uint32_t* vblk_offs, const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
 hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* totals, const uint64_t* cand, uint64_t* bits);
+                            const SelState* st, const uint32_t* vblk_offs, const uint32_t* totals,
+                            const uint64_t* cand, uint64_t* bits);
 
 // bits
 hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);
