@@ -18,8 +18,9 @@
 //  2. k_filter reads every key once: d > hi becomes a mask bit (one wave
 //     ballot per 64-element word, written as whole words, whose popcounts add
 //     up to the exact count above the window); lo <= d <= hi becomes a
-//     (key, layer position) record in the layer's own slice of the record
-//     buffer (staged per wave in LDS, one global atomic per flush).
+//     (key, layer position) record.  Records are staged per wave in LDS and
+//     stored in the element range of their record segment (a run of tiles of
+//     one layer), with one reservation per workgroup on the segment's counter.
 //  3. A first record pass histograms d of the records; with the count above
 //     the window, k_select_first finds the exact bucket d1 of the k-th key.  If
 //     d1 is outside the window (a sampling miss), k_hist_full and
@@ -28,9 +29,11 @@
 //  4. Up to five refinement passes over the records: key bits 19..10, key
 //     bits 9..0, then - only if the threshold key T is tied beyond what is
 //     needed - position bits 30..20, 19..10, 9..0 from the smallest position
-//     upward.  Each pass is a histogram kernel and a per-layer select.
-//  5. k_cand_mark sets the bits of the selected records with 64-bit atomic ORs
-//     on the words the filter wrote.
+//     upward.  Each pass marks the records its layer's decided prefix already
+//     selects (64-bit atomic ORs on the words the filter wrote), drops those
+//     it rules out, and histograms and compacts the undecided rest, so every
+//     pass reads only what the previous one left; a per-layer select kernel
+//     then fixes the next digit.  A last pass marks what remains selected.
 //
 // Histogram rows are left zeroed by every select kernel, so a row is clean
 // for the next pass.
@@ -247,29 +250,29 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 // 2. the pass over every key
 
 constexpr int kFilterWords = 8;                 // words per wave per trip
-constexpr int kWaveStage = 1024;                // LDS records per wave (8 KB)
+constexpr int kWaveStage = 256;                 // LDS records per wave (2 KB): 8 KB per workgroup keeps occupancy high
 
-// Flush a wave's staged records to the layer's slice (one atomic per flush).
-__device__ __forceinline__ void wave_flush(uint64_t* stage, uint32_t n, uint32_t* counter, const LayerDesc& L,
+// Write n staged records of a wave at slot `first` of segment G.
+__device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, uint32_t first, const SegDesc& G,
                                            uint64_t* __restrict__ cand) {
-    if (n == 0) return;
-    uint32_t base = 0;
-    if (lane_id() == 0) base = atomicAdd(counter, n);
-    base = __shfl(base, 0, 64);
     for (uint32_t i = lane_id(); i < n; i += 64) {
-        const uint32_t slot = base + i;
-        if (slot < L.n) cand[(size_t)L.off + slot] = stage[i];
+        const uint32_t slot = first + i;
+        if (slot < G.size) cand[(size_t)G.base + slot] = stage[i];
     }
 }
 
 // Keys of a tile: digit d >= sel_from -> mask bit; cand_lo <= d <= cand_hi ->
-// record; `above` gets the number of bits set.  Every word of the tile is
-// written.  Each wave works alone: no workgroup barrier.
-__device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, uint32_t sel_from, uint32_t cand_lo,
-                                         uint32_t cand_hi, const uint32_t* __restrict__ key,
-                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
-                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+// record.  Every word of the tile is written.  The waves work alone until the
+// end of the tile, where one reservation on the segment's counter places all
+// of the workgroup's records (a wave whose staging fills up mid-tile reserves
+// on its own), and the count of bits set is added to the segment's total.
+// Must be called by every thread of the workgroup.
+__device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, const SegDesc& G, uint32_t sel_from,
+                                         uint32_t cand_lo, uint32_t cand_hi, const uint32_t* __restrict__ key,
+                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
+                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
     __shared__ uint64_t s_rec[kWaves][kWaveStage];
+    __shared__ uint32_t s_n[kWaves], s_ab[kWaves], s_base;
     const uint32_t lend = L.off + L.n;
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
@@ -305,41 +308,61 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
                 const bool cnd = inl && cand_lo <= d && d <= cand_hi;
                 const uint64_t cb = __ballot(cnd);
                 if (cb) {
+                    if (n_st > (uint32_t)(kWaveStage - 64)) {  // no room for a whole word: flush
+                        uint32_t first = 0;
+                        if (lane == 0) first = atomicAdd(&seg_fill[t.seg], n_st);
+                        wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
+                        n_st = 0;
+                    }
                     if (cnd) stage[n_st + lanes_below(cb)] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
                     n_st += (uint32_t)__popcll(cb);
                 }
             }
         }
         if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) bits[w0 + lane] = mine;
-        if (n_st > (uint32_t)(kWaveStage - kFilterWords * 64)) {  // room for one more trip
-            wave_flush(stage, n_st, &cand_fill[t.layer], L, cand);
-            n_st = 0;
-        }
     }
-    wave_flush(stage, n_st, &cand_fill[t.layer], L, cand);
-    if (lane == 0 && n_above) atomicAdd(&above[t.layer], n_above);
+    if (lane == 0) {
+        s_n[wave] = n_st;
+        s_ab[wave] = n_above;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0, ab = 0;
+        for (int q = 0; q < kWaves; ++q) {
+            tot += s_n[q];
+            ab += s_ab[q];
+        }
+        s_base = tot ? atomicAdd(&seg_fill[t.seg], tot) : 0u;
+        if (ab) atomicAdd(&seg_above[t.seg], ab);
+    }
+    __syncthreads();
+    uint32_t first = s_base;
+    for (uint32_t q = 0; q < wave; ++q) first += s_n[q];
+    wave_store(stage, n_st, first, G, cand);
 }
 
 __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
                                                    const LayerDesc* __restrict__ layers,
+                                                   const SegDesc* __restrict__ segs,
                                                    const SelState* __restrict__ st, const uint32_t* __restrict__ key,
-                                                   uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
-                                                   uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+                                                   uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
+                                                   uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
     const TileDesc t = tiles[blockIdx.x];
     const LayerDesc L = layers[t.layer];
+    const SegDesc G = segs[t.seg];
     const SelState S = st[t.layer];
     const bool win = S.n_lo <= S.n_hi && L.k > 0;
     // no window (nothing to select, or an empty sample): no bits, no records
-    key_pass(t, L, win ? S.n_hi + 1 : (uint32_t)kDigit1Bins, win ? S.n_lo : 1u, win ? S.n_hi : 0u, key, bits,
-             cand_fill, cand, above);
+    key_pass(t, L, G, win ? S.n_hi + 1 : (uint32_t)kDigit1Bins, win ? S.n_lo : 1u, win ? S.n_hi : 0u, key, bits,
+             seg_fill, cand, seg_above);
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill, uint64_t* cand,
-                         uint32_t* above) {
+                         const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, bits, cand_fill, cand,
-                       above);
+    hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, segs, st, key, bits, seg_fill,
+                       cand, seg_above);
     return hipGetLastError();
 }
 
@@ -362,21 +385,31 @@ __device__ __forceinline__ void init_found(SelState& S, uint32_t k, uint32_t buc
     }
 }
 
-// first_pass = true: hist holds the records' first digits and above[l] the
-// exact count above the window.  first_pass = false: only layers in
-// kModeFullHist, whose hist row now holds every key.
+// first_pass = true: hist holds the records' first digits, and the layer's
+// segments hold the exact count above the window.  first_pass = false: only
+// layers in kModeFullHist, whose hist row now holds every key.
 __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool first_pass,
                                                          const LayerDesc* __restrict__ layers,
+                                                         const uint32_t* __restrict__ layer_seg0,
                                                          uint32_t* __restrict__ hist, SelState* __restrict__ st,
-                                                         const uint32_t* __restrict__ above,
-                                                         uint32_t* __restrict__ cand_fill) {
+                                                         const uint32_t* __restrict__ seg_above,
+                                                         uint32_t* __restrict__ seg_fill) {
     __shared__ uint32_t scratch[kWaves];
-    __shared__ uint32_t s_bucket, s_before, s_count;
+    __shared__ uint32_t s_bucket, s_before, s_count, s_above;
     const int l = layer0 + blockIdx.x;
     const SelState old = st[l];
     if (!first_pass && old.mode != kModeFullHist) return;  // uniform
     const uint32_t k = layers[l].k;
-    const uint32_t a = first_pass ? above[l] : 0u;
+    const uint32_t sg0 = layer_seg0[l], sg1 = layer_seg0[l + 1];
+    if (threadIdx.x == 0) s_above = 0;
+    __syncthreads();
+    if (first_pass) {
+        uint32_t part = 0;
+        for (uint32_t g = sg0 + threadIdx.x; g < sg1; g += kBlock) part += seg_above[g];
+        if (part) atomicAdd(&s_above, part);
+    }
+    __syncthreads();
+    const uint32_t a = s_above;
     const bool win = old.n_lo <= old.n_hi;
     // bucket search over the row, starting from the count above the window
     const uint32_t need = (first_pass && a >= k) ? 0u : k - a;
@@ -385,9 +418,6 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
     SelState S{};
     S.n_lo = old.n_lo;
     S.n_hi = old.n_hi;
-    S.vblk_off = old.vblk_off;
-    S.cand_off = old.cand_off;
-    S.cand_count = old.cand_count;
     if (k == 0) {
         S.none = 1;
         S.phase = kPhaseDone;
@@ -398,7 +428,7 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
         S.mode = kModeFullHist;
         S.none = 1;  // provisional; the second pass decides
         S.phase = kPhaseDone;
-        cand_fill[l] = 0;
+        for (uint32_t g = sg0; g < sg1; ++g) seg_fill[g] = 0;  // the exact pass makes new records
     } else if (s_bucket == kNone) {  // cannot happen with a full row; select nothing rather than guess
         S.none = 1;
         S.phase = kPhaseDone;
@@ -411,11 +441,11 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
 }
 
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
-                               const LayerDesc* layers, uint32_t* hist, SelState* st, const uint32_t* above,
-                               uint32_t* cand_fill) {
+                               const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
+                               const uint32_t* seg_above, uint32_t* seg_fill) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, first_pass, layers, hist, st, above,
-                       cand_fill);
+    hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, first_pass, layers, layer_seg0,
+                       hist, st, seg_above, seg_fill);
     return hipGetLastError();
 }
 
@@ -452,46 +482,51 @@ hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_til
 // kModeReclassify.
 __global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restrict__ tiles,
                                                          const LayerDesc* __restrict__ layers,
+                                                         const SegDesc* __restrict__ segs,
                                                          const SelState* __restrict__ st,
                                                          const uint32_t* __restrict__ key,
-                                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ cand_fill,
-                                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ above) {
+                                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
+                                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
     const TileDesc t = tiles[blockIdx.x];
     const SelState S = st[t.layer];
     if (S.mode != kModeReclassify || S.none) return;  // uniform per workgroup
     const LayerDesc L = layers[t.layer];
+    const SegDesc G = segs[t.seg];
     if (S.all_bucket)  // keys in the threshold bucket and above, no records
-        key_pass(t, L, S.d1, 1, 0, key, bits, cand_fill, cand, above);
+        key_pass(t, L, G, S.d1, 1, 0, key, bits, seg_fill, cand, seg_above);
     else  // above the bucket: bits; in it: records
-        key_pass(t, L, S.d1 + 1, S.d1, S.d1, key, bits, cand_fill, cand, above);
+        key_pass(t, L, G, S.d1 + 1, S.d1, S.d1, key, bits, seg_fill, cand, seg_above);
 }
 
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                               const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
-                               uint64_t* cand, uint32_t* above) {
+                               const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_filter_exact, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, bits, cand_fill,
-                       cand, above);
+    hipLaunchKernelGGL(k_filter_exact, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, segs, st, key, bits,
+                       seg_fill, cand, seg_above);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // 4. records
 
-// Virtual-block numbering of each layer's records [L.off, L.off + count),
-// kCandChunk records per block.  One workgroup of 1024 threads, each owning a
-// contiguous run of layers.
-__global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_layers,
-                                                    const LayerDesc* __restrict__ layers,
-                                                    SelState* __restrict__ st, const uint32_t* __restrict__ cand_fill,
-                                                    uint32_t* __restrict__ vblk_offs, uint32_t* __restrict__ totals) {
+// Record blocks: each segment's records are cut into blocks of at most
+// kCandChunk; block v holds vb_count[v] records starting at cand[vb[v].p0].
+// One workgroup of 1024 threads numbers the blocks of the segments
+// [seg0, seg0 + n_segs), each thread owning a contiguous run of segments, and
+// writes every block's descriptor and initial count.
+__global__ __launch_bounds__(1024) void k_cand_scan(uint32_t seg0, uint32_t n_segs,
+                                                    const SegDesc* __restrict__ segs,
+                                                    const uint32_t* __restrict__ seg_fill,
+                                                    VblockDesc* __restrict__ vb, uint32_t* __restrict__ vb_count,
+                                                    uint32_t* __restrict__ totals) {
     __shared__ uint32_t sv[1024];
-    const int per = (n_layers + 1023) / 1024;
-    const int a = threadIdx.x * per;
-    const int b = min(a + per, n_layers);
+    const uint32_t per = (n_segs + 1023) / 1024;
+    const uint32_t a = threadIdx.x * per;
+    const uint32_t b = min(a + per, n_segs);
     uint32_t v = 0;
-    for (int i = a; i < b; ++i) {
-        const uint32_t n = min(cand_fill[layer0 + i], layers[layer0 + i].n);
+    for (uint32_t i = a; i < b; ++i) {
+        const uint32_t n = min(seg_fill[seg0 + i], segs[seg0 + i].size);
         v += (n + kCandChunk - 1) / kCandChunk;
     }
     sv[threadIdx.x] = v;
@@ -503,94 +538,110 @@ __global__ __launch_bounds__(1024) void k_cand_scan(int32_t layer0, int32_t n_la
         __syncthreads();
     }
     uint32_t ov = sv[threadIdx.x] - v;
-    for (int i = a; i < b; ++i) {
-        const uint32_t n = min(cand_fill[layer0 + i], layers[layer0 + i].n);
-        SelState* S = &st[layer0 + i];
-        S->cand_count = n;
-        S->cand_off = layers[layer0 + i].off;
-        S->vblk_off = ov;
-        vblk_offs[i] = ov;
-        ov += (n + kCandChunk - 1) / kCandChunk;
+    for (uint32_t i = a; i < b; ++i) {
+        const SegDesc G = segs[seg0 + i];
+        const uint32_t n = min(seg_fill[seg0 + i], G.size);
+        for (uint32_t c = 0; c < n; c += kCandChunk, ++ov) {
+            vb[ov] = VblockDesc{G.base + c, G.layer};
+            vb_count[ov] = min((uint32_t)kCandChunk, n - c);
+        }
     }
     if (threadIdx.x == 1023) totals[1] = sv[1023];
 }
 
-hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
-                            const uint32_t* cand_fill, uint32_t* vblk_offs, uint32_t* totals) {
-    if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, layer0, n_layers, layers, st, cand_fill, vblk_offs,
-                       totals);
+hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
+                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals) {
+    if (n_segs == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, seg0, n_segs, segs, seg_fill, vb, vb_count, totals);
     return hipGetLastError();
-}
-
-// Virtual record blocks -> layers.  vblk_offs[i] is the first virtual block
-// of layer layer0 + i (non-decreasing; a layer without records shares its
-// successor's offset).  A workgroup copies the offsets into LDS once and
-// searches there; the layer of block v is the last i with offs[i] <= v, which
-// skips record-less layers because their range is empty.
-constexpr int kLdsLayers = 4096;
-
-struct VblockMap {
-    const uint32_t* offs;  // LDS copy, or the global array when the layer count exceeds kLdsLayers
-    int n;
-    int layer0;
-};
-
-__device__ VblockMap load_vblock_map(uint32_t* s_offs, const uint32_t* __restrict__ vblk_offs, int32_t layer0,
-                                     int32_t n_layers) {
-    if (n_layers <= kLdsLayers) {
-        for (int i = threadIdx.x; i < n_layers; i += kBlock) s_offs[i] = vblk_offs[i];
-        __syncthreads();
-        return VblockMap{s_offs, n_layers, layer0};
-    }
-    return VblockMap{vblk_offs, n_layers, layer0};
-}
-
-__device__ __forceinline__ int layer_of_vblock(const VblockMap& mp, uint32_t v) {
-    int lo = 0, hi = mp.n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (mp.offs[mid] <= v) lo = mid;
-        else hi = mid - 1;
-    }
-    return mp.layer0 + lo;
 }
 
 __device__ __forceinline__ int phase_bins(uint32_t phase) {
     return (phase == kPhasePos1 || phase == kPhaseKey1) ? 2048 : 1024;
 }
 
-// Record histogram for one phase.  Each workgroup takes a contiguous range of
-// virtual blocks and flushes its LDS row only when the layer changes.  Only
-// layers whose state is in `phase` take part; records are filtered by the
-// phase's prefix.
-__global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t layer0, int32_t n_layers,
-                                                      const SelState* __restrict__ st,
-                                                      const uint32_t* __restrict__ vblk_offs,
+// One record under the state of its layer: 1 = selected, 2 = undecided (its
+// digit goes to the phase's histogram), 0 = not selected.  The records a
+// layer still holds are exactly the ones left undecided by its previous
+// phase, so each rule only has to split those.  Keys rank descending,
+// positions ascending.
+__device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, uint32_t kv, uint32_t jl,
+                                             uint32_t* digit) {
+    switch (phase) {
+        case kPhaseKey1:
+            *digit = kv >> 20;
+            return 2;
+        case kPhaseKey2: {
+            const uint32_t d = kv >> 20;
+            *digit = (kv >> 10) & 1023u;
+            return d > S.d1 ? 1u : (d == S.d1 ? 2u : 0u);
+        }
+        case kPhaseKey3: {
+            const uint32_t p = kv >> 10;
+            *digit = kv & 1023u;
+            return p > S.kprefix ? 1u : (p == S.kprefix ? 2u : 0u);
+        }
+        case kPhasePos1:
+            *digit = jl >> 20;
+            return kv > S.T ? 1u : (kv == S.T ? 2u : 0u);
+        case kPhasePos2: {  // every record left has key T
+            const uint32_t p = jl >> 20;
+            *digit = (jl >> 10) & 1023u;
+            return p < S.jprefix ? 1u : (p == S.jprefix ? 2u : 0u);
+        }
+        case kPhasePos3: {
+            const uint32_t p = jl >> 10;
+            *digit = jl & 1023u;
+            return p < S.jprefix ? 1u : (p == S.jprefix ? 2u : 0u);
+        }
+        default:  // done: the final rule
+            *digit = 0;
+            return (kv > S.T || (kv == S.T && jl <= S.J)) ? 1u : 0u;
+    }
+}
+
+constexpr int kRecPerThread = kCandChunk / kBlock;  // 32 records held in registers per thread
+
+// One pass over the record blocks.  phase == kPhaseKey1: histogram of every
+// record's first digit, nothing else.  Otherwise, for each block, by the
+// state of its layer: a layer in `phase` has its selected records marked,
+// its undecided ones histogrammed and compacted to the front of the block,
+// the rest dropped; a layer already done has its selected records marked and
+// the block emptied.  Each workgroup takes a contiguous range of blocks and
+// flushes its LDS histogram only when the layer changes.
+__global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const VblockDesc* __restrict__ vb,
+                                                      uint32_t* __restrict__ vb_count,
                                                       const uint32_t* __restrict__ totals,
-                                                      const uint64_t* __restrict__ cand,
-                                                      uint32_t* __restrict__ hist) {
+                                                      const LayerDesc* __restrict__ layers,
+                                                      const SelState* __restrict__ st,
+                                                      uint64_t* __restrict__ cand, uint32_t* __restrict__ hist,
+                                                      uint64_t* __restrict__ bits) {
     __shared__ uint32_t h[2048];
-    __shared__ uint32_t s_offs[kLdsLayers];
-    __shared__ int s_layer;
+    __shared__ uint32_t s_wsum[kWaves];
     const uint32_t nv = totals[1];
-    const VblockMap mp = load_vblock_map(s_offs, vblk_offs, layer0, n_layers);
     const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
     const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
-    const int nb = phase_bins(phase);
+    const bool hist_only = phase == kPhaseKey1;
+    const int nb = phase == kPhaseDone ? 0 : phase_bins(phase);
+    const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
     int cur = -1;
     for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
     for (uint32_t v = v0; v < v1; ++v) {
-        if (threadIdx.x == 0) s_layer = layer_of_vblock(mp, v);
-        __syncthreads();
-        const int l = s_layer;
+        const uint32_t cnt = vb_count[v];
+        if (cnt == 0) continue;  // uniform
+        const VblockDesc D = vb[v];
+        const int l = D.layer;
         const SelState S = st[l];
-        __syncthreads();
-        const uint32_t sphase = phase == kPhaseKey1 ? (S.mode == kModeWindow && !S.none ? kPhaseKey1 : kPhaseDone)
-                                                    : S.phase;
-        if (sphase != phase) continue;  // uniform
-        if (l != cur) {
+        if (!hist_only && S.none) {
+            if (threadIdx.x == 0) vb_count[v] = 0;
+            continue;
+        }
+        const uint32_t cph = hist_only ? kPhaseKey1 : S.phase;
+        if (cph != phase && cph != kPhaseDone) continue;  // not reached: a layer is in this phase or done
+        const bool hist_on = cph != kPhaseDone;
+        if (hist_on && l != cur) {
             if (cur >= 0) {
+                __syncthreads();
                 hist_flush(h, hist + (size_t)cur * kHistBins, nb);
                 __syncthreads();
                 for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
@@ -598,26 +649,50 @@ __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t la
             cur = l;
             __syncthreads();
         }
-        const uint32_t chunk = v - S.vblk_off;
-        const uint32_t p0 = S.cand_off + chunk * kCandChunk;
-        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, S.cand_off + S.cand_count);
-        for (uint32_t base = p0; base < p1; base += kBlock) {
-            const uint32_t p = base + threadIdx.x;
-            bool take = false;
+        const uint32_t off = layers[l].off, n = layers[l].n;
+        uint64_t rec[kRecPerThread];
+#pragma unroll
+        for (int i = 0; i < kRecPerThread; ++i) {
+            const uint32_t p = threadIdx.x + i * kBlock;
+            rec[i] = p < cnt ? cand[(size_t)D.p0 + p] : 0ull;
+        }
+        uint32_t und = 0;  // bit i: record i undecided
+#pragma unroll
+        for (int i = 0; i < kRecPerThread; ++i) {
+            if ((uint32_t)(i * kBlock) + wave * 64u >= cnt) break;  // uniform per wave
+            const uint32_t p = threadIdx.x + i * kBlock;
+            const uint32_t kv = (uint32_t)(rec[i] >> 32), jl = (uint32_t)rec[i];
             uint32_t digit = 0;
-            if (p < p1) {
-                const uint64_t rec = cand[p];
-                const uint32_t kv = (uint32_t)(rec >> 32), jl = (uint32_t)rec;
-                switch (phase) {
-                    case kPhaseKey1: take = true; digit = kv >> 20; break;
-                    case kPhaseKey2: take = (kv >> 20) == S.d1; digit = (kv >> 10) & 1023u; break;
-                    case kPhaseKey3: take = (kv >> 10) == S.kprefix; digit = kv & 1023u; break;
-                    case kPhasePos1: take = kv == S.T; digit = jl >> 20; break;
-                    case kPhasePos2: take = kv == S.T && (jl >> 20) == S.jprefix; digit = (jl >> 10) & 1023u; break;
-                    default: take = kv == S.T && (jl >> 10) == S.jprefix; digit = jl & 1023u; break;
-                }
+            const uint32_t c = p < cnt ? classify(cph, S, kv, jl, &digit) : 0u;
+            if (c == 1u && jl < n) {
+                const uint32_t jj = off + jl;
+                atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
             }
-            hist_add_wave(h, digit, take);
+            if (hist_on) hist_add_wave(h, digit, c == 2u);
+            if (c == 2u) und |= 1u << i;
+        }
+        if (!hist_only) {
+            // compaction in place: every record of the block is in registers
+            // once the barrier is passed, so the writes cannot clobber a
+            // record not yet read
+            uint32_t wsum = 0;
+#pragma unroll
+            for (int i = 0; i < kRecPerThread; ++i) wsum += (uint32_t)__popcll(__ballot((und >> i) & 1u));
+            if (lane == 0) s_wsum[wave] = wsum;
+            __syncthreads();
+            uint32_t base = 0, total = 0;
+            for (uint32_t q = 0; q < (uint32_t)kWaves; ++q) {
+                if (q < wave) base += s_wsum[q];
+                total += s_wsum[q];
+            }
+#pragma unroll
+            for (int i = 0; i < kRecPerThread; ++i) {
+                const bool u = (und >> i) & 1u;
+                const uint64_t bm = __ballot(u);
+                if (u) cand[(size_t)D.p0 + base + lanes_below(bm)] = rec[i];
+                base += (uint32_t)__popcll(bm);
+            }
+            if (threadIdx.x == 0) vb_count[v] = total;
         }
         __syncthreads();
     }
@@ -627,11 +702,11 @@ __global__ __launch_bounds__(kBlock) void k_cand_hist(uint32_t phase, int32_t la
     }
 }
 
-hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* vblk_offs, const uint32_t* totals, const uint64_t* cand, uint32_t* hist) {
-    if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_hist, dim3(1024), dim3(kBlock), 0, s, phase, layer0, n_layers, st, vblk_offs, totals,
-                       cand, hist);
+hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
+                            const uint32_t* totals, const LayerDesc* layers, const SelState* st, uint64_t* cand,
+                            uint32_t* hist, uint64_t* bits) {
+    hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kBlock), 0, s, phase, vb, vb_count, totals, layers, st, cand,
+                       hist, bits);
     return hipGetLastError();
 }
 
@@ -693,48 +768,5 @@ hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int
     return hipGetLastError();
 }
 
-
-__global__ __launch_bounds__(kBlock) void k_cand_mark(int32_t layer0, int32_t n_layers,
-                                                      const LayerDesc* __restrict__ layers,
-                                                      const SelState* __restrict__ st,
-                                                      const uint32_t* __restrict__ vblk_offs,
-                                                      const uint32_t* __restrict__ totals,
-                                                      const uint64_t* __restrict__ cand,
-                                                      uint64_t* __restrict__ bits) {
-    __shared__ uint32_t s_offs[kLdsLayers];
-    __shared__ int s_layer;
-    const uint32_t nv = totals[1];
-    const VblockMap mp = load_vblock_map(s_offs, vblk_offs, layer0, n_layers);
-    for (uint32_t v = blockIdx.x; v < nv; v += gridDim.x) {
-        if (threadIdx.x == 0) s_layer = layer_of_vblock(mp, v);
-        __syncthreads();
-        const int l = s_layer;
-        const SelState S = st[l];
-        const uint32_t off = layers[l].off;
-        const uint32_t n = layers[l].n;
-        __syncthreads();
-        if (S.none) continue;
-        const uint32_t chunk = v - S.vblk_off;
-        const uint32_t p0 = S.cand_off + chunk * kCandChunk;
-        const uint32_t p1 = min(p0 + (uint32_t)kCandChunk, S.cand_off + S.cand_count);
-        for (uint32_t p = p0 + threadIdx.x; p < p1; p += kBlock) {
-            const uint64_t rec = cand[p];
-            const uint32_t kv = (uint32_t)(rec >> 32), jl = (uint32_t)rec;
-            if (jl < n && (kv > S.T || (kv == S.T && jl <= S.J))) {
-                const uint32_t jj = off + jl;
-                atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
-            }
-        }
-    }
-}
-
-hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* vblk_offs, const uint32_t* totals,
-                            const uint64_t* cand, uint64_t* bits) {
-    if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_mark, dim3(1024), dim3(kBlock), 0, s, layer0, n_layers, layers, st, vblk_offs, totals,
-                       cand, bits);
-    return hipGetLastError();
-}
 
 }  // namespace scape

@@ -128,6 +128,8 @@ struct scape_ctx {
     std::vector<int32_t> owner;
     std::vector<TileDesc> tiles;
     std::vector<uint32_t> layer_tile0;  // first tile of each layer (L+1 entries)
+    std::vector<SegDesc> segs;
+    std::vector<uint32_t> layer_seg0;   // first record segment of each layer (L+1 entries)
     uint32_t n_words = 0;
     uint32_t n_index_blocks = 0;
     uint32_t cand_cap = 0;
@@ -136,15 +138,20 @@ struct scape_ctx {
     TileDesc* d_tiles = nullptr;
     uint32_t* d_hist = nullptr;
     SelState* d_sel = nullptr;
-    uint32_t* d_cand_fill = nullptr;
+    SegDesc* d_segs = nullptr;
+    uint32_t* d_layer_seg0 = nullptr;
+    uint32_t* d_seg_fill = nullptr;   // per segment: records
+    uint32_t* d_seg_above = nullptr;  // per segment: keys above the window
+    VblockDesc* d_vb = nullptr;       // record blocks
+    uint32_t* d_vb_count = nullptr;   // records per block
+    size_t vb_cap = 0;
     uint32_t* d_totals = nullptr;
     uint64_t* d_cand = nullptr;
     uint32_t* d_key = nullptr;
     uint32_t* d_block_sums = nullptr;
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
-    uint32_t* d_counts = nullptr;     // per layer: sampled keys, keys above the window
+    uint32_t* d_counts = nullptr;     // per layer: sampled keys
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
-    uint32_t* d_vblk_offs = nullptr;  // per layer: first virtual record block
     // profiling
     bool prof_on = false;
     ProfSlot prof[kProfSlots]{};
@@ -161,7 +168,12 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_tiles);
     hipFree(c->d_hist);
     hipFree(c->d_sel);
-    hipFree(c->d_cand_fill);
+    hipFree(c->d_segs);
+    hipFree(c->d_layer_seg0);
+    hipFree(c->d_seg_fill);
+    hipFree(c->d_seg_above);
+    hipFree(c->d_vb);
+    hipFree(c->d_vb_count);
     hipFree(c->d_totals);
     hipFree(c->d_cand);
     hipFree(c->d_key);
@@ -169,7 +181,6 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
     hipFree(c->d_m_stash);
-    hipFree(c->d_vblk_offs);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -237,32 +248,45 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
                hipStream_t s) {
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
-    const uint32_t L = (uint32_t)c->lay.L;
+    const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
+    if (ns == 0) return SCAPE_OK;  // every layer in the range is empty: no bits to set
     uint32_t* sample_count = c->d_counts;
-    uint32_t* above = c->d_counts + L;
-    SCAPE_HIP(launch_fill_u32(s, c->d_cand_fill + la, (uint64_t)nl, 0u), "fill");
+    SCAPE_HIP(launch_fill_u32(s, c->d_seg_fill + sa, (uint64_t)ns, 0u), "fill");
+    SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, sample_count + la, (uint64_t)nl, 0u), "fill");
-    SCAPE_HIP(launch_fill_u32(s, above + la, (uint64_t)nl, 0u), "fill");
     SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
     SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel), "estimate");
-    SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
+    SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
+                            c->d_seg_above),
               "filter");
-    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_vblk_offs + la, c->d_totals), "cand_scan");
-    SCAPE_HIP(launch_cand_hist(s, kPhaseKey1, la, nl, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
-    SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_hist, c->d_sel, above, c->d_cand_fill),
+    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
+              "cand_scan");
+    SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+                               c->d_hist, bits),
+              "cand_pass");
+    SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
+                                  c->d_seg_above, c->d_seg_fill),
               "select_first");
     // sampling misses: full histogram, exact bucket, reclassification
     SCAPE_HIP(launch_hist_full(s, tiles, nt, c->d_layers, c->d_sel, key, c->d_hist), "hist_full");
-    SCAPE_HIP(launch_select_first(s, la, nl, false, c->d_layers, c->d_hist, c->d_sel, above, c->d_cand_fill),
+    SCAPE_HIP(launch_select_first(s, la, nl, false, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
+                                  c->d_seg_above, c->d_seg_fill),
               "select_first");
-    SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_sel, key, bits, c->d_cand_fill, c->d_cand, above),
+    SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill,
+                                  c->d_cand, c->d_seg_above),
               "filter_exact");
-    SCAPE_HIP(launch_cand_scan(s, la, nl, c->d_layers, c->d_sel, c->d_cand_fill, c->d_vblk_offs + la, c->d_totals), "cand_scan");
+    // radix passes with shrinking record sets, then the final marking
+    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
+              "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
-        SCAPE_HIP(launch_cand_hist(s, phase, la, nl, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, c->d_hist), "cand_hist");
+        SCAPE_HIP(launch_cand_pass(s, phase, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+                                   c->d_hist, bits),
+                  "cand_pass");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
-    SCAPE_HIP(launch_cand_mark(s, la, nl, c->d_layers, c->d_sel, c->d_vblk_offs + la, c->d_totals, c->d_cand, bits), "cand_mark");
+    SCAPE_HIP(launch_cand_pass(s, kPhaseDone, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+                               c->d_hist, bits),
+              "cand_pass");
     return SCAPE_OK;
 }
 
@@ -345,11 +369,30 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
             t.layer = l;
             t.w0 = w;
             t.w1 = w + kTileWords < w1 ? w + kTileWords : w1;
-            t.pad = 0;
+            t.seg = 0;
             c->tiles.push_back(t);
         }
     }
     c->layer_tile0[c->lay.L] = (uint32_t)c->tiles.size();
+    // record segments: runs of kSegTiles tiles inside each layer
+    c->layer_seg0.assign(c->lay.L + 1, 0);
+    for (int32_t l = 0; l < c->lay.L; ++l) {
+        c->layer_seg0[l] = (uint32_t)c->segs.size();
+        for (uint32_t t0 = c->layer_tile0[l]; t0 < c->layer_tile0[l + 1]; t0 += kSegTiles) {
+            const uint32_t t1 = std::min<uint32_t>(t0 + kSegTiles, c->layer_tile0[l + 1]);
+            SegDesc g;
+            g.layer = l;
+            g.base = c->tiles[t0].w0 * 64u;
+            g.size = (c->tiles[t1 - 1].w1 - c->tiles[t0].w0) * 64u;
+            g.pad = 0;
+            for (uint32_t t = t0; t < t1; ++t) c->tiles[t].seg = (uint32_t)c->segs.size();
+            c->segs.push_back(g);
+        }
+    }
+    c->layer_seg0[c->lay.L] = (uint32_t)c->segs.size();
+    const size_t n_segs = c->segs.size();
+    // a segment of s records makes ceil(s / kCandChunk) blocks
+    c->vb_cap = (size_t)(c->lay.n_pad / kCandChunk) + n_segs + 1;
     std::vector<uint16_t> winfo(c->n_words, 0);
     for (int32_t l = 0; l < c->lay.L; ++l) {
         const int64_t off = c->lay.off[l], n = c->lay.n[l];
@@ -369,20 +412,29 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     const size_t L = (size_t)c->lay.L;
     if ((rc = dev_alloc(&c->d_layers, L, "layer table")) || (rc = dev_alloc(&c->d_tiles, c->tiles.size(), "tile table")) ||
         (rc = dev_alloc(&c->d_hist, L * kHistBins, "histograms")) || (rc = dev_alloc(&c->d_sel, L, "selection state")) ||
-        (rc = dev_alloc(&c->d_cand_fill, L, "candidate counters")) || (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
+        (rc = dev_alloc(&c->d_segs, n_segs, "segment table")) ||
+        (rc = dev_alloc(&c->d_layer_seg0, L + 1, "layer segment table")) ||
+        (rc = dev_alloc(&c->d_seg_fill, n_segs, "segment record counters")) ||
+        (rc = dev_alloc(&c->d_seg_above, n_segs, "segment bit counters")) ||
+        (rc = dev_alloc(&c->d_vb, c->vb_cap, "record blocks")) ||
+        (rc = dev_alloc(&c->d_vb_count, c->vb_cap, "record block counts")) ||
+        (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
         (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
         (rc = dev_alloc(&c->d_key, (size_t)c->lay.n_pad, "statistic keys")) ||
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
-        (rc = dev_alloc(&c->d_counts, 2 * L, "per-layer counters")) ||
-        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
-        (rc = dev_alloc(&c->d_vblk_offs, L, "record block offsets"))) {
+        (rc = dev_alloc(&c->d_counts, L, "per-layer counters")) ||
+        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash"))) {
         free_ctx(c);
         return rc;
     }
     e = hipMemcpy(c->d_layers, ld.data(), L * sizeof(LayerDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess && !c->tiles.empty())
         e = hipMemcpy(c->d_tiles, c->tiles.data(), c->tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess && n_segs)
+        e = hipMemcpy(c->d_segs, c->segs.data(), n_segs * sizeof(SegDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(c->d_layer_seg0, c->layer_seg0.data(), (L + 1) * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess && c->n_words)
         e = hipMemcpy(c->d_word_info, winfo.data(), (size_t)c->n_words * sizeof(uint16_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(c->d_hist, 0, L * kHistBins * sizeof(uint32_t));

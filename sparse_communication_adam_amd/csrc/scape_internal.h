@@ -27,11 +27,24 @@ constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kHistBins = 2048;         // histogram row per layer (>= every digit's bins)
 constexpr int kIndexWordsPerBlock = 2048;  // words per workgroup in the index passes
 constexpr int kCandChunk = 8192;        // candidate records per virtual block
+constexpr int kSegTiles = 16;           // tiles per record segment
 
 struct TileDesc {
     int32_t layer;
-    uint32_t w0;  // first word
-    uint32_t w1;  // one past the last word
+    uint32_t w0;   // first word
+    uint32_t w1;   // one past the last word
+    uint32_t seg;  // record segment holding this tile's records
+};
+
+// A record segment: up to kSegTiles consecutive tiles of one layer.  Their
+// candidate records are stored in the segment's own element range of the
+// record buffer, [base, base + size), so a segment can never overflow, and
+// the workgroups in flight at one time reserve space on many different
+// counters instead of one per layer.
+struct SegDesc {
+    int32_t layer;
+    uint32_t base;  // first element of the first tile
+    uint32_t size;  // elements covered by the segment's tiles
     uint32_t pad;
 };
 
@@ -65,12 +78,15 @@ struct SelState {
     uint32_t jprefix;     // resolved high bits of J
     uint32_t T;
     uint32_t J;
-    uint32_t cand_count;  // candidate records of this layer
-    uint32_t cand_off;    // first record of this layer
-    uint32_t vblk_off;    // first virtual candidate block of this layer
     uint32_t n_lo, n_hi;  // first-digit window the filter made records for (n_lo > n_hi: none)
     uint32_t mode;        // 0 decided by the window, 1 reclassified, 2 full histogram needed
-    uint32_t pad[3];
+    uint32_t pad[6];
+};
+
+// A block of at most kCandChunk candidate records of one layer.
+struct VblockDesc {
+    uint32_t p0;  // first record
+    int32_t layer;
 };
 
 struct WorkerPtrs {
@@ -105,26 +121,26 @@ hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_t
                               const uint32_t* key, uint32_t* hist, uint32_t* sample_count);
 hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
                            const uint32_t* sample_count, SelState* st);
+// Record segments: `segs`, `seg_fill` (records per segment) and `seg_above`
+// (keys above the window per segment) are indexed by global segment number.
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill, uint64_t* cand,
-                         uint32_t* above);
+                         const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
-                               const LayerDesc* layers, uint32_t* hist, SelState* st, const uint32_t* above,
-                               uint32_t* cand_fill);
+                               const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
+                               const uint32_t* seg_above, uint32_t* seg_fill);
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                             const SelState* st, const uint32_t* key, uint32_t* hist);
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                               const SelState* st, const uint32_t* key, uint64_t* bits, uint32_t* cand_fill,
-                               uint64_t* cand, uint32_t* above);
-hipError_t launch_cand_scan(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, SelState* st,
-                            const uint32_t* cand_fill, uint32_t* vblk_offs, uint32_t* totals);
-hipError_t launch_cand_hist(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, const SelState* st,
-                            const uint32_t* vblk_offs, const uint32_t* totals, const uint64_t* cand, uint32_t* hist);
+                               const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
+hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
+                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals);
+hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
+                            const uint32_t* totals, const LayerDesc* layers, const SelState* st, uint64_t* cand,
+                            uint32_t* hist, uint64_t* bits);
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
-hipError_t launch_cand_mark(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* vblk_offs, const uint32_t* totals,
-                            const uint64_t* cand, uint64_t* bits);
 
 // bits
 hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);

@@ -158,6 +158,53 @@ def test_mask_build_heavy_ties_across_many_candidate_blocks():
         ctx.destroy()
 
 
+def test_mask_build_more_segments_than_lds_map():
+    """Over 4096 record segments (one per tiny layer): the record passes look
+    segments up in global memory instead of their LDS copy."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(11)
+    sizes = [int(x) for x in rng.integers(1, 300, 5000)] + [600_000]
+    for keep in [(1, 10), (1, 2)]:
+        ctx = _ctx(sizes, W=2, keep=keep)
+        lay = oracle.layout(sizes, keep[0], keep[1], 2)
+        mt = (rng.standard_normal(lay.n_pad) * 1e-3).astype(np.float32)
+        out = sc.alloc_mask(ctx.layout)
+        sc.scape_mask_build(ctx, torch.from_numpy(mt).cuda(), out)
+        exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+        assert np.array_equal(u64(out.bits), exp), keep
+        idx, pre, cnt = oracle.mask_index(exp)
+        assert np.array_equal(u32(out.idx)[:cnt], idx) and np.array_equal(u32(out.block_prefix), pre)
+        ctx.destroy()
+
+
+def test_mask_build_empty_layers():
+    """Zero-size layers own no words, tiles or record segments; a shard that
+    owns only empty layers writes nothing."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(12)
+    sizes = [0, 100, 0, 0, 5000, 0]
+    ctx = _ctx(sizes, W=2, keep=(1, 10))
+    lay = oracle.layout(sizes, 1, 10, 2)
+    mt = (rng.standard_normal(lay.n_pad) * 1e-3).astype(np.float32)
+    d_mt = torch.from_numpy(mt).cuda()
+    out = sc.alloc_mask(ctx.layout)
+    sc.scape_mask_build(ctx, d_mt, out)
+    exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+    assert np.array_equal(u64(out.bits), exp)
+    owners = sc.scape_owner_map(ctx.cfg, 6)
+    for s in range(6):
+        out.bits.fill_(7)
+        sc.scape_mask_build(ctx, d_mt, out, num_shards=6, shard=s)
+        got = u64(out.bits)
+        for l in range(lay.L):
+            w0, w1 = lay.off[l] // 64, (lay.off[l] + lay.sizes[l] + 63) // 64
+            want = exp[w0:w1] if owners[l] == s else np.full(w1 - w0, 7, np.uint64)
+            assert np.array_equal(got[w0:w1], want), (s, l)
+    ctx.destroy()
+
+
 @pytest.mark.parametrize("P", [3, 32])
 def test_mask_build_one_shard_at_a_time(P):
     import torch
