@@ -9,8 +9,7 @@
 // and store of a wave is one contiguous 128- or 256-byte segment, the mask
 // word is a wave-uniform scalar, and a masked element's slot in the sparse
 // buffer is block_prefix[word] + (set bits of the word below the lane), a
-// single mbcnt.  The first radix digit of the key is histogrammed in LDS per
-// tile and flushed once per tile.
+// single mbcnt.
 //
 // Sparse pass (k_reduce_update): one lane per masked position: the W-way mean
 // of the sparse buffers in worker order, the reconstruction of the averaged
@@ -46,13 +45,10 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
     const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
     if (w >= n_words) return;
     const uint32_t lane = lane_id();
-    const uint32_t info = word_info[w];
-    const uint64_t word = cur_bits[w];
-    const uint32_t pre = cur_prefix[w];
-    const uint32_t count = info & 127u;
-    const int owner = (int)((info >> 8) & 63u);
     const int W = WT > 0 ? WT : sc.W;
-    if (lane >= count) return;  // padding lanes of a layer's last word
+    // every array holds n_pad elements, so all 64 lanes of a word may load:
+    // the element loads go out at once, beside the word's descriptors, and
+    // the padding lanes are dropped only before the stores
     const size_t j = (size_t)w * 64u + lane;
     const float mo = m[j];
     float rv[WMAX];
@@ -63,6 +59,12 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
         rv[i] = wp.r[i][j];
         gv[i] = wp.g[i][j];
     }
+    const uint32_t info = word_info[w];
+    const uint64_t word = cur_bits[w];
+    const uint32_t pre = cur_prefix[w];
+    const uint32_t count = info & 127u;
+    const int owner = (int)((info >> 8) & 63u);
+    if (lane >= count) return;  // padding lanes of a layer's last word
     const uint32_t rank = pre + lanes_below(word);
     const bool msk = ((word >> lane) & 1ull) && rank < k_cap;
     const float bm = sc.beta1 * mo;
@@ -108,47 +110,13 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
     return hipGetLastError();
 }
 
-// First-digit histogram of the statistic keys, per layer: LDS row per tile,
-// flushed once per tile (global atomics stay at a few hundred per tile).
-__global__ __launch_bounds__(kBlock) void k_key_hist(const TileDesc* __restrict__ tiles,
-                                                     const LayerDesc* __restrict__ layers,
-                                                     const uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
-    constexpr int E = kWordsPerWaveIter;
-    __shared__ uint32_t h[kDigit1Bins];
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
-    __syncthreads();
-    const TileDesc t = tiles[blockIdx.x];
-    const LayerDesc L = layers[t.layer];
-    const uint32_t lend = L.off + L.n;
-    const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
-    for (uint32_t w0 = t.w0 + wave * E; w0 < t.w1; w0 += kWaves * E) {
-        uint32_t kk[E];
-        bool inl[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const uint32_t jj = (w0 + e) * 64u + lane;
-            inl[e] = w0 + e < t.w1 && jj < lend;
-            kk[e] = inl[e] ? key[jj] : 0u;
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) hist_add_wave(h, kk[e] >> (31 - kDigit1Bits), inl[e]);
-    }
-    __syncthreads();
-    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
-}
-
-hipError_t launch_key_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                           const uint32_t* key, uint32_t* hist) {
-    if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_key_hist, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, key, hist);
-    return hipGetLastError();
-}
-
 // Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
 // by the workgroup size so that idx, the sparse buffers and the m stash are
 // read contiguously), every load issued before the arithmetic.
-constexpr int kUpdatePer = 4;
+#ifndef SCAPE_UPDATE_PER
+#define SCAPE_UPDATE_PER 4
+#endif
+constexpr int kUpdatePer = SCAPE_UPDATE_PER;
 
 template <int WT>
 __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepScalars sc, float* __restrict__ x,

@@ -11,13 +11,9 @@ namespace scape {
 
 // ---------------------------------------------------------------------------
 // Launch geometry.  A "tile" is a run of whole 64-element words inside one
-// layer; the elementwise and filter kernels give one tile to a workgroup.
+// layer; the key-sampling and filter kernels give one tile to a workgroup.
 constexpr int kBlock = 256;             // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
-#ifndef SCAPE_EF_WORDS
-#define SCAPE_EF_WORDS 8
-#endif
-constexpr int kWordsPerWaveIter = SCAPE_EF_WORDS;  // words a wave handles per loop trip
 #ifndef SCAPE_TILE_WORDS
 #define SCAPE_TILE_WORDS 512
 #endif
