@@ -68,6 +68,8 @@ def lib():
         L.oracle_step.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                                   vp, vp, vp]
         L.oracle_step.restype = i64
+        L.oracle_dense_step.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp]
+        L.oracle_dense_step.restype = None
         _lib = L
     return _lib
 
@@ -274,3 +276,18 @@ def step(lay: Layout, hp: Hyper, st: State, grads: Sequence[np.ndarray], cur_wor
                             _p(cur_words), _p(sp), _p(bbar), cap, _p(key), _p(nw), _p(nidx), _p(npre))
     assert cnt >= 0
     return StepOut([s[:cnt] for s in sent], bbar[:cnt], key, nw, nidx[:int(npre[-1])], npre, int(cnt))
+
+
+def dense_step(lay: Layout, hp: Hyper, x: np.ndarray, m: np.ndarray, v: np.ndarray,
+               grads: Sequence[np.ndarray]) -> None:
+    """One dense AdamS step (the comparison baseline); updates x, m, v in place."""
+    W = len(grads)
+    grads = [np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
+    for a in (x, m, v):
+        assert a.dtype == np.float32 and a.size == lay.n_pad and a.flags.c_contiguous
+    for g in grads:
+        assert g.size == lay.n_pad
+    prob = _Problem(lay.L, _p(lay.off), _p(lay.sizes), _p(lay.k), _p(lay.owner), lay.n_pad, W,
+                    hp.beta1, hp.beta2, hp.lr, hp.eps, hp.weight_decay)
+    gp = _ptrs(grads)
+    lib().oracle_dense_step(ctypes.byref(prob), _p(x), _p(m), _p(v), _p(gp))

@@ -34,6 +34,11 @@
  *                 position; keys are the bit patterns of |candidate|.
  *   R-layout      tensors are concatenated, each starting on a 64-element
  *                 boundary; mask bits are LSB-first in 64-bit words.
+ *   R-dense       the dense AdamS step the pages compare against is plain
+ *                 data parallelism: the workers' gradients are averaged
+ *                 (sum in order 0..W-1, then division by W) on every element
+ *                 and that average drives the same AdamS update as
+ *                 R-normaliser, with no residual and no mask.
  *
  * Precision: every floating-point value is fp32, every operation rounds to
  * nearest even, and nothing is contracted into a fused multiply-add (the file
@@ -43,7 +48,9 @@
  *
  * Parity pins (tests/test_oracle_pins.py) tie each function to something
  * outside itself: brute-force ranking, library packbits/cumsum, exact dyadic
- * arithmetic, a dense fp64 average, a dense fp64 AdamS, power-of-two scaling.
+ * arithmetic, a dense fp64 average, a dense fp64 AdamS, power-of-two scaling;
+ * the dense step by a hand-worked dyadic example, by agreement with the
+ * SCAPE step under a full mask, and by exact scaling and sign symmetries.
  * The AdamS normaliser form itself (R-normaliser) is a reading the pages do
  * not fix: parity unpinned for that form beyond its algebraic special cases.
  */
@@ -308,4 +315,39 @@ int64_t oracle_step(const oracle_problem* P, float* x, float* m, float* v, float
 
     free(pos);
     return cnt;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The dense AdamS step (the comparison baseline)                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One dense AdamS step on W simulated workers: the baseline the pages measure
+ * SCAPE against ([abs]: per-step speedup over dense AdamS; TS Results, Per-Step
+ * Speedup).  Reading R-dense: on every element of every layer the workers'
+ * bf16 gradients are averaged in worker order, and the average drives the
+ * AdamS update of R-normaliser.  Padding elements are not touched.
+ */
+void oracle_dense_step(const oracle_problem* P, float* x, float* m, float* v, const uint16_t* const* g) {
+    const float b1 = P->beta1, b2 = P->beta2;
+    const float c1 = 1.0f - b1;
+    const float c2 = 1.0f - b2;
+    for (int32_t l = 0; l < P->L; ++l) {
+        for (int64_t e = 0; e < P->n[l]; ++e) {
+            const int64_t j = P->off[l] + e;
+            /* the dense all-reduce of the gradients, as a mean (R-dense) */
+            float s = bf16_to_f32(g[0][j]);
+            for (int32_t i = 1; i < P->W; ++i) s = s + bf16_to_f32(g[i][j]);
+            const float gbar = s / (float)P->W;
+            /* AdamS: the new first moment, the normaliser from the previous
+             * first moment and the gradient, then the parameter update */
+            const float mo = m[j];
+            const float mn = b1 * mo + c1 * gbar;
+            v[j] = b2 * (mo * mo) + c2 * (gbar * gbar);
+            m[j] = mn;
+            float u = mn / (sqrtf(v[j]) + P->eps);
+            if (P->weight_decay != 0.0f) u = u + P->weight_decay * x[j];
+            x[j] = x[j] - P->lr * u;
+        }
+    }
 }

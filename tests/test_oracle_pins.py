@@ -3,7 +3,9 @@
 Each test checks the oracle against something it does not compute itself: a
 hand-worked dyadic example, brute-force ranking, numpy's packbits/cumsum/
 lexsort, exact rational arithmetic, an fp64 dense average, an fp64 dense AdamS,
-or a metamorphic relation.  The passages behind each rule are cited in
+or a metamorphic relation.  The dense AdamS step (the comparison baseline) is
+pinned by a hand-worked dyadic example, by its agreement with the SCAPE step
+under a full mask, and by exact scaling and sign symmetries.  The passages behind each rule are cited in
 oracle/scape_oracle.c.
 """
 import os
@@ -221,9 +223,9 @@ def test_reduce_sums_in_worker_order():
 # the step
 
 
-def _parse_golden():
+def _parse_golden(name="worked_step.txt"):
     d = {}
-    for line in open(os.path.join(GOLDEN, "worked_step.txt")):
+    for line in open(os.path.join(GOLDEN, name)):
         line = line.split("#")[0].strip()
         if "=" in line:
             k, v = [p.strip() for p in line.split("=", 1)]
@@ -516,3 +518,131 @@ def test_sub_layout_reproduces_full_run_on_its_layers():
                 assert np.array_equal(x[fs], y[ssl])
             assert np.array_equal(oracle.unpack(of.next_words, full.n_pad)[fs],
                                   oracle.unpack(os_.next_words, sub.n_pad)[ssl])
+
+
+# --------------------------------------------------------------------------
+# the dense AdamS step (comparison baseline)
+
+
+def _bf16_layer(lay, vals_by_layer):
+    g = np.zeros(lay.n_pad, np.uint16)
+    for l, vals in enumerate(vals_by_layer):
+        g[lay.off[l]:lay.off[l] + len(vals)] = bf16_bits(vals)
+    return g
+
+
+@pytest.mark.parametrize("run,steps", [("A", 2), ("B", 1)])
+def test_dense_golden_worked_steps(run, steps):
+    d = _parse_golden("dense_adams.txt")
+    n, W = int(d[f"{run}.n"]), int(d[f"{run}.W"])
+    lay = oracle.layout([n], 1, 1, W)
+    hp = oracle.Hyper(float(d[f"{run}.beta1"]), float(d[f"{run}.beta2"]), float(d[f"{run}.lr"]),
+                      float(d[f"{run}.eps"]), float(d[f"{run}.wd"]))
+    x = np.zeros(lay.n_pad, np.float32)
+    x[:n] = _vals(d[f"{run}.x0"])
+    m, v = np.zeros_like(x), np.zeros_like(x)
+    for t in range(1, steps + 1):
+        gs = [_bf16_layer(lay, [_vals(d[f"{run}.step{t}.g{i}"])]) for i in range(W)]
+        oracle.dense_step(lay, hp, x, m, v, gs)
+        assert np.array_equal(m[:n], _vals(d[f"{run}.step{t}.m"])), t
+        assert np.array_equal(v[:n], _vals(d[f"{run}.step{t}.v"])), t
+        assert np.array_equal(x[:n], _vals(d[f"{run}.step{t}.x"])), t
+        assert not x[n:].any() and not m[n:].any() and not v[n:].any()  # padding untouched
+
+
+def test_dense_agrees_with_scape_under_a_full_mask():
+    """With every position masked at every step and zero residuals, the SCAPE
+    step reaches m, v, x through the synchronized first-moment buffer and the
+    reconstructed gradient; the dense step computes them from the averaged
+    gradient directly.  Both are fp32 evaluations of the same exact values, so
+    they differ by at most the sum of their rounding-error bounds (the bound of
+    the keep=1 pin, propagated over the steps, taken for each side)."""
+    W, T = 4, 5
+    wl = synth.ragged()
+    lay = oracle.layout(wl.layer_sizes, 1, 1, W)
+    hp = oracle.Hyper()
+    rng = np.random.default_rng(21)
+    x0 = (rng.standard_normal(lay.n_pad) * 0.02).astype(np.float32)
+    inl = layer_mask(lay)
+    x0[~inl] = 0
+    cur = oracle.pack(inl.astype(np.uint8))
+    grads = {t: random_grads(rng, lay, W) for t in range(1, T + 1)}
+    hist = _run(lay, W, T, hp, lambda t: grads[t], cur=cur, x=x0)
+    x, m, v = x0.copy(), np.zeros_like(x0), np.zeros_like(x0)
+    b1, b2 = np.float64(np.float32(0.9)), np.float64(np.float32(0.95))
+    c1, c2 = 1 - b1, 1 - b2
+    lr, eps = np.float64(np.float32(1e-3)), np.float64(np.float32(1e-8))
+    Em, Ex = np.zeros(lay.n_pad), np.zeros(lay.n_pad)
+    m64 = np.zeros(lay.n_pad)
+    for t, (prev, gs, _, out, post) in enumerate(hist, 1):
+        oracle.dense_step(lay, hp, x, m, v, gs)
+        # magnitudes for the bound, from the exact values in fp64
+        g = np.array([bf16_to_f64(gi) for gi in gs])
+        gbar = g.mean(0)
+        mo = m64
+        v64 = b2 * mo * mo + c2 * gbar * gbar
+        m64 = b1 * mo + c1 * gbar
+        mt_abs = b1 * np.abs(mo) + c1 * np.abs(g).max(0)
+        Em_new = b1 * Em + (W + 3) * U * mt_abs
+        Eg = (Em_new + b1 * Em + 3 * U * (np.abs(m64) + b1 * np.abs(mo))) / c1 + U * np.abs(gbar)
+        Ev = 2 * b2 * np.abs(mo) * Em + 2 * c2 * np.abs(gbar) * Eg + c2 * Eg * Eg + 4 * U * v64
+        den = np.sqrt(v64) + eps
+        Eq = Em_new / den + np.abs(m64) * (Ev / (2 * np.sqrt(v64) + 1e-300)) / den ** 2 + 4 * U * np.abs(m64) / den
+        Ex = Ex + lr * Eq + 2 * U * (np.abs(post.x) + lr * np.abs(m64) / den)
+        Em = Em_new
+        sl = inl
+        assert np.all(np.abs(m[sl] - post.m[sl]) <= 4 * Em[sl]), t
+        assert np.all(np.abs(v[sl] - post.v[sl]) <= 4 * Ev[sl]), t
+        assert np.all(np.abs(x[sl] - post.x[sl]) <= 4 * Ex[sl]), t
+        assert not x[~inl].any() and not m[~inl].any() and not v[~inl].any()
+    # the two are different computations, not the same one twice
+    assert not np.array_equal(m[inl], hist[-1][4].m[inl])
+    # and the bound is tight enough to matter
+    assert np.median(Ex[inl] / np.abs(x[inl])) < 1e-5
+
+
+def test_dense_power_of_two_scaling_is_exact():
+    """Gradients times 2^p from a zero start with eps=0: m scales by 2^p, v by
+    4^p, and the update m/sqrt(v) - hence x - is unchanged, bit for bit."""
+    W = 3
+    lay = oracle.layout([1000, 37, 4096], 1, 1, W)
+    rng = np.random.default_rng(22)
+    hp = oracle.Hyper(eps=0.0)
+    x0 = (rng.standard_normal(lay.n_pad) * 0.02).astype(np.float32)
+    gseq = [random_grads(rng, lay, W) for _ in range(3)]
+    ref = (x0.copy(), np.zeros_like(x0), np.zeros_like(x0))
+    for gs in gseq:
+        oracle.dense_step(lay, hp, *ref, gs)
+    for p in (-5, 3):
+        got = (x0.copy(), np.zeros_like(x0), np.zeros_like(x0))
+        for gs in gseq:
+            sg = [bf16_bits((gi.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** p)) for gi in gs]
+            oracle.dense_step(lay, hp, *got, sg)
+        assert np.array_equal(ref[0], got[0], equal_nan=True)
+        assert np.array_equal(ref[1] * np.float32(2.0 ** p), got[1])
+        assert np.array_equal(ref[2] * np.float32(4.0 ** p), got[2])
+
+
+def test_dense_sign_symmetry_is_exact():
+    """Negated gradients from x = m = v = 0 give negated m and x and the same
+    v (round to nearest even is symmetric), and a single worker's step sees its
+    own gradient unchanged by the mean."""
+    W = 2
+    lay = oracle.layout([3000, 65], 1, 1, W)
+    rng = np.random.default_rng(23)
+    hp = oracle.Hyper()
+    gseq = [random_grads(rng, lay, W) for _ in range(3)]
+    a = [np.zeros(lay.n_pad, np.float32) for _ in range(3)]
+    b = [np.zeros(lay.n_pad, np.float32) for _ in range(3)]
+    for gs in gseq:
+        oracle.dense_step(lay, hp, *a, gs)
+        oracle.dense_step(lay, hp, *b, [gi ^ np.uint16(0x8000) for gi in gs])
+    assert np.array_equal(a[0], -b[0]) and np.array_equal(a[1], -b[1]) and np.array_equal(a[2], b[2])
+    # W = 2 with identical workers equals W = 1: the mean of equal values is exact
+    one = [np.zeros(lay.n_pad, np.float32) for _ in range(3)]
+    two = [np.zeros(lay.n_pad, np.float32) for _ in range(3)]
+    for gs in gseq:
+        oracle.dense_step(lay, hp, *one, [gs[0]])
+        oracle.dense_step(lay, hp, *two, [gs[0], gs[0]])
+    for u, w in zip(one, two):
+        assert np.array_equal(u, w)
