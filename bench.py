@@ -13,7 +13,9 @@ Prints one JSON line.  `value` is parameters per second (N / step time).
 timed with HIP events on the step's stream: algorithmic bytes per launch
 divided by its mean duration, against the 8 TB/s HBM peak.  `cpu_baseline`
 is the oracle (plain single-threaded C) timed on this host on a bounded
-sample of the same workload.
+sample of the same workload.  `dense_adams` times the dense AdamS step (the
+baseline the pages measure SCAPE against) on the same workload, state and
+gradient batches, with HIP events on its stream.
 """
 from __future__ import annotations
 
@@ -101,6 +103,42 @@ def cpu_baseline(wl, steps_needed: int = 2):
             "seconds": times[-1]}
 
 
+def dense_alg_bytes(N: int, W: int) -> float:
+    """Algorithmic bytes of one dense AdamS step: read the W bf16 gradients,
+    read m and x, write m, v and x."""
+    return N * (2 * W + 20)
+
+
+def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> dict:
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
+                         owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
+                         weight_decay=wl.weight_decay)
+    ctx = sc.scape_init(cfg)
+    x = torch.zeros(n_pad, dtype=torch.float32, device="cuda")
+    synth.params_flat_gpu(wl, layer_offset, x)
+    m, v = torch.zeros_like(x), torch.zeros_like(x)
+    for s in range(warmup):
+        sc.scape_dense_step(ctx, x, m, v, sets[s % len(sets)])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(steps):
+        sc.scape_dense_step(ctx, x, m, v, sets[(warmup + s) % len(sets)])
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    ctx.destroy()
+    del x, m, v
+    torch.cuda.empty_cache()
+    N = wl.numel
+    gbps = dense_alg_bytes(N, wl.W) / (ms * 1e-3) / 1e9
+    return {"kernel": "scape_k_dense_adams", "ms_per_step": ms, "params_per_s": N / (ms * 1e-3),
+            "alg_bytes_per_step": dense_alg_bytes(N, wl.W), "alg_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
+
+
 def copy_bandwidth(nbytes: int = 4 << 30) -> float:
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -126,6 +164,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(CPU_SAMPLE))
     ap.add_argument("--grad-sets", type=int, default=2, help="distinct gradient batches cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -191,8 +230,16 @@ def main() -> int:
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
     step_gbps = step_b / (ms * 1e-3) / 1e9
     traffic = counter_traffic(wl.name)
+    offsets, n_pad = list(lay.layer_offset), lay.n_pad
     state.destroy()
-    del sets, state
+    del state
+    torch.cuda.empty_cache()
+    dense = None
+    if not args.no_dense:
+        dense = dense_adams(wl, offsets, n_pad, sets, args.steps, args.warmup)
+        dense["scape_step_over_dense"] = ms / dense["ms_per_step"]
+        log(f"dense AdamS step: {dense['ms_per_step']:.3f} ms ({dense['alg_GBps']:.0f} GB/s algorithmic)")
+    del sets
     torch.cuda.empty_cache()
     copy_gbps = copy_bandwidth()
     log(f"device copy: {copy_gbps:.0f} GB/s")
@@ -211,6 +258,8 @@ def main() -> int:
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic},
     }
+    if dense is not None:
+        result["dense_adams"] = dense
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

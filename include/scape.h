@@ -169,6 +169,25 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
                void* stream);
 
 /*
+ * One dense AdamS step on W simulated workers: the baseline the pages measure
+ * SCAPE's per-step speedup against ([abs]; [TS-4] Per-Step Speedup).  The
+ * pages do not define it; the reading taken is plain data parallelism, in
+ * which the dense all-reduce of the gradients drives the same AdamS update as
+ * scape_step.  Per element j of every tensor, with mo = m[j] before the step:
+ *   gbar  = ((float(g_0[j]) + float(g_1[j])) + ... + float(g_{W-1}[j])) / W
+ *   m_new = beta1*mo + (1-beta1)*gbar
+ *   v[j]  = beta2*mo^2 + (1-beta2)*gbar^2
+ *   m[j]  = m_new
+ *   x[j]  = x[j] - lr*(m_new/(sqrt(v[j]) + eps) + weight_decay*x[j])
+ * No residual and no mask.  Padding elements (past the end of a tensor) are
+ * not touched.  Same fp32 rules as scape_step.
+ * Arguments (device, n_pad elements): x, m, v fp32 state, updated in place;
+ *   g[W] bfloat16 gradient bits of each worker, read only.
+ * Errors: INVALID_ARG, ALIGN, HIP.
+ */
+int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream);
+
+/*
  * Mask build alone, from first-moment statistics mtilde (fp32, n_pad): per
  * layer, the k_l positions with the largest |mtilde| (bit pattern order),
  * ties to the lower position ([TS-2] Partitioned Mask Synchronization).

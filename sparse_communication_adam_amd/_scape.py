@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "scape_init": [cfgp, ctypes.POINTER(vp)],
             "scape_destroy": [vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
+            "scape_dense_step": [vp, vp, vp, vp, vp, vp],
             "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
             "scape_mask_index": [vp, maskp, vp],
             "scape_pack": [vp, i64, vp, vp],
@@ -267,6 +268,18 @@ def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next:
     c, nx = cur._c(), next._c()
     _check(lib().scape_step(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
                             _stream(stream)))
+
+
+def scape_dense_step(ctx: Context, x, m, v, g: Sequence, stream=None) -> None:
+    import torch
+    n, W = ctx.layout.n_pad, ctx.cfg.workers
+    if len(g) != W:
+        raise ValueError(f"g needs {W} entries")
+    xp = _dev(x, torch.float32, n, "x")
+    mp = _dev(m, torch.float32, n, "m")
+    vp = _dev(v, torch.float32, n, "v")
+    gp = _ptr_array([_dev(t, (torch.int16, torch.bfloat16, torch.uint16), n, f"g[{i}]") for i, t in enumerate(g)])
+    _check(lib().scape_dense_step(ctx.handle, xp, mp, vp, gp, _stream(stream)))
 
 
 def scape_mask_build(ctx: Context, mtilde, out: Mask, num_shards: int = 0, shard: int = -1, stream=None) -> None:

@@ -11,6 +11,10 @@
 // buffer is block_prefix[word] + (set bits of the word below the lane), a
 // single mbcnt.
 //
+// Dense AdamS pass (k_dense_adams): the comparison baseline, the same one-shot
+// layout as the dense SCAPE pass: the W gradients averaged in worker order and
+// the AdamS update of x, m, v on every element.
+//
 // Sparse pass (k_reduce_update): one lane per masked position: the W-way mean
 // of the sparse buffers in worker order, the reconstruction of the averaged
 // gradient from that one buffer, the AdamS normaliser, and the m/v/x update.
@@ -107,6 +111,69 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
                                cur_prefix, k_cap, key, m_stash);
     }
 #undef SCAPE_EF_CASE
+    return hipGetLastError();
+}
+
+// Dense AdamS step: one 64-element word per wave, four words per workgroup,
+// every load issued before the word's descriptor is consulted (all arrays
+// hold n_pad elements); the padding lanes of a layer's last word store
+// nothing.
+template <int WT>
+__global__ __launch_bounds__(kBlock) void k_dense_adams(const uint16_t* __restrict__ word_info, uint32_t n_words,
+                                                        WorkerPtrs wp, StepScalars sc, float* __restrict__ x,
+                                                        float* __restrict__ m, float* __restrict__ v) {
+    constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
+    const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
+    if (w >= n_words) return;
+    const uint32_t lane = lane_id();
+    const int W = WT > 0 ? WT : sc.W;
+    const size_t j = (size_t)w * 64u + lane;
+    const float mo = m[j];
+    const float xo = x[j];
+    uint16_t gv[WMAX];
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+        if (i >= W) break;
+        gv[i] = wp.g[i][j];
+    }
+    const uint32_t count = word_info[w] & 127u;
+    if (lane >= count) return;  // padding lanes of a layer's last word
+    float s = bf16_bits_to_f32(gv[0]);
+#pragma unroll
+    for (int i = 1; i < WMAX; ++i) {
+        if (i >= W) break;
+        s = s + bf16_bits_to_f32(gv[i]);
+    }
+    const float gbar = s / (float)W;
+    const float mn = sc.beta1 * mo + sc.c1 * gbar;
+    const float vv = sc.beta2 * (mo * mo) + sc.c2 * (gbar * gbar);
+    float u = mn / (sqrtf(vv) + sc.eps);
+    if (sc.wd != 0.0f) u = u + sc.wd * xo;
+    v[j] = vv;
+    m[j] = mn;
+    x[j] = xo - sc.lr * u;
+}
+
+hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
+                              const StepScalars& sc, float* x, float* m, float* v) {
+    if (n_words == 0) return hipSuccess;
+    const dim3 grid((n_words + kWaves - 1) / kWaves);
+#define SCAPE_DENSE_CASE(WV)                                                                                  \
+    case WV:                                                                                                  \
+        hipLaunchKernelGGL(k_dense_adams<WV>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, x, m, v); \
+        break;
+    switch (sc.W) {
+        SCAPE_DENSE_CASE(1)
+        SCAPE_DENSE_CASE(2)
+        SCAPE_DENSE_CASE(3)
+        SCAPE_DENSE_CASE(4)
+        SCAPE_DENSE_CASE(8)
+        SCAPE_DENSE_CASE(16)
+        SCAPE_DENSE_CASE(32)
+        default:
+            hipLaunchKernelGGL(k_dense_adams<0>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, x, m, v);
+    }
+#undef SCAPE_DENSE_CASE
     return hipGetLastError();
 }
 

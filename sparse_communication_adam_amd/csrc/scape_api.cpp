@@ -520,6 +520,35 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
     return SCAPE_OK;
 }
 
+int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
+        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    if (!g) return fail(SCAPE_ERR_INVALID_ARG, "g must not be NULL");
+    const int W = ctx->cfg.workers;
+    WorkerPtrs wp{};
+    for (int i = 0; i < W; ++i) {
+        if (!g[i]) return fail(SCAPE_ERR_INVALID_ARG, "g[%d] is NULL", i);
+        if (!aligned(g[i], 16)) return fail(SCAPE_ERR_ALIGN, "g[%d] must be 16-byte aligned", i);
+        wp.g[i] = g[i];
+    }
+    int rc;
+    if ((rc = check_device(ctx))) return rc;
+    StepScalars sc;
+    sc.beta1 = ctx->cfg.beta1;
+    sc.beta2 = ctx->cfg.beta2;
+    sc.c1 = 1.0f - ctx->cfg.beta1;
+    sc.c2 = 1.0f - ctx->cfg.beta2;
+    sc.lr = ctx->cfg.lr;
+    sc.eps = ctx->cfg.eps;
+    sc.wd = ctx->cfg.weight_decay;
+    sc.W = W;
+    SCAPE_HIP(launch_dense_adams((hipStream_t)stream, ctx->d_word_info, ctx->n_words, wp, sc, x, m, v),
+              "dense_adams");
+    return SCAPE_OK;
+}
+
 int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, int32_t shard, const scape_mask* out,
                      void* stream) {
     if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");

@@ -107,6 +107,8 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
                                 float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
                                 uint32_t n_words, uint32_t n_pad, uint32_t k_cap);
+hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
+                              const StepScalars& sc, float* x, float* m, float* v);
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
                                    const float* mtilde, uint32_t* key);
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);

@@ -237,3 +237,60 @@ def release(run) -> None:
     gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+def run_dense_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, W=None,
+                     weight_decay=None) -> Dict[str, int]:
+    """The dense AdamS step through the C ABI against the oracle's, on every
+    layer or on the sampled ones, for every step: x, m and v within the parity
+    bar (bit-exact expected), padding untouched."""
+    import dataclasses
+    import torch
+    import sparse_communication_adam_amd as sc
+    W = W or wl.W
+    if weight_decay is not None:
+        wl = dataclasses.replace(wl, weight_decay=weight_decay)
+    full = oracle_layout(wl, None, W)
+    tensors = list(range(len(wl.tensors))) if sample is None else list(sample)
+    lay = full if sample is None else oracle.sub_layout(full, tensors)
+    log(f"dense {wl.name}: W={W} L={full.L} n_pad={full.n_pad} steps={steps} wd={wl.weight_decay} "
+        f"oracle layers={len(tensors)} ({lay.n_pad} elements)")
+    ctx = sc.scape_init(scape_config(wl, None, W))
+    offs = ctx.layout.layer_offset
+    assert list(offs) == full.off.tolist()
+    n = full.n_pad
+    x = torch.zeros(n, dtype=torch.float32, device="cuda")
+    synth.params_flat_gpu(wl, offs, x)
+    m = torch.zeros_like(x)
+    v = torch.zeros_like(x)
+    x_pad0 = x.clone()
+    grads = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(W)]
+    ox = synth.params_flat(wl, lay.off, lay.n_pad, tensors)
+    om, ov = np.zeros(lay.n_pad, np.float32), np.zeros(lay.n_pad, np.float32)
+    hp = hyper(wl)
+    stats: Dict[str, int] = {}
+    for t in range(1, steps + 1):
+        for i, g in enumerate(grads):
+            synth.grads_flat_gpu(wl, offs, g, t, i)
+        sc.scape_dense_step(ctx, x, m, v, grads)
+        oracle.dense_step(lay, hp, ox, om, ov, oracle_inputs(wl, lay, tensors, t, W))
+        torch.cuda.synchronize()
+        for a, l in enumerate(tensors):
+            fs = slice(int(full.off[l]), int(full.off[l] + full.sizes[l]))
+            os_ = slice(int(lay.off[a]), int(lay.off[a] + lay.sizes[a]))
+            tag = f"dense step {t} layer {l} ({wl.tensors[l].name})"
+            check_float(f"{tag} x", to_np(x[fs]), ox[os_], stats)
+            check_float(f"{tag} m", to_np(m[fs]), om[os_], stats)
+            check_float(f"{tag} v", to_np(v[fs]), ov[os_], stats)
+            pad = slice(fs.stop, int((fs.stop + 63) // 64 * 64))
+            assert not to_np(m[pad]).any() and not to_np(v[pad]).any(), f"{tag}: padding written"
+            assert np.array_equal(to_np(x[pad]), to_np(x_pad0[pad])), f"{tag}: padding written"
+        log(f"dense step {t}: sampled ok (float values so far {stats['float_values']}, "
+            f"not bit-exact {stats['float_not_bitexact']})")
+    ctx.destroy()
+    del x, m, v, grads, x_pad0
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return stats
