@@ -70,6 +70,8 @@ def lib():
         L.oracle_step.restype = i64
         L.oracle_dense_step.argtypes = [ctypes.POINTER(_Problem), vp, vp, vp, vp]
         L.oracle_dense_step.restype = None
+        L.oracle_union_mask.argtypes = [i32, vp, vp, vp, i32, vp, vp]
+        L.oracle_union_mask.restype = None
         _lib = L
     return _lib
 
@@ -196,6 +198,18 @@ def mask_from_keys(lay: Layout, keys: np.ndarray, shard: int = -1, owner_map=Non
         words = np.zeros(lay.n_words, np.uint64)
     lib().oracle_mask_from_keys(lay.L, _p(lay.off), _p(lay.sizes), _p(lay.k), _p(own), shard,
                                 _p(keys), _p(words))
+    return words
+
+
+def union_mask(lay: Layout, keys: Sequence[np.ndarray]) -> np.ndarray:
+    """The fill-in union: each worker's per-layer top-k of its own keys over
+    every layer, OR-ed into one packed mask."""
+    keys = [np.ascontiguousarray(kk, dtype=np.uint32) for kk in keys]
+    for kk in keys:
+        assert kk.size == lay.n_pad
+    words = np.zeros(lay.n_words, np.uint64)
+    kp = _ptrs(keys)
+    lib().oracle_union_mask(lay.L, _p(lay.off), _p(lay.sizes), _p(lay.k), len(keys), _p(kp), _p(words))
     return words
 
 

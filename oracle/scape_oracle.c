@@ -34,6 +34,10 @@
  *                 position; keys are the bit patterns of |candidate|.
  *   R-layout      tensors are concatenated, each starting on a 64-element
  *                 boundary; mask bits are LSB-first in 64-bit words.
+ *   R-fillin      the "fill-in" alternative to partitioned masks: every
+ *                 worker ranks every layer on its own first-moment candidate
+ *                 (the same per-layer top-k and tie rule as R-k) and the
+ *                 global mask is the union of the workers' masks.
  *   R-dense       the dense AdamS step the pages compare against is plain
  *                 data parallelism: the workers' gradients are averaged
  *                 (sum in order 0..W-1, then division by W) on every element
@@ -50,7 +54,9 @@
  * outside itself: brute-force ranking, library packbits/cumsum, exact dyadic
  * arithmetic, a dense fp64 average, a dense fp64 AdamS, power-of-two scaling;
  * the dense step by a hand-worked dyadic example, by agreement with the
- * SCAPE step under a full mask, and by exact scaling and sign symmetries.
+ * SCAPE step under a full mask, and by exact scaling and sign symmetries;
+ * the fill-in union by a brute-force ranking in the tests, by its bounds
+ * (k to W*k set bits per layer), monotonicity in W and disjoint supports.
  * The AdamS normaliser form itself (R-normaliser) is a reading the pages do
  * not fix: parity unpinned for that form beyond its algebraic special cases.
  */
@@ -182,6 +188,23 @@ void oracle_mask_from_keys(int32_t L, const int64_t* off, const int64_t* n, cons
         for (int64_t j = 0; j < n[l]; ++j)
             if (sel[j]) words[(off[l] + j) / 64] |= (uint64_t)1 << ((off[l] + j) % 64);
         free(sel);
+    }
+}
+
+/* The fill-in union (R-fillin): worker i's per-layer top-k of its own keys
+ * keys[i] over every layer, OR-ed into words (the caller zeroes words first).
+ * This is what Partitioned Mask Synchronization (TS-2) avoids: when every
+ * worker builds a mask for every layer, the union fills in as W grows. */
+void oracle_union_mask(int32_t L, const int64_t* off, const int64_t* n, const int64_t* k, int32_t W,
+                       const uint32_t* const* keys, uint64_t* words) {
+    for (int32_t i = 0; i < W; ++i) {
+        for (int32_t l = 0; l < L; ++l) {
+            uint8_t* sel = (uint8_t*)malloc((size_t)(n[l] > 0 ? n[l] : 1));
+            oracle_topk(keys[i] + off[l], n[l], k[l], sel);
+            for (int64_t j = 0; j < n[l]; ++j)
+                if (sel[j]) words[(off[l] + j) / 64] |= (uint64_t)1 << ((off[l] + j) % 64);
+            free(sel);
+        }
     }
 }
 

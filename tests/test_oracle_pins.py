@@ -646,3 +646,82 @@ def test_dense_sign_symmetry_is_exact():
         oracle.dense_step(lay, hp, *two, [gs[0], gs[0]])
     for u, w in zip(one, two):
         assert np.array_equal(u, w)
+
+
+# --------------------------------------------------------------------------
+# the fill-in union (each worker ranks every layer; the masks are OR-ed)
+
+
+def _union_brute(lay, keys):
+    sel = np.zeros(lay.n_pad, bool)
+    for kk in keys:
+        for l in range(lay.L):
+            o, n, k = int(lay.off[l]), int(lay.sizes[l]), int(lay.k[l])
+            order = sorted(range(n), key=lambda j: (-int(kk[o + j]), j))
+            for j in order[:k]:
+                sel[o + j] = True
+    return sel
+
+
+def test_union_hand_example_with_ties():
+    """Two workers, one layer of 6, k = 2 (keep 1/3).  Worker 0's keys
+    [5,5,5,1,1,1] tie three ways at the top: positions 0 and 1 win.  Worker 1's
+    [0,0,9,9,9,0]: positions 2 and 3.  The union is {0,1,2,3}: four bits, the
+    fill-in of two masks of two."""
+    lay = oracle.layout([6], 1, 3, 2)
+    k0 = np.zeros(lay.n_pad, np.uint32)
+    k1 = np.zeros(lay.n_pad, np.uint32)
+    k0[:6] = [5, 5, 5, 1, 1, 1]
+    k1[:6] = [0, 0, 9, 9, 9, 0]
+    got = oracle.unpack(oracle.union_mask(lay, [k0, k1]), lay.n_pad)
+    assert np.flatnonzero(got).tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("W", [1, 2, 5])
+@pytest.mark.parametrize("levels", [3, 50, 1 << 31])
+def test_union_matches_brute_force(W, levels):
+    rng = np.random.default_rng(W * 1000 + levels % 997)
+    lay = oracle.layout([1, 7, 64, 130, 333], 1, 4, W)
+    keys = [rng.integers(0, levels, lay.n_pad).astype(np.uint32) for _ in range(W)]
+    got = oracle.unpack(oracle.union_mask(lay, keys), lay.n_pad).astype(bool)
+    assert np.array_equal(got, _union_brute(lay, keys))
+
+
+def test_union_bounds_and_monotone_in_workers():
+    """Per layer the union has between k and min(n, W*k) bits, and adding a
+    worker never removes one."""
+    rng = np.random.default_rng(31)
+    lay = oracle.layout([5000, 777, 64, 1], 1, 20, 8)
+    keys = [rng.integers(0, 1 << 20, lay.n_pad).astype(np.uint32) for _ in range(8)]
+    prev = None
+    for w in range(1, 9):
+        bits = oracle.unpack(oracle.union_mask(lay, keys[:w]), lay.n_pad).astype(bool)
+        for l in range(lay.L):
+            c = int(bits[lay.off[l]:lay.off[l] + lay.sizes[l]].sum())
+            assert lay.k[l] <= c <= min(lay.sizes[l], w * lay.k[l]), (w, l, c)
+            assert not bits[lay.off[l] + lay.sizes[l]:lay.off[l] + (lay.sizes[l] + 63) // 64 * 64].any()
+        if prev is not None:
+            assert np.all(bits[prev])
+        prev = bits
+
+
+def test_union_of_disjoint_and_of_identical_workers():
+    """Worker i's largest keys on its own block of k positions: the union is
+    exactly the first W*k positions.  W identical workers: the union is one
+    worker's mask."""
+    W, k = 4, 25
+    n = 3 * W * k
+    lay = oracle.layout([n], k, n, W)
+    assert lay.k.tolist() == [k]
+    rng = np.random.default_rng(32)
+    keys = []
+    for i in range(W):
+        kk = np.zeros(lay.n_pad, np.uint32)
+        kk[:n] = rng.integers(0, 1000, n)
+        kk[i * k:(i + 1) * k] = rng.integers(10_000, 20_000, k)
+        keys.append(kk)
+    got = oracle.unpack(oracle.union_mask(lay, keys), lay.n_pad)
+    assert np.flatnonzero(got).tolist() == list(range(W * k))
+    one = oracle.union_mask(lay, keys[:1])
+    assert np.array_equal(oracle.union_mask(lay, [keys[0]] * W), one)
+    assert np.array_equal(one, oracle.mask_from_keys(lay, keys[0]))
