@@ -15,7 +15,10 @@ divided by its mean duration, against the 8 TB/s HBM peak.  `cpu_baseline`
 is the oracle (plain single-threaded C) timed on this host on a bounded
 sample of the same workload.  `dense_adams` times the dense AdamS step (the
 baseline the pages measure SCAPE against) on the same workload, state and
-gradient batches, with HIP events on its stream.
+gradient batches, with HIP events on its stream.  `fill_in` measures the
+alternative the pages' partitioned masks avoid: the union of per-worker masks
+over every layer, its density as workers are added, and the time to add one
+worker's mask.
 """
 from __future__ import annotations
 
@@ -33,14 +36,15 @@ sys.path.insert(0, ROOT)
 METRIC = "fused SCAPE step: params/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "llama-1.75b"
-# oracle sample per workload: a contiguous run of tensors (one transformer block
-# or its equivalent), timed on the host for one step with a built mask
+# oracle sample per workload: a contiguous run of tensors (a few transformer
+# blocks or their equivalent, about 10-15 s of single-threaded oracle work per
+# step), timed on the host for one step with a built mask
 CPU_SAMPLE = {
     "single-1024x1024": [0],
-    "gpt-345m": list(range(2, 14)),
-    "llama-0.55b": list(range(1, 7)),
-    "llama-1.75b": list(range(1, 7)),
-    "adversarial-ties": list(range(1, 18)),
+    "gpt-345m": list(range(2, 2 + 12 * 6)),        # six blocks, 75.6M params, W = 8
+    "llama-0.55b": list(range(1, 1 + 6 * 3)),      # three blocks, 84.9M params, W = 8
+    "llama-1.75b": list(range(1, 1 + 6 * 3)),      # three blocks, 151.8M params, W = 4
+    "adversarial-ties": list(range(1, 1 + 17 * 4)),  # four blocks, 16.8M params, W = 32
 }
 
 
@@ -139,6 +143,45 @@ def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> 
             "alg_bytes_per_step": dense_alg_bytes(N, wl.W), "alg_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
+FILL_IN_WORKERS = (1, 2, 4, 8, 16, 32)
+
+
+def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
+    """Union density of per-worker per-layer top-k masks over every layer as
+    workers are added.  Worker i's statistic is its step-1 gradient widened
+    to fp32: at step 1 the candidate is (1 - beta1) times the gradient, so its
+    per-layer ranking is the gradient's."""
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    ctx = sc.scape_init(cfg)
+    g = torch.zeros(n_pad, dtype=torch.int16, device="cuda")
+    acc = torch.zeros(n_pad // 64, dtype=torch.int64, device="cuda")
+    mask = sc.alloc_mask(ctx.layout)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    add_ms, density = [], {}
+    for i in range(max(FILL_IN_WORKERS)):
+        synth.grads_flat_gpu(wl, layer_offset, g, 1, i)
+        mt = g.view(torch.bfloat16).float()
+        ev0.record()
+        sc.scape_mask_union_add(ctx, mt, acc)
+        ev1.record()
+        torch.cuda.synchronize()
+        add_ms.append(ev0.elapsed_time(ev1))
+        del mt
+        if i + 1 in FILL_IN_WORKERS:
+            mask.bits.copy_(acc)
+            sc.scape_mask_index(ctx, mask)
+            torch.cuda.synchronize()
+            density[str(i + 1)] = int(mask.block_prefix[-1].item()) / wl.numel
+    k_total = ctx.layout.k_total
+    ctx.destroy()
+    del g, acc, mask
+    torch.cuda.empty_cache()
+    return {"statistic": "workers' step-1 gradients (independent draws)", "one_mask_density": k_total / wl.numel,
+            "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
+
+
 def copy_bandwidth(nbytes: int = 4 << 30) -> float:
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -165,6 +208,7 @@ def main() -> int:
     ap.add_argument("--grad-sets", type=int, default=2, help="distinct gradient batches cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
+    ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -241,6 +285,10 @@ def main() -> int:
         log(f"dense AdamS step: {dense['ms_per_step']:.3f} ms ({dense['alg_GBps']:.0f} GB/s algorithmic)")
     del sets
     torch.cuda.empty_cache()
+    fill = None
+    if not args.no_fill_in:
+        fill = fill_in(wl, cfg, offsets, n_pad)
+        log("fill-in union density by workers: " + ", ".join(f"{w}: {d:.4%}" for w, d in fill["union_density"].items()))
     copy_gbps = copy_bandwidth()
     log(f"device copy: {copy_gbps:.0f} GB/s")
 
@@ -260,6 +308,8 @@ def main() -> int:
     }
     if dense is not None:
         result["dense_adams"] = dense
+    if fill is not None:
+        result["fill_in"] = fill
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -202,6 +202,22 @@ int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_
 int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, int32_t shard,
                      const scape_mask* out, void* stream);
 
+/*
+ * The "fill-in" alternative to partitioned masks, one worker at a time: the
+ * per-layer top-k of |mtilde| (same rule as scape_mask_build) over every
+ * layer, OR-ed into acc_bits.  [TS-2] Partitioned Mask Synchronization names
+ * the union of such per-worker global masks, which fills in as workers are
+ * added, as what owner-partitioned masks avoid; this entry point measures it.
+ * Usage: zero acc_bits (n_pad/64 words), call once per worker with that
+ * worker's first-moment candidates, then scape_mask_index on a mask whose
+ * bits are acc_bits: block_prefix[n_pad/64] is the size of the union (idx
+ * keeps at most k_total positions).
+ * Arguments: mtilde fp32 device (n_pad); acc_bits device (n_pad/64 words),
+ *   read and written.
+ * Errors: INVALID_ARG, ALIGN, HIP.
+ */
+int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits, void* stream);
+
 /* idx and block_prefix of a mask from its bits (all n_pad/64 words).  At most
  * k_total positions are stored in idx; block_prefix counts every set bit.
  * Errors: INVALID_ARG, ALIGN, HIP. */

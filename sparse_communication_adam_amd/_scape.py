@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "scape_destroy": [vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_dense_step": [vp, vp, vp, vp, vp, vp],
+            "scape_mask_union_add": [vp, vp, vp, vp],
             "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
             "scape_mask_index": [vp, maskp, vp],
             "scape_pack": [vp, i64, vp, vp],
@@ -287,6 +288,13 @@ def scape_mask_build(ctx: Context, mtilde, out: Mask, num_shards: int = 0, shard
     mp = _dev(mtilde, torch.float32, ctx.layout.n_pad, "mtilde")
     o = out._c()
     _check(lib().scape_mask_build(ctx.handle, mp, num_shards, shard, ctypes.byref(o), _stream(stream)))
+
+
+def scape_mask_union_add(ctx: Context, mtilde, acc_bits, stream=None) -> None:
+    import torch
+    mp = _dev(mtilde, torch.float32, ctx.layout.n_pad, "mtilde")
+    ap = _dev(acc_bits, torch.int64, ctx.layout.n_pad // 64, "acc_bits")
+    _check(lib().scape_mask_union_add(ctx.handle, mp, ap, _stream(stream)))
 
 
 def scape_mask_index(ctx: Context, mask: Mask, stream=None) -> None:

@@ -118,6 +118,20 @@ hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_wor
     return hipGetLastError();
 }
 
+// acc |= src over n_words words (the fill-in union of per-worker masks).
+__global__ __launch_bounds__(kBlock) void k_or_words(const uint64_t* __restrict__ src, uint64_t* __restrict__ acc,
+                                                     uint32_t n_words) {
+    for (uint32_t w = blockIdx.x * kBlock + threadIdx.x; w < n_words; w += gridDim.x * kBlock) acc[w] |= src[w];
+}
+
+hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, uint32_t n_words) {
+    if (n_words == 0) return hipSuccess;
+    uint32_t blocks = (n_words + kBlock - 1) / kBlock;
+    if (blocks > 16384u) blocks = 16384u;
+    hipLaunchKernelGGL(k_or_words, dim3(blocks), dim3(kBlock), 0, s, src, acc, n_words);
+    return hipGetLastError();
+}
+
 // Pack: one wave per word, lane l tests element 64*word + l.
 __global__ __launch_bounds__(kBlock) void k_pack(const uint8_t* __restrict__ pred, uint64_t n, uint64_t n_words,
                                                  uint64_t* __restrict__ bits) {

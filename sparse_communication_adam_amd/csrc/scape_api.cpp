@@ -142,6 +142,7 @@ struct scape_ctx {
     uint32_t* d_layer_seg0 = nullptr;
     uint32_t* d_seg_fill = nullptr;   // per segment: records
     uint32_t* d_seg_above = nullptr;  // per segment: keys above the window
+    uint64_t* d_union_bits = nullptr;  // one worker's mask before it is OR-ed into a fill-in union
     VblockDesc* d_vb = nullptr;       // record blocks
     uint32_t* d_vb_count = nullptr;   // records per block
     size_t vb_cap = 0;
@@ -172,6 +173,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_layer_seg0);
     hipFree(c->d_seg_fill);
     hipFree(c->d_seg_above);
+    hipFree(c->d_union_bits);
     hipFree(c->d_vb);
     hipFree(c->d_vb_count);
     hipFree(c->d_totals);
@@ -424,7 +426,8 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(&c->d_counts, L, "per-layer counters")) ||
-        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash"))) {
+        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
+        (rc = dev_alloc(&c->d_union_bits, (size_t)c->n_words, "union staging bits"))) {
         free_ctx(c);
         return rc;
     }
@@ -582,6 +585,23 @@ int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, in
     SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, wa, wb, mtilde, ctx->d_key), "keys");
     if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key, out->bits, s))) return rc;
     if (all && (rc = run_index(ctx, out, s))) return rc;
+    return SCAPE_OK;
+}
+
+int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits, void* stream) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!mtilde || !acc_bits) return fail(SCAPE_ERR_INVALID_ARG, "mtilde and acc_bits must not be NULL");
+    if (!aligned(mtilde, 16) || !aligned(acc_bits, 16))
+        return fail(SCAPE_ERR_ALIGN, "mtilde and acc_bits must be 16-byte aligned");
+    int rc;
+    if ((rc = check_device(ctx))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int32_t L = ctx->lay.L;
+    if (L == 0 || ctx->tiles.empty()) return SCAPE_OK;
+    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
+    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, 0, ctx->n_words, mtilde, ctx->d_key), "keys");
+    if ((rc = run_select(ctx, 0, L, 0, (uint32_t)ctx->tiles.size(), ctx->d_key, ctx->d_union_bits, s))) return rc;
+    SCAPE_HIP(launch_or_words(s, ctx->d_union_bits, acc_bits, ctx->n_words), "or_words");
     return SCAPE_OK;
 }
 

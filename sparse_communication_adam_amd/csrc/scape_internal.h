@@ -145,6 +145,7 @@ hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_wo
 hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blocks);
 hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,
                              uint32_t* idx, uint32_t k_cap, uint32_t* prefix);
+hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, uint32_t n_words);
 hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits);
 hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred);
 
