@@ -18,7 +18,8 @@ baseline the pages measure SCAPE against) on the same workload, state and
 gradient batches, with HIP events on its stream.  `fill_in` measures the
 alternative the pages' partitioned masks avoid: the union of per-worker masks
 over every layer, its density as workers are added, and the time to add one
-worker's mask.
+worker's mask.  `offload` times the step with the W residuals in pinned host
+memory (scape_step_offload), whose rate is bound by the PCIe copies.
 """
 from __future__ import annotations
 
@@ -143,6 +144,32 @@ def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> 
             "alg_bytes_per_step": dense_alg_bytes(N, wl.W), "alg_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
+def offload_step(cfg, wl, sets, steps: int, warmup: int) -> dict:
+    """The step with the residuals in pinned host memory: W*N*4 bytes copied
+    in and out over PCIe per step."""
+    import torch
+    import synth
+    from sparse_communication_adam_amd.state import ScapeState
+    state = ScapeState(cfg, offload=True)
+    lay = state.layout
+    synth.params_flat_gpu(wl, lay.layer_offset, state.x)
+    torch.cuda.synchronize()
+    for s in range(warmup):
+        state.step(sets[s % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        state.step(sets[(warmup + s) % len(sets)])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    state.destroy()
+    del state
+    torch.cuda.empty_cache()
+    pcie = 2 * wl.W * lay.n_pad * 4
+    return {"ms_per_step": ms, "params_per_s": wl.numel / (ms * 1e-3), "residuals_on_host_GB": pcie / 2 / 1e9,
+            "pcie_bytes_per_step": pcie, "pcie_GBps": pcie / (ms * 1e-3) / 1e9, "steps": steps, "warmup": warmup}
+
+
 FILL_IN_WORKERS = (1, 2, 4, 8, 16, 32)
 
 
@@ -209,6 +236,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
+    ap.add_argument("--no-offload", action="store_true", help="skip the host-residual (offload) step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -283,6 +311,10 @@ def main() -> int:
         dense = dense_adams(wl, offsets, n_pad, sets, args.steps, args.warmup)
         dense["scape_step_over_dense"] = ms / dense["ms_per_step"]
         log(f"dense AdamS step: {dense['ms_per_step']:.3f} ms ({dense['alg_GBps']:.0f} GB/s algorithmic)")
+    offload = None
+    if not args.no_offload:
+        offload = offload_step(cfg, wl, sets, 3, 2)
+        log(f"offloaded-residual step: {offload['ms_per_step']:.1f} ms ({offload['pcie_GBps']:.1f} GB/s over PCIe)")
     del sets
     torch.cuda.empty_cache()
     fill = None
@@ -310,6 +342,8 @@ def main() -> int:
         result["dense_adams"] = dense
     if fill is not None:
         result["fill_in"] = fill
+    if offload is not None:
+        result["offload"] = offload
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

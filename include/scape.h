@@ -169,6 +169,28 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
                void* stream);
 
 /*
+ * scape_step with the W residuals in pinned host memory: CPU offloading of
+ * the residual buffers with double buffering ([TS-2] Memory Optimization).
+ * Same computation and results as scape_step, bit for bit.  The residuals
+ * move through the GPU in chunks of 4,194,304 elements: host -> one of two
+ * device staging slots on a copy-in stream, the dense pass on `stream`,
+ * staging -> host on a copy-out stream, the two slots alternating so the
+ * PCIe copies of one chunk overlap the dense pass of the other.  The rest of
+ * the step does not touch the residuals, so the last copies back overlap it.
+ * The step is complete on `stream` only once every residual chunk is back.
+ * Arguments as scape_step, except r_host: a host array of W pointers to
+ * pinned host memory (hipHostMalloc, or a pinned torch tensor), n_pad fp32
+ * each, 16-byte aligned; pageable memory also works but copies synchronously.
+ * The host must not touch r_host while a step is in flight.  The context
+ * holds the staging slots (2 x W x 16 MiB at most) and the two copy streams
+ * (default priority) from scape_init.
+ * Errors: as scape_step.
+ */
+int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* const* r_host, const uint16_t* const* g,
+                       const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+                       void* stream);
+
+/*
  * One dense AdamS step on W simulated workers: the baseline the pages measure
  * SCAPE's per-step speedup against ([abs]; [TS-4] Per-Step Speedup).  The
  * pages do not define it; the reading taken is plain data parallelism, in

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "scape_init": [cfgp, ctypes.POINTER(vp)],
             "scape_destroy": [vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
+            "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_dense_step": [vp, vp, vp, vp, vp, vp],
             "scape_mask_union_add": [vp, vp, vp, vp],
             "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
@@ -182,6 +183,24 @@ def _dev(t, dtype, numel: Optional[int], name: str) -> int:
     return t.data_ptr()
 
 
+def _host(t, dtype, numel: Optional[int], name: str) -> int:
+    """A pinned host tensor (the offloaded residuals)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be in host memory (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be pinned host memory (pin_memory=True)")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
 def _ptr_array(ptrs) -> ctypes.Array:
     return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
 
@@ -269,6 +288,25 @@ def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next:
     c, nx = cur._c(), next._c()
     _check(lib().scape_step(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
                             _stream(stream)))
+
+
+def scape_step_offload(ctx: Context, x, m, v, r_host: Sequence, g: Sequence, cur: Mask, next: Mask,
+                       sparse_bufs: Sequence, key_out=None, stream=None) -> None:
+    """scape_step with the residuals in pinned host tensors."""
+    import torch
+    n, W, k = ctx.layout.n_pad, ctx.cfg.workers, ctx.layout.k_total
+    if len(r_host) != W or len(g) != W or len(sparse_bufs) != W:
+        raise ValueError(f"r_host, g and sparse_bufs need {W} entries each")
+    xp = _dev(x, torch.float32, n, "x")
+    mp = _dev(m, torch.float32, n, "m")
+    vp = _dev(v, torch.float32, n, "v")
+    rp = _ptr_array([_host(t, torch.float32, n, f"r_host[{i}]") for i, t in enumerate(r_host)])
+    gp = _ptr_array([_dev(t, (torch.int16, torch.bfloat16, torch.uint16), n, f"g[{i}]") for i, t in enumerate(g)])
+    bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
+    kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
+    c, nx = cur._c(), next._c()
+    _check(lib().scape_step_offload(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
+                                    _stream(stream)))
 
 
 def scape_dense_step(ctx: Context, x, m, v, g: Sequence, stream=None) -> None:

@@ -120,6 +120,8 @@ constexpr int kProfSlots = 64;
 
 }  // namespace
 
+constexpr uint32_t kOffloadChunkWords = 1u << 16;  // 4,194,304 elements per residual transfer
+
 struct scape_ctx {
     int device = 0;
     scape_config cfg{};
@@ -153,6 +155,12 @@ struct scape_ctx {
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
+    // residual offload: two staging slots of W chunks, a copy-in and a copy-out stream
+    float* d_stage = nullptr;         // [2][W][chunk_words * 64]
+    uint32_t chunk_words = 0;
+    hipStream_t s_in = nullptr, s_out = nullptr;
+    hipEvent_t ev_in[2] = {}, ev_k[2] = {}, ev_out[2] = {};
+    bool offload_ready = false;
     // profiling
     bool prof_on = false;
     ProfSlot prof[kProfSlots]{};
@@ -183,6 +191,14 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
     hipFree(c->d_m_stash);
+    hipFree(c->d_stage);
+    for (int b = 0; b < 2; ++b) {
+        if (c->ev_in[b]) hipEventDestroy(c->ev_in[b]);
+        if (c->ev_k[b]) hipEventDestroy(c->ev_k[b]);
+        if (c->ev_out[b]) hipEventDestroy(c->ev_out[b]);
+    }
+    if (c->s_in) hipStreamDestroy(c->s_in);
+    if (c->s_out) hipStreamDestroy(c->s_out);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -298,6 +314,126 @@ int run_index(scape_ctx* c, const scape_mask* mk, hipStream_t s) {
     SCAPE_HIP(launch_index_emit(s, mk->bits, c->n_words, c->d_block_sums, mk->idx, (uint32_t)c->lay.k_total,
                                 mk->block_prefix),
               "index_emit");
+    return SCAPE_OK;
+}
+
+// The dense pass with the residuals in pinned host memory (Memory
+// Optimization, gist.science Technical Summary s.2: CPU offloading with double
+// buffering).  Words are independent in the dense pass, so it runs chunk by
+// chunk on the step's stream with every pointer offset to the chunk; the W
+// residual chunks move host -> staging slot on s_in and back on s_out, two
+// slots alternating so that the copies of one chunk overlap the dense pass of
+// the other.  The events order, per slot: copy in -> dense pass -> copy out ->
+// the next copy into that slot.
+int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const StepScalars& sc, const float* m,
+               const scape_mask* cur, uint32_t k_cap, uint32_t* key, hipStream_t s) {
+    const int W = c->cfg.workers;
+    const uint32_t cw = c->chunk_words;
+    const size_t slot_elems = (size_t)cw * 64;
+    uint32_t chunk = 0;
+    for (uint32_t w0 = 0; w0 < c->n_words; w0 += cw, ++chunk) {
+        const uint32_t nw = std::min(cw, c->n_words - w0);
+        const int b = (int)(chunk & 1u);
+        const size_t j0 = (size_t)w0 * 64, bytes = (size_t)nw * 64 * sizeof(float);
+        float* stage = c->d_stage + (size_t)b * W * slot_elems;
+        SCAPE_HIP(hipStreamWaitEvent(c->s_in, c->ev_out[b], 0), "offload wait");
+        for (int i = 0; i < W; ++i)
+            SCAPE_HIP(hipMemcpyAsync(stage + (size_t)i * slot_elems, r_host[i] + j0, bytes, hipMemcpyHostToDevice,
+                                     c->s_in),
+                      "offload copy in");
+        SCAPE_HIP(hipEventRecord(c->ev_in[b], c->s_in), "offload event");
+        SCAPE_HIP(hipStreamWaitEvent(s, c->ev_in[b], 0), "offload wait");
+        WorkerPtrs cp = wp;
+        for (int i = 0; i < W; ++i) {
+            cp.r[i] = stage + (size_t)i * slot_elems;
+            cp.g[i] = wp.g[i] + j0;
+        }
+        SCAPE_HIP(launch_ef_compact(s, c->d_word_info + w0, nw, cp, sc, m + j0, cur->bits + w0,
+                                    cur->block_prefix + w0, k_cap, key + j0, c->d_m_stash),
+                  "ef_compact");
+        SCAPE_HIP(hipEventRecord(c->ev_k[b], s), "offload event");
+        SCAPE_HIP(hipStreamWaitEvent(c->s_out, c->ev_k[b], 0), "offload wait");
+        for (int i = 0; i < W; ++i)
+            SCAPE_HIP(hipMemcpyAsync(r_host[i] + j0, stage + (size_t)i * slot_elems, bytes, hipMemcpyDeviceToHost,
+                                     c->s_out),
+                      "offload copy out");
+        SCAPE_HIP(hipEventRecord(c->ev_out[b], c->s_out), "offload event");
+    }
+    return SCAPE_OK;
+}
+
+int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
+                const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+                void* stream, bool r_on_host) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
+        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    if (!r || !g || !sparse_bufs) return fail(SCAPE_ERR_INVALID_ARG, "r, g and sparse_bufs must not be NULL");
+    const int W = ctx->cfg.workers;
+    for (int i = 0; i < W; ++i) {
+        if (!r[i] || !g[i]) return fail(SCAPE_ERR_INVALID_ARG, "r[%d] or g[%d] is NULL", i, i);
+        if (!aligned(r[i], 16) || !aligned(g[i], 16))
+            return fail(SCAPE_ERR_ALIGN, "r[%d] and g[%d] must be 16-byte aligned", i, i);
+        if (ctx->lay.k_total > 0) {
+            if (!sparse_bufs[i]) return fail(SCAPE_ERR_INVALID_ARG, "sparse_bufs[%d] is NULL", i);
+            if (!aligned(sparse_bufs[i], 4)) return fail(SCAPE_ERR_ALIGN, "sparse_bufs[%d] must be 4-byte aligned", i);
+        }
+    }
+    if (key_out && !aligned(key_out, 16)) return fail(SCAPE_ERR_ALIGN, "key_out must be 16-byte aligned");
+    int rc;
+    if ((rc = check_mask(cur, true, "cur")) || (rc = check_mask(next, true, "next"))) return rc;
+    if (cur->bits == next->bits || cur->idx == next->idx || cur->block_prefix == next->block_prefix)
+        return fail(SCAPE_ERR_STATE, "next must not alias cur (the mask built now is used at the next step)");
+    if ((rc = check_device(ctx))) return rc;
+    if (r_on_host && !ctx->offload_ready && ctx->n_words > 0)
+        return fail(SCAPE_ERR_STATE, "the context has no offload resources");
+
+    hipStream_t s = (hipStream_t)stream;
+    WorkerPtrs wp{};
+    for (int i = 0; i < W; ++i) {
+        wp.r[i] = r_on_host ? nullptr : r[i];
+        wp.g[i] = g[i];
+        wp.b[i] = ctx->lay.k_total > 0 ? sparse_bufs[i] : nullptr;
+    }
+    StepScalars sc;
+    sc.beta1 = ctx->cfg.beta1;
+    sc.beta2 = ctx->cfg.beta2;
+    sc.c1 = 1.0f - ctx->cfg.beta1;
+    sc.c2 = 1.0f - ctx->cfg.beta2;
+    sc.lr = ctx->cfg.lr;
+    sc.eps = ctx->cfg.eps;
+    sc.wd = ctx->cfg.weight_decay;
+    sc.W = W;
+    uint32_t* key = key_out ? key_out : ctx->d_key;
+    const uint32_t k_cap = (uint32_t)ctx->lay.k_total;
+    const uint32_t n_tiles = (uint32_t)ctx->tiles.size();
+    const int32_t L = ctx->lay.L;
+
+    const int slot = prof_begin(ctx);
+    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
+    prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
+    if (r_on_host) {
+        if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, key, s))) return rc;
+    } else {
+        SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
+                                    k_cap, key, ctx->d_m_stash),
+                  "ef_compact");
+    }
+    prof_mark(ctx, slot, 1, s);
+    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash, ctx->n_words,
+                                   (uint32_t)ctx->lay.n_pad, k_cap),
+              "reduce_update");
+    prof_mark(ctx, slot, 2, s);
+    if ((rc = run_select(ctx, 0, L, 0, n_tiles, key, next->bits, s))) return rc;
+    prof_mark(ctx, slot, 3, s);
+    if ((rc = run_index(ctx, next, s))) return rc;
+    if (r_on_host && ctx->n_words > 0) {
+        // the step completes on `stream` only once every residual chunk is home
+        SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[0], 0), "offload wait");
+        SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[1], 0), "offload wait");
+    }
+    prof_mark(ctx, slot, 4, s);
     return SCAPE_OK;
 }
 
@@ -431,6 +567,27 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         free_ctx(c);
         return rc;
     }
+    // residual offload resources (default-priority streams; the events only order work)
+    c->chunk_words = std::min<uint32_t>(c->n_words, kOffloadChunkWords);
+    if (c->chunk_words > 0) {
+        if ((rc = dev_alloc(&c->d_stage, (size_t)2 * cfg->workers * c->chunk_words * 64, "offload staging"))) {
+            free_ctx(c);
+            return rc;
+        }
+        e = hipStreamCreateWithFlags(&c->s_in, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->s_out, hipStreamNonBlocking);
+        for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+            e = hipEventCreateWithFlags(&c->ev_in[b], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_k[b], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_out[b], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventRecord(c->ev_out[b], c->s_out);  // both slots start free
+        }
+        if (e != hipSuccess) {
+            free_ctx(c);
+            return hip_fail(e, "creating offload streams and events");
+        }
+        c->offload_ready = true;
+    }
     e = hipMemcpy(c->d_layers, ld.data(), L * sizeof(LayerDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess && !c->tiles.empty())
         e = hipMemcpy(c->d_tiles, c->tiles.data(), c->tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice);
@@ -462,65 +619,13 @@ int scape_destroy(scape_ctx* ctx) {
 int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
                const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
                void* stream) {
-    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
-    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
-    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
-        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
-    if (!r || !g || !sparse_bufs) return fail(SCAPE_ERR_INVALID_ARG, "r, g and sparse_bufs must not be NULL");
-    const int W = ctx->cfg.workers;
-    for (int i = 0; i < W; ++i) {
-        if (!r[i] || !g[i]) return fail(SCAPE_ERR_INVALID_ARG, "r[%d] or g[%d] is NULL", i, i);
-        if (!aligned(r[i], 16) || !aligned(g[i], 16))
-            return fail(SCAPE_ERR_ALIGN, "r[%d] and g[%d] must be 16-byte aligned", i, i);
-        if (ctx->lay.k_total > 0) {
-            if (!sparse_bufs[i]) return fail(SCAPE_ERR_INVALID_ARG, "sparse_bufs[%d] is NULL", i);
-            if (!aligned(sparse_bufs[i], 4)) return fail(SCAPE_ERR_ALIGN, "sparse_bufs[%d] must be 4-byte aligned", i);
-        }
-    }
-    if (key_out && !aligned(key_out, 16)) return fail(SCAPE_ERR_ALIGN, "key_out must be 16-byte aligned");
-    int rc;
-    if ((rc = check_mask(cur, true, "cur")) || (rc = check_mask(next, true, "next"))) return rc;
-    if (cur->bits == next->bits || cur->idx == next->idx || cur->block_prefix == next->block_prefix)
-        return fail(SCAPE_ERR_STATE, "next must not alias cur (the mask built now is used at the next step)");
-    if ((rc = check_device(ctx))) return rc;
+    return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, false);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    WorkerPtrs wp{};
-    for (int i = 0; i < W; ++i) {
-        wp.r[i] = r[i];
-        wp.g[i] = g[i];
-        wp.b[i] = ctx->lay.k_total > 0 ? sparse_bufs[i] : nullptr;
-    }
-    StepScalars sc;
-    sc.beta1 = ctx->cfg.beta1;
-    sc.beta2 = ctx->cfg.beta2;
-    sc.c1 = 1.0f - ctx->cfg.beta1;
-    sc.c2 = 1.0f - ctx->cfg.beta2;
-    sc.lr = ctx->cfg.lr;
-    sc.eps = ctx->cfg.eps;
-    sc.wd = ctx->cfg.weight_decay;
-    sc.W = W;
-    uint32_t* key = key_out ? key_out : ctx->d_key;
-    const uint32_t k_cap = (uint32_t)ctx->lay.k_total;
-    const uint32_t n_tiles = (uint32_t)ctx->tiles.size();
-    const int32_t L = ctx->lay.L;
-
-    const int slot = prof_begin(ctx);
-    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
-    prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
-    SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix, k_cap,
-                                key, ctx->d_m_stash),
-              "ef_compact");
-    prof_mark(ctx, slot, 1, s);
-    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash, ctx->n_words,
-                                   (uint32_t)ctx->lay.n_pad, k_cap),
-              "reduce_update");
-    prof_mark(ctx, slot, 2, s);
-    if ((rc = run_select(ctx, 0, L, 0, n_tiles, key, next->bits, s))) return rc;
-    prof_mark(ctx, slot, 3, s);
-    if ((rc = run_index(ctx, next, s))) return rc;
-    prof_mark(ctx, slot, 4, s);
-    return SCAPE_OK;
+int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* const* r_host, const uint16_t* const* g,
+                       const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+                       void* stream) {
+    return step_common(ctx, x, m, v, r_host, g, cur, next, sparse_bufs, key_out, stream, true);
 }
 
 int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream) {

@@ -4,17 +4,19 @@ Holds the fp32 master parameters x, moments m and v, the W residuals, the two
 mask slots and the W sparse buffers as torch tensors on one GPU, and calls
 ``scape_step``.  The mask built at step t is used at step t+1 (Delayed Mask
 Usage, gist.science Technical Summary s.2): after each step the two mask
-slots swap roles.  The first step uses an all-zero mask.
+slots swap roles.  The first step uses an all-zero mask.  With
+``offload=True`` the residuals live in pinned host memory and each step calls
+``scape_step_offload`` (Memory Optimization, same section).
 """
 from __future__ import annotations
 
 from typing import Optional, Sequence
 
-from ._scape import Context, Mask, ScapeConfig, alloc_mask, scape_step
+from ._scape import Context, Mask, ScapeConfig, alloc_mask, scape_step, scape_step_offload
 
 
 class ScapeState:
-    def __init__(self, cfg: ScapeConfig, device: str = "cuda", x=None):
+    def __init__(self, cfg: ScapeConfig, device: str = "cuda", x=None, offload: bool = False):
         import torch
         self.cfg = cfg
         self.ctx = Context(cfg)
@@ -24,7 +26,11 @@ class ScapeState:
         self.x = torch.zeros(n, **f32) if x is None else x
         self.m = torch.zeros(n, **f32)
         self.v = torch.zeros(n, **f32)
-        self.r = [torch.zeros(n, **f32) for _ in range(W)]
+        self.offload = offload
+        if offload:
+            self.r = [torch.zeros(n, dtype=torch.float32, pin_memory=True) for _ in range(W)]
+        else:
+            self.r = [torch.zeros(n, **f32) for _ in range(W)]
         self.sparse = [torch.zeros(max(k, 1), **f32) for _ in range(W)]
         self.key = torch.zeros(n, dtype=torch.int32, device=device)
         self.masks = [alloc_mask(self.layout, device), alloc_mask(self.layout, device)]
@@ -42,8 +48,9 @@ class ScapeState:
 
     def step(self, grads: Sequence, stream=None, key_out: Optional[bool] = True) -> None:
         """One step with the W workers' bfloat16 gradients (int16 views)."""
-        scape_step(self.ctx, self.x, self.m, self.v, self.r, grads, self.cur_mask, self.next_mask, self.sparse,
-                   self.key if key_out else None, stream)
+        fn = scape_step_offload if self.offload else scape_step
+        fn(self.ctx, self.x, self.m, self.v, self.r, grads, self.cur_mask, self.next_mask, self.sparse,
+           self.key if key_out else None, stream)
         self._cur = 1 - self._cur
         self.t += 1
 

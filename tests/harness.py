@@ -91,6 +91,7 @@ class GpuRun:
     init_mask_all: bool = False
     x_zero: bool = False
     grad_override: Optional[object] = None  # callable(step, worker, tensor) -> np.uint16 array
+    offload: bool = False  # residuals in pinned host memory (scape_step_offload)
     state: object = None
     grads: List[object] = field(default_factory=list)
 
@@ -98,7 +99,7 @@ class GpuRun:
         import torch
         from sparse_communication_adam_amd.state import ScapeState
         cfg = scape_config(self.wl, self.keep, self.W)
-        self.state = ScapeState(cfg)
+        self.state = ScapeState(cfg, offload=self.offload)
         self.layout = self.state.layout
         n = self.layout.n_pad
         if not self.x_zero:
@@ -146,7 +147,8 @@ def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int]
 
 
 def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, keep=None, W=None,
-               init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True) -> Dict[str, int]:
+               init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True,
+               offload=False) -> Dict[str, int]:
     """Run `steps` steps on the GPU (all layers) and the oracle (all layers, or
     the sampled ones) and compare every output of every step."""
     import torch
@@ -155,8 +157,8 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
     tensors = list(range(len(wl.tensors))) if sample is None else list(sample)
     lay = full if sample is None else oracle.sub_layout(full, tensors)
     log(f"{wl.name}: W={W} L={full.L} n_pad={full.n_pad} k_total={full.k_total} steps={steps} "
-        f"oracle layers={len(tensors)} ({lay.n_pad} elements)")
-    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override)
+        f"oracle layers={len(tensors)} ({lay.n_pad} elements){' residuals on the host' if offload else ''}")
+    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total
     assert list(glay.layer_offset) == full.off.tolist() and list(glay.layer_k) == full.k.tolist()

@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["scape_init", "scape_destroy", "scape_layout", "scape_step", "scape_dense_step", "scape_mask_build",
+    for n in ["scape_init", "scape_destroy", "scape_layout", "scape_step", "scape_step_offload", "scape_dense_step",
+              "scape_mask_build",
               "scape_mask_index", "scape_mask_union_add",
               "scape_pack", "scape_unpack", "scape_reduce_sparse", "scape_last_error", "scape_version"]:
         assert n in names
@@ -102,6 +103,7 @@ def test_null_arguments_rejected_before_any_launch(sc):
     assert lib.scape_step(None, None, None, None, None, None, None, None, None, None, None) == -1
     assert "ctx" in sc.scape_last_error()
     assert lib.scape_dense_step(None, None, None, None, None, None) == -1
+    assert lib.scape_step_offload(None, None, None, None, None, None, None, None, None, None, None) == -1
     assert lib.scape_mask_union_add(None, None, None, None) == -1
     assert lib.scape_mask_build(None, None, 0, -1, None, None) == -1
     assert lib.scape_mask_index(None, None, None) == -1
