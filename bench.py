@@ -61,11 +61,18 @@ def alg_bytes(N: int, W: int, ksum: int):
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("k_elementwise.hip", "scape_device.h", "scape_internal.h"):
-        with open(os.path.join(ROOT, "sparse_communication_adam_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Hash of what the dense pass is compiled from: its kernel and launcher,
+    the device helpers, and the constants and argument structs it uses."""
+    csrc = os.path.join(ROOT, "sparse_communication_adam_amd", "csrc")
+    el = open(os.path.join(csrc, "k_elementwise.hip")).read()
+    a = el.index("__global__ __launch_bounds__(kBlock) void k_ef_compact")
+    b = el.index("#undef SCAPE_EF_CASE", a)
+    parts = [el[a:b], open(os.path.join(csrc, "scape_device.h")).read()]
+    hdr = open(os.path.join(csrc, "scape_internal.h")).read()
+    for pat in (r"constexpr int kBlock = .*?;", r"constexpr int kWaves = .*?;", r"struct WorkerPtrs \{.*?\};",
+                r"struct StepScalars \{.*?\};"):
+        parts.append(re.search(pat, hdr, re.S).group(0))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
 def counter_traffic(workload: str):
