@@ -54,9 +54,15 @@ def log(msg: str) -> None:
 
 
 def alg_bytes(N: int, W: int, ksum: int):
-    """Algorithmic bytes of one step and of its dense pass."""
-    dense = N * (10 * W + 8.125) + 4 * W * ksum
-    step = N * (10 * W + 12.25) + ksum * (8 * W + 28)
+    """Algorithmic bytes of one step and of its dense pass.  Per element the
+    dense pass reads W bf16 gradients, W fp32 residuals, m and the mask bit,
+    and writes the W residuals and a 16-bit statistic key (10W + 6.125); at
+    each masked element it also writes the W sparse-buffer entries.  The step
+    adds the key's read by the selection and the new mask's bits (10W + 8.25
+    per element), and per masked element the buffers' reads and the
+    idx / m / x reads and x / m / v / next-idx writes (8W + 28)."""
+    dense = N * (10 * W + 6.125) + 4 * W * ksum
+    step = N * (10 * W + 8.25) + ksum * (8 * W + 28)
     return dense, step
 
 
@@ -162,11 +168,11 @@ def offload_step(cfg, wl, sets, steps: int, warmup: int) -> dict:
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
     torch.cuda.synchronize()
     for s in range(warmup):
-        state.step(sets[s % len(sets)])
+        state.step(sets[s % len(sets)], key_out=False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        state.step(sets[(warmup + s) % len(sets)])
+        state.step(sets[(warmup + s) % len(sets)], key_out=False)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     state.destroy()
@@ -279,7 +285,7 @@ def main() -> int:
     log(f"state and {args.grad_sets} gradient batches resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
 
     for s in range(args.warmup):
-        state.step(sets[s % len(sets)])
+        state.step(sets[s % len(sets)], key_out=False)
     torch.cuda.synchronize()
     log(f"{args.warmup} warmup steps done")
 
@@ -287,7 +293,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        state.step(sets[(args.warmup + s) % len(sets)])
+        state.step(sets[(args.warmup + s) % len(sets)], key_out=False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     phase_ms, nrec = sc.scape_profile_read(state.ctx)

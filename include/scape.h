@@ -160,8 +160,13 @@ int scape_destroy(scape_ctx* ctx);
  *   next          M_{t+1}, written; must not alias `cur`;
  *   sparse_bufs[W] fp32 device arrays of k_total entries, written (4-byte
  *                 alignment suffices);
- *   key_out       uint32 statistic array (n_pad), written; NULL uses the
- *                 context's own buffer.
+ *   key_out       uint32 array (n_pad) for the full statistic keys, written
+ *                 when not NULL (4 more bytes per element); may be NULL.  The
+ *                 selection itself reads the top 16 bits of each key (bits
+ *                 30..15) from the context, and takes a candidate's full key
+ *                 from key_out, or else recomputes it from m (unchanged off
+ *                 the mask), the owner's residual and its sparse buffer with
+ *                 the same fp32 operations; the mask is the same either way.
  * Errors: INVALID_ARG, ALIGN, STATE (next aliases cur), HIP.
  */
 int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,

@@ -2,9 +2,10 @@
 // of the SCAPE step, for gfx950 (wave64).
 //
 // Dense pass (k_ef_compact): one read of every worker's gradient and
-// residual, one write of every residual, one read of m, one write of the
-// statistic key; at the positions of the current mask it also writes each
-// worker's first-moment candidate into that worker's compacted sparse buffer.
+// residual, one write of every residual, one read of m, one write of the top
+// 16 bits of the statistic key (the full key only on request); at the
+// positions of the current mask it also writes each worker's first-moment
+// candidate into that worker's compacted sparse buffer.
 // Lane l of a wave handles element l of each 64-element word, so every load
 // and store of a wave is one contiguous 128- or 256-byte segment, the mask
 // word is a wave-uniform scalar, and a masked element's slot in the sparse
@@ -39,12 +40,31 @@ namespace scape {
 // 16-bit descriptor gives the owner worker (bits 8..13) and the number of
 // elements of the word inside its layer (bits 0..6, 1..64; 0 = padding).
 // Every worker's loads are issued before any store.
-template <int WT>
+#ifndef SCAPE_EF_NT
+#define SCAPE_EF_NT 1
+#endif
+// Streamed element loads and stores of the dense pass (bit 0: loads, bit 1:
+// stores non-temporal).  Non-temporal loads of the streamed arrays keep the
+// sparse buffers and the m stash, which the update pass reads next, in the
+// caches; non-temporal stores measured slower for the update pass.
+template <typename T>
+__device__ __forceinline__ T ef_load(const T* p) {
+    if (SCAPE_EF_NT & 1) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <typename T>
+__device__ __forceinline__ void ef_store(T v, T* p) {
+    if (SCAPE_EF_NT & 2) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <int WT, bool K32>
 __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
                                                        WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
-                                                       uint32_t* __restrict__ key, float* __restrict__ m_stash) {
+                                                       uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
+                                                       float* __restrict__ m_stash) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
     if (w >= n_words) return;
@@ -54,14 +74,14 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
     // the element loads go out at once, beside the word's descriptors, and
     // the padding lanes are dropped only before the stores
     const size_t j = (size_t)w * 64u + lane;
-    const float mo = m[j];
+    const float mo = ef_load(&m[j]);
     float rv[WMAX];
     uint16_t gv[WMAX];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
         if (i >= W) break;
-        rv[i] = wp.r[i][j];
-        gv[i] = wp.g[i][j];
+        rv[i] = ef_load(&wp.r[i][j]);
+        gv[i] = ef_load(&wp.g[i][j]);
     }
     const uint32_t info = word_info[w];
     const uint64_t word = cur_bits[w];
@@ -79,10 +99,13 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
         const float a = rv[i] + bf16_bits_to_f32(gv[i]);
         const float mt = bm + sc.c1 * a;
         if (i == owner) kk = magnitude_key(mt);
-        wp.r[i][j] = msk ? 0.0f : a;
+        ef_store(msk ? 0.0f : a, &wp.r[i][j]);
         if (msk) wp.b[i][rank] = mt;
     }
-    key[j] = kk;
+    // the selection reads the top 16 bits; candidates get their full key
+    // back from the state (or from key32 when it is asked for)
+    ef_store((uint16_t)(kk >> kKeyShift), &key16[j]);
+    if (K32) key32[j] = kk;
     // m before the step, compacted like the sparse buffers: the update pass
     // reads it contiguously instead of gathering one cache line per position
     if (msk) m_stash[rank] = mo;
@@ -90,13 +113,17 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
 
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, float* m_stash) {
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
+                             float* m_stash) {
     if (n_words == 0) return hipSuccess;
     const dim3 grid((n_words + kWaves - 1) / kWaves);
-#define SCAPE_EF_CASE(WV)                                                                                 \
-    case WV:                                                                                              \
-        hipLaunchKernelGGL(k_ef_compact<WV>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
-                           cur_prefix, k_cap, key, m_stash);                                              \
+#define SCAPE_EF_LAUNCH(WV, K)                                                                                  \
+    hipLaunchKernelGGL((k_ef_compact<WV, K>), grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
+                       cur_prefix, k_cap, key16, key32, m_stash)
+#define SCAPE_EF_CASE(WV)                    \
+    case WV:                                 \
+        if (key32) SCAPE_EF_LAUNCH(WV, true); \
+        else SCAPE_EF_LAUNCH(WV, false);      \
         break;
     switch (sc.W) {
         SCAPE_EF_CASE(1)
@@ -107,9 +134,10 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
         SCAPE_EF_CASE(16)
         SCAPE_EF_CASE(32)
         default:
-            hipLaunchKernelGGL(k_ef_compact<0>, grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits,
-                               cur_prefix, k_cap, key, m_stash);
+            if (key32) SCAPE_EF_LAUNCH(0, true);
+            else SCAPE_EF_LAUNCH(0, false);
     }
+#undef SCAPE_EF_LAUNCH
 #undef SCAPE_EF_CASE
     return hipGetLastError();
 }
@@ -183,6 +211,11 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 4
 #endif
+// The update pass's scattered x gather and x/m/v stores bypass the cache
+// hierarchy's normal allocation (measured faster).
+#ifndef SCAPE_UPDATE_NT
+#define SCAPE_UPDATE_NT 1
+#endif
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;
 
 template <int WT>
@@ -208,7 +241,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         jj[u] = ok[u] ? idx[q] : 0u;
         ok[u] = ok[u] && jj[u] < n_pad;
         mo[u] = ok[u] ? m_stash[q] : 0.0f;
+#if SCAPE_UPDATE_NT
+        xv[u] = ok[u] ? __builtin_nontemporal_load(&x[jj[u]]) : 0.0f;
+#else
         xv[u] = ok[u] ? x[jj[u]] : 0.0f;
+#endif
         s[u] = ok[u] ? wp.b[0][q] : 0.0f;
     }
 #pragma unroll
@@ -226,11 +263,17 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         const float bb = s[u] / fW;
         const float ghat = (bb - sc.beta1 * mo[u]) / sc.c1;
         const float vv = sc.beta2 * (mo[u] * mo[u]) + sc.c2 * (ghat * ghat);
-        v[jj[u]] = vv;
-        m[jj[u]] = bb;
         float upd = bb / (sqrtf(vv) + sc.eps);
         if (sc.wd != 0.0f) upd = upd + sc.wd * xv[u];
+#if SCAPE_UPDATE_NT
+        __builtin_nontemporal_store(vv, &v[jj[u]]);
+        __builtin_nontemporal_store(bb, &m[jj[u]]);
+        __builtin_nontemporal_store(xv[u] - sc.lr * upd, &x[jj[u]]);
+#else
+        v[jj[u]] = vv;
+        m[jj[u]] = bb;
         x[jj[u]] = xv[u] - sc.lr * upd;
+#endif
     }
 }
 
@@ -264,20 +307,20 @@ hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepS
 // per wave, one-shot like the dense pass.
 __global__ __launch_bounds__(kBlock) void k_keys_from_mtilde(const uint16_t* __restrict__ word_info, uint32_t w_begin,
                                                              uint32_t w_end, const float* __restrict__ mtilde,
-                                                             uint32_t* __restrict__ key) {
+                                                             uint16_t* __restrict__ key16) {
     const uint32_t w = w_begin + blockIdx.x * kWaves + threadIdx.x / 64;
     if (w >= w_end) return;
     const uint32_t lane = lane_id();
     if (lane >= (word_info[w] & 127u)) return;
     const size_t j = (size_t)w * 64u + lane;
-    key[j] = magnitude_key(mtilde[j]);
+    key16[j] = (uint16_t)(magnitude_key(mtilde[j]) >> kKeyShift);
 }
 
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
-                                   const float* mtilde, uint32_t* key) {
+                                   const float* mtilde, uint16_t* key16) {
     if (w_end <= w_begin) return hipSuccess;
     hipLaunchKernelGGL(k_keys_from_mtilde, dim3((w_end - w_begin + kWaves - 1) / kWaves), dim3(kBlock), 0, s,
-                       word_info, w_begin, w_end, mtilde, key);
+                       word_info, w_begin, w_end, mtilde, key16);
     return hipGetLastError();
 }
 

@@ -5,8 +5,11 @@
 // statistics: gist.science Technical Summary s.2, Partitioned Mask
 // Synchronization; the tie rule is the reading this library adopts).  That is
 // the top k of the 62-bit composite (key, ~position), found by radix
-// selection: first on the 11-bit digit d = bits 30..20 of the key, then on
-// the remaining key bits and, for ties, on the position.
+// selection: first on the 13-bit digit d = bits 30..18 of the key (buckets of
+// 1/32 octave), then on key bits 17..15, 14..6 and 5..0 and, for ties, on the
+// position.  The selection reads 16-bit keys (bits 30..15); the full key of a
+// candidate still undecided after the first two digits comes from a
+// KeySource.
 //
 //  1. k_sample_hist histograms d over a 1/16 sample of each layer's words
 //     (words picked by a hash of their index, so that no row or column
@@ -26,8 +29,8 @@
 //     d1 is outside the window (a sampling miss), k_hist_full and
 //     k_filter_exact redo that layer from all its keys, so the result is exact
 //     in every case.
-//  4. Up to five refinement passes over the records: key bits 19..10, key
-//     bits 9..0, then - only if the threshold key T is tied beyond what is
+//  4. Up to six refinement passes over the records: key bits 17..15, 14..6
+//     and 5..0, then - only if the threshold key T is tied beyond what is
 //     needed - position bits 30..20, 19..10, 9..0 from the smallest position
 //     upward.  Each pass marks the records its layer's decided prefix already
 //     selects (64-bit atomic ORs on the words the filter wrote), drops those
@@ -43,44 +46,39 @@ namespace scape {
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-// Generic per-layer bucket search over `nbins` bins of `h`.  Scan order is
-// from the top bin down when `descending`, else from bin 0 up.  Returns (via
-// LDS) the bucket where the running count first reaches `need`, the count
-// before it and the bucket's own count; zeroes the row afterwards.
+// Generic per-layer bucket search over `nbins` bins of `h` (a multiple of
+// kBlock).  Scan order is from the top bin down when `descending`, else from
+// bin 0 up.  Returns (via LDS) the bucket where the running count first
+// reaches `need`, the count before it and the bucket's own count; zeroes the
+// row afterwards.  Each thread owns a contiguous run of bins in scan order:
+// one pass sums it, a workgroup scan places it, and the one thread whose run
+// holds the target walks it again.
 __device__ void find_bucket(uint32_t* h, int nbins, bool descending, uint32_t need, uint32_t* s_bucket,
                             uint32_t* s_before, uint32_t* s_count, uint32_t* scan_scratch) {
-    const int per = nbins / kBlock;  // 8 or 4
-    uint32_t c[8];
+    const int per = nbins / kBlock;
+    auto bin = [&](int o) { return descending ? nbins - 1 - o : o; };
     uint32_t sum = 0;
-    for (int e = 0; e < per; ++e) {
-        const int o = threadIdx.x * per + e;
-        const int b = descending ? nbins - 1 - o : o;
-        c[e] = h[b];
-        sum += c[e];
-    }
+    for (int e = 0; e < per; ++e) sum += h[bin(threadIdx.x * per + e)];
     if (threadIdx.x == 0) *s_bucket = kNone;
-    uint32_t before = block_exclusive_scan(sum, scan_scratch, nullptr);
+    const uint32_t before = block_exclusive_scan(sum, scan_scratch, nullptr);
     if (need > 0 && before < need && before + sum >= need) {
         uint32_t cum = before;
         for (int e = 0; e < per; ++e) {
-            if (cum + c[e] >= need) {
-                const int o = threadIdx.x * per + e;
-                *s_bucket = (uint32_t)(descending ? nbins - 1 - o : o);
+            const int b = bin(threadIdx.x * per + e);
+            const uint32_t c = h[b];
+            if (cum + c >= need) {
+                *s_bucket = (uint32_t)b;
                 *s_before = cum;
-                *s_count = c[e];
+                *s_count = c;
                 break;
             }
-            cum += c[e];
+            cum += c;
         }
     }
-    for (int e = 0; e < per; ++e) {
-        const int o = threadIdx.x * per + e;
-        h[descending ? nbins - 1 - o : o] = 0;
-    }
+    __syncthreads();
+    for (int e = 0; e < per; ++e) h[bin(threadIdx.x * per + e)] = 0;
     __syncthreads();
 }
-
-
 
 constexpr uint32_t kSampleShift = 4;            // 1 word in 16
 constexpr uint32_t kFullSampleWords = 4096;     // layers up to 262144 elements are taken whole
@@ -99,7 +97,11 @@ __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
 // ---------------------------------------------------------------------------
 // 1. sample and window
 
-constexpr int kSampleTiles = 8;  // tiles per workgroup in the sampling pass
+#ifndef SCAPE_SAMPLE_TILES
+#define SCAPE_SAMPLE_TILES 16
+#endif
+constexpr int kSampleTiles = SCAPE_SAMPLE_TILES;  // tiles per workgroup in the sampling pass
+constexpr int kSampleBatch = 8;   // sampled words a wave loads at once
 
 // In each aligned group of 16 words of a layer, the sampled word is the one at
 // offset hash(group) & 15; layers of up to kFullSampleWords words are taken
@@ -107,7 +109,7 @@ constexpr int kSampleTiles = 8;  // tiles per workgroup in the sampling pass
 // row when the layer changes.
 __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                         const LayerDesc* __restrict__ layers,
-                                                        const uint32_t* __restrict__ key,
+                                                        const uint16_t* __restrict__ key,
                                                         uint32_t* __restrict__ hist,
                                                         uint32_t* __restrict__ sample_words) {
     __shared__ uint32_t h[kDigit1Bins];
@@ -136,23 +138,28 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
         }
         if (L.k == 0) continue;  // nothing to select: no sample
         const uint32_t lw0 = L.off / 64u, lwords = (L.n + 63) / 64, lend = L.off + L.n;
+        const bool whole = lwords <= kFullSampleWords;
+        // the sampled words of this tile, in this wave's share: every word of a
+        // wholly sampled layer, else one hashed word per aligned group of 16
+        // (tiles start on multiples of 16 words within the layer)
+        const uint32_t g0 = whole ? t.w0 : (t.w0 - lw0) >> kSampleShift;
+        const uint32_t g1 = whole ? t.w1 : (t.w1 - lw0 + 15) >> kSampleShift;
         uint32_t nw = 0;
-        if (lwords <= kFullSampleWords) {
-            for (uint32_t w = t.w0 + wave; w < t.w1; w += kWaves) {
+        for (uint32_t gb = g0 + wave; gb < g1; gb += kWaves * kSampleBatch) {
+            uint32_t kv[kSampleBatch];
+            bool inl[kSampleBatch];
+#pragma unroll
+            for (int u = 0; u < kSampleBatch; ++u) {  // the batch's loads go out together
+                const uint32_t g = gb + u * kWaves;
+                const uint32_t w = whole ? g : lw0 + (g << kSampleShift) + (word_hash(lw0 + (g << kSampleShift)) & 15u);
                 const uint32_t jj = w * 64u + lane;
-                const bool inl = jj < lend;
-                hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
-                nw += (uint32_t)__popcll(__ballot(inl));
+                inl[u] = g < g1 && w < t.w1 && jj < lend;
+                kv[u] = inl[u] ? (uint32_t)key[jj] : 0u;
             }
-        } else {
-            // groups of 16 words: tiles start on multiples of 16 words within the layer
-            const uint32_t g0 = (t.w0 - lw0) >> kSampleShift, g1 = (t.w1 - lw0 + 15) >> kSampleShift;
-            for (uint32_t g = g0 + wave; g < g1; g += kWaves) {
-                const uint32_t w = lw0 + (g << kSampleShift) + (word_hash(lw0 + (g << kSampleShift)) & 15u);
-                const uint32_t jj = w * 64u + lane;
-                const bool inl = w < t.w1 && jj < lend;
-                hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
-                nw += (uint32_t)__popcll(__ballot(inl));
+#pragma unroll
+            for (int u = 0; u < kSampleBatch; ++u) {
+                hist_add_wave(h, kv[u] >> kDigit1FromKey16, inl[u]);
+                nw += (uint32_t)__popcll(__ballot(inl[u]));
             }
         }
         if (lane == 0 && nw) atomicAdd(&s_cnt, nw);
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
 }
 
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                              const uint32_t* key, uint32_t* hist, uint32_t* sample_count) {
+                              const uint16_t* key, uint32_t* hist, uint32_t* sample_count) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_sample_hist, dim3((n_tiles + kSampleTiles - 1) / kSampleTiles), dim3(kBlock), 0, s, tiles,
                        n_tiles, layers, key, hist, sample_count);
@@ -187,18 +194,14 @@ __global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const Layer
     const int l = layer0 + blockIdx.x;
     const LayerDesc L = layers[l];
     uint32_t* row = hist + (size_t)l * kHistBins;
-    // per thread 8 bins from the top; suffix[b] = sampled count at or above b
+    // per thread a run of bins from the top; suffix[b] = sampled count at or above b
     constexpr int per = kDigit1Bins / kBlock;
-    uint32_t c[per], sum = 0;
-    for (int e = 0; e < per; ++e) {
-        const int b = kDigit1Bins - 1 - (threadIdx.x * per + e);
-        c[e] = row[b];
-        sum += c[e];
-    }
+    uint32_t sum = 0;
+    for (int e = 0; e < per; ++e) sum += row[kDigit1Bins - 1 - (threadIdx.x * per + e)];
     uint32_t run = block_exclusive_scan(sum, scratch, nullptr);
     for (int e = 0; e < per; ++e) {
         const int b = kDigit1Bins - 1 - (threadIdx.x * per + e);
-        run += c[e];
+        run += row[b];
         suffix[b] = run;
         row[b] = 0;  // leave the row clean
     }
@@ -249,8 +252,57 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 // ---------------------------------------------------------------------------
 // 2. the pass over every key
 
-constexpr int kFilterWords = 8;                 // words per wave per trip
-constexpr int kWaveStage = 256;                 // LDS records per wave (2 KB): 8 KB per workgroup keeps occupancy high
+#ifndef SCAPE_FILTER_WORDS
+#define SCAPE_FILTER_WORDS 8
+#endif
+constexpr int kFilterWords = SCAPE_FILTER_WORDS;  // words per wave per trip
+constexpr int kWaveStage = 256;                 // staged records per wave (2 KB): 8 KB per workgroup
+
+// Full keys of up to 8 records of layer L (the bits of `sel` say which), in
+// place.  All loads are issued unconditionally at safe indices so that the
+// eight gathers overlap: first the mask word, prefix, residual and m of each
+// record, then the sparse-buffer entries those select.
+__device__ __forceinline__ void candidate_keys8(const KeySource& ks, const LayerDesc& L, uint64_t* rec,
+                                                uint32_t sel) {
+    uint32_t jj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) jj[u] = L.off + (((sel >> u) & 1u) ? (uint32_t)rec[u] : 0u);
+    uint32_t kk[8];
+    if (ks.mtilde || ks.key32) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kk[u] = ks.mtilde ? magnitude_key(ks.mtilde[jj[u]]) : ks.key32[jj[u]];
+    } else {
+        const float* r = ks.r[L.owner];
+        uint64_t word[8];
+        uint32_t pre[8];
+        float rv[8], mv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            word[u] = ks.cur_bits[jj[u] >> 6];
+            pre[u] = ks.cur_prefix[jj[u] >> 6];
+            rv[u] = r[jj[u]];
+            mv[u] = ks.m[jj[u]];
+        }
+        bool on[8];
+        float bv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t bit = jj[u] & 63u;
+            const uint32_t rank = pre[u] + (uint32_t)__popcll(word[u] & ((1ull << bit) - 1ull));
+            on[u] = ((word[u] >> bit) & 1ull) && rank < ks.k_cap;
+            bv[u] = 0.0f;
+            if (ks.k_cap) bv[u] = ks.b[L.owner][on[u] ? rank : 0u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float bm = ks.beta1 * mv[u];
+            kk[u] = on[u] ? magnitude_key(bv[u]) : magnitude_key(bm + ks.c1 * rv[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if ((sel >> u) & 1u) rec[u] = ((uint64_t)kk[u] << 32) | (rec[u] & 0xFFFFFFFFull);
+}
 
 // Write n staged records of a wave at slot `first` of segment G.
 __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, uint32_t first, const SegDesc& G,
@@ -261,14 +313,16 @@ __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, ui
     }
 }
 
-// Keys of a tile: digit d >= sel_from -> mask bit; cand_lo <= d <= cand_hi ->
-// record.  Every word of the tile is written.  The waves work alone until the
-// end of the tile, where one reservation on the segment's counter places all
-// of the workgroup's records (a wave whose staging fills up mid-tile reserves
-// on its own), and the count of bits set is added to the segment's total.
-// Must be called by every thread of the workgroup.
+// Keys of a tile: first digit d >= sel_from -> mask bit; cand_lo <= d <=
+// cand_hi -> record, holding the 16 stored key bits (the low 15 bits zero;
+// the pass over key bits 17..9 fetches the full key of the records it still
+// needs).  Every word of the tile is written.  The waves work
+// alone until the end of the tile, where one reservation on the segment's
+// counter places all of the workgroup's records (a wave whose staging fills
+// up mid-tile reserves on its own), and the count of bits set is added to the
+// segment's total.  Must be called by every thread of the workgroup.
 __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, const SegDesc& G, uint32_t sel_from,
-                                         uint32_t cand_lo, uint32_t cand_hi, const uint32_t* __restrict__ key,
+                                         uint32_t cand_lo, uint32_t cand_hi, const uint16_t* __restrict__ key,
                                          uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
                                          uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
     __shared__ uint64_t s_rec[kWaves][kWaveStage];
@@ -286,7 +340,7 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
-            kv[e] = (w0 + e < t.w1 && jj < lend) ? key[jj] : 0u;
+            kv[e] = (w0 + e < t.w1 && jj < lend) ? (uint32_t)key[jj] : 0u;
         }
     };
     load_keys(t.w0 + wave * kFilterWords, nxt);
@@ -300,7 +354,7 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
         for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
             const bool inl = (w0 + e < t.w1) && jj < lend;
-            const uint32_t d = kv[e] >> (31 - kDigit1Bits);
+            const uint32_t d = kv[e] >> kDigit1FromKey16;
             const uint64_t word = __ballot(inl && d >= sel_from);
             n_above += (uint32_t)__popcll(word);
             if (lane == (uint32_t)e) mine = word;
@@ -314,7 +368,8 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
                         wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
                         n_st = 0;
                     }
-                    if (cnd) stage[n_st + lanes_below(cb)] = ((uint64_t)kv[e] << 32) | (uint64_t)(jj - L.off);
+                    if (cnd)
+                        stage[n_st + lanes_below(cb)] = ((uint64_t)(kv[e] << kKeyShift) << 32) | (uint64_t)(jj - L.off);
                     n_st += (uint32_t)__popcll(cb);
                 }
             }
@@ -344,7 +399,7 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
 __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
                                                    const LayerDesc* __restrict__ layers,
                                                    const SegDesc* __restrict__ segs,
-                                                   const SelState* __restrict__ st, const uint32_t* __restrict__ key,
+                                                   const SelState* __restrict__ st, const uint16_t* __restrict__ key,
                                                    uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
                                                    uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
     const TileDesc t = tiles[blockIdx.x];
@@ -358,7 +413,7 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                         const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                          uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, segs, st, key, bits, seg_fill,
@@ -377,9 +432,9 @@ __device__ __forceinline__ void init_found(SelState& S, uint32_t k, uint32_t buc
     S.need = need;
     S.all_bucket = need == count;
     S.J = 0xFFFFFFFFu;
-    if (S.all_bucket) {  // the whole bucket is kept: key >= d1 << 20
+    if (S.all_bucket) {  // the whole bucket is kept: key >= d1 << kDigit1Shift
         S.phase = kPhaseDone;
-        S.T = bucket << (31 - kDigit1Bits);
+        S.T = bucket << kDigit1Shift;
     } else {
         S.phase = kPhaseKey2;
     }
@@ -449,61 +504,72 @@ hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, 
     return hipGetLastError();
 }
 
+// The sampling-miss path.  Normally no layer needs it, so both kernels run as
+// a small grid that walks the tile table and skips tiles of other layers.
+constexpr uint32_t kFallbackGrid = 1024;
+
 // Full first-digit histogram of the layers in kModeFullHist.
-__global__ __launch_bounds__(kBlock) void k_hist_full(const TileDesc* __restrict__ tiles,
+__global__ __launch_bounds__(kBlock) void k_hist_full(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                       const LayerDesc* __restrict__ layers,
                                                       const SelState* __restrict__ st,
-                                                      const uint32_t* __restrict__ key, uint32_t* __restrict__ hist) {
+                                                      const uint16_t* __restrict__ key, uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[kDigit1Bins];
-    const TileDesc t = tiles[blockIdx.x];
-    if (st[t.layer].mode != kModeFullHist) return;  // uniform
-    const LayerDesc L = layers[t.layer];
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
-    __syncthreads();
-    const uint32_t lend = L.off + L.n;
     const uint32_t lane = lane_id();
-    for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kWaves) {
-        const uint32_t jj = w * 64u + lane;
-        const bool inl = jj < lend;
-        hist_add_wave(h, (inl ? key[jj] : 0u) >> (31 - kDigit1Bits), inl);
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+        const TileDesc t = tiles[ti];
+        if (st[t.layer].mode != kModeFullHist) continue;  // uniform
+        const LayerDesc L = layers[t.layer];
+        for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+        __syncthreads();
+        const uint32_t lend = L.off + L.n;
+        for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kWaves) {
+            const uint32_t jj = w * 64u + lane;
+            const bool inl = jj < lend;
+            hist_add_wave(h, (inl ? (uint32_t)key[jj] : 0u) >> kDigit1FromKey16, inl);
+        }
+        __syncthreads();
+        hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
+        __syncthreads();
     }
-    __syncthreads();
-    hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins);
 }
 
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* key, uint32_t* hist) {
+                            const SelState* st, const uint16_t* key, uint32_t* hist) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_hist_full, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, st, key, hist);
+    hipLaunchKernelGGL(k_hist_full, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, tiles, n_tiles, layers, st,
+                       key, hist);
     return hipGetLastError();
 }
 
 // Reclassification (bits and records from the exact bucket) of the layers in
 // kModeReclassify.
-__global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restrict__ tiles,
+__global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                          const LayerDesc* __restrict__ layers,
                                                          const SegDesc* __restrict__ segs,
                                                          const SelState* __restrict__ st,
-                                                         const uint32_t* __restrict__ key,
+                                                         const uint16_t* __restrict__ key,
                                                          uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
                                                          uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
-    const TileDesc t = tiles[blockIdx.x];
-    const SelState S = st[t.layer];
-    if (S.mode != kModeReclassify || S.none) return;  // uniform per workgroup
-    const LayerDesc L = layers[t.layer];
-    const SegDesc G = segs[t.seg];
-    if (S.all_bucket)  // keys in the threshold bucket and above, no records
-        key_pass(t, L, G, S.d1, 1, 0, key, bits, seg_fill, cand, seg_above);
-    else  // above the bucket: bits; in it: records
-        key_pass(t, L, G, S.d1 + 1, S.d1, S.d1, key, bits, seg_fill, cand, seg_above);
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+        const TileDesc t = tiles[ti];
+        const SelState S = st[t.layer];
+        if (S.mode != kModeReclassify || S.none) continue;  // uniform per workgroup
+        const LayerDesc L = layers[t.layer];
+        const SegDesc G = segs[t.seg];
+        if (S.all_bucket)  // keys in the threshold bucket and above, no records
+            key_pass(t, L, G, S.d1, 1, 0, key, bits, seg_fill, cand, seg_above);
+        else  // above the bucket: bits; in it: records
+            key_pass(t, L, G, S.d1 + 1, S.d1, S.d1, key, bits, seg_fill, cand, seg_above);
+        __syncthreads();  // the next tile reuses the LDS staging
+    }
 }
 
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                               const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                               const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                                uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_filter_exact, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, segs, st, key, bits,
-                       seg_fill, cand, seg_above);
+    hipLaunchKernelGGL(k_filter_exact, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, tiles, n_tiles, layers,
+                       segs, st, key, bits, seg_fill, cand, seg_above);
     return hipGetLastError();
 }
 
@@ -556,8 +622,16 @@ hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const
     return hipGetLastError();
 }
 
+constexpr int kPassBins = 2048;  // LDS histogram of a record pass
+
+// Bins of a refinement digit (the first digit is histogrammed relative to the
+// layer's window instead).
 __device__ __forceinline__ int phase_bins(uint32_t phase) {
-    return (phase == kPhasePos1 || phase == kPhaseKey1) ? 2048 : 1024;
+    // bucket searches walk whole kBlock-multiples of bins; the narrow digits
+    // use the first 2^bits of 256
+    if (phase == kPhaseKey2 || phase == kPhaseKey4) return 256;
+    if (phase == kPhaseKey3) return 1 << kKey3Bits;
+    return phase == kPhasePos1 ? 2048 : 1024;
 }
 
 // One record under the state of its layer: 1 = selected, 2 = undecided (its
@@ -569,16 +643,21 @@ __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, 
                                              uint32_t* digit) {
     switch (phase) {
         case kPhaseKey1:
-            *digit = kv >> 20;
+            *digit = kv >> kDigit1Shift;
             return 2;
-        case kPhaseKey2: {
-            const uint32_t d = kv >> 20;
-            *digit = (kv >> 10) & 1023u;
+        case kPhaseKey2: {  // stored bits suffice
+            const uint32_t d = kv >> kDigit1Shift;
+            *digit = (kv >> kKeyShift) & ((1u << kKey2Bits) - 1u);
             return d > S.d1 ? 1u : (d == S.d1 ? 2u : 0u);
         }
-        case kPhaseKey3: {
-            const uint32_t p = kv >> 10;
-            *digit = kv & 1023u;
+        case kPhaseKey3: {  // classified on the stored bits; the digit of a kept record is taken after its fetch
+            const uint32_t p = kv >> kKeyShift;
+            *digit = 0;
+            return p > S.kprefix ? 1u : (p == S.kprefix ? 2u : 0u);
+        }
+        case kPhaseKey4: {
+            const uint32_t p = kv >> kKey4Bits;
+            *digit = kv & ((1u << kKey4Bits) - 1u);
             return p > S.kprefix ? 1u : (p == S.kprefix ? 2u : 0u);
         }
         case kPhasePos1:
@@ -602,8 +681,14 @@ __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, 
 
 constexpr int kRecPerThread = kCandChunk / kBlock;  // 32 records held in registers per thread
 
+// A layer already done at the passes over key bits 17..15 or 14..6 was
+// decided on the stored bits (T a multiple of 2^15, J = all positions), so
+// the final rule holds on the filter's partial keys too.
+//
 // One pass over the record blocks.  phase == kPhaseKey1: histogram of every
-// record's first digit, nothing else.  Otherwise, for each block, by the
+// record's first digit, nothing else; the digits of a layer's records lie in
+// its window [n_lo, n_hi], so the LDS bins are relative to n_lo (a window
+// wider than kPassBins buckets counts straight into the global row).  Otherwise, for each block, by the
 // state of its layer: a layer in `phase` has its selected records marked,
 // its undecided ones histogrammed and compacted to the front of the block,
 // the rest dropped; a layer already done has its selected records marked and
@@ -613,19 +698,20 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
                                                       uint32_t* __restrict__ vb_count,
                                                       const uint32_t* __restrict__ totals,
                                                       const LayerDesc* __restrict__ layers,
-                                                      const SelState* __restrict__ st,
+                                                      const SelState* __restrict__ st, KeySource ks,
                                                       uint64_t* __restrict__ cand, uint32_t* __restrict__ hist,
                                                       uint64_t* __restrict__ bits) {
-    __shared__ uint32_t h[2048];
+    __shared__ uint32_t h[kPassBins];
     __shared__ uint32_t s_wsum[kWaves];
     const uint32_t nv = totals[1];
     const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
     const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
     const bool hist_only = phase == kPhaseKey1;
-    const int nb = phase == kPhaseDone ? 0 : phase_bins(phase);
     const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
     int cur = -1;
-    for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+    uint32_t* cur_row = nullptr;  // global bins of the LDS row (first bin)
+    int cur_nb = 0;               // bins to flush; 0 when counting straight into the row
+    for (int b = threadIdx.x; b < kPassBins; b += kBlock) h[b] = 0;
     for (uint32_t v = v0; v < v1; ++v) {
         const uint32_t cnt = vb_count[v];
         if (cnt == 0) continue;  // uniform
@@ -639,17 +725,31 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
         const uint32_t cph = hist_only ? kPhaseKey1 : S.phase;
         if (cph != phase && cph != kPhaseDone) continue;  // not reached: a layer is in this phase or done
         const bool hist_on = cph != kPhaseDone;
+        uint32_t lo = 0;  // first digit histogrammed
+        int nbl = hist_on ? phase_bins(cph) : 0;
+        if (hist_only) {
+            lo = S.n_lo;
+            const uint32_t width = S.n_hi - S.n_lo + 1u;
+            nbl = width <= (uint32_t)kPassBins ? (int)width : 0;
+        }
         if (hist_on && l != cur) {
             if (cur >= 0) {
                 __syncthreads();
-                hist_flush(h, hist + (size_t)cur * kHistBins, nb);
+                if (cur_nb) hist_flush(h, cur_row, cur_nb);
                 __syncthreads();
-                for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+                for (int b = threadIdx.x; b < kPassBins; b += kBlock) h[b] = 0;
             }
             cur = l;
+            cur_row = hist + (size_t)l * kHistBins + lo;
+            cur_nb = nbl;
             __syncthreads();
         }
-        const uint32_t off = layers[l].off, n = layers[l].n;
+        const LayerDesc Ld = layers[l];
+        const uint32_t off = Ld.off, n = Ld.n;
+        // the filter's records carry only the 16 stored key bits: enough for
+        // the first two digits and for a layer decided on them; the pass over
+        // key bits 14..6 fetches the full key of each record it keeps
+        const bool fetch = cph == kPhaseKey3;
         uint64_t rec[kRecPerThread];
 #pragma unroll
         for (int i = 0; i < kRecPerThread; ++i) {
@@ -668,8 +768,25 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
                 const uint32_t jj = off + jl;
                 atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
             }
-            if (hist_on) hist_add_wave(h, digit, c == 2u);
+            if (hist_on && !fetch) {
+                if (cur_nb) hist_add_wave(h, digit - lo, c == 2u);
+                else if (c == 2u) atomicAdd(&cur_row[digit - lo], 1u);  // wide first-digit window
+            }
             if (c == 2u) und |= 1u << i;
+        }
+        if (fetch) {
+#pragma unroll
+            for (int g = 0; g < kRecPerThread; g += 8) {
+                const uint32_t sel = (und >> g) & 0xFFu;
+                if (__ballot(sel != 0u) == 0) continue;  // the wave holds none of these eight
+                candidate_keys8(ks, Ld, &rec[g], sel);
+            }
+#pragma unroll
+            for (int i = 0; i < kRecPerThread; ++i) {
+                if ((uint32_t)(i * kBlock) + wave * 64u >= cnt) break;  // uniform per wave
+                const uint32_t digit = ((uint32_t)(rec[i] >> 32) >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
+                hist_add_wave(h, digit, (und >> i) & 1u);
+            }
         }
         if (!hist_only) {
             // compaction in place: every record of the block is in registers
@@ -698,14 +815,14 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
     }
     if (cur >= 0) {
         __syncthreads();
-        hist_flush(h, hist + (size_t)cur * kHistBins, nb);
+        if (cur_nb) hist_flush(h, cur_row, cur_nb);
     }
 }
 
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
-                            const uint32_t* totals, const LayerDesc* layers, const SelState* st, uint64_t* cand,
-                            uint32_t* hist, uint64_t* bits) {
-    hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kBlock), 0, s, phase, vb, vb_count, totals, layers, st, cand,
+                            const uint32_t* totals, const LayerDesc* layers, const SelState* st,
+                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits) {
+    hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kBlock), 0, s, phase, vb, vb_count, totals, layers, st, ks, cand,
                        hist, bits);
     return hipGetLastError();
 }
@@ -717,7 +834,7 @@ __global__ __launch_bounds__(kBlock) void k_select_next(uint32_t phase, int32_t 
     const int l = layer0 + blockIdx.x;
     SelState S = st[l];
     if (S.phase != phase) return;  // uniform
-    const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3;
+    const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3 || phase == kPhaseKey4;
     find_bucket(hist + (size_t)l * kHistBins, phase_bins(phase), desc, S.need, &s_bucket, &s_before, &s_count,
                 scratch);
     if (threadIdx.x != 0) return;
@@ -734,12 +851,17 @@ __global__ __launch_bounds__(kBlock) void k_select_next(uint32_t phase, int32_t 
     S.need = need;
     switch (phase) {
         case kPhaseKey2:
-            S.kprefix = (S.kprefix << 10) | b;
-            if (exact) { S.T = S.kprefix << 10; S.J = 0xFFFFFFFFu; S.phase = kPhaseDone; }
+            S.kprefix = (S.kprefix << kKey2Bits) | b;
+            if (exact) { S.T = S.kprefix << kKeyShift; S.J = 0xFFFFFFFFu; S.phase = kPhaseDone; }
             else S.phase = kPhaseKey3;
             break;
         case kPhaseKey3:
-            S.T = (S.kprefix << 10) | b;
+            S.kprefix = (S.kprefix << kKey3Bits) | b;
+            if (exact) { S.T = S.kprefix << kKey4Bits; S.J = 0xFFFFFFFFu; S.phase = kPhaseDone; }
+            else S.phase = kPhaseKey4;
+            break;
+        case kPhaseKey4:
+            S.T = (S.kprefix << kKey4Bits) | b;
             if (exact) { S.J = 0xFFFFFFFFu; S.phase = kPhaseDone; }
             else S.phase = kPhasePos1;
             break;

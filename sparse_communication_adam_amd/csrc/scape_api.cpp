@@ -150,7 +150,8 @@ struct scape_ctx {
     size_t vb_cap = 0;
     uint32_t* d_totals = nullptr;
     uint64_t* d_cand = nullptr;
-    uint32_t* d_key = nullptr;
+    uint16_t* d_key16 = nullptr;      // statistic keys, bits 30..15 (what the selection reads)
+    uint32_t* d_key32 = nullptr;      // full statistic keys, for the offloaded step
     uint32_t* d_block_sums = nullptr;
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys
@@ -186,7 +187,8 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_vb_count);
     hipFree(c->d_totals);
     hipFree(c->d_cand);
-    hipFree(c->d_key);
+    hipFree(c->d_key16);
+    hipFree(c->d_key32);
     hipFree(c->d_block_sums);
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
@@ -260,10 +262,10 @@ int prof_begin(scape_ctx* c) {
     return slot;
 }
 
-// Mask selection over layers [la, la+nl) and tiles [ta, tb), keys in d_key,
-// bits into `bits`.
-int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint32_t* key, uint64_t* bits,
-               hipStream_t s) {
+// Mask selection over layers [la, la+nl) and tiles [ta, tb), from 16-bit keys
+// and the source of candidates' full keys, bits into `bits`.
+int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
+               const KeySource& ks, uint64_t* bits, hipStream_t s) {
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
     const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
@@ -279,7 +281,7 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
               "filter");
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
               "cand_scan");
-    SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+    SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                c->d_hist, bits),
               "cand_pass");
     SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
@@ -297,12 +299,12 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
               "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
-        SCAPE_HIP(launch_cand_pass(s, phase, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+        SCAPE_HIP(launch_cand_pass(s, phase, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                    c->d_hist, bits),
                   "cand_pass");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
-    SCAPE_HIP(launch_cand_pass(s, kPhaseDone, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, c->d_cand,
+    SCAPE_HIP(launch_cand_pass(s, kPhaseDone, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                c->d_hist, bits),
               "cand_pass");
     return SCAPE_OK;
@@ -326,7 +328,7 @@ int run_index(scape_ctx* c, const scape_mask* mk, hipStream_t s) {
 // the other.  The events order, per slot: copy in -> dense pass -> copy out ->
 // the next copy into that slot.
 int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const StepScalars& sc, const float* m,
-               const scape_mask* cur, uint32_t k_cap, uint32_t* key, hipStream_t s) {
+               const scape_mask* cur, uint32_t k_cap, uint16_t* key16, uint32_t* key32, hipStream_t s) {
     const int W = c->cfg.workers;
     const uint32_t cw = c->chunk_words;
     const size_t slot_elems = (size_t)cw * 64;
@@ -349,7 +351,7 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
             cp.g[i] = wp.g[i] + j0;
         }
         SCAPE_HIP(launch_ef_compact(s, c->d_word_info + w0, nw, cp, sc, m + j0, cur->bits + w0,
-                                    cur->block_prefix + w0, k_cap, key + j0, c->d_m_stash),
+                                    cur->block_prefix + w0, k_cap, key16 + j0, key32 + j0, c->d_m_stash),
                   "ef_compact");
         SCAPE_HIP(hipEventRecord(c->ev_k[b], s), "offload event");
         SCAPE_HIP(hipStreamWaitEvent(c->s_out, c->ev_k[b], 0), "offload wait");
@@ -405,7 +407,23 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     sc.eps = ctx->cfg.eps;
     sc.wd = ctx->cfg.weight_decay;
     sc.W = W;
-    uint32_t* key = key_out ? key_out : ctx->d_key;
+    // The selection reads 16-bit keys.  Candidates' full keys come from
+    // key_out when the caller asks for the keys, from the context's full-key
+    // array when the residuals are on the host, and otherwise are recomputed
+    // from m, the owner's residual and its sparse buffer.
+    uint32_t* key32 = key_out ? key_out : (r_on_host ? ctx->d_key32 : nullptr);
+    KeySource ks{};
+    ks.key32 = key32;
+    ks.m = m;
+    for (int i = 0; i < W; ++i) {
+        ks.r[i] = r_on_host ? nullptr : r[i];
+        ks.b[i] = wp.b[i];
+    }
+    ks.cur_bits = cur->bits;
+    ks.cur_prefix = cur->block_prefix;
+    ks.k_cap = (uint32_t)ctx->lay.k_total;
+    ks.beta1 = sc.beta1;
+    ks.c1 = sc.c1;
     const uint32_t k_cap = (uint32_t)ctx->lay.k_total;
     const uint32_t n_tiles = (uint32_t)ctx->tiles.size();
     const int32_t L = ctx->lay.L;
@@ -414,10 +432,10 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
     if (r_on_host) {
-        if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, key, s))) return rc;
+        if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
         SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
-                                    k_cap, key, ctx->d_m_stash),
+                                    k_cap, ctx->d_key16, key32, ctx->d_m_stash),
                   "ef_compact");
     }
     prof_mark(ctx, slot, 1, s);
@@ -425,7 +443,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
                                    (uint32_t)ctx->lay.n_pad, k_cap),
               "reduce_update");
     prof_mark(ctx, slot, 2, s);
-    if ((rc = run_select(ctx, 0, L, 0, n_tiles, key, next->bits, s))) return rc;
+    if ((rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s))) return rc;
     prof_mark(ctx, slot, 3, s);
     if ((rc = run_index(ctx, next, s))) return rc;
     if (r_on_host && ctx->n_words > 0) {
@@ -558,7 +576,8 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_vb_count, c->vb_cap, "record block counts")) ||
         (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
         (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
-        (rc = dev_alloc(&c->d_key, (size_t)c->lay.n_pad, "statistic keys")) ||
+        (rc = dev_alloc(&c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
+        (rc = dev_alloc(&c->d_key32, (size_t)c->lay.n_pad, "full statistic keys")) ||
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(&c->d_counts, L, "per-layer counters")) ||
@@ -687,8 +706,10 @@ int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, in
     const uint32_t wa = (uint32_t)(ctx->lay.off[la] / 64), wb = ctx->layer_tile0[lb] > ctx->layer_tile0[la]
                                                                  ? ctx->tiles[ctx->layer_tile0[lb] - 1].w1
                                                                  : wa;
-    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, wa, wb, mtilde, ctx->d_key), "keys");
-    if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key, out->bits, s))) return rc;
+    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, wa, wb, mtilde, ctx->d_key16), "keys");
+    KeySource ks{};
+    ks.mtilde = mtilde;
+    if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key16, ks, out->bits, s))) return rc;
     if (all && (rc = run_index(ctx, out, s))) return rc;
     return SCAPE_OK;
 }
@@ -704,8 +725,11 @@ int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits
     const int32_t L = ctx->lay.L;
     if (L == 0 || ctx->tiles.empty()) return SCAPE_OK;
     SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
-    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, 0, ctx->n_words, mtilde, ctx->d_key), "keys");
-    if ((rc = run_select(ctx, 0, L, 0, (uint32_t)ctx->tiles.size(), ctx->d_key, ctx->d_union_bits, s))) return rc;
+    SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, 0, ctx->n_words, mtilde, ctx->d_key16), "keys");
+    KeySource ks{};
+    ks.mtilde = mtilde;
+    if ((rc = run_select(ctx, 0, L, 0, (uint32_t)ctx->tiles.size(), ctx->d_key16, ks, ctx->d_union_bits, s)))
+        return rc;
     SCAPE_HIP(launch_or_words(s, ctx->d_union_bits, acc_bits, ctx->n_words), "or_words");
     return SCAPE_OK;
 }

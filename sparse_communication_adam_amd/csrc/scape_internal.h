@@ -18,9 +18,20 @@ constexpr int kWaves = kBlock / 64;
 #define SCAPE_TILE_WORDS 512
 #endif
 constexpr int kTileWords = SCAPE_TILE_WORDS;  // words per tile (512 words = 32768 elements)
-constexpr int kDigit1Bits = 11;         // first radix digit of the 31-bit key
-constexpr int kDigit1Bins = 1 << kDigit1Bits;
-constexpr int kHistBins = 2048;         // histogram row per layer (>= every digit's bins)
+// Radix digits of the 31-bit key: the first digit is bits 30..18 (8
+// exponent bits and 5 mantissa bits: buckets of 1/32 octave), then key bits
+// 17..15, 14..6 and 5..0; ties are split on the layer position, bits 30..20,
+// 19..10 and 9..0.  The stored keys are bits 30..15, so the first two digits
+// need no full key.
+constexpr int kDigit1Bits = 13;
+constexpr int kDigit1Shift = 31 - kDigit1Bits;  // 18
+constexpr int kDigit1Bins = 1 << kDigit1Bits;   // 8192
+constexpr int kKeyShift = 15;                   // a 16-bit stored key is bits 30..15 of the 31-bit key
+constexpr int kDigit1FromKey16 = kDigit1Shift - kKeyShift;  // first digit = stored 16-bit key >> 3
+constexpr int kKey2Bits = kDigit1Shift - kKeyShift;         // 3: bits 17..15
+constexpr int kKey3Bits = 9;                                // bits 14..6
+constexpr int kKey4Bits = kKeyShift - kKey3Bits;            // 6: bits 5..0
+constexpr int kHistBins = kDigit1Bins;          // histogram row per layer (>= every digit's bins)
 constexpr int kIndexWordsPerBlock = 2048;  // words per workgroup in the index passes
 constexpr int kCandChunk = 8192;        // candidate records per virtual block
 constexpr int kSegTiles = 16;           // tiles per record segment
@@ -55,13 +66,14 @@ struct LayerDesc {
 //   selected(j) = !none && (key > T || (key == T && jl <= J))
 // where jl is the layer-local position.
 enum SelPhase : uint32_t {
-    kPhaseKey1 = 6,   // first key digit of the records (threshold bucket) pending
     kPhaseDone = 0,
-    kPhaseKey2 = 1,   // key bits 19..10 pending
-    kPhaseKey3 = 2,   // key bits 9..0 pending
-    kPhasePos1 = 3,   // tie position bits 30..20 pending
-    kPhasePos2 = 4,   // tie position bits 19..10 pending
-    kPhasePos3 = 5,   // tie position bits 9..0 pending
+    kPhaseKey2 = 1,   // key bits 17..15 pending
+    kPhaseKey3 = 2,   // key bits 14..6 pending (its pass fetches the full keys)
+    kPhaseKey4 = 3,   // key bits 5..0 pending
+    kPhasePos1 = 4,   // tie position bits 30..20 pending
+    kPhasePos2 = 5,   // tie position bits 19..10 pending
+    kPhasePos3 = 6,   // tie position bits 9..0 pending
+    kPhaseKey1 = 7,   // first key digit of the records (threshold bucket) pending
 };
 
 struct SelState {
@@ -91,6 +103,26 @@ struct WorkerPtrs {
     float* b[SCAPE_MAX_WORKERS];
 };
 
+// Where the selection finds the full 31-bit key of a candidate (the stored
+// keys keep only their top 16 bits):
+//   mtilde != nullptr: the magnitude bits of mtilde[j];
+//   else key32 != nullptr: key32[j];
+//   else recomputed from the step's state: on the current mask (rank below
+//   k_cap) the owner's sparse buffer entry, off it beta1*m[j] + c1*r_owner[j]
+//   (m is unchanged and r holds the error-compensated gradient there), the
+//   same fp32 operations in the same order as the dense pass.
+struct KeySource {
+    const float* mtilde;
+    const uint32_t* key32;
+    const float* m;
+    const float* r[SCAPE_MAX_WORKERS];
+    const float* b[SCAPE_MAX_WORKERS];
+    const uint64_t* cur_bits;
+    const uint32_t* cur_prefix;
+    uint32_t k_cap;
+    float beta1, c1;
+};
+
 struct StepScalars {
     float beta1, beta2, c1, c2, lr, eps, wd;
     int32_t W;
@@ -103,40 +135,41 @@ struct StepScalars {
 // histogram; then reduction + reconstruction + update.
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
-                             const uint32_t* cur_prefix, uint32_t k_cap, uint32_t* key, float* m_stash);
+                             const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
+                             float* m_stash);
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
                                 float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
                                 uint32_t n_words, uint32_t n_pad, uint32_t k_cap);
 hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                               const StepScalars& sc, float* x, float* m, float* v);
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
-                                   const float* mtilde, uint32_t* key);
+                                   const float* mtilde, uint16_t* key16);
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t value);
 
 // selection
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                              const uint32_t* key, uint32_t* hist, uint32_t* sample_count);
+                              const uint16_t* key, uint32_t* hist, uint32_t* sample_count);
 hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
                            const uint32_t* sample_count, SelState* st);
 // Record segments: `segs`, `seg_fill` (records per segment) and `seg_above`
 // (keys above the window per segment) are indexed by global segment number.
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                         const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                         const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                          uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
                                const uint32_t* seg_above, uint32_t* seg_fill);
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                            const SelState* st, const uint32_t* key, uint32_t* hist);
+                            const SelState* st, const uint16_t* key, uint32_t* hist);
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                               const SegDesc* segs, const SelState* st, const uint32_t* key, uint64_t* bits,
+                               const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                                uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
 hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
                             const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals);
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
-                            const uint32_t* totals, const LayerDesc* layers, const SelState* st, uint64_t* cand,
-                            uint32_t* hist, uint64_t* bits);
+                            const uint32_t* totals, const LayerDesc* layers, const SelState* st,
+                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits);
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
 

@@ -47,7 +47,9 @@ class ScapeState:
         return self.masks[1 - self._cur]
 
     def step(self, grads: Sequence, stream=None, key_out: Optional[bool] = True) -> None:
-        """One step with the W workers' bfloat16 gradients (int16 views)."""
+        """One step with the W workers' bfloat16 gradients (int16 views).
+        key_out=True also writes the full statistic keys into ``self.key``
+        (4 bytes per element more); the mask does not depend on it."""
         fn = scape_step_offload if self.offload else scape_step
         fn(self.ctx, self.x, self.m, self.v, self.r, grads, self.cur_mask, self.next_mask, self.sparse,
            self.key if key_out else None, stream)

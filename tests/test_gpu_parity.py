@@ -333,3 +333,30 @@ FULL_SAMPLES = {
 def test_step_parity_full_size_sampled_layers(name):
     wl = synth.WORKLOADS[name]
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name]))
+
+
+# Without key_out the step keeps only 16-bit keys and recomputes each
+# candidate's full key from m, the owner's residual and its sparse buffer:
+# the configuration bench.py times.
+
+
+@pytest.mark.parametrize("name", ["single-1024x1024", "gpt-345m", "llama-0.55b", "llama-1.75b", "adversarial-ties"])
+def test_step_recomputed_keys_oracle_sized(name):
+    wl = synth.WORKLOADS[name]
+    small = wl if name == "single-1024x1024" else synth.reduced(wl)
+    _assert_bitexact(run_parity(small, wl.steps, key_out=False))
+
+
+def test_step_recomputed_keys_edge_cases():
+    wl = synth.ragged()
+    _assert_bitexact(run_parity(wl, 5, key_out=False))
+    _assert_bitexact(run_parity(wl, 3, W=1, key_out=False))
+    _assert_bitexact(run_parity(wl, 3, keep=(1, 1), init_mask_all=True, key_out=False))
+    zero = lambda step, worker, tensor: np.zeros(wl.tensors[tensor].numel, np.uint16)  # noqa: E731
+    _assert_bitexact(run_parity(wl, 3, grad_override=zero, key_out=False))
+
+
+@pytest.mark.parametrize("name", ["llama-1.75b", "adversarial-ties"])
+def test_step_recomputed_keys_full_size_sampled_layers(name):
+    wl = synth.WORKLOADS[name]
+    _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name], key_out=False))
