@@ -205,6 +205,75 @@ def test_mask_build_empty_layers():
     ctx.destroy()
 
 
+def _sampled_words(lw0, lwords):
+    """Words the key-sampling pass reads in a layer of more than 4096 words:
+    one per aligned group of 16, at a hashed offset (the kernel's rule,
+    restated here to build inputs that defeat the sample)."""
+    out = []
+    for g in range((lwords + 15) // 16):
+        w = lw0 + (g << 4)
+        h = (w * 0x9E3779B1) & 0xFFFFFFFF
+        h ^= h >> 15
+        h = (h * 0x85EBCA77) & 0xFFFFFFFF
+        h ^= h >> 13
+        if (g << 4) + (h & 15) < lwords:
+            out.append(w + (h & 15))
+    return np.array(out, np.int64)
+
+
+@pytest.mark.parametrize("sampled_small", [True, False])
+def test_mask_build_exact_after_a_sampling_miss(sampled_small):
+    """The sampled words hold values unlike the rest of the layer, so the
+    sample's window misses the k-th key: the exact fallback (full first-digit
+    histogram and reclassification) must still give the oracle's mask."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(41 + sampled_small)
+    sizes = [400_000, 5000]
+    keep = (1, 10)
+    ctx = _ctx(sizes, W=2, keep=keep)
+    lay = oracle.layout(sizes, keep[0], keep[1], 2)
+    n0 = sizes[0]
+    small = (rng.random(lay.n_pad) * 0.5 + 0.5).astype(np.float32) * np.float32(2.0 ** -10)
+    large = (rng.random(lay.n_pad) * 0.5 + 0.5).astype(np.float32) * np.float32(2.0 ** 10)
+    sampled = np.zeros(lay.n_pad, bool)
+    for w in _sampled_words(0, (n0 + 63) // 64):
+        sampled[w * 64:(w + 1) * 64] = True
+    sampled[n0:] = False
+    mt = np.where(sampled == sampled_small, small, large).astype(np.float32)
+    mt[lay.off[1]:lay.off[1] + sizes[1]] = rng.standard_normal(sizes[1]).astype(np.float32)
+    out = sc.alloc_mask(ctx.layout)
+    sc.scape_mask_build(ctx, torch.from_numpy(mt).cuda(), out)
+    exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+    assert np.array_equal(u64(out.bits), exp)
+    idx, pre, cnt = oracle.mask_index(exp)
+    assert np.array_equal(u32(out.idx)[:cnt], idx) and np.array_equal(u32(out.block_prefix), pre)
+    ctx.destroy()
+
+
+def test_mask_build_window_wider_than_the_record_histogram():
+    """Half of a sampled layer near 2^60, half near 2^-60, keep 1/2: the k-th
+    key sits at the edge of an empty gap of about 120 octaves, so the
+    sampled window spans thousands of first-digit buckets and the record
+    pass counts straight into the global histogram row."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(43)
+    sizes = [600_000]
+    keep = (1, 2)
+    ctx = _ctx(sizes, W=2, keep=keep)
+    lay = oracle.layout(sizes, keep[0], keep[1], 2)
+    n = sizes[0]
+    mag = np.where(rng.random(n) < 0.5, 2.0 ** 60, 2.0 ** -60) * (1.0 + rng.random(n))
+    mt = np.zeros(lay.n_pad, np.float32)
+    mt[:n] = (mag * np.where(rng.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    out = sc.alloc_mask(ctx.layout)
+    sc.scape_mask_build(ctx, torch.from_numpy(mt).cuda(), out)
+    exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+    assert np.array_equal(u64(out.bits), exp)
+    ctx.destroy()
+
+
 @pytest.mark.parametrize("P", [3, 32])
 def test_mask_build_one_shard_at_a_time(P):
     import torch
