@@ -102,12 +102,14 @@ __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
 #endif
 constexpr int kSampleTiles = SCAPE_SAMPLE_TILES;  // tiles per workgroup in the sampling pass
 constexpr int kSampleBatch = 8;   // sampled words a wave loads at once
+constexpr int kSampleBlock = 1024;  // 16 waves share one 32 KB LDS row: 8 waves per SIMD
+constexpr int kSampleWaves = kSampleBlock / 64;
 
 // In each aligned group of 16 words of a layer, the sampled word is the one at
 // offset hash(group) & 15; layers of up to kFullSampleWords words are taken
 // whole.  A workgroup walks kSampleTiles consecutive tiles and flushes its LDS
 // row when the layer changes.
-__global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
+__global__ __launch_bounds__(kSampleBlock) void k_sample_hist(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                         const LayerDesc* __restrict__ layers,
                                                         const uint16_t* __restrict__ key,
                                                         uint32_t* __restrict__ hist,
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
     const uint32_t wave = threadIdx.x / 64;
     const uint32_t t0 = blockIdx.x * kSampleTiles, t1 = min(t0 + kSampleTiles, n_tiles);
     int cur = -1;
-    for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+    for (int b = threadIdx.x; b < kDigit1Bins; b += kSampleBlock) h[b] = 0;
     if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
     for (uint32_t ti = t0; ti < t1; ++ti) {
@@ -127,10 +129,10 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
         if (t.layer != cur) {  // uniform
             if (cur >= 0) {
                 __syncthreads();
-                hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins);
+                hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins, kSampleBlock);
                 if (threadIdx.x == 0 && s_cnt) atomicAdd(&sample_words[cur], s_cnt);
                 __syncthreads();
-                for (int b = threadIdx.x; b < kDigit1Bins; b += kBlock) h[b] = 0;
+                for (int b = threadIdx.x; b < kDigit1Bins; b += kSampleBlock) h[b] = 0;
                 if (threadIdx.x == 0) s_cnt = 0;
                 __syncthreads();
             }
@@ -145,12 +147,12 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
         const uint32_t g0 = whole ? t.w0 : (t.w0 - lw0) >> kSampleShift;
         const uint32_t g1 = whole ? t.w1 : (t.w1 - lw0 + 15) >> kSampleShift;
         uint32_t nw = 0;
-        for (uint32_t gb = g0 + wave; gb < g1; gb += kWaves * kSampleBatch) {
+        for (uint32_t gb = g0 + wave; gb < g1; gb += kSampleWaves * kSampleBatch) {
             uint32_t kv[kSampleBatch];
             bool inl[kSampleBatch];
 #pragma unroll
             for (int u = 0; u < kSampleBatch; ++u) {  // the batch's loads go out together
-                const uint32_t g = gb + u * kWaves;
+                const uint32_t g = gb + u * kSampleWaves;
                 const uint32_t w = whole ? g : lw0 + (g << kSampleShift) + (word_hash(lw0 + (g << kSampleShift)) & 15u);
                 const uint32_t jj = w * 64u + lane;
                 inl[u] = g < g1 && w < t.w1 && jj < lend;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
     }
     if (cur >= 0) {
         __syncthreads();
-        hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins);
+        hist_flush(h, hist + (size_t)cur * kHistBins, kDigit1Bins, kSampleBlock);
         if (threadIdx.x == 0 && s_cnt) atomicAdd(&sample_words[cur], s_cnt);
     }
 }
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_hist(const TileDesc* __restri
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                               const uint16_t* key, uint32_t* hist, uint32_t* sample_count) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sample_hist, dim3((n_tiles + kSampleTiles - 1) / kSampleTiles), dim3(kBlock), 0, s, tiles,
+    hipLaunchKernelGGL(k_sample_hist, dim3((n_tiles + kSampleTiles - 1) / kSampleTiles), dim3(kSampleBlock), 0, s, tiles,
                        n_tiles, layers, key, hist, sample_count);
     return hipGetLastError();
 }
@@ -258,35 +260,37 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 constexpr int kFilterWords = SCAPE_FILTER_WORDS;  // words per wave per trip
 constexpr int kWaveStage = 256;                 // staged records per wave (2 KB): 8 KB per workgroup
 
-// Full keys of up to 8 records of layer L (the bits of `sel` say which), in
-// place.  All loads are issued unconditionally at safe indices so that the
-// eight gathers overlap: first the mask word, prefix, residual and m of each
-// record, then the sparse-buffer entries those select.
-__device__ __forceinline__ void candidate_keys8(const KeySource& ks, const LayerDesc& L, uint64_t* rec,
-                                                uint32_t sel) {
-    uint32_t jj[8];
+// Full keys of up to kFetch records of layer L (the bits of `sel` say
+// which), in place.  All loads are issued unconditionally at safe indices so
+// that the gathers overlap: first the mask word, prefix, residual and m of
+// each record, then the sparse-buffer entries those select.
+constexpr int kFetch = 4;
+
+__device__ __forceinline__ void candidate_keys(const KeySource& ks, const LayerDesc& L, uint64_t* rec,
+                                               uint32_t sel) {
+    uint32_t jj[kFetch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) jj[u] = L.off + (((sel >> u) & 1u) ? (uint32_t)rec[u] : 0u);
-    uint32_t kk[8];
+    for (int u = 0; u < kFetch; ++u) jj[u] = L.off + (((sel >> u) & 1u) ? (uint32_t)rec[u] : 0u);
+    uint32_t kk[kFetch];
     if (ks.mtilde || ks.key32) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kk[u] = ks.mtilde ? magnitude_key(ks.mtilde[jj[u]]) : ks.key32[jj[u]];
+        for (int u = 0; u < kFetch; ++u) kk[u] = ks.mtilde ? magnitude_key(ks.mtilde[jj[u]]) : ks.key32[jj[u]];
     } else {
         const float* r = ks.r[L.owner];
-        uint64_t word[8];
-        uint32_t pre[8];
-        float rv[8], mv[8];
+        uint64_t word[kFetch];
+        uint32_t pre[kFetch];
+        float rv[kFetch], mv[kFetch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kFetch; ++u) {
             word[u] = ks.cur_bits[jj[u] >> 6];
             pre[u] = ks.cur_prefix[jj[u] >> 6];
             rv[u] = r[jj[u]];
             mv[u] = ks.m[jj[u]];
         }
-        bool on[8];
-        float bv[8];
+        bool on[kFetch];
+        float bv[kFetch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kFetch; ++u) {
             const uint32_t bit = jj[u] & 63u;
             const uint32_t rank = pre[u] + (uint32_t)__popcll(word[u] & ((1ull << bit) - 1ull));
             on[u] = ((word[u] >> bit) & 1ull) && rank < ks.k_cap;
@@ -294,13 +298,13 @@ __device__ __forceinline__ void candidate_keys8(const KeySource& ks, const Layer
             if (ks.k_cap) bv[u] = ks.b[L.owner][on[u] ? rank : 0u];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kFetch; ++u) {
             const float bm = ks.beta1 * mv[u];
             kk[u] = on[u] ? magnitude_key(bv[u]) : magnitude_key(bm + ks.c1 * rv[u]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kFetch; ++u)
         if ((sel >> u) & 1u) rec[u] = ((uint64_t)kk[u] << 32) | (rec[u] & 0xFFFFFFFFull);
 }
 
@@ -679,7 +683,9 @@ __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, 
     }
 }
 
-constexpr int kRecPerThread = kCandChunk / kBlock;  // 32 records held in registers per thread
+constexpr int kPassBlock = 512;                          // threads per workgroup of a record pass
+constexpr int kPassWaves = kPassBlock / 64;
+constexpr int kRecPerThread = kCandChunk / kPassBlock;  // 16 records held in registers per thread
 
 // A layer already done at the passes over key bits 17..15 or 14..6 was
 // decided on the stored bits (T a multiple of 2^15, J = all positions), so
@@ -694,7 +700,7 @@ constexpr int kRecPerThread = kCandChunk / kBlock;  // 32 records held in regist
 // the rest dropped; a layer already done has its selected records marked and
 // the block emptied.  Each workgroup takes a contiguous range of blocks and
 // flushes its LDS histogram only when the layer changes.
-__global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const VblockDesc* __restrict__ vb,
+__global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const VblockDesc* __restrict__ vb,
                                                       uint32_t* __restrict__ vb_count,
                                                       const uint32_t* __restrict__ totals,
                                                       const LayerDesc* __restrict__ layers,
@@ -702,7 +708,7 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
                                                       uint64_t* __restrict__ cand, uint32_t* __restrict__ hist,
                                                       uint64_t* __restrict__ bits) {
     __shared__ uint32_t h[kPassBins];
-    __shared__ uint32_t s_wsum[kWaves];
+    __shared__ uint32_t s_wsum[kPassWaves];
     const uint32_t nv = totals[1];
     const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
     const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
@@ -711,7 +717,7 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
     int cur = -1;
     uint32_t* cur_row = nullptr;  // global bins of the LDS row (first bin)
     int cur_nb = 0;               // bins to flush; 0 when counting straight into the row
-    for (int b = threadIdx.x; b < kPassBins; b += kBlock) h[b] = 0;
+    for (int b = threadIdx.x; b < kPassBins; b += kPassBlock) h[b] = 0;
     for (uint32_t v = v0; v < v1; ++v) {
         const uint32_t cnt = vb_count[v];
         if (cnt == 0) continue;  // uniform
@@ -735,9 +741,9 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
         if (hist_on && l != cur) {
             if (cur >= 0) {
                 __syncthreads();
-                if (cur_nb) hist_flush(h, cur_row, cur_nb);
+                if (cur_nb) hist_flush(h, cur_row, cur_nb, kPassBlock);
                 __syncthreads();
-                for (int b = threadIdx.x; b < kPassBins; b += kBlock) h[b] = 0;
+                for (int b = threadIdx.x; b < kPassBins; b += kPassBlock) h[b] = 0;
             }
             cur = l;
             cur_row = hist + (size_t)l * kHistBins + lo;
@@ -753,14 +759,14 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
         uint64_t rec[kRecPerThread];
 #pragma unroll
         for (int i = 0; i < kRecPerThread; ++i) {
-            const uint32_t p = threadIdx.x + i * kBlock;
+            const uint32_t p = threadIdx.x + i * kPassBlock;
             rec[i] = p < cnt ? cand[(size_t)D.p0 + p] : 0ull;
         }
         uint32_t und = 0;  // bit i: record i undecided
 #pragma unroll
         for (int i = 0; i < kRecPerThread; ++i) {
-            if ((uint32_t)(i * kBlock) + wave * 64u >= cnt) break;  // uniform per wave
-            const uint32_t p = threadIdx.x + i * kBlock;
+            if ((uint32_t)(i * kPassBlock) + wave * 64u >= cnt) break;  // uniform per wave
+            const uint32_t p = threadIdx.x + i * kPassBlock;
             const uint32_t kv = (uint32_t)(rec[i] >> 32), jl = (uint32_t)rec[i];
             uint32_t digit = 0;
             const uint32_t c = p < cnt ? classify(cph, S, kv, jl, &digit) : 0u;
@@ -776,14 +782,14 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
         }
         if (fetch) {
 #pragma unroll
-            for (int g = 0; g < kRecPerThread; g += 8) {
-                const uint32_t sel = (und >> g) & 0xFFu;
-                if (__ballot(sel != 0u) == 0) continue;  // the wave holds none of these eight
-                candidate_keys8(ks, Ld, &rec[g], sel);
+            for (int g = 0; g < kRecPerThread; g += kFetch) {
+                const uint32_t sel = (und >> g) & ((1u << kFetch) - 1u);
+                if (__ballot(sel != 0u) == 0) continue;  // the wave holds none of these
+                candidate_keys(ks, Ld, &rec[g], sel);
             }
 #pragma unroll
             for (int i = 0; i < kRecPerThread; ++i) {
-                if ((uint32_t)(i * kBlock) + wave * 64u >= cnt) break;  // uniform per wave
+                if ((uint32_t)(i * kPassBlock) + wave * 64u >= cnt) break;  // uniform per wave
                 const uint32_t digit = ((uint32_t)(rec[i] >> 32) >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
                 hist_add_wave(h, digit, (und >> i) & 1u);
             }
@@ -798,7 +804,7 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
             if (lane == 0) s_wsum[wave] = wsum;
             __syncthreads();
             uint32_t base = 0, total = 0;
-            for (uint32_t q = 0; q < (uint32_t)kWaves; ++q) {
+            for (uint32_t q = 0; q < (uint32_t)kPassWaves; ++q) {
                 if (q < wave) base += s_wsum[q];
                 total += s_wsum[q];
             }
@@ -815,14 +821,14 @@ __global__ __launch_bounds__(kBlock) void k_cand_pass(uint32_t phase, const Vblo
     }
     if (cur >= 0) {
         __syncthreads();
-        if (cur_nb) hist_flush(h, cur_row, cur_nb);
+        if (cur_nb) hist_flush(h, cur_row, cur_nb, kPassBlock);
     }
 }
 
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
                             const uint32_t* totals, const LayerDesc* layers, const SelState* st,
                             const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits) {
-    hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kBlock), 0, s, phase, vb, vb_count, totals, layers, st, ks, cand,
+    hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kPassBlock), 0, s, phase, vb, vb_count, totals, layers, st, ks, cand,
                        hist, bits);
     return hipGetLastError();
 }

@@ -67,9 +67,10 @@ __device__ __forceinline__ void hist_add_wave(uint32_t* lds_hist, uint32_t bin, 
     }
 }
 
-// Flush a workgroup's LDS histogram row into the global per-layer row.
-__device__ __forceinline__ void hist_flush(const uint32_t* lds_hist, uint32_t* row, int bins) {
-    for (int b = threadIdx.x; b < bins; b += kBlock) {
+// Flush a workgroup's LDS histogram row into the global per-layer row
+// (`threads` is the workgroup size).
+__device__ __forceinline__ void hist_flush(const uint32_t* lds_hist, uint32_t* row, int bins, int threads = kBlock) {
+    for (int b = threadIdx.x; b < bins; b += threads) {
         uint32_t c = lds_hist[b];
         if (c) atomicAdd(&row[b], c);
     }
