@@ -40,22 +40,12 @@ namespace scape {
 // 16-bit descriptor gives the owner worker (bits 8..13) and the number of
 // elements of the word inside its layer (bits 0..6, 1..64; 0 = padding).
 // Every worker's loads are issued before any store.
-#ifndef SCAPE_EF_NT
-#define SCAPE_EF_NT 1
-#endif
-// Streamed element loads and stores of the dense pass (bit 0: loads, bit 1:
-// stores non-temporal).  Non-temporal loads of the streamed arrays keep the
+// The dense pass loads its streamed arrays non-temporally: that keeps the
 // sparse buffers and the m stash, which the update pass reads next, in the
-// caches; non-temporal stores measured slower for the update pass.
+// caches (measured faster; non-temporal stores here made the update slower).
 template <typename T>
-__device__ __forceinline__ T ef_load(const T* p) {
-    if (SCAPE_EF_NT & 1) return __builtin_nontemporal_load(p);
-    return *p;
-}
-template <typename T>
-__device__ __forceinline__ void ef_store(T v, T* p) {
-    if (SCAPE_EF_NT & 2) __builtin_nontemporal_store(v, p);
-    else *p = v;
+__device__ __forceinline__ T stream_load(const T* p) {
+    return __builtin_nontemporal_load(p);
 }
 
 template <int WT, bool K32>
@@ -74,14 +64,14 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
     // the element loads go out at once, beside the word's descriptors, and
     // the padding lanes are dropped only before the stores
     const size_t j = (size_t)w * 64u + lane;
-    const float mo = ef_load(&m[j]);
+    const float mo = stream_load(&m[j]);
     float rv[WMAX];
     uint16_t gv[WMAX];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
         if (i >= W) break;
-        rv[i] = ef_load(&wp.r[i][j]);
-        gv[i] = ef_load(&wp.g[i][j]);
+        rv[i] = stream_load(&wp.r[i][j]);
+        gv[i] = stream_load(&wp.g[i][j]);
     }
     const uint32_t info = word_info[w];
     const uint64_t word = cur_bits[w];
@@ -99,12 +89,12 @@ __global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restric
         const float a = rv[i] + bf16_bits_to_f32(gv[i]);
         const float mt = bm + sc.c1 * a;
         if (i == owner) kk = magnitude_key(mt);
-        ef_store(msk ? 0.0f : a, &wp.r[i][j]);
+        wp.r[i][j] = msk ? 0.0f : a;
         if (msk) wp.b[i][rank] = mt;
     }
     // the selection reads the top 16 bits; candidates get their full key
     // back from the state (or from key32 when it is asked for)
-    ef_store((uint16_t)(kk >> kKeyShift), &key16[j]);
+    key16[j] = (uint16_t)(kk >> kKeyShift);
     if (K32) key32[j] = kk;
     // m before the step, compacted like the sparse buffers: the update pass
     // reads it contiguously instead of gathering one cache line per position
@@ -211,11 +201,7 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 4
 #endif
-// The update pass's scattered x gather and x/m/v stores bypass the cache
-// hierarchy's normal allocation (measured faster).
-#ifndef SCAPE_UPDATE_NT
-#define SCAPE_UPDATE_NT 1
-#endif
+
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;
 
 template <int WT>
@@ -241,11 +227,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         jj[u] = ok[u] ? idx[q] : 0u;
         ok[u] = ok[u] && jj[u] < n_pad;
         mo[u] = ok[u] ? m_stash[q] : 0.0f;
-#if SCAPE_UPDATE_NT
         xv[u] = ok[u] ? __builtin_nontemporal_load(&x[jj[u]]) : 0.0f;
-#else
-        xv[u] = ok[u] ? x[jj[u]] : 0.0f;
-#endif
         s[u] = ok[u] ? wp.b[0][q] : 0.0f;
     }
 #pragma unroll
@@ -265,15 +247,10 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         const float vv = sc.beta2 * (mo[u] * mo[u]) + sc.c2 * (ghat * ghat);
         float upd = bb / (sqrtf(vv) + sc.eps);
         if (sc.wd != 0.0f) upd = upd + sc.wd * xv[u];
-#if SCAPE_UPDATE_NT
+        // the scattered gather and stores are non-temporal (measured faster)
         __builtin_nontemporal_store(vv, &v[jj[u]]);
         __builtin_nontemporal_store(bb, &m[jj[u]]);
         __builtin_nontemporal_store(xv[u] - sc.lr * upd, &x[jj[u]]);
-#else
-        v[jj[u]] = vv;
-        m[jj[u]] = bb;
-        x[jj[u]] = xv[u] - sc.lr * upd;
-#endif
     }
 }
 

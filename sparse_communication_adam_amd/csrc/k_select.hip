@@ -344,7 +344,7 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) {
             const uint32_t jj = (w0 + e) * 64u + lane;
-            kv[e] = (w0 + e < t.w1 && jj < lend) ? (uint32_t)key[jj] : 0u;
+            kv[e] = (w0 + e < t.w1) ? (uint32_t)key[jj] : 0u;  // padding lanes are in bounds; inl drops them
         }
     };
     load_keys(t.w0 + wave * kFilterWords, nxt);
