@@ -290,12 +290,16 @@ def main() -> int:
     log(f"{args.warmup} warmup steps done")
 
     sc.scape_profile_enable(state.ctx, True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    evs[0].record()
     for s in range(args.steps):
         state.step(sets[(args.warmup + s) % len(sets)], key_out=False)
+        evs[s + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     phase_ms, nrec = sc.scape_profile_read(state.ctx)
     sc.scape_profile_enable(state.ctx, False)
     ms = (t1 - t0) * 1e3 / args.steps
@@ -344,6 +348,8 @@ def main() -> int:
         "config": {"workload": wl.name, "params": N, "tensors": len(wl.tensors), "workers": W,
                    "keep": f"{wl.keep_num}/{wl.keep_den}", "kept_total": ksum, "grad_dtype": "bf16",
                    "gradient_batches": args.grad_sets},
+        "step_ms_median": step_ms[len(step_ms) // 2], "step_ms_min": step_ms[0],
+        "worker_elements_per_s": W * N / (ms * 1e-3),
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
         "device_copy_GBps": copy_gbps,

@@ -138,3 +138,17 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(s, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         s.lib()
+
+
+def test_binding_requires_pinned_host_residuals(sc):
+    """The offloaded step's residuals must be pinned host memory: a device
+    tensor, a pageable host tensor or a wrong dtype is refused before any
+    call into the library."""
+    import torch
+    from sparse_communication_adam_amd._scape import _host
+    with pytest.raises(ValueError, match="pinned"):
+        _host(torch.zeros(16, dtype=torch.float32), torch.float32, 16, "r_host[0]")
+    with pytest.raises(TypeError):
+        _host(torch.zeros(16, dtype=torch.float64), torch.float32, 16, "r_host[0]")
+    with pytest.raises(TypeError):
+        _host(np.zeros(16, np.float32), torch.float32, 16, "r_host[0]")
