@@ -222,6 +222,21 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
             "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
 
 
+def spin_up(seconds: float) -> None:
+    """Plain device-to-device copies for `seconds`: an idle GPU takes a while
+    to reach its steady memory and fabric clocks."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
 def copy_bandwidth(nbytes: int = 4 << 30) -> float:
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -250,6 +265,9 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
     ap.add_argument("--no-offload", action="store_true", help="skip the host-residual (offload) step")
+    ap.add_argument("--spinup-s", type=float, default=1.0,
+                    help="seconds of plain device copies before anything else, so the GPU runs at steady clocks "
+                         "(the optimizer state is untouched: warmup steps would advance it)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -266,6 +284,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     sc.lib()
+    if args.spinup_s > 0:
+        spin_up(args.spinup_s)
     wl = synth.WORKLOADS[args.workload]
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
