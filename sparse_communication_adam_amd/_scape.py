@@ -239,6 +239,7 @@ def alloc_mask(layout: Layout, device="cuda") -> Mask:
 
 class Context:
     def __init__(self, cfg: ScapeConfig):
+        self._h = None
         self.cfg = cfg
         self.layout = scape_layout(cfg)
         h = ctypes.c_void_p()

@@ -630,8 +630,14 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
 
 int scape_destroy(scape_ctx* ctx) {
     if (!ctx) return SCAPE_OK;
+    // wait for the context's own device, free its workspaces there, and leave
+    // the caller's current device as it was
+    int prev = -1;
+    const bool switched = hipGetDevice(&prev) == hipSuccess && prev != ctx->device &&
+                          hipSetDevice(ctx->device) == hipSuccess;
     hipDeviceSynchronize();
     free_ctx(ctx);
+    if (switched) hipSetDevice(prev);
     return SCAPE_OK;
 }
 
