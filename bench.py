@@ -71,8 +71,8 @@ def kernel_source_hash() -> str:
     the device helpers, and the constants and argument structs it uses."""
     csrc = os.path.join(ROOT, "sparse_communication_adam_amd", "csrc")
     el = open(os.path.join(csrc, "k_elementwise.hip")).read()
-    a = el.index("__global__ __launch_bounds__(kBlock) void k_ef_compact")
-    b = el.index("#undef SCAPE_EF_CASE", a)
+    a = el.index("// Dense pass, one-shot layout")   # the dense pass's section: helpers, knobs, kernel
+    b = el.index("#undef SCAPE_EF_CASE", a)         # ... through its launcher
     parts = [el[a:b], open(os.path.join(csrc, "scape_device.h")).read()]
     hdr = open(os.path.join(csrc, "scape_internal.h")).read()
     for pat in (r"constexpr int kBlock = .*?;", r"constexpr int kWaves = .*?;", r"struct WorkerPtrs \{.*?\};",

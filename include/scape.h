@@ -265,7 +265,10 @@ int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream);
 int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream);
 
 /* Optional per-phase timing of scape_step with HIP events recorded on the
- * step's stream.  Phases: */
+ * step's stream (and on the context's update stream).  The W-way reduction
+ * and update run on the context's own stream beside the mask selection (they
+ * share no data the other writes), so those two phases overlap: both are
+ * measured from the end of the dense pass.  Phases: */
 #define SCAPE_PHASE_EF_COMPACT 0    /* error feedback, candidates, compaction, statistic */
 #define SCAPE_PHASE_REDUCE_UPDATE 1 /* W-way reduction, reconstruction, v/m/x update     */
 #define SCAPE_PHASE_MASK_SELECT 2   /* per-layer top-k into bits                        */

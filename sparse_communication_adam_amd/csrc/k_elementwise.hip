@@ -48,15 +48,21 @@ __device__ __forceinline__ T stream_load(const T* p) {
     return __builtin_nontemporal_load(p);
 }
 
+#ifndef SCAPE_EF_BLOCK
+#define SCAPE_EF_BLOCK 256
+#endif
+constexpr int kEfBlock = SCAPE_EF_BLOCK;  // threads per workgroup of the dense pass (one word per wave)
+constexpr int kEfWaves = kEfBlock / 64;
+
 template <int WT, bool K32>
-__global__ __launch_bounds__(kBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
+__global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
                                                        WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
                                                        uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
                                                        float* __restrict__ m_stash) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
-    const uint32_t w = blockIdx.x * kWaves + threadIdx.x / 64;
+    const uint32_t w = blockIdx.x * kEfWaves + threadIdx.x / 64;
     if (w >= n_words) return;
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
@@ -106,9 +112,9 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
                              float* m_stash) {
     if (n_words == 0) return hipSuccess;
-    const dim3 grid((n_words + kWaves - 1) / kWaves);
+    const dim3 grid((n_words + kEfWaves - 1) / kEfWaves);
 #define SCAPE_EF_LAUNCH(WV, K)                                                                                  \
-    hipLaunchKernelGGL((k_ef_compact<WV, K>), grid, dim3(kBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
+    hipLaunchKernelGGL((k_ef_compact<WV, K>), grid, dim3(kEfBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
                        cur_prefix, k_cap, key16, key32, m_stash)
 #define SCAPE_EF_CASE(WV)                    \
     case WV:                                 \
@@ -197,12 +203,20 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 
 // Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
 // by the workgroup size so that idx, the sparse buffers and the m stash are
-// read contiguously), every load issued before the arithmetic.
+// read contiguously), every load issued before the arithmetic.  The pass runs
+// beside the mask selection on another stream; its grid is capped at a
+// workgroup per CU and strides over the positions, which leaves the
+// selection's latency-bound passes more of the memory system (measured: the
+// two together finish sooner than with one workgroup per chunk, or in turn).
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 4
 #endif
+#ifndef SCAPE_UPDATE_GRID
+#define SCAPE_UPDATE_GRID 256
+#endif
 
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;
+constexpr uint32_t kUpdateGrid = SCAPE_UPDATE_GRID;  // workgroups at most (0: one per chunk)
 
 template <int WT>
 __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepScalars sc, float* __restrict__ x,
@@ -216,7 +230,9 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
     const uint32_t cnt = total < k_cap ? total : k_cap;
     const int W = WT > 0 ? WT : sc.W;
     const float fW = (float)W;
-    const uint32_t q0 = blockIdx.x * (kBlock * kUpdatePer) + threadIdx.x;
+    constexpr uint32_t chunk = kBlock * kUpdatePer;
+    for (uint32_t base = blockIdx.x * chunk; base < cnt; base += gridDim.x * chunk) {
+    const uint32_t q0 = base + threadIdx.x;
     uint32_t jj[kUpdatePer];
     float mo[kUpdatePer], xv[kUpdatePer], s[kUpdatePer];
     bool ok[kUpdatePer];
@@ -252,13 +268,16 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         __builtin_nontemporal_store(bb, &m[jj[u]]);
         __builtin_nontemporal_store(xv[u] - sc.lr * upd, &x[jj[u]]);
     }
+    }
 }
 
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
                                 float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
                                 uint32_t n_words, uint32_t n_pad, uint32_t k_cap) {
     if (k_cap == 0) return hipSuccess;
-    const dim3 grid((k_cap + kBlock * kUpdatePer - 1) / (kBlock * kUpdatePer));
+    uint32_t blocks = (k_cap + kBlock * kUpdatePer - 1) / (kBlock * kUpdatePer);
+    if (kUpdateGrid > 0 && blocks > kUpdateGrid) blocks = kUpdateGrid;
+    const dim3 grid(blocks);
 #define SCAPE_RU_CASE(WV)                                                                                     \
     case WV:                                                                                                  \
         hipLaunchKernelGGL(k_reduce_update<WV>, grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix, \

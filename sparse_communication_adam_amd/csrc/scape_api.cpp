@@ -156,6 +156,9 @@ struct scape_ctx {
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
+    // the update runs on its own stream beside the mask selection
+    hipStream_t s_upd = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // residual offload: two staging slots of W chunks, a copy-in and a copy-out stream
     float* d_stage = nullptr;         // [2][W][chunk_words * 64]
     uint32_t chunk_words = 0;
@@ -199,6 +202,9 @@ void free_ctx(scape_ctx* c) {
         if (c->ev_k[b]) hipEventDestroy(c->ev_k[b]);
         if (c->ev_out[b]) hipEventDestroy(c->ev_out[b]);
     }
+    if (c->ev_fork) hipEventDestroy(c->ev_fork);
+    if (c->ev_join) hipEventDestroy(c->ev_join);
+    if (c->s_upd) hipStreamDestroy(c->s_upd);
     if (c->s_in) hipStreamDestroy(c->s_in);
     if (c->s_out) hipStreamDestroy(c->s_out);
     if (c->prof_events)
@@ -245,9 +251,15 @@ void prof_collect(scape_ctx* c, int slot) {
     ProfSlot& p = c->prof[slot];
     if (!p.pending) return;
     hipEventSynchronize(p.ev[SCAPE_PHASE_COUNT]);
+    // points: 0 start, 1 end of the dense pass (where the update and the
+    // selection fork), 2 end of the update, 3 end of the selection, 4 end of
+    // the index and the join.  The update and the selection run side by side,
+    // so both are measured from point 1.
+    static const int from[SCAPE_PHASE_COUNT] = {0, 1, 1, 3};
+    static const int to[SCAPE_PHASE_COUNT] = {1, 2, 3, 4};
     for (int i = 0; i < SCAPE_PHASE_COUNT; ++i) {
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, p.ev[i], p.ev[i + 1]) == hipSuccess) c->prof_ms[i] += ms;
+        if (hipEventElapsedTime(&ms, p.ev[from[i]], p.ev[to[i]]) == hipSuccess) c->prof_ms[i] += ms;
     }
     c->prof_steps += 1;
     p.pending = false;
@@ -439,13 +451,28 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
                   "ef_compact");
     }
     prof_mark(ctx, slot, 1, s);
-    SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash, ctx->n_words,
-                                   (uint32_t)ctx->lay.n_pad, k_cap),
+    // The update touches x, v, and m on the mask only; the selection reads
+    // the keys, m off the mask, the owner's residual and the sparse buffers.
+    // Nothing one writes is read by the other, so the update runs on its own
+    // stream beside the selection, and `stream` waits for it at the end.
+    SCAPE_HIP(hipEventRecord(ctx->ev_fork, s), "fork");
+    rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s);
+    if (rc) return rc;  // nothing was queued on the update's stream
+    SCAPE_HIP(hipStreamWaitEvent(ctx->s_upd, ctx->ev_fork, 0), "fork");
+    SCAPE_HIP(launch_reduce_update(ctx->s_upd, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash,
+                                   ctx->n_words, (uint32_t)ctx->lay.n_pad, k_cap),
               "reduce_update");
-    prof_mark(ctx, slot, 2, s);
-    if ((rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s))) return rc;
+    prof_mark(ctx, slot, 2, ctx->s_upd);
+    const hipError_t je = hipEventRecord(ctx->ev_join, ctx->s_upd);
+    if (je != hipSuccess) {  // no event to join on: the update must still not outlive the step
+        hipStreamSynchronize(ctx->s_upd);
+        return hip_fail(je, "join");
+    }
     prof_mark(ctx, slot, 3, s);
-    if ((rc = run_index(ctx, next, s))) return rc;
+    rc = run_index(ctx, next, s);
+    // join even after a failed launch
+    SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_join, 0), "join");
+    if (rc) return rc;
     if (r_on_host && ctx->n_words > 0) {
         // the step completes on `stream` only once every residual chunk is home
         SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[0], 0), "offload wait");
@@ -585,6 +612,14 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_union_bits, (size_t)c->n_words, "union staging bits"))) {
         free_ctx(c);
         return rc;
+    }
+    // the update's stream and its fork/join events (default priority; the events only order work)
+    e = hipStreamCreateWithFlags(&c->s_upd, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        free_ctx(c);
+        return hip_fail(e, "creating the update stream and events");
     }
     // residual offload resources (default-priority streams; the events only order work)
     c->chunk_words = std::min<uint32_t>(c->n_words, kOffloadChunkWords);
