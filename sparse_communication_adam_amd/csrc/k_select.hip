@@ -101,7 +101,9 @@ __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
 #define SCAPE_SAMPLE_TILES 16
 #endif
 constexpr int kSampleTiles = SCAPE_SAMPLE_TILES;  // tiles per workgroup in the sampling pass
-constexpr int kSampleBatch = 8;   // sampled words a wave loads at once
+// Sampled words a wave loads at once: a 512-word tile holds 32 sampled words,
+// two for each of the 16 waves, so a larger batch would only add empty slots.
+constexpr int kSampleBatch = 2;
 constexpr int kSampleBlock = 1024;  // 16 waves share one 32 KB LDS row: 8 waves per SIMD
 constexpr int kSampleWaves = kSampleBlock / 64;
 
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample_hist(const TileDesc* __
     __shared__ uint32_t h[kDigit1Bins];
     __shared__ uint32_t s_cnt;
     const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const uint32_t t0 = blockIdx.x * kSampleTiles, t1 = min(t0 + kSampleTiles, n_tiles);
     int cur = -1;
     for (int b = threadIdx.x; b < kDigit1Bins; b += kSampleBlock) h[b] = 0;
@@ -146,25 +148,29 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample_hist(const TileDesc* __
         // (tiles start on multiples of 16 words within the layer)
         const uint32_t g0 = whole ? t.w0 : (t.w0 - lw0) >> kSampleShift;
         const uint32_t g1 = whole ? t.w1 : (t.w1 - lw0 + 15) >> kSampleShift;
-        uint32_t nw = 0;
+        uint32_t nk = 0;  // keys this wave sampled
         for (uint32_t gb = g0 + wave; gb < g1; gb += kSampleWaves * kSampleBatch) {
-            uint32_t kv[kSampleBatch];
-            bool inl[kSampleBatch];
+            // The batch's words are wave-uniform.  Every load is issued, at a
+            // word of the tile (a sampled word outside it loads the tile's
+            // first word and is skipped), before any key is used, so the
+            // batch's loads are in flight together.
+            uint32_t wv[kSampleBatch], kv[kSampleBatch];
 #pragma unroll
-            for (int u = 0; u < kSampleBatch; ++u) {  // the batch's loads go out together
+            for (int u = 0; u < kSampleBatch; ++u) {
                 const uint32_t g = gb + u * kSampleWaves;
                 const uint32_t w = whole ? g : lw0 + (g << kSampleShift) + (word_hash(lw0 + (g << kSampleShift)) & 15u);
-                const uint32_t jj = w * 64u + lane;
-                inl[u] = g < g1 && w < t.w1 && jj < lend;
-                kv[u] = inl[u] ? (uint32_t)key[jj] : 0u;
+                wv[u] = (g < g1 && w < t.w1) ? w : kNone;
+                kv[u] = key[(size_t)(wv[u] != kNone ? w : t.w0) * 64u + lane];
             }
 #pragma unroll
             for (int u = 0; u < kSampleBatch; ++u) {
-                hist_add_wave(h, kv[u] >> kDigit1FromKey16, inl[u]);
-                nw += (uint32_t)__popcll(__ballot(inl[u]));
+                if (wv[u] == kNone) continue;
+                const uint32_t left = lend - wv[u] * 64u;  // keys of the word inside the layer (>= 1)
+                hist_add_wave(h, kv[u] >> kDigit1FromKey16, lane < left);
+                nk += left < 64u ? left : 64u;
             }
         }
-        if (lane == 0 && nw) atomicAdd(&s_cnt, nw);
+        if (lane == 0 && nk) atomicAdd(&s_cnt, nk);
     }
     if (cur >= 0) {
         __syncthreads();
@@ -325,26 +331,61 @@ __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, ui
 // counter places all of the workgroup's records (a wave whose staging fills
 // up mid-tile reserves on its own), and the count of bits set is added to the
 // segment's total.  Must be called by every thread of the workgroup.
-__device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, const SegDesc& G, uint32_t sel_from,
-                                         uint32_t cand_lo, uint32_t cand_hi, const uint16_t* __restrict__ key,
-                                         uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
-                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
-    __shared__ uint64_t s_rec[kWaves][kWaveStage];
-    __shared__ uint32_t s_n[kWaves], s_ab[kWaves], s_base;
+// LDS of the key pass: each wave's staged records, and the workgroup's
+// record and bit counts.
+struct KeyPassLds {
+    uint64_t rec[kWaves][kWaveStage];
+    uint32_t n[kWaves], ab[kWaves], base;
+};
+
+template <bool kRecords>
+__device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
+                                         uint32_t sel_from, uint32_t cand_lo, uint32_t cand_hi,
+                                         const uint16_t* __restrict__ key, uint64_t* __restrict__ bits,
+                                         uint32_t* __restrict__ seg_fill, uint64_t* __restrict__ cand,
+                                         uint32_t* __restrict__ seg_above) {
     const uint32_t lend = L.off + L.n;
     const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
-    uint64_t* stage = s_rec[wave];
-    const bool records = cand_lo <= cand_hi;
-    uint32_t n_st = 0, n_above = 0;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    uint64_t* stage = lds.rec[wave];
+    // the digit tests on the stored 16-bit key (digit = key >> 3): above is
+    // key >= k_above, a record key - k_lo <= k_span (unsigned)
+    const uint32_t k_above = sel_from << kDigit1FromKey16;
+    const uint32_t k_lo = cand_lo << kDigit1FromKey16;
+    const uint32_t k_span = kRecords ? ((cand_hi - cand_lo) << kDigit1FromKey16) | ((1u << kDigit1FromKey16) - 1u) : 0u;
+    uint32_t n_st = 0;
+    uint32_t above_lane = 0;  // bits set in the mask words this lane wrote
     constexpr uint32_t kStride = kWaves * kFilterWords;
-    // the next trip's keys are loaded before this trip is processed
+    // The next trip's keys are loaded before this trip is processed.  Every
+    // load is issued, at a word of the tile (a word past its end loads the
+    // tile's last word and is skipped), so the count of loads in flight is
+    // the same on every path and the next trip's loads stay in flight while
+    // this one is processed.
     uint32_t nxt[kFilterWords];
     auto load_keys = [&](uint32_t w0, uint32_t* kv) {
 #pragma unroll
-        for (int e = 0; e < kFilterWords; ++e) {
-            const uint32_t jj = (w0 + e) * 64u + lane;
-            kv[e] = (w0 + e < t.w1) ? (uint32_t)key[jj] : 0u;  // padding lanes are in bounds; inl drops them
+        for (int e = 0; e < kFilterWords; ++e) kv[e] = key[(size_t)min(w0 + e, t.w1 - 1u) * 64u + lane];
+    };
+    // One word: its mask word (kept by lane e) and its records.  `left` is
+    // the number of its keys inside the layer (64 for every word but a
+    // layer's last).
+    auto one_word = [&](uint32_t w, uint32_t kw, int e, uint32_t left, uint64_t lmask, uint64_t& mine) {
+        const uint64_t word = wave_ballot(kw >= k_above) & lmask;
+        if (lane == (uint32_t)e) mine = word;
+        if (kRecords) {
+            const bool in_range = kw - k_lo <= k_span;
+            const uint64_t cb = wave_ballot(in_range) & lmask;
+            if (cb) {
+                if (n_st > (uint32_t)(kWaveStage - 64)) {  // no room for a whole word: flush
+                    uint32_t first = 0;
+                    if (lane == 0) first = atomicAdd(&seg_fill[t.seg], n_st);
+                    wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
+                    n_st = 0;
+                }
+                if (in_range && lane < left)
+                    stage[n_st + lanes_below(cb)] = ((uint64_t)(kw << kKeyShift) << 32) | (uint64_t)(w * 64u + lane - L.off);
+                n_st += (uint32_t)__popcll(cb);
+            }
         }
     };
     load_keys(t.w0 + wave * kFilterWords, nxt);
@@ -352,51 +393,44 @@ __device__ __forceinline__ void key_pass(const TileDesc& t, const LayerDesc& L, 
         uint32_t kv[kFilterWords];
 #pragma unroll
         for (int e = 0; e < kFilterWords; ++e) kv[e] = nxt[e];
-        if (w0 + kStride < t.w1) load_keys(w0 + kStride, nxt);
-        uint64_t mine = 0;
+        load_keys(w0 + kStride, nxt);
+        uint64_t mine = 0;  // lane e: the mask word of word w0 + e
+        if (w0 + kFilterWords <= t.w1 && (w0 + kFilterWords) * 64u <= lend) {
+            // every word of the trip is in the tile and wholly in the layer
 #pragma unroll
-        for (int e = 0; e < kFilterWords; ++e) {
-            const uint32_t jj = (w0 + e) * 64u + lane;
-            const bool inl = (w0 + e < t.w1) && jj < lend;
-            const uint32_t d = kv[e] >> kDigit1FromKey16;
-            const uint64_t word = __ballot(inl && d >= sel_from);
-            n_above += (uint32_t)__popcll(word);
-            if (lane == (uint32_t)e) mine = word;
-            if (records) {
-                const bool cnd = inl && cand_lo <= d && d <= cand_hi;
-                const uint64_t cb = __ballot(cnd);
-                if (cb) {
-                    if (n_st > (uint32_t)(kWaveStage - 64)) {  // no room for a whole word: flush
-                        uint32_t first = 0;
-                        if (lane == 0) first = atomicAdd(&seg_fill[t.seg], n_st);
-                        wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
-                        n_st = 0;
-                    }
-                    if (cnd)
-                        stage[n_st + lanes_below(cb)] = ((uint64_t)(kv[e] << kKeyShift) << 32) | (uint64_t)(jj - L.off);
-                    n_st += (uint32_t)__popcll(cb);
-                }
+            for (int e = 0; e < kFilterWords; ++e) one_word(w0 + e, kv[e], e, 64u, ~0ull, mine);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kFilterWords; ++e) {
+                const uint32_t w = w0 + e;
+                if (w >= t.w1) break;
+                const uint32_t left = lend - w * 64u;  // >= 1 for a word of the tile
+                one_word(w, kv[e], e, left, left >= 64u ? ~0ull : (1ull << left) - 1ull, mine);
             }
         }
-        if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) bits[w0 + lane] = mine;
+        if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) {
+            bits[w0 + lane] = mine;
+            above_lane += (uint32_t)__popcll(mine);
+        }
     }
+    const uint32_t n_above = wave_sum(above_lane);
     if (lane == 0) {
-        s_n[wave] = n_st;
-        s_ab[wave] = n_above;
+        lds.n[wave] = n_st;
+        lds.ab[wave] = n_above;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t tot = 0, ab = 0;
         for (int q = 0; q < kWaves; ++q) {
-            tot += s_n[q];
-            ab += s_ab[q];
+            tot += lds.n[q];
+            ab += lds.ab[q];
         }
-        s_base = tot ? atomicAdd(&seg_fill[t.seg], tot) : 0u;
+        lds.base = tot ? atomicAdd(&seg_fill[t.seg], tot) : 0u;
         if (ab) atomicAdd(&seg_above[t.seg], ab);
     }
     __syncthreads();
-    uint32_t first = s_base;
-    for (uint32_t q = 0; q < wave; ++q) first += s_n[q];
+    uint32_t first = lds.base;
+    for (uint32_t q = 0; q < wave; ++q) first += lds.n[q];
     wave_store(stage, n_st, first, G, cand);
 }
 
@@ -411,9 +445,12 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
     const SegDesc G = segs[t.seg];
     const SelState S = st[t.layer];
     const bool win = S.n_lo <= S.n_hi && L.k > 0;
+    __shared__ KeyPassLds lds;
     // no window (nothing to select, or an empty sample): no bits, no records
-    key_pass(t, L, G, win ? S.n_hi + 1 : (uint32_t)kDigit1Bins, win ? S.n_lo : 1u, win ? S.n_hi : 0u, key, bits,
-             seg_fill, cand, seg_above);
+    if (win)
+        key_pass<true>(lds, t, L, G, S.n_hi + 1, S.n_lo, S.n_hi, key, bits, seg_fill, cand, seg_above);
+    else  // no window (nothing to select, or an empty sample): no bits, no records
+        key_pass<false>(lds, t, L, G, (uint32_t)kDigit1Bins, 1u, 0u, key, bits, seg_fill, cand, seg_above);
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
@@ -554,6 +591,7 @@ __global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restr
                                                          const uint16_t* __restrict__ key,
                                                          uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
                                                          uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
+    __shared__ KeyPassLds lds;
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const TileDesc t = tiles[ti];
         const SelState S = st[t.layer];
@@ -561,9 +599,9 @@ __global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restr
         const LayerDesc L = layers[t.layer];
         const SegDesc G = segs[t.seg];
         if (S.all_bucket)  // keys in the threshold bucket and above, no records
-            key_pass(t, L, G, S.d1, 1, 0, key, bits, seg_fill, cand, seg_above);
+            key_pass<false>(lds, t, L, G, S.d1, 1, 0, key, bits, seg_fill, cand, seg_above);
         else  // above the bucket: bits; in it: records
-            key_pass(t, L, G, S.d1 + 1, S.d1, S.d1, key, bits, seg_fill, cand, seg_above);
+            key_pass<true>(lds, t, L, G, S.d1 + 1, S.d1, S.d1, key, bits, seg_fill, cand, seg_above);
         __syncthreads();  // the next tile reuses the LDS staging
     }
 }

@@ -10,6 +10,18 @@ namespace scape {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// Mask of the active lanes for which `p` holds.  The compiler builtin takes
+// the compare result as it is; the HIP wrapper first widens the predicate to
+// an integer and compares it again, two more vector instructions per use.
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Sum of x over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -55,15 +67,18 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // counting lane of the wave hits one bin (heavy ties), a single atomic adds
 // the whole wave's count.
 __device__ __forceinline__ void hist_add_wave(uint32_t* lds_hist, uint32_t bin, bool take) {
-    const uint64_t act = __ballot(take);
+    const uint64_t act = wave_ballot(take);
     if (act == 0) return;
-    const uint32_t first = (uint32_t)__builtin_ctzll(act);
-    const uint32_t bin0 = __shfl(bin, (int)first, 64);
-    const uint64_t same = __ballot(take && bin == bin0);
-    if (same == act) {
-        if (lane_id() == first) atomicAdd(&lds_hist[bin0], (uint32_t)__popcll(act));
-    } else if (take) {
-        atomicAdd(&lds_hist[bin], 1u);
+    if (take) {
+        // only the counting lanes run here: the first one's bin, and whether
+        // every counting lane has it
+        const uint32_t bin0 = __builtin_amdgcn_readfirstlane(bin);
+        const uint64_t same = wave_ballot(bin == bin0);
+        if (same == act) {
+            if (lane_id() == (uint32_t)__builtin_ctzll(act)) atomicAdd(&lds_hist[bin0], (uint32_t)__popcll(act));
+        } else {
+            atomicAdd(&lds_hist[bin], 1u);
+        }
     }
 }
 
