@@ -53,6 +53,13 @@ __device__ __forceinline__ T stream_load(const T* p) {
 #endif
 constexpr int kEfBlock = SCAPE_EF_BLOCK;  // threads per workgroup of the dense pass (one word per wave)
 constexpr int kEfWaves = kEfBlock / 64;
+// Each XCD streams one contiguous eighth of the words (measured: the dense
+// pass 0.3-0.9 ms faster on the 1.75B workload, most where the process's
+// buffers map worst).
+#ifndef SCAPE_EF_XCD
+#define SCAPE_EF_XCD 1
+#endif
+constexpr bool kEfXcd = SCAPE_EF_XCD != 0;
 
 template <int WT, bool K32>
 __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
@@ -62,7 +69,8 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
                                                        uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
                                                        float* __restrict__ m_stash) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
-    const uint32_t w = blockIdx.x * kEfWaves + threadIdx.x / 64;
+    const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t w = blk * kEfWaves + threadIdx.x / 64;
     if (w >= n_words) return;
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
@@ -204,15 +212,14 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 // Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
 // by the workgroup size so that idx, the sparse buffers and the m stash are
 // read contiguously), every load issued before the arithmetic.  The pass runs
-// beside the mask selection on another stream; its grid is capped at a
-// workgroup per CU and strides over the positions, which leaves the
-// selection's latency-bound passes more of the memory system (measured: the
-// two together finish sooner than with one workgroup per chunk, or in turn).
+// beside the mask selection on another stream.  The grid may be capped, the
+// workgroups then striding over the positions; one workgroup per chunk (no
+// cap) measured as fast beside the selection as any cap, and faster alone.
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 4
 #endif
 #ifndef SCAPE_UPDATE_GRID
-#define SCAPE_UPDATE_GRID 256
+#define SCAPE_UPDATE_GRID 0
 #endif
 
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;

@@ -15,6 +15,17 @@ __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 // an integer and compares it again, two more vector instructions per use.
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8),
+// each with its own L2 and translation caches.  xcd_block(b, n) renumbers the
+// n workgroups so that each XCD's share is one contiguous run of [0, n), in
+// dispatch order.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t n) {
+    const uint32_t q = n / kXcds, r = n % kXcds;
+    const uint32_t x = b % kXcds, k = b / kXcds;
+    return x * q + (x < r ? x : r) + k;
+}
+
 // Sum of x over the wave, in every lane.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 #pragma unroll
