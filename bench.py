@@ -237,6 +237,28 @@ def spin_up(seconds: float) -> None:
     torch.cuda.empty_cache()
 
 
+def stream_copy_bandwidth(nbytes: int = 4 << 30) -> float:
+    """Read + write bytes per second of the library's plain one-shot copy
+    kernel (scape_copy_probe): the practical stream ceiling of this GPU."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    sc.scape_copy_probe(a, b)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    ev0.record()
+    for _ in range(reps):
+        sc.scape_copy_probe(a, b)
+    ev1.record()
+    torch.cuda.synchronize()
+    dt = ev0.elapsed_time(ev1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
+
+
 def copy_bandwidth(nbytes: int = 4 << 30) -> float:
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -359,7 +381,8 @@ def main() -> int:
         fill = fill_in(wl, cfg, offsets, n_pad)
         log("fill-in union density by workers: " + ", ".join(f"{w}: {d:.4%}" for w, d in fill["union_density"].items()))
     copy_gbps = copy_bandwidth()
-    log(f"device copy: {copy_gbps:.0f} GB/s")
+    stream_gbps = stream_copy_bandwidth()
+    log(f"device copy: torch {copy_gbps:.0f} GB/s, one-shot stream copy {stream_gbps:.0f} GB/s")
 
     result = {
         "metric": METRIC, "value": N / (ms * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
@@ -372,10 +395,11 @@ def main() -> int:
         "worker_elements_per_s": W * N / (ms * 1e-3),
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
-        "device_copy_GBps": copy_gbps,
+        "device_copy_GBps": copy_gbps, "stream_copy_GBps": stream_gbps,
         "roofline": {"kernel": "scape_k_ef_compact (dense pass)", "bound": "hbm", "achieved": ef_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
-                     "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic},
+                     "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
+                     "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps},
     }
     if dense is not None:
         result["dense_adams"] = dense

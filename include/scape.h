@@ -264,6 +264,14 @@ int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream);
  * aligned); 1 <= W <= 32; k >= 0.  Errors: INVALID_ARG, ALIGN, SHAPE, HIP. */
 int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream);
 
+/* Measurement helper, not a step of the method: copy `bytes` from src to dst
+ * (device, 16-byte aligned, not overlapping; bytes a multiple of 16) with a
+ * plain one-shot kernel of the dense pass's kind (16 bytes per thread,
+ * non-temporal loads and stores).  Timing it gives the stream-copy rate of
+ * the GPU, the practical ceiling the step's HBM-bound kernels are compared
+ * with.  bytes = 0 enqueues nothing.  Errors: INVALID_ARG, ALIGN, SHAPE, HIP. */
+int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream);
+
 /* Optional per-phase timing of scape_step with HIP events recorded on the
  * step's stream (and on the context's update stream).  The W-way reduction
  * and update run on the context's own stream beside the mask selection (they

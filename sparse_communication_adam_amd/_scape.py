@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "scape_reduce_sparse": [vp, i32, i64, vp, vp],
             "scape_profile_enable": [vp, i32],
             "scape_profile_read": [vp, vp, vp],
+            "scape_copy_probe": [vp, vp, ctypes.c_uint64, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -363,6 +364,20 @@ def scape_reduce_sparse(bufs: Sequence, out, k: Optional[int] = None, stream=Non
     ptrs = _ptr_array([_dev(b, torch.float32, k, f"bufs[{i}]") for i, b in enumerate(bufs)])
     op = _dev(out, torch.float32, k, "out")
     _check(lib().scape_reduce_sparse(ptrs, len(bufs), k, op, _stream(stream)))
+
+
+def scape_copy_probe(src, dst, nbytes: Optional[int] = None, stream=None) -> None:
+    """Copy nbytes (default: all of src) from src to dst, both device tensors
+    (16-byte aligned, nbytes a multiple of 16), with the library's plain
+    stream-copy kernel."""
+    import torch
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name} is smaller than {nbytes} bytes")
+    _check(lib().scape_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)))
 
 
 def scape_profile_enable(ctx: Context, enable: bool = True) -> None:

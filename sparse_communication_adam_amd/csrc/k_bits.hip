@@ -168,4 +168,24 @@ hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t
     return hipGetLastError();
 }
 
+// Plain device copy for measuring the stream-copy rate the step's kernels
+// are compared with: one-shot, 16 bytes per thread, non-temporal loads and
+// stores, workgroups in the same XCD-aware order as the dense pass.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kBlock) void k_copy_probe(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       uint64_t n16) {
+    const uint64_t i = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
+    if (i >= n16) return;
+    __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
+}
+
+hipError_t launch_copy_probe(hipStream_t s, const void* src, void* dst, uint64_t n16) {
+    if (n16 == 0) return hipSuccess;
+    const uint64_t blocks = (n16 + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(k_copy_probe, dim3((uint32_t)blocks), dim3(kBlock), 0, s, (const u32x4*)src, (u32x4*)dst,
+                       n16);
+    return hipGetLastError();
+}
+
 }  // namespace scape

@@ -803,6 +803,16 @@ int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream) {
     return SCAPE_OK;
 }
 
+int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream) {
+    if (bytes == 0) return SCAPE_OK;
+    if (!src || !dst) return fail(SCAPE_ERR_INVALID_ARG, "src and dst must not be NULL");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(SCAPE_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    if (bytes % 16 != 0) return fail(SCAPE_ERR_SHAPE, "bytes must be a multiple of 16");
+    if (bytes / 16 > (uint64_t)0xFFFFFFFFu * kBlock) return fail(SCAPE_ERR_SHAPE, "bytes too large");
+    SCAPE_HIP(launch_copy_probe((hipStream_t)stream, src, dst, bytes / 16), "copy_probe");
+    return SCAPE_OK;
+}
+
 int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream) {
     if (W < 1 || W > SCAPE_MAX_WORKERS) return fail(SCAPE_ERR_INVALID_ARG, "W must be in 1..%d", SCAPE_MAX_WORKERS);
     if (k < 0) return fail(SCAPE_ERR_INVALID_ARG, "k must be >= 0");

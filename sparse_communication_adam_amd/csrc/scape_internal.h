@@ -181,5 +181,6 @@ hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_wor
 hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, uint32_t n_words);
 hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits);
 hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred);
+hipError_t launch_copy_probe(hipStream_t s, const void* src, void* dst, uint64_t n16);
 
 }  // namespace scape
