@@ -196,9 +196,10 @@ hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_t
 __global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const LayerDesc* __restrict__ layers,
                                                      uint32_t* __restrict__ hist,
                                                      const uint32_t* __restrict__ sample_count,
-                                                     SelState* __restrict__ st) {
+                                                     SelState* __restrict__ st, uint32_t* __restrict__ miss) {
     __shared__ uint32_t suffix[kDigit1Bins];
     __shared__ uint32_t scratch[kWaves];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *miss = 0;  // no layer has missed its window yet
     const int l = layer0 + blockIdx.x;
     const LayerDesc L = layers[l];
     uint32_t* row = hist + (size_t)l * kHistBins;
@@ -251,9 +252,9 @@ __global__ __launch_bounds__(kBlock) void k_estimate(int32_t layer0, const Layer
 }
 
 hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
-                           const uint32_t* sample_count, SelState* st) {
+                           const uint32_t* sample_count, SelState* st, uint32_t* miss) {
     if (n_layers <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_estimate, dim3(n_layers), dim3(kBlock), 0, s, layer0, layers, hist, sample_count, st);
+    hipLaunchKernelGGL(k_estimate, dim3(n_layers), dim3(kBlock), 0, s, layer0, layers, hist, sample_count, st, miss);
     return hipGetLastError();
 }
 
@@ -489,7 +490,8 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
                                                          const uint32_t* __restrict__ layer_seg0,
                                                          uint32_t* __restrict__ hist, SelState* __restrict__ st,
                                                          const uint32_t* __restrict__ seg_above,
-                                                         uint32_t* __restrict__ seg_fill) {
+                                                         uint32_t* __restrict__ seg_fill,
+                                                         uint32_t* __restrict__ miss) {
     __shared__ uint32_t scratch[kWaves];
     __shared__ uint32_t s_bucket, s_before, s_count, s_above;
     const int l = layer0 + blockIdx.x;
@@ -525,6 +527,7 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
         S.none = 1;  // provisional; the second pass decides
         S.phase = kPhaseDone;
         for (uint32_t g = sg0; g < sg1; ++g) seg_fill[g] = 0;  // the exact pass makes new records
+        atomicOr(miss, 1u);  // the fallback kernels have work
     } else if (s_bucket == kNone) {  // cannot happen with a full row; select nothing rather than guess
         S.none = 1;
         S.phase = kPhaseDone;
@@ -538,10 +541,10 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
 
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
-                               const uint32_t* seg_above, uint32_t* seg_fill) {
+                               const uint32_t* seg_above, uint32_t* seg_fill, uint32_t* miss) {
     if (n_layers <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, first_pass, layers, layer_seg0,
-                       hist, st, seg_above, seg_fill);
+                       hist, st, seg_above, seg_fill, miss);
     return hipGetLastError();
 }
 
@@ -553,8 +556,10 @@ constexpr uint32_t kFallbackGrid = 1024;
 __global__ __launch_bounds__(kBlock) void k_hist_full(const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                                                       const LayerDesc* __restrict__ layers,
                                                       const SelState* __restrict__ st,
-                                                      const uint16_t* __restrict__ key, uint32_t* __restrict__ hist) {
+                                                      const uint16_t* __restrict__ key, uint32_t* __restrict__ hist,
+                                                      const uint32_t* __restrict__ miss) {
     __shared__ uint32_t h[kDigit1Bins];
+    if (*miss == 0) return;  // no layer missed its window: nothing to count
     const uint32_t lane = lane_id();
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const TileDesc t = tiles[ti];
@@ -575,10 +580,10 @@ __global__ __launch_bounds__(kBlock) void k_hist_full(const TileDesc* __restrict
 }
 
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                            const SelState* st, const uint16_t* key, uint32_t* hist) {
+                            const SelState* st, const uint16_t* key, uint32_t* hist, const uint32_t* miss) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_hist_full, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, tiles, n_tiles, layers, st,
-                       key, hist);
+                       key, hist, miss);
     return hipGetLastError();
 }
 
@@ -590,8 +595,10 @@ __global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restr
                                                          const SelState* __restrict__ st,
                                                          const uint16_t* __restrict__ key,
                                                          uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
-                                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
+                                                         uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above,
+                                                         const uint32_t* __restrict__ miss) {
     __shared__ KeyPassLds lds;
+    if (*miss == 0) return;  // no layer missed its window: nothing to reclassify
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const TileDesc t = tiles[ti];
         const SelState S = st[t.layer];
@@ -608,10 +615,11 @@ __global__ __launch_bounds__(kBlock) void k_filter_exact(const TileDesc* __restr
 
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                                const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
-                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
+                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above,
+                               const uint32_t* miss) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_filter_exact, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, tiles, n_tiles, layers,
-                       segs, st, key, bits, seg_fill, cand, seg_above);
+                       segs, st, key, bits, seg_fill, cand, seg_above, miss);
     return hipGetLastError();
 }
 

@@ -149,6 +149,7 @@ struct scape_ctx {
     uint32_t* d_vb_count = nullptr;   // records per block
     size_t vb_cap = 0;
     uint32_t* d_totals = nullptr;
+    uint32_t* d_miss = nullptr;  // set when a layer's threshold fell outside its sampled window
     uint64_t* d_cand = nullptr;
     uint16_t* d_key16 = nullptr;      // statistic keys, bits 30..15 (what the selection reads)
     uint32_t* d_key32 = nullptr;      // full statistic keys, for the offloaded step
@@ -189,6 +190,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_vb);
     hipFree(c->d_vb_count);
     hipFree(c->d_totals);
+    hipFree(c->d_miss);
     hipFree(c->d_cand);
     hipFree(c->d_key16);
     hipFree(c->d_key32);
@@ -287,7 +289,7 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, sample_count + la, (uint64_t)nl, 0u), "fill");
     SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
-    SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel), "estimate");
+    SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel, c->d_miss), "estimate");
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
                             c->d_seg_above),
               "filter");
@@ -297,15 +299,15 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
                                c->d_hist, bits),
               "cand_pass");
     SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
-                                  c->d_seg_above, c->d_seg_fill),
+                                  c->d_seg_above, c->d_seg_fill, c->d_miss),
               "select_first");
     // sampling misses: full histogram, exact bucket, reclassification
-    SCAPE_HIP(launch_hist_full(s, tiles, nt, c->d_layers, c->d_sel, key, c->d_hist), "hist_full");
+    SCAPE_HIP(launch_hist_full(s, tiles, nt, c->d_layers, c->d_sel, key, c->d_hist, c->d_miss), "hist_full");
     SCAPE_HIP(launch_select_first(s, la, nl, false, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
-                                  c->d_seg_above, c->d_seg_fill),
+                                  c->d_seg_above, c->d_seg_fill, c->d_miss),
               "select_first");
     SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill,
-                                  c->d_cand, c->d_seg_above),
+                                  c->d_cand, c->d_seg_above, c->d_miss),
               "filter_exact");
     // radix passes with shrinking record sets, then the final marking
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
@@ -601,7 +603,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_seg_above, n_segs, "segment bit counters")) ||
         (rc = dev_alloc(&c->d_vb, c->vb_cap, "record blocks")) ||
         (rc = dev_alloc(&c->d_vb_count, c->vb_cap, "record block counts")) ||
-        (rc = dev_alloc(&c->d_totals, 4, "totals")) ||
+        (rc = dev_alloc(&c->d_totals, 4, "totals")) || (rc = dev_alloc(&c->d_miss, 1, "miss flag")) ||
         (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
         (rc = dev_alloc(&c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
         (rc = dev_alloc(&c->d_key32, (size_t)c->lay.n_pad, "full statistic keys")) ||

@@ -151,7 +151,10 @@ hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t valu
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                               const uint16_t* key, uint32_t* hist, uint32_t* sample_count);
 hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, const LayerDesc* layers, uint32_t* hist,
-                           const uint32_t* sample_count, SelState* st);
+                           const uint32_t* sample_count, SelState* st, uint32_t* miss);
+// `miss` is one word: k_estimate clears it, k_select_first sets it when a
+// layer's threshold falls outside its window, and the fallback kernels
+// (k_hist_full, k_filter_exact) return at once while it is clear.
 // Record segments: `segs`, `seg_fill` (records per segment) and `seg_above`
 // (keys above the window per segment) are indexed by global segment number.
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
@@ -159,12 +162,12 @@ hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles,
                          uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
-                               const uint32_t* seg_above, uint32_t* seg_fill);
+                               const uint32_t* seg_above, uint32_t* seg_fill, uint32_t* miss);
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
-                            const SelState* st, const uint16_t* key, uint32_t* hist);
+                            const SelState* st, const uint16_t* key, uint32_t* hist, const uint32_t* miss);
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                                const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
-                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
+                               uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above, const uint32_t* miss);
 hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
                             const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals);
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
