@@ -120,7 +120,14 @@ constexpr int kProfSlots = 64;
 
 }  // namespace
 
-constexpr uint32_t kOffloadChunkWords = 1u << 16;  // 4,194,304 elements per residual transfer
+// Residual offload: two staging slots, each with its own copy streams, of
+// 512 MB each (W residual chunks).  Larger copies move faster over PCIe: on
+// the 1.75B workload (W = 4) chunks of 2^16, 2^18, 2^19 and 2^21 words took
+// about 1.5, 1.25, 0.97 and 0.94 s per step.  More slots (3 or 4) were not
+// faster.
+constexpr int kOffloadSlots = 2;
+constexpr size_t kOffloadSlotBytes = size_t(512) << 20;
+constexpr uint32_t kOffloadMinChunkWords = 1u << 12;
 
 struct scape_ctx {
     int device = 0;
@@ -161,10 +168,10 @@ struct scape_ctx {
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // residual offload: two staging slots of W chunks, a copy-in and a copy-out stream
-    float* d_stage = nullptr;         // [2][W][chunk_words * 64]
+    float* d_stage = nullptr;         // [kOffloadSlots][W][chunk_words * 64]
     uint32_t chunk_words = 0;
-    hipStream_t s_in = nullptr, s_out = nullptr;
-    hipEvent_t ev_in[2] = {}, ev_k[2] = {}, ev_out[2] = {};
+    hipStream_t s_in[kOffloadSlots] = {}, s_out[kOffloadSlots] = {};
+    hipEvent_t ev_in[kOffloadSlots] = {}, ev_k[kOffloadSlots] = {}, ev_out[kOffloadSlots] = {};
     bool offload_ready = false;
     // profiling
     bool prof_on = false;
@@ -199,16 +206,16 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_counts);
     hipFree(c->d_m_stash);
     hipFree(c->d_stage);
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kOffloadSlots; ++b) {
         if (c->ev_in[b]) hipEventDestroy(c->ev_in[b]);
         if (c->ev_k[b]) hipEventDestroy(c->ev_k[b]);
         if (c->ev_out[b]) hipEventDestroy(c->ev_out[b]);
+        if (c->s_in[b]) hipStreamDestroy(c->s_in[b]);
+        if (c->s_out[b]) hipStreamDestroy(c->s_out[b]);
     }
     if (c->ev_fork) hipEventDestroy(c->ev_fork);
     if (c->ev_join) hipEventDestroy(c->ev_join);
     if (c->s_upd) hipStreamDestroy(c->s_upd);
-    if (c->s_in) hipStreamDestroy(c->s_in);
-    if (c->s_out) hipStreamDestroy(c->s_out);
     if (c->prof_events)
         for (auto& s : c->prof)
             for (auto& e : s.ev) hipEventDestroy(e);
@@ -337,10 +344,10 @@ int run_index(scape_ctx* c, const scape_mask* mk, hipStream_t s) {
 // Optimization, gist.science Technical Summary s.2: CPU offloading with double
 // buffering).  Words are independent in the dense pass, so it runs chunk by
 // chunk on the step's stream with every pointer offset to the chunk; the W
-// residual chunks move host -> staging slot on s_in and back on s_out, two
-// slots alternating so that the copies of one chunk overlap the dense pass of
-// the other.  The events order, per slot: copy in -> dense pass -> copy out ->
-// the next copy into that slot.
+// residual chunks move host -> staging slot on the slot's copy-in stream and
+// back on its copy-out stream, the slots taken in turn so that the copies of
+// one chunk overlap the dense pass of another.  The events order, per slot:
+// copy in -> dense pass -> copy out -> the next copy into that slot.
 int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const StepScalars& sc, const float* m,
                const scape_mask* cur, uint32_t k_cap, uint16_t* key16, uint32_t* key32, hipStream_t s) {
     const int W = c->cfg.workers;
@@ -349,15 +356,15 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
     uint32_t chunk = 0;
     for (uint32_t w0 = 0; w0 < c->n_words; w0 += cw, ++chunk) {
         const uint32_t nw = std::min(cw, c->n_words - w0);
-        const int b = (int)(chunk & 1u);
+        const int b = (int)(chunk % kOffloadSlots);
         const size_t j0 = (size_t)w0 * 64, bytes = (size_t)nw * 64 * sizeof(float);
         float* stage = c->d_stage + (size_t)b * W * slot_elems;
-        SCAPE_HIP(hipStreamWaitEvent(c->s_in, c->ev_out[b], 0), "offload wait");
+        SCAPE_HIP(hipStreamWaitEvent(c->s_in[b], c->ev_out[b], 0), "offload wait");
         for (int i = 0; i < W; ++i)
             SCAPE_HIP(hipMemcpyAsync(stage + (size_t)i * slot_elems, r_host[i] + j0, bytes, hipMemcpyHostToDevice,
-                                     c->s_in),
+                                     c->s_in[b]),
                       "offload copy in");
-        SCAPE_HIP(hipEventRecord(c->ev_in[b], c->s_in), "offload event");
+        SCAPE_HIP(hipEventRecord(c->ev_in[b], c->s_in[b]), "offload event");
         SCAPE_HIP(hipStreamWaitEvent(s, c->ev_in[b], 0), "offload wait");
         WorkerPtrs cp = wp;
         for (int i = 0; i < W; ++i) {
@@ -368,12 +375,12 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
                                     cur->block_prefix + w0, k_cap, key16 + j0, key32 + j0, c->d_m_stash),
                   "ef_compact");
         SCAPE_HIP(hipEventRecord(c->ev_k[b], s), "offload event");
-        SCAPE_HIP(hipStreamWaitEvent(c->s_out, c->ev_k[b], 0), "offload wait");
+        SCAPE_HIP(hipStreamWaitEvent(c->s_out[b], c->ev_k[b], 0), "offload wait");
         for (int i = 0; i < W; ++i)
             SCAPE_HIP(hipMemcpyAsync(r_host[i] + j0, stage + (size_t)i * slot_elems, bytes, hipMemcpyDeviceToHost,
-                                     c->s_out),
+                                     c->s_out[b]),
                       "offload copy out");
-        SCAPE_HIP(hipEventRecord(c->ev_out[b], c->s_out), "offload event");
+        SCAPE_HIP(hipEventRecord(c->ev_out[b], c->s_out[b]), "offload event");
     }
     return SCAPE_OK;
 }
@@ -477,8 +484,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     if (rc) return rc;
     if (r_on_host && ctx->n_words > 0) {
         // the step completes on `stream` only once every residual chunk is home
-        SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[0], 0), "offload wait");
-        SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[1], 0), "offload wait");
+        for (int b = 0; b < kOffloadSlots; ++b) SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[b], 0), "offload wait");
     }
     prof_mark(ctx, slot, 4, s);
     return SCAPE_OK;
@@ -624,19 +630,22 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         return hip_fail(e, "creating the update stream and events");
     }
     // residual offload resources (default-priority streams; the events only order work)
-    c->chunk_words = std::min<uint32_t>(c->n_words, kOffloadChunkWords);
+    c->chunk_words = std::min<uint32_t>(
+        c->n_words, std::max<uint32_t>(kOffloadMinChunkWords,
+                                       (uint32_t)(kOffloadSlotBytes / ((size_t)cfg->workers * 64 * sizeof(float)))));
     if (c->chunk_words > 0) {
-        if ((rc = dev_alloc(&c->d_stage, (size_t)2 * cfg->workers * c->chunk_words * 64, "offload staging"))) {
+        if ((rc = dev_alloc(&c->d_stage, (size_t)kOffloadSlots * cfg->workers * c->chunk_words * 64,
+                            "offload staging"))) {
             free_ctx(c);
             return rc;
         }
-        e = hipStreamCreateWithFlags(&c->s_in, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->s_out, hipStreamNonBlocking);
-        for (int b = 0; b < 2 && e == hipSuccess; ++b) {
-            e = hipEventCreateWithFlags(&c->ev_in[b], hipEventDisableTiming);
+        for (int b = 0; b < kOffloadSlots && e == hipSuccess; ++b) {
+            e = hipStreamCreateWithFlags(&c->s_in[b], hipStreamNonBlocking);
+            if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->s_out[b], hipStreamNonBlocking);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_in[b], hipEventDisableTiming);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_k[b], hipEventDisableTiming);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_out[b], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventRecord(c->ev_out[b], c->s_out);  // both slots start free
+            if (e == hipSuccess) e = hipEventRecord(c->ev_out[b], c->s_out[b]);  // every slot starts free
         }
         if (e != hipSuccess) {
             free_ctx(c);

@@ -2,7 +2,8 @@
 (scape_step_offload: CPU offloading with double buffering, Memory
 Optimization in the gist.science Technical Summary, s.2) with the oracle, on
 a GPU.  The offloaded step runs the same kernels as scape_step over chunks of
-4,194,304 elements, so every output is expected bit-exact.
+512 MB of residuals (2^27 / W elements), so every output is expected
+bit-exact.
 """
 import gc
 
@@ -37,13 +38,27 @@ def test_offload_step_ragged_single_chunk():
     _assert_bitexact(run_parity(synth.ragged(), 5, offload=True))
 
 
+def _pad64(n):
+    return (n + 63) // 64 * 64
+
+
 def test_offload_step_three_chunks_with_boundaries_inside_layers():
-    """10.5M elements: three residual chunks, both staging slots reused, and
-    chunk boundaries falling inside layers."""
-    ts = [Tensor("a", (3_000_001,)), Tensor("b", (37,)), Tensor("c", (2000, 2500)), Tensor("d", (64,)),
-          Tensor("e", (2_500_000,))]
+    """About 87M elements at W = 4 (33,554,432 elements per chunk, the
+    library's 512 MB staging slot): three residual chunks, staging slot 0
+    reused, and the two chunk boundaries falling inside small layers, which
+    the oracle checks (the large filler layers run on the GPU only)."""
+    W = 4
+    chunk = (512 << 20) // (W * 4)
+    ts = [Tensor("fill0", (33_550_000,)), Tensor("across1", (10_000,)), Tensor("fill1", (33_540_000,)),
+          Tensor("across2", (20_000,)), Tensor("fill2", (20_000_000,)), Tensor("tail", (4097,))]
+    off = [0]
+    for t in ts[:-1]:
+        off.append(off[-1] + _pad64(t.numel))
+    n_pad = off[-1] + _pad64(ts[-1].numel)
+    assert off[1] < chunk < off[1] + ts[1].numel and off[3] < 2 * chunk < off[3] + ts[3].numel
+    assert 2 * chunk < n_pad <= 3 * chunk
     wl = synth.ragged().with_tensors(ts, name="offload-chunks")
-    _assert_bitexact(run_parity(wl, 4, offload=True))
+    _assert_bitexact(run_parity(wl, 4, sample=[1, 3, 5], W=W, offload=True))
 
 
 def test_offload_step_reduced_llama():
