@@ -177,19 +177,24 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
  * scape_step with the W residuals in pinned host memory: CPU offloading of
  * the residual buffers with double buffering ([TS-2] Memory Optimization).
  * Same computation and results as scape_step, bit for bit.  The residuals
- * move through the GPU in chunks of 4,194,304 elements: host -> one of two
- * device staging slots on a copy-in stream, the dense pass on `stream`,
- * staging -> host on a copy-out stream, the two slots alternating so the
- * PCIe copies of one chunk overlap the dense pass of the other.  The rest of
- * the step does not touch the residuals, so the last copies back overlap it.
+ * move through the GPU in chunks of 2^27 / W elements per worker (512 MB of
+ * residuals per chunk, the whole n_pad if smaller): host -> one of two device
+ * staging slots on that slot's copy-in stream, the dense pass on `stream`,
+ * staging -> host on the slot's copy-out stream, the two slots alternating so
+ * the PCIe copies of one chunk overlap the dense pass and copies of the
+ * other.  The rest of the step does not touch the residuals, so the last
+ * copies back overlap it.
  * The step is complete on `stream` only once every residual chunk is back.
  * Arguments as scape_step, except r_host: a host array of W pointers to
  * pinned host memory (hipHostMalloc, or a pinned torch tensor), n_pad fp32
  * each, 16-byte aligned; pageable memory also works but copies synchronously.
- * The host must not touch r_host while a step is in flight.  The context
- * holds the staging slots (2 x W x 16 MiB at most) and the two copy streams
- * (default priority) from scape_init.
- * Errors: as scape_step.
+ * The host must not touch r_host while a step is in flight.  The first call
+ * on a context allocates what only this entry point uses, kept until
+ * scape_destroy: a full-key array (n_pad x 4 bytes; the selection cannot
+ * recompute candidates' keys without the residuals on the device), the
+ * staging slots (2 x 512 MB at most) and four copy streams (default
+ * priority); that call may block like hipMalloc.
+ * Errors: as scape_step, and OOM.
  */
 int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* const* r_host, const uint16_t* const* g,
                        const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,

@@ -385,6 +385,37 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
     return SCAPE_OK;
 }
 
+// The offloaded step's resources, made by its first call on a context: the
+// full-key array (without the residuals on the device, the selection cannot
+// recompute candidates' keys), the staging slots, and each slot's copy
+// streams and events (default priority; the events only order work).
+// Whatever a failed attempt made is kept and freed with the context.
+int ensure_offload(scape_ctx* c) {
+    if (c->offload_ready || c->n_words == 0) return SCAPE_OK;
+    int rc;
+    if (!c->d_key32 && (rc = dev_alloc(&c->d_key32, (size_t)c->lay.n_pad, "full statistic keys"))) return rc;
+    c->chunk_words = std::min<uint32_t>(
+        c->n_words, std::max<uint32_t>(kOffloadMinChunkWords, (uint32_t)(kOffloadSlotBytes / ((size_t)c->cfg.workers *
+                                                                                             64 * sizeof(float)))));
+    if (!c->d_stage && (rc = dev_alloc(&c->d_stage, (size_t)kOffloadSlots * c->cfg.workers * c->chunk_words * 64,
+                                       "offload staging")))
+        return rc;
+    hipError_t e = hipSuccess;
+    for (int b = 0; b < kOffloadSlots && e == hipSuccess; ++b) {
+        if (!c->s_in[b]) e = hipStreamCreateWithFlags(&c->s_in[b], hipStreamNonBlocking);
+        if (e == hipSuccess && !c->s_out[b]) e = hipStreamCreateWithFlags(&c->s_out[b], hipStreamNonBlocking);
+        if (e == hipSuccess && !c->ev_in[b]) e = hipEventCreateWithFlags(&c->ev_in[b], hipEventDisableTiming);
+        if (e == hipSuccess && !c->ev_k[b]) e = hipEventCreateWithFlags(&c->ev_k[b], hipEventDisableTiming);
+        if (e == hipSuccess && !c->ev_out[b]) {
+            e = hipEventCreateWithFlags(&c->ev_out[b], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventRecord(c->ev_out[b], c->s_out[b]);  // every slot starts free
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "creating offload streams and events");
+    c->offload_ready = true;
+    return SCAPE_OK;
+}
+
 int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
                 const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
                 void* stream, bool r_on_host) {
@@ -409,8 +440,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     if (cur->bits == next->bits || cur->idx == next->idx || cur->block_prefix == next->block_prefix)
         return fail(SCAPE_ERR_STATE, "next must not alias cur (the mask built now is used at the next step)");
     if ((rc = check_device(ctx))) return rc;
-    if (r_on_host && !ctx->offload_ready && ctx->n_words > 0)
-        return fail(SCAPE_ERR_STATE, "the context has no offload resources");
+    if (r_on_host && (rc = ensure_offload(ctx))) return rc;
 
     hipStream_t s = (hipStream_t)stream;
     WorkerPtrs wp{};
@@ -612,7 +642,6 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(&c->d_totals, 4, "totals")) || (rc = dev_alloc(&c->d_miss, 1, "miss flag")) ||
         (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
         (rc = dev_alloc(&c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
-        (rc = dev_alloc(&c->d_key32, (size_t)c->lay.n_pad, "full statistic keys")) ||
         (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(&c->d_counts, L, "per-layer counters")) ||
@@ -628,30 +657,6 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     if (e != hipSuccess) {
         free_ctx(c);
         return hip_fail(e, "creating the update stream and events");
-    }
-    // residual offload resources (default-priority streams; the events only order work)
-    c->chunk_words = std::min<uint32_t>(
-        c->n_words, std::max<uint32_t>(kOffloadMinChunkWords,
-                                       (uint32_t)(kOffloadSlotBytes / ((size_t)cfg->workers * 64 * sizeof(float)))));
-    if (c->chunk_words > 0) {
-        if ((rc = dev_alloc(&c->d_stage, (size_t)kOffloadSlots * cfg->workers * c->chunk_words * 64,
-                            "offload staging"))) {
-            free_ctx(c);
-            return rc;
-        }
-        for (int b = 0; b < kOffloadSlots && e == hipSuccess; ++b) {
-            e = hipStreamCreateWithFlags(&c->s_in[b], hipStreamNonBlocking);
-            if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->s_out[b], hipStreamNonBlocking);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_in[b], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_k[b], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_out[b], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventRecord(c->ev_out[b], c->s_out[b]);  // every slot starts free
-        }
-        if (e != hipSuccess) {
-            free_ctx(c);
-            return hip_fail(e, "creating offload streams and events");
-        }
-        c->offload_ready = true;
     }
     e = hipMemcpy(c->d_layers, ld.data(), L * sizeof(LayerDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess && !c->tiles.empty())
