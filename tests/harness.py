@@ -57,12 +57,14 @@ def u32(t) -> np.ndarray:
 
 
 def check_float(name: str, got: np.ndarray, exp: np.ndarray, stats: Dict[str, int]) -> None:
-    """Parity bar for fp32 state: |got-exp| <= ATOL + RTOL*|exp| everywhere
-    (NaN only where the oracle has NaN); bit-exact positions are counted."""
+    """Parity bar for fp32 state: |got-exp| <= ATOL + RTOL*|exp| everywhere,
+    equal values (infinities included) match, and NaN only where the oracle
+    has NaN; bit-exact positions are counted."""
     assert got.shape == exp.shape, (name, got.shape, exp.shape)
     g64, e64 = got.astype(np.float64), exp.astype(np.float64)
     both_nan = np.isnan(g64) & np.isnan(e64)
-    ok = both_nan | (np.abs(g64 - e64) <= ATOL + RTOL * np.abs(e64))
+    with np.errstate(invalid="ignore"):  # inf - inf, only where the values are equal or infinite
+        ok = both_nan | (g64 == e64) | (np.abs(g64 - e64) <= ATOL + RTOL * np.abs(e64))
     if not ok.all():
         bad = np.flatnonzero(~ok)
         i = bad[0]

@@ -371,6 +371,34 @@ def test_step_zero_gradients_tie_everywhere():
     _assert_bitexact(run_parity(wl, 3, grad_override=zero, x_zero=True))
 
 
+# bfloat16 bit patterns of special gradient values: +-Inf, +-0, subnormals
+# (smallest and largest), the largest finite value, and quiet NaNs.  Keys are
+# the bits of |m-tilde| with the sign cleared, so the NaN an invalid
+# operation makes is 0x7FC00000 on both sides whatever its sign.
+SPECIAL_BF16 = np.array([0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F, 0x7F7F, 0xFF7F, 0x7FC0, 0xFFC0], np.uint16)
+
+
+def _special_grads(wl):
+    def grad(step, worker, t):
+        n = wl.tensors[t].numel
+        rng = np.random.default_rng([step, worker, t, 77])
+        g = (rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)).view(np.uint32)
+        g = ((g + 0x7FFF + ((g >> 16) & 1)) >> 16).astype(np.uint16)  # round to nearest even bf16
+        hit = rng.random(n) < 0.01
+        g[hit] = SPECIAL_BF16[rng.integers(0, SPECIAL_BF16.size, int(hit.sum()))]
+        return g
+    return grad
+
+
+@pytest.mark.parametrize("key_out", [True, False])
+def test_step_special_gradient_values(key_out):
+    """1% of every worker's gradients are +-Inf, +-0, subnormal, the largest
+    finite bfloat16 or NaN: the masks, indices and keys stay bit-exact and
+    the state matches (NaN where the oracle has NaN)."""
+    wl = synth.ragged()
+    _assert_bitexact(run_parity(wl, 4, grad_override=_special_grads(wl), key_out=key_out))
+
+
 def test_step_is_deterministic():
     import torch
     wl = synth.reduced(synth.ADVERSARIAL)
