@@ -212,14 +212,15 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 // Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
 // by the workgroup size so that idx, the sparse buffers and the m stash are
 // read contiguously), every load issued before the arithmetic.  The pass runs
-// beside the mask selection on another stream.  The grid may be capped, the
-// workgroups then striding over the positions; one workgroup per chunk (no
-// cap) measured as fast beside the selection as any cap, and faster alone.
+// beside the mask selection's record passes on another stream; its grid is
+// capped at a workgroup per CU, striding over the positions, so that it
+// leaves those latency-bound passes room on every CU (with one workgroup per
+// chunk it filled the GPU and they waited for it to finish).
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 4
 #endif
 #ifndef SCAPE_UPDATE_GRID
-#define SCAPE_UPDATE_GRID 0
+#define SCAPE_UPDATE_GRID 256
 #endif
 
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;

@@ -167,7 +167,8 @@ struct scape_ctx {
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    // residual offload: two staging slots of W chunks, a copy-in and a copy-out stream
+    // residual offload (made by the first offloaded step): staging slots of W
+    // chunks, each slot with its own copy-in and copy-out stream
     float* d_stage = nullptr;         // [kOffloadSlots][W][chunk_words * 64]
     uint32_t chunk_words = 0;
     hipStream_t s_in[kOffloadSlots] = {}, s_out[kOffloadSlots] = {};
@@ -285,12 +286,17 @@ int prof_begin(scape_ctx* c) {
 
 // Mask selection over layers [la, la+nl) and tiles [ta, tb), from 16-bit keys
 // and the source of candidates' full keys, bits into `bits`.
+// `fork`, when given, is recorded on `s` once the key filter is queued (at
+// once if there is nothing to select): the step's update starts there.
 int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
-               const KeySource& ks, uint64_t* bits, hipStream_t s) {
+               const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork = nullptr) {
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
     const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
-    if (ns == 0) return SCAPE_OK;  // every layer in the range is empty: no bits to set
+    if (ns == 0) {  // every layer in the range is empty: no bits to set
+        if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
+        return SCAPE_OK;
+    }
     uint32_t* sample_count = c->d_counts;
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_fill + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
@@ -300,6 +306,7 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
                             c->d_seg_above),
               "filter");
+    if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
               "cand_scan");
     SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
@@ -493,9 +500,11 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     // The update touches x, v, and m on the mask only; the selection reads
     // the keys, m off the mask, the owner's residual and the sparse buffers.
     // Nothing one writes is read by the other, so the update runs on its own
-    // stream beside the selection, and `stream` waits for it at the end.
-    SCAPE_HIP(hipEventRecord(ctx->ev_fork, s), "fork");
-    rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s);
+    // stream beside the selection, and `stream` waits for it at the end.  It
+    // starts after the key filter: the sampling and filter passes stream the
+    // keys and run best alone, while the record passes that follow are
+    // latency-bound and share the GPU well with the update.
+    rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s, ctx->ev_fork);
     if (rc) return rc;  // nothing was queued on the update's stream
     SCAPE_HIP(hipStreamWaitEvent(ctx->s_upd, ctx->ev_fork, 0), "fork");
     SCAPE_HIP(launch_reduce_update(ctx->s_upd, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash,
