@@ -40,6 +40,8 @@
 //
 // Histogram rows are left zeroed by every select kernel, so a row is clean
 // for the next pass.
+#include <type_traits>
+
 #include "scape_device.h"
 
 namespace scape {
@@ -370,7 +372,8 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
     // One word: its mask word (kept by lane e) and its records.  `left` is
     // the number of its keys inside the layer (64 for every word but a
     // layer's last).
-    auto one_word = [&](uint32_t w, uint32_t kw, int e, uint32_t left, uint64_t lmask, uint64_t& mine) {
+    auto one_word = [&](auto partial, uint32_t w, uint32_t kw, int e, uint32_t left, uint64_t lmask,
+                        uint64_t& mine) {
         const uint64_t word = wave_ballot(kw >= k_above) & lmask;
         if (lane == (uint32_t)e) mine = word;
         if (kRecords) {
@@ -383,7 +386,7 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
                     wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
                     n_st = 0;
                 }
-                if (in_range && lane < left)
+                if (in_range && (!decltype(partial)::value || lane < left))
                     stage[n_st + lanes_below(cb)] = ((uint64_t)(kw << kKeyShift) << 32) | (uint64_t)(w * 64u + lane - L.off);
                 n_st += (uint32_t)__popcll(cb);
             }
@@ -399,14 +402,14 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
         if (w0 + kFilterWords <= t.w1 && (w0 + kFilterWords) * 64u <= lend) {
             // every word of the trip is in the tile and wholly in the layer
 #pragma unroll
-            for (int e = 0; e < kFilterWords; ++e) one_word(w0 + e, kv[e], e, 64u, ~0ull, mine);
+            for (int e = 0; e < kFilterWords; ++e) one_word(std::false_type{}, w0 + e, kv[e], e, 64u, ~0ull, mine);
         } else {
 #pragma unroll
             for (int e = 0; e < kFilterWords; ++e) {
                 const uint32_t w = w0 + e;
                 if (w >= t.w1) break;
                 const uint32_t left = lend - w * 64u;  // >= 1 for a word of the tile
-                one_word(w, kv[e], e, left, left >= 64u ? ~0ull : (1ull << left) - 1ull, mine);
+                one_word(std::true_type{}, w, kv[e], e, left, left >= 64u ? ~0ull : (1ull << left) - 1ull, mine);
             }
         }
         if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) {
