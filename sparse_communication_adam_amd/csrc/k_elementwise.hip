@@ -217,7 +217,7 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 // leaves those latency-bound passes room on every CU (with one workgroup per
 // chunk it filled the GPU and they waited for it to finish).
 #ifndef SCAPE_UPDATE_PER
-#define SCAPE_UPDATE_PER 4
+#define SCAPE_UPDATE_PER 8  // with few workgroups, more positions in flight per thread
 #endif
 #ifndef SCAPE_UPDATE_GRID
 #define SCAPE_UPDATE_GRID 256
