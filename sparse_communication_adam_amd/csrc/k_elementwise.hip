@@ -160,13 +160,15 @@ __global__ __launch_bounds__(kBlock) void k_dense_adams(const uint16_t* __restri
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
     const size_t j = (size_t)w * 64u + lane;
-    const float mo = m[j];
-    const float xo = x[j];
+    // every array is streamed once: non-temporal loads and stores (measured
+    // 8.5 against 8.7-8.9 ms per step on the 1.75B workload)
+    const float mo = stream_load(&m[j]);
+    const float xo = stream_load(&x[j]);
     uint16_t gv[WMAX];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
         if (i >= W) break;
-        gv[i] = wp.g[i][j];
+        gv[i] = stream_load(&wp.g[i][j]);
     }
     const uint32_t count = word_info[w] & 127u;
     if (lane >= count) return;  // padding lanes of a layer's last word
@@ -181,9 +183,9 @@ __global__ __launch_bounds__(kBlock) void k_dense_adams(const uint16_t* __restri
     const float vv = sc.beta2 * (mo * mo) + sc.c2 * (gbar * gbar);
     float u = mn / (sqrtf(vv) + sc.eps);
     if (sc.wd != 0.0f) u = u + sc.wd * xo;
-    v[j] = vv;
-    m[j] = mn;
-    x[j] = xo - sc.lr * u;
+    __builtin_nontemporal_store(vv, &v[j]);
+    __builtin_nontemporal_store(mn, &m[j]);
+    __builtin_nontemporal_store(xo - sc.lr * u, &x[j]);
 }
 
 hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
