@@ -287,9 +287,10 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
     ap.add_argument("--no-offload", action="store_true", help="skip the host-residual (offload) step")
-    ap.add_argument("--spinup-s", type=float, default=1.0,
-                    help="seconds of plain device copies before anything else, so the GPU runs at steady clocks "
-                         "(the optimizer state is untouched: warmup steps would advance it)")
+    ap.add_argument("--spinup-s", type=float, default=0.0,
+                    help="seconds of plain device copies before anything else (off by default: allocating and "
+                         "freeing its buffers just before the state left the state in memory where the dense "
+                         "pass ran 15.3 instead of 13.5-14.2 ms)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
