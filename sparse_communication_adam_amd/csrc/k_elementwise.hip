@@ -215,14 +215,14 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 // by the workgroup size so that idx, the sparse buffers and the m stash are
 // read contiguously), every load issued before the arithmetic.  The pass runs
 // beside the mask selection's record passes on another stream; its grid is
-// capped at a workgroup per CU, striding over the positions, so that it
-// leaves those latency-bound passes room on every CU (with one workgroup per
-// chunk it filled the GPU and they waited for it to finish).
+// capped at two workgroups per CU, striding over the positions (measured on
+// the 0.35B, 0.55B and 1.75B workloads: 512 and no cap were equally fast,
+// 256 and 128 starved the pass where it is long, W = 8 at keep 1/10).
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 8  // with few workgroups, more positions in flight per thread
 #endif
 #ifndef SCAPE_UPDATE_GRID
-#define SCAPE_UPDATE_GRID 256
+#define SCAPE_UPDATE_GRID 512
 #endif
 
 constexpr int kUpdatePer = SCAPE_UPDATE_PER;
@@ -244,27 +244,32 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
     constexpr uint32_t chunk = kBlock * kUpdatePer;
     for (uint32_t base = blockIdx.x * chunk; base < cnt; base += gridDim.x * chunk) {
     const uint32_t q0 = base + threadIdx.x;
-    uint32_t jj[kUpdatePer];
+    // Every load is unconditional, at a position clamped into [0, cnt) and an
+    // element index clamped into [0, n_pad) (idx, the m stash and the sparse
+    // buffers hold k_cap >= cnt entries, x holds n_pad): a guarded load
+    // compiles to a branch and a wait for all outstanding loads, which
+    // serialized the positions.  Only the stores are guarded.
+    uint32_t qc[kUpdatePer], jj[kUpdatePer];
     float mo[kUpdatePer], xv[kUpdatePer], s[kUpdatePer];
     bool ok[kUpdatePer];
 #pragma unroll
     for (int u = 0; u < kUpdatePer; ++u) {
         const uint32_t q = q0 + u * kBlock;
-        ok[u] = q < cnt;
-        jj[u] = ok[u] ? idx[q] : 0u;
-        ok[u] = ok[u] && jj[u] < n_pad;
-        mo[u] = ok[u] ? m_stash[q] : 0.0f;
-        xv[u] = ok[u] ? x[jj[u]] : 0.0f;  // cached: the store below merges into the line in L2
-        s[u] = ok[u] ? wp.b[0][q] : 0.0f;
+        qc[u] = q < cnt ? q : cnt - 1u;
+        jj[u] = idx[qc[u]];
+        ok[u] = q < cnt && jj[u] < n_pad;
+    }
+#pragma unroll
+    for (int u = 0; u < kUpdatePer; ++u) {
+        mo[u] = m_stash[qc[u]];
+        xv[u] = x[jj[u] < n_pad ? jj[u] : 0u];  // cached: the store below merges into the line in L2
+        s[u] = wp.b[0][qc[u]];
     }
 #pragma unroll
     for (int i = 1; i < WMAX; ++i) {
         if (i >= W) break;
 #pragma unroll
-        for (int u = 0; u < kUpdatePer; ++u) {
-            const uint32_t q = q0 + u * kBlock;
-            if (ok[u]) s[u] = s[u] + wp.b[i][q];
-        }
+        for (int u = 0; u < kUpdatePer; ++u) s[u] = s[u] + wp.b[i][qc[u]];
     }
 #pragma unroll
     for (int u = 0; u < kUpdatePer; ++u) {
