@@ -20,6 +20,8 @@ alternative the pages' partitioned masks avoid: the union of per-worker masks
 over every layer, its density as workers are added, and the time to add one
 worker's mask.  `offload` times the step with the W residuals in pinned host
 memory (scape_step_offload), whose rate is bound by the PCIe copies.
+`workloads` times the same step on every other workload shape (a few steps
+each, after everything above), with the same byte accounting.
 """
 from __future__ import annotations
 
@@ -222,6 +224,52 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
             "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
 
 
+def other_workload(name: str, steps: int, warmup: int) -> dict:
+    """The fused step on another workload shape: state and two gradient
+    batches resident, `warmup` untimed steps, then `steps` timed ones."""
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    from sparse_communication_adam_amd.state import ScapeState
+    wl = synth.WORKLOADS[name]
+    cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
+                         owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
+                         weight_decay=wl.weight_decay)
+    state = ScapeState(cfg)
+    lay = state.layout
+    synth.params_flat_gpu(wl, lay.layer_offset, state.x)
+    sets = []
+    for s in range(2):
+        gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
+        for i, g in enumerate(gs):
+            synth.grads_flat_gpu(wl, lay.layer_offset, g, s + 1, i)
+        sets.append(gs)
+    for s in range(warmup):
+        state.step(sets[s % 2], key_out=False)
+    torch.cuda.synchronize()
+    sc.scape_profile_enable(state.ctx, True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(steps):
+        state.step(sets[(warmup + s) % 2], key_out=False)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    phase_ms, nrec = sc.scape_profile_read(state.ctx)
+    N, ksum = wl.numel, lay.k_total
+    state.destroy()
+    del state, sets
+    torch.cuda.empty_cache()
+    dense_b, step_b = alg_bytes(N, wl.W, ksum)
+    ef_ms = phase_ms["ef_compact"] / nrec
+    return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}", "steps": steps, "warmup": warmup,
+            "ms_per_step": ms, "params_per_s": N / (ms * 1e-3), "worker_elements_per_s": wl.W * N / (ms * 1e-3),
+            "step_alg_GBps": step_b / (ms * 1e-3) / 1e9, "step_hbm_frac": step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "dense_pass_ms": ef_ms, "dense_pass_GBps": dense_b / (ef_ms * 1e-3) / 1e9,
+            "dense_pass_hbm_frac": dense_b / (ef_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "phase_ms": {k: v / nrec for k, v in phase_ms.items()}}
+
+
 def spin_up(seconds: float) -> None:
     """Plain device-to-device copies for `seconds`: an idle GPU takes a while
     to reach its steady memory and fabric clocks."""
@@ -287,6 +335,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
     ap.add_argument("--no-offload", action="store_true", help="skip the host-residual (offload) step")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the step on the other workload shapes")
     ap.add_argument("--spinup-s", type=float, default=0.0,
                     help="seconds of plain device copies before anything else (off by default: allocating and "
                          "freeing its buffers just before the state left the state in memory where the dense "
@@ -381,6 +431,15 @@ def main() -> int:
     if not args.no_fill_in:
         fill = fill_in(wl, cfg, offsets, n_pad)
         log("fill-in union density by workers: " + ", ".join(f"{w}: {d:.4%}" for w, d in fill["union_density"].items()))
+    others = {}
+    if not args.no_other_workloads:
+        for name in sorted(synth.WORKLOADS):
+            if name == wl.name:
+                continue
+            others[name] = other_workload(name, 5, 2)
+            o = others[name]
+            log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
+                f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
     copy_gbps = copy_bandwidth()
     stream_gbps = stream_copy_bandwidth()
     log(f"device copy: torch {copy_gbps:.0f} GB/s, one-shot stream copy {stream_gbps:.0f} GB/s")
@@ -408,6 +467,8 @@ def main() -> int:
         result["fill_in"] = fill
     if offload is not None:
         result["offload"] = offload
+    if others:
+        result["workloads"] = others
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
