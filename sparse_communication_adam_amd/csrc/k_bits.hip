@@ -20,11 +20,19 @@ __global__ __launch_bounds__(kBlock) void k_index_count(const uint64_t* __restri
                                                         uint32_t* __restrict__ block_sums) {
     __shared__ uint32_t scratch[kWaves];
     const uint32_t wb = blockIdx.x * kIndexWordsPerBlock;
+    // unconditional loads at a clamped word (n_words >= 1), so all eight are
+    // in flight together; a guarded load becomes a branch and a full wait
+    uint64_t w[kWordsPerThread];
+#pragma unroll
+    for (int e = 0; e < kWordsPerThread; ++e) {
+        const uint32_t wi = wb + e * kBlock + threadIdx.x;
+        w[e] = bits[wi < n_words ? wi : n_words - 1u];
+    }
     uint32_t c = 0;
 #pragma unroll
     for (int e = 0; e < kWordsPerThread; ++e) {
         const uint32_t wi = wb + e * kBlock + threadIdx.x;
-        if (wi < n_words) c += (uint32_t)__popcll(bits[wi]);
+        c += wi < n_words ? (uint32_t)__popcll(w[e]) : 0u;
     }
     uint32_t total = 0;
     block_exclusive_scan(c, scratch, &total);
@@ -45,8 +53,17 @@ __global__ __launch_bounds__(1024) void k_index_scan(uint32_t* __restrict__ bloc
     const uint32_t per = (n_blocks + 1023) / 1024;
     const uint32_t a = threadIdx.x * per;
     const uint32_t b = min(a + per, n_blocks);
+    // the run's sums, eight loads in flight at a time (clamped to the run's
+    // last entry, so a thread reads only its own run, and counted only inside it)
+    constexpr uint32_t kBatch = 8;
     uint32_t c = 0;
-    for (uint32_t i = a; i < b; ++i) c += block_sums[i];
+    for (uint32_t i0 = a; i0 < b; i0 += kBatch) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (uint32_t e = 0; e < kBatch; ++e) v[e] = block_sums[min(i0 + e, b - 1u)];
+#pragma unroll
+        for (uint32_t e = 0; e < kBatch; ++e) c += i0 + e < b ? v[e] : 0u;
+    }
     sc[threadIdx.x] = c;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
@@ -56,10 +73,17 @@ __global__ __launch_bounds__(1024) void k_index_scan(uint32_t* __restrict__ bloc
         __syncthreads();
     }
     uint32_t off = sc[threadIdx.x] - c;
-    for (uint32_t i = a; i < b; ++i) {
-        const uint32_t v = block_sums[i];
-        block_sums[i] = off;
-        off += v;
+    for (uint32_t i0 = a; i0 < b; i0 += kBatch) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (uint32_t e = 0; e < kBatch; ++e) v[e] = block_sums[min(i0 + e, b - 1u)];
+#pragma unroll
+        for (uint32_t e = 0; e < kBatch; ++e) {
+            if (i0 + e < b) {
+                block_sums[i0 + e] = off;
+                off += v[e];
+            }
+        }
     }
     if (threadIdx.x == 1023) block_sums[n_blocks] = sc[1023];
 }

@@ -281,9 +281,18 @@ __device__ __forceinline__ void candidate_keys(const KeySource& ks, const LayerD
 #pragma unroll
     for (int u = 0; u < kFetch; ++u) jj[u] = L.off + (((sel >> u) & 1u) ? (uint32_t)rec[u] : 0u);
     uint32_t kk[kFetch];
-    if (ks.mtilde || ks.key32) {
+    // each source in a branch of its own, so that its kFetch loads are issued
+    // before any is used (a select inside the loop compiled to one branch and
+    // one wait per record)
+    if (ks.mtilde) {
+        float f[kFetch];
 #pragma unroll
-        for (int u = 0; u < kFetch; ++u) kk[u] = ks.mtilde ? magnitude_key(ks.mtilde[jj[u]]) : ks.key32[jj[u]];
+        for (int u = 0; u < kFetch; ++u) f[u] = ks.mtilde[jj[u]];
+#pragma unroll
+        for (int u = 0; u < kFetch; ++u) kk[u] = magnitude_key(f[u]);
+    } else if (ks.key32) {
+#pragma unroll
+        for (int u = 0; u < kFetch; ++u) kk[u] = ks.key32[jj[u]];
     } else {
         const float* r = ks.r[L.owner];
         uint64_t word[kFetch];
@@ -297,14 +306,19 @@ __device__ __forceinline__ void candidate_keys(const KeySource& ks, const LayerD
             mv[u] = ks.m[jj[u]];
         }
         bool on[kFetch];
-        float bv[kFetch];
+        float bv[kFetch] = {};
+        uint32_t rk[kFetch];
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) {
             const uint32_t bit = jj[u] & 63u;
             const uint32_t rank = pre[u] + (uint32_t)__popcll(word[u] & ((1ull << bit) - 1ull));
             on[u] = ((word[u] >> bit) & 1ull) && rank < ks.k_cap;
-            bv[u] = 0.0f;
-            if (ks.k_cap) bv[u] = ks.b[L.owner][on[u] ? rank : 0u];
+            rk[u] = on[u] ? rank : 0u;
+        }
+        if (ks.k_cap) {  // uniform: with no buffer there is no mask to read from
+            const float* b = ks.b[L.owner];
+#pragma unroll
+            for (int u = 0; u < kFetch; ++u) bv[u] = b[rk[u]];
         }
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) {
@@ -805,12 +819,17 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
         // the first two digits and for a layer decided on them; the pass over
         // key bits 14..6 fetches the full key of each record it keeps
         const bool fetch = cph == kPhaseKey3;
+        // every record load is unconditional, at a slot clamped to the block's
+        // last record (cnt >= 1 here), so the 16 loads are in flight together
         uint64_t rec[kRecPerThread];
 #pragma unroll
         for (int i = 0; i < kRecPerThread; ++i) {
             const uint32_t p = threadIdx.x + i * kPassBlock;
-            rec[i] = p < cnt ? cand[(size_t)D.p0 + p] : 0ull;
+            rec[i] = cand[(size_t)D.p0 + (p < cnt ? p : cnt - 1u)];
         }
+#pragma unroll
+        for (int i = 0; i < kRecPerThread; ++i)
+            if (threadIdx.x + i * kPassBlock >= cnt) rec[i] = 0ull;
         uint32_t und = 0;  // bit i: record i undecided
 #pragma unroll
         for (int i = 0; i < kRecPerThread; ++i) {
