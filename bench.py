@@ -22,6 +22,9 @@ worker's mask.  `offload` times the step with the W residuals in pinned host
 memory (scape_step_offload), whose rate is bound by the PCIe copies.
 `workloads` times the same step on every other workload shape (a few steps
 each, after everything above), with the same byte accounting.
+`shard_mask_build` times the mask build one worker runs on its own
+layer-aligned 1/32 shard (scape_mask_build with num_shards = 32), shard by
+shard, beside the build over every layer.
 """
 from __future__ import annotations
 
@@ -270,6 +273,65 @@ def other_workload(name: str, steps: int, warmup: int) -> dict:
             "phase_ms": {k: v / nrec for k, v in phase_ms.items()}}
 
 
+def shard_mask_build(name: str) -> dict:
+    """The per-layer top-k one worker builds on its own layer-aligned shard:
+    scape_mask_build(num_shards = shard_P, shard = s) for every s, from worker
+    0's step-1 gradient widened to fp32 as the statistic (at step 1 the
+    candidate is (1 - beta1) times the gradient, so the ranking is the
+    gradient's), each build timed with HIP events, beside one build over
+    every layer.  Algorithmic bytes of a build: read the statistic (4 B per
+    element), write and read its 16-bit key, write the mask bits."""
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    wl = synth.WORKLOADS[name]
+    P = wl.shard_P
+    # the build's shard count is a per-call argument; the config keeps the
+    # step's owners (at most W shards)
+    cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
+                         owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
+                         weight_decay=wl.weight_decay)
+    ctx = sc.scape_init(cfg)
+    lay = ctx.layout
+    g = torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda")
+    synth.grads_flat_gpu(wl, lay.layer_offset, g, 1, 0)
+    mt = g.view(torch.bfloat16).float()
+    del g
+    mask = sc.alloc_mask(lay)
+    owner = sc.scape_owner_map(cfg, P)
+    sizes = wl.layer_sizes
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(shards: int, shard: int, reps: int = 3) -> float:
+        sc.scape_mask_build(ctx, mt, mask, shards, shard)
+        ev0.record()
+        for _ in range(reps):
+            sc.scape_mask_build(ctx, mt, mask, shards, shard)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    per, elems = [], []
+    for s in range(P):
+        n_s = sum(n for n, o in zip(sizes, owner) if o == s)
+        if n_s == 0:
+            continue
+        per.append(timed(P, s))
+        elems.append(n_s)
+    full_ms = timed(0, -1)
+    ctx.destroy()
+    del mt, mask
+    torch.cuda.empty_cache()
+    bpe = 4 + 2 + 2 + 0.125
+    rates = [bpe * n / (t * 1e-3) / 1e9 for n, t in zip(elems, per)]
+    imax = max(range(len(per)), key=lambda i: per[i])
+    return {"num_shards": P, "shards_with_layers": len(per), "shard_ms_mean": sum(per) / len(per),
+            "shard_ms_max": per[imax], "shard_elements_max": elems[imax],
+            "shard_elements_mean": sum(elems) / len(elems), "shard_alg_GBps_of_largest": rates[imax],
+            "all_layers_ms": full_ms, "all_layers_alg_GBps": bpe * wl.numel / (full_ms * 1e-3) / 1e9,
+            "alg_bytes_per_element": bpe}
+
+
 def spin_up(seconds: float) -> None:
     """Plain device-to-device copies for `seconds`: an idle GPU takes a while
     to reach its steady memory and fabric clocks."""
@@ -337,6 +399,8 @@ def main() -> int:
     ap.add_argument("--no-offload", action="store_true", help="skip the host-residual (offload) step")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the step on the other workload shapes")
+    ap.add_argument("--no-shard-build", action="store_true",
+                    help="skip timing the per-worker mask build on one layer-aligned shard")
     ap.add_argument("--spinup-s", type=float, default=0.0,
                     help="seconds of plain device copies before anything else (off by default: allocating and "
                          "freeing its buffers just before the state left the state in memory where the dense "
@@ -440,6 +504,12 @@ def main() -> int:
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
+    shard_builds = {}
+    if not args.no_shard_build:
+        for name in ("gpt-345m", "llama-0.55b", "llama-1.75b"):
+            shard_builds[name] = sb = shard_mask_build(name)
+            log(f"shard mask build {name}: {sb['shard_ms_mean']:.3f} ms mean, {sb['shard_ms_max']:.3f} ms max over "
+                f"{sb['shards_with_layers']} of {sb['num_shards']} shards; all layers {sb['all_layers_ms']:.3f} ms")
     copy_gbps = copy_bandwidth()
     stream_gbps = stream_copy_bandwidth()
     log(f"device copy: torch {copy_gbps:.0f} GB/s, one-shot stream copy {stream_gbps:.0f} GB/s")
@@ -469,6 +539,8 @@ def main() -> int:
         result["offload"] = offload
     if others:
         result["workloads"] = others
+    if shard_builds:
+        result["shard_mask_build"] = shard_builds
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -316,23 +316,44 @@ hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepS
     return hipGetLastError();
 }
 
-// Statistic keys from a given m-tilde (the standalone mask build), one word
-// per wave, one-shot like the dense pass.
-__global__ __launch_bounds__(kBlock) void k_keys_from_mtilde(const uint16_t* __restrict__ word_info, uint32_t w_begin,
-                                                             uint32_t w_end, const float* __restrict__ mtilde,
-                                                             uint16_t* __restrict__ key16) {
-    const uint32_t w = w_begin + blockIdx.x * kWaves + threadIdx.x / 64;
-    if (w >= w_end) return;
+// Statistic keys from a given m-tilde (the standalone mask build): a wave
+// handles kKeyWords consecutive words, one-shot and in the dense pass's
+// XCD-aware order.  All of the wave's loads (m-tilde non-temporally, and the
+// words' descriptors) are issued before any key is formed, at words clamped
+// into the range, so that enough bytes are in flight per wave: with one 256-byte
+// word per wave the pass ran at about 2.2 TB/s.  m-tilde holds n_pad
+// elements, so every lane may load; the padding lanes of a layer's last word
+// store nothing.
+constexpr uint32_t kKeyWords = 8;
+
+__global__ __launch_bounds__(kEfBlock) void k_keys_from_mtilde(const uint16_t* __restrict__ word_info,
+                                                               uint32_t w_begin, uint32_t w_end,
+                                                               const float* __restrict__ mtilde,
+                                                               uint16_t* __restrict__ key16) {
+    const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t w0 = w_begin + (blk * kEfWaves + threadIdx.x / 64) * kKeyWords;
+    if (w0 >= w_end) return;
     const uint32_t lane = lane_id();
-    if (lane >= (word_info[w] & 127u)) return;
-    const size_t j = (size_t)w * 64u + lane;
-    key16[j] = (uint16_t)(magnitude_key(mtilde[j]) >> kKeyShift);
+    float mt[kKeyWords];
+    uint32_t info[kKeyWords];
+#pragma unroll
+    for (uint32_t e = 0; e < kKeyWords; ++e) {
+        const uint32_t w = min(w0 + e, w_end - 1u);
+        mt[e] = stream_load(&mtilde[(size_t)w * 64u + lane]);
+        info[e] = word_info[w];
+    }
+#pragma unroll
+    for (uint32_t e = 0; e < kKeyWords; ++e) {
+        if (w0 + e < w_end && lane < (info[e] & 127u))
+            key16[(size_t)(w0 + e) * 64u + lane] = (uint16_t)(magnitude_key(mt[e]) >> kKeyShift);
+    }
 }
 
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,
                                    const float* mtilde, uint16_t* key16) {
     if (w_end <= w_begin) return hipSuccess;
-    hipLaunchKernelGGL(k_keys_from_mtilde, dim3((w_end - w_begin + kWaves - 1) / kWaves), dim3(kBlock), 0, s,
+    const uint32_t per_block = kEfWaves * kKeyWords;
+    hipLaunchKernelGGL(k_keys_from_mtilde, dim3((w_end - w_begin + per_block - 1) / per_block), dim3(kEfBlock), 0, s,
                        word_info, w_begin, w_end, mtilde, key16);
     return hipGetLastError();
 }
@@ -341,11 +362,26 @@ struct BufPtrs {
     const float* b[SCAPE_MAX_WORKERS];
 };
 
-__global__ __launch_bounds__(kBlock) void k_reduce_sparse(BufPtrs bp, int32_t W, uint64_t k, float* __restrict__ out) {
+// The W-way mean on its own: the W loads of a position are issued together
+// (W fixed at compile time for the common counts), then summed in worker order.
+template <int WT>
+__global__ __launch_bounds__(kBlock) void k_reduce_sparse(BufPtrs bp, int32_t w_rt, uint64_t k, float* __restrict__ out) {
+    constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
+    const int W = WT > 0 ? WT : w_rt;
     const float fW = (float)W;
     for (uint64_t q = (uint64_t)blockIdx.x * kBlock + threadIdx.x; q < k; q += (uint64_t)gridDim.x * kBlock) {
-        float s = bp.b[0][q];
-        for (int i = 1; i < W; ++i) s = s + bp.b[i][q];
+        float v[WMAX];
+#pragma unroll
+        for (int i = 0; i < WMAX; ++i) {
+            if (i >= W) break;
+            v[i] = bp.b[i][q];
+        }
+        float s = v[0];
+#pragma unroll
+        for (int i = 1; i < WMAX; ++i) {
+            if (i >= W) break;
+            s = s + v[i];
+        }
         out[q] = s / fW;
     }
 }
@@ -356,7 +392,23 @@ hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t
     for (int i = 0; i < W; ++i) bp.b[i] = bufs[i];
     uint64_t blocks = ((uint64_t)k + kBlock - 1) / kBlock;
     if (blocks > 16384u) blocks = 16384u;
-    hipLaunchKernelGGL(k_reduce_sparse, dim3((uint32_t)blocks), dim3(kBlock), 0, s, bp, W, (uint64_t)k, out);
+    const dim3 grid((uint32_t)blocks);
+#define SCAPE_RS_CASE(WV)                                                                                 \
+    case WV:                                                                                              \
+        hipLaunchKernelGGL(k_reduce_sparse<WV>, grid, dim3(kBlock), 0, s, bp, W, (uint64_t)k, out); \
+        break;
+    switch (W) {
+        SCAPE_RS_CASE(1)
+        SCAPE_RS_CASE(2)
+        SCAPE_RS_CASE(3)
+        SCAPE_RS_CASE(4)
+        SCAPE_RS_CASE(8)
+        SCAPE_RS_CASE(16)
+        SCAPE_RS_CASE(32)
+        default:
+            hipLaunchKernelGGL(k_reduce_sparse<0>, grid, dim3(kBlock), 0, s, bp, W, (uint64_t)k, out);
+    }
+#undef SCAPE_RS_CASE
     return hipGetLastError();
 }
 
