@@ -24,7 +24,9 @@ memory (scape_step_offload), whose rate is bound by the PCIe copies.
 each, after everything above), with the same byte accounting.
 `shard_mask_build` times the mask build one worker runs on its own
 layer-aligned 1/32 shard (scape_mask_build with num_shards = 32), shard by
-shard, beside the build over every layer.
+shard, beside the build over every layer.  `one_worker_step` times the step
+of the main workload with W = 1: one GPU's share when every worker has a GPU
+of its own (its residual and gradient, the whole model's x, m and v).
 """
 from __future__ import annotations
 
@@ -227,14 +229,18 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
             "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
 
 
-def other_workload(name: str, steps: int, warmup: int) -> dict:
-    """The fused step on another workload shape: state and two gradient
-    batches resident, `warmup` untimed steps, then `steps` timed ones."""
+def other_workload(name: str, steps: int, warmup: int, workers: int = 0) -> dict:
+    """The fused step on another workload shape (with `workers` workers instead
+    of the workload's own W when given): state and two gradient batches
+    resident, `warmup` untimed steps, then `steps` timed ones."""
+    import dataclasses
     import torch
     import synth
     import sparse_communication_adam_amd as sc
     from sparse_communication_adam_amd.state import ScapeState
     wl = synth.WORKLOADS[name]
+    if workers:
+        wl = dataclasses.replace(wl, W=workers, P=0)
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
@@ -504,6 +510,11 @@ def main() -> int:
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
+    one_worker = None
+    if not args.no_other_workloads:
+        one_worker = other_workload(wl.name, 5, 2, workers=1)
+        log(f"one worker (W = 1) on {wl.name}: {one_worker['ms_per_step']:.3f} ms/step, dense pass "
+            f"{one_worker['dense_pass_GBps']:.0f} GB/s")
     shard_builds = {}
     if not args.no_shard_build:
         for name in ("gpt-345m", "llama-0.55b", "llama-1.75b"):
@@ -539,6 +550,8 @@ def main() -> int:
         result["offload"] = offload
     if others:
         result["workloads"] = others
+    if one_worker is not None:
+        result["one_worker_step"] = one_worker
     if shard_builds:
         result["shard_mask_build"] = shard_builds
     if not args.no_cpu_baseline:

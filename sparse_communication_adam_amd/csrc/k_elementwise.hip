@@ -61,6 +61,26 @@ constexpr int kEfWaves = kEfBlock / 64;
 #endif
 constexpr bool kEfXcd = SCAPE_EF_XCD != 0;
 
+// Consecutive words per wave: a one-shot wave must keep enough bytes in
+// flight.  Measured on the 1.75B shape: at W = 1 (640 bytes per word) the pass
+// took 7.0-7.4 ms with one word per wave, 5.2 with four and 5.0 with eight; at
+// W = 2, 9.4-9.7 against 7.5-8.1 with four; at W = 4 (1.8 KB per word) one,
+// two and four words were within the run-to-run spread (13.1-13.5 ms).  At
+// larger W one word already holds enough.
+#ifndef SCAPE_EF_W1
+#define SCAPE_EF_W1 8
+#endif
+#ifndef SCAPE_EF_W2
+#define SCAPE_EF_W2 4
+#endif
+#ifndef SCAPE_EF_W4
+#define SCAPE_EF_W4 4
+#endif
+template <int WT>
+constexpr uint32_t ef_words() {
+    return WT == 1 ? SCAPE_EF_W1 : WT == 2 ? SCAPE_EF_W2 : (WT == 3 || WT == 4) ? SCAPE_EF_W4 : 1;
+}
+
 template <int WT, bool K32>
 __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
                                                        WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
@@ -69,50 +89,62 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
                                                        uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
                                                        float* __restrict__ m_stash) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
+    constexpr uint32_t kWords = ef_words<WT>();
     const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
-    const uint32_t w = blk * kEfWaves + threadIdx.x / 64;
-    if (w >= n_words) return;
+    const uint32_t w0 = (blk * kEfWaves + threadIdx.x / 64) * kWords;
+    if (w0 >= n_words) return;
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
     // every array holds n_pad elements, so all 64 lanes of a word may load:
-    // the element loads go out at once, beside the word's descriptors, and
-    // the padding lanes are dropped only before the stores
-    const size_t j = (size_t)w * 64u + lane;
-    const float mo = stream_load(&m[j]);
-    float rv[WMAX];
-    uint16_t gv[WMAX];
+    // the element loads of all the wave's words (clamped to the last word) go
+    // out at once, beside the words' descriptors, and the padding lanes are
+    // dropped only before the stores
+    float mo[kWords];
+    float rv[kWords][WMAX];
+    uint16_t gv[kWords][WMAX];
 #pragma unroll
-    for (int i = 0; i < WMAX; ++i) {
-        if (i >= W) break;
-        rv[i] = stream_load(&wp.r[i][j]);
-        gv[i] = stream_load(&wp.g[i][j]);
-    }
-    const uint32_t info = word_info[w];
-    const uint64_t word = cur_bits[w];
-    const uint32_t pre = cur_prefix[w];
-    const uint32_t count = info & 127u;
-    const int owner = (int)((info >> 8) & 63u);
-    if (lane >= count) return;  // padding lanes of a layer's last word
-    const uint32_t rank = pre + lanes_below(word);
-    const bool msk = ((word >> lane) & 1ull) && rank < k_cap;
-    const float bm = sc.beta1 * mo;
-    uint32_t kk = 0;
+    for (uint32_t e = 0; e < kWords; ++e) {
+        const size_t j = (size_t)min(w0 + e, n_words - 1u) * 64u + lane;
+        mo[e] = stream_load(&m[j]);
 #pragma unroll
-    for (int i = 0; i < WMAX; ++i) {
-        if (i >= W) break;
-        const float a = rv[i] + bf16_bits_to_f32(gv[i]);
-        const float mt = bm + sc.c1 * a;
-        if (i == owner) kk = magnitude_key(mt);
-        wp.r[i][j] = msk ? 0.0f : a;
-        if (msk) wp.b[i][rank] = mt;
+        for (int i = 0; i < WMAX; ++i) {
+            if (i >= W) break;
+            rv[e][i] = stream_load(&wp.r[i][j]);
+            gv[e][i] = stream_load(&wp.g[i][j]);
+        }
     }
-    // the selection reads the top 16 bits; candidates get their full key
-    // back from the state (or from key32 when it is asked for)
-    key16[j] = (uint16_t)(kk >> kKeyShift);
-    if (K32) key32[j] = kk;
-    // m before the step, compacted like the sparse buffers: the update pass
-    // reads it contiguously instead of gathering one cache line per position
-    if (msk) m_stash[rank] = mo;
+#pragma unroll
+    for (uint32_t e = 0; e < kWords; ++e) {
+        const uint32_t w = w0 + e;
+        if (w >= n_words) break;
+        const size_t j = (size_t)w * 64u + lane;
+        const uint32_t info = word_info[w];
+        const uint64_t word = cur_bits[w];
+        const uint32_t pre = cur_prefix[w];
+        const uint32_t count = info & 127u;
+        const int owner = (int)((info >> 8) & 63u);
+        if (lane >= count) continue;  // padding lanes of a layer's last word
+        const uint32_t rank = pre + lanes_below(word);
+        const bool msk = ((word >> lane) & 1ull) && rank < k_cap;
+        const float bm = sc.beta1 * mo[e];
+        uint32_t kk = 0;
+#pragma unroll
+        for (int i = 0; i < WMAX; ++i) {
+            if (i >= W) break;
+            const float a = rv[e][i] + bf16_bits_to_f32(gv[e][i]);
+            const float mt = bm + sc.c1 * a;
+            if (i == owner) kk = magnitude_key(mt);
+            wp.r[i][j] = msk ? 0.0f : a;
+            if (msk) wp.b[i][rank] = mt;
+        }
+        // the selection reads the top 16 bits; candidates get their full key
+        // back from the state (or from key32 when it is asked for)
+        key16[j] = (uint16_t)(kk >> kKeyShift);
+        if (K32) key32[j] = kk;
+        // m before the step, compacted like the sparse buffers: the update pass
+        // reads it contiguously instead of gathering one cache line per position
+        if (msk) m_stash[rank] = mo[e];
+    }
 }
 
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
@@ -120,10 +152,11 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
                              float* m_stash) {
     if (n_words == 0) return hipSuccess;
-    const dim3 grid((n_words + kEfWaves - 1) / kEfWaves);
-#define SCAPE_EF_LAUNCH(WV, K)                                                                                  \
-    hipLaunchKernelGGL((k_ef_compact<WV, K>), grid, dim3(kEfBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, \
-                       cur_prefix, k_cap, key16, key32, m_stash)
+#define SCAPE_EF_LAUNCH(WV, K)                                                                                 \
+    hipLaunchKernelGGL((k_ef_compact<WV, K>),                                                                  \
+                       dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())),          \
+                       dim3(kEfBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, cur_prefix, k_cap, key16, \
+                       key32, m_stash)
 #define SCAPE_EF_CASE(WV)                    \
     case WV:                                 \
         if (key32) SCAPE_EF_LAUNCH(WV, true); \
