@@ -352,6 +352,14 @@ def test_step_parity_ragged_layout():
     _assert_bitexact(run_parity(synth.ragged(), 5))
 
 
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_step_parity_ragged_layout_worker_counts(W):
+    """The dense pass takes 8 consecutive words per wave at W = 1 and 4 at
+    W = 2..4: the ragged layout's word count leaves the last workgroup
+    partly past the end, and its layers end inside words."""
+    _assert_bitexact(run_parity(synth.ragged(), 4, W=W))
+
+
 def test_step_keep_all_is_dense_from_full_mask():
     wl = synth.ragged()
     _assert_bitexact(run_parity(wl, 4, keep=(1, 1), init_mask_all=True))
