@@ -40,7 +40,7 @@ def test_dense_step_oracle_sized(name):
     _assert_bitexact(run_dense_parity(small, 3))
 
 
-@pytest.mark.parametrize("W", [1, 5, 32])
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 32])
 def test_dense_step_worker_counts(W):
     """W = 1, a count without its own kernel instance (5), and the maximum."""
     _assert_bitexact(run_dense_parity(synth.ragged(), 3, W=W))
