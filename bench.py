@@ -27,6 +27,7 @@ layer-aligned 1/32 shard (scape_mask_build with num_shards = 32), shard by
 shard, beside the build over every layer.  `one_worker_step` times the step
 of the main workload with W = 1: one GPU's share when every worker has a GPU
 of its own (its residual and gradient, the whole model's x, m and v).
+`pack_unpack` times the standalone 1-bit pack and unpack over N elements.
 """
 from __future__ import annotations
 
@@ -338,6 +339,34 @@ def shard_mask_build(name: str) -> dict:
             "alg_bytes_per_element": bpe}
 
 
+def pack_unpack(n: int) -> dict:
+    """The standalone 1-bit pack and unpack over n elements (one byte per
+    predicate, a bit per element), each timed with HIP events over 5 calls
+    after one untimed; algorithmic bytes n + n/8 each way."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    g = torch.Generator(device="cuda").manual_seed(7)
+    pred = (torch.rand(n, device="cuda", generator=g) < 0.01).to(torch.uint8)
+    bits = torch.empty((n + 63) // 64, dtype=torch.int64, device="cuda")
+    back = torch.empty_like(pred)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {"elements": n, "alg_bytes": n + n / 8}
+    for name, call in (("pack", lambda: sc.scape_pack(pred, bits)), ("unpack", lambda: sc.scape_unpack(bits, back))):
+        call()
+        ev0.record()
+        for _ in range(5):
+            call()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / 5
+        out[f"{name}_ms"] = ms
+        out[f"{name}_alg_GBps"] = (n + n / 8) / (ms * 1e-3) / 1e9
+    out["round_trip_exact"] = bool(torch.equal(back, pred))
+    del pred, bits, back
+    torch.cuda.empty_cache()
+    return out
+
+
 def spin_up(seconds: float) -> None:
     """Plain device-to-device copies for `seconds`: an idle GPU takes a while
     to reach its steady memory and fabric clocks."""
@@ -406,7 +435,8 @@ def main() -> int:
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the step on the other workload shapes")
     ap.add_argument("--no-shard-build", action="store_true",
-                    help="skip timing the per-worker mask build on one layer-aligned shard")
+                    help="skip timing the per-worker mask build on one layer-aligned shard and the "
+                         "standalone pack / unpack")
     ap.add_argument("--spinup-s", type=float, default=0.0,
                     help="seconds of plain device copies before anything else (off by default: allocating and "
                          "freeing its buffers just before the state left the state in memory where the dense "
@@ -515,6 +545,11 @@ def main() -> int:
         one_worker = other_workload(wl.name, 5, 2, workers=1)
         log(f"one worker (W = 1) on {wl.name}: {one_worker['ms_per_step']:.3f} ms/step, dense pass "
             f"{one_worker['dense_pass_GBps']:.0f} GB/s")
+    pu = None
+    if not args.no_shard_build:
+        pu = pack_unpack(N)
+        log(f"pack / unpack of {N} elements: {pu['pack_ms']:.3f} / {pu['unpack_ms']:.3f} ms "
+            f"({pu['pack_alg_GBps']:.0f} / {pu['unpack_alg_GBps']:.0f} GB/s)")
     shard_builds = {}
     if not args.no_shard_build:
         for name in ("gpt-345m", "llama-0.55b", "llama-1.75b"):
@@ -554,6 +589,8 @@ def main() -> int:
         result["one_worker_step"] = one_worker
     if shard_builds:
         result["shard_mask_build"] = shard_builds
+    if pu is not None:
+        result["pack_unpack"] = pu
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

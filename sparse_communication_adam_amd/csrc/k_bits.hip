@@ -156,46 +156,96 @@ hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, ui
     return hipGetLastError();
 }
 
-// Pack: one wave per word, lane l tests element 64*word + l.
+// Pack and unpack: a lane takes 16 consecutive elements, so a wave covers a
+// 1024-element chunk (16 words) per trip.  The 16 predicate bytes are one
+// 16-byte load (or store) when `pred` is 16-byte aligned and the 16 elements
+// are inside n; otherwise byte by byte.  Element j is bit j & 63 of word
+// j >> 6, so lane l holds bits 16 (l % 4) .. 16 (l % 4) + 15 of word l / 4 of
+// its chunk, and lanes 4q .. 4q + 3 together form that word.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint64_t kChunk = 1024;  // elements per wave per trip
+
+// bit b of the result: byte b of x is nonzero (b < 4)
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    const uint32_t t = ((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x;  // top bit of each byte: byte != 0
+    return ((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) | ((t >> 28) & 8u);
+}
+
+// bytes 0..3 of the result: bits 0..3 of x (each 0 or 1)
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t x) {
+    return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+}
+
 __global__ __launch_bounds__(kBlock) void k_pack(const uint8_t* __restrict__ pred, uint64_t n, uint64_t n_words,
-                                                 uint64_t* __restrict__ bits) {
+                                                 uint64_t* __restrict__ bits, bool vec) {
     const uint32_t lane = lane_id();
     const uint64_t waves = (uint64_t)gridDim.x * kWaves;
-    for (uint64_t w = (uint64_t)blockIdx.x * kWaves + threadIdx.x / 64; w < n_words; w += waves) {
-        const uint64_t j = w * 64 + lane;
-        const bool p = j < n && pred[j] != 0;
-        const uint64_t word = __ballot(p);
-        if (lane == 0) bits[w] = word;
+    const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
+    for (uint64_t c = (uint64_t)blockIdx.x * kWaves + threadIdx.x / 64; c < n_chunks; c += waves) {
+        const uint64_t j0 = c * kChunk + lane * 16u;
+        uint32_t m16 = 0;
+        if (vec && j0 + 16u <= n) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(pred + j0);
+            m16 = nonzero_bytes(v.x) | (nonzero_bytes(v.y) << 4) | (nonzero_bytes(v.z) << 8) |
+                  (nonzero_bytes(v.w) << 12);
+        } else {
+            for (uint32_t e = 0; e < 16u; ++e)
+                if (j0 + e < n && pred[j0 + e] != 0) m16 |= 1u << e;
+        }
+        const uint32_t m1 = __shfl_down(m16, 1), m2 = __shfl_down(m16, 2), m3 = __shfl_down(m16, 3);
+        const uint64_t w = c * (kChunk / 64u) + lane / 4u;
+        if ((lane & 3u) == 0 && w < n_words)
+            bits[w] = (uint64_t)m16 | ((uint64_t)m1 << 16) | ((uint64_t)m2 << 32) | ((uint64_t)m3 << 48);
     }
 }
 
 hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits) {
     if (n <= 0) return hipSuccess;
     const uint64_t nw = ((uint64_t)n + 63) / 64;
-    uint64_t blocks = (nw + kWaves - 1) / kWaves;
+    const uint64_t chunks = ((uint64_t)n + kChunk - 1) / kChunk;
+    uint64_t blocks = (chunks + kWaves - 1) / kWaves;
     if (blocks > 16384u) blocks = 16384u;
-    hipLaunchKernelGGL(k_pack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, pred, (uint64_t)n, nw, bits);
+    const bool vec = ((uintptr_t)pred % 16u) == 0;
+    hipLaunchKernelGGL(k_pack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, pred, (uint64_t)n, nw, bits, vec);
     return hipGetLastError();
 }
 
 __global__ __launch_bounds__(kBlock) void k_unpack(const uint64_t* __restrict__ bits, uint64_t n,
-                                                   uint8_t* __restrict__ pred) {
-    for (uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += (uint64_t)gridDim.x * kBlock)
-        pred[j] = (uint8_t)((bits[j >> 6] >> (j & 63)) & 1ull);
+                                                   uint8_t* __restrict__ pred, bool vec) {
+    const uint32_t lane = lane_id();
+    const uint64_t waves = (uint64_t)gridDim.x * kWaves;
+    const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
+    for (uint64_t c = (uint64_t)blockIdx.x * kWaves + threadIdx.x / 64; c < n_chunks; c += waves) {
+        const uint64_t j0 = c * kChunk + lane * 16u;
+        if (j0 >= n) continue;
+        const uint32_t m16 = (uint32_t)(bits[j0 >> 6] >> (j0 & 63u)) & 0xFFFFu;
+        if (vec && j0 + 16u <= n) {
+            u32x4 v;
+            v.x = spread_nibble(m16);
+            v.y = spread_nibble(m16 >> 4);
+            v.z = spread_nibble(m16 >> 8);
+            v.w = spread_nibble(m16 >> 12);
+            *reinterpret_cast<u32x4*>(pred + j0) = v;
+        } else {
+            for (uint32_t e = 0; e < 16u; ++e)
+                if (j0 + e < n) pred[j0 + e] = (uint8_t)((m16 >> e) & 1u);
+        }
+    }
 }
 
 hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred) {
     if (n <= 0) return hipSuccess;
-    uint64_t blocks = ((uint64_t)n + kBlock - 1) / kBlock;
+    const uint64_t chunks = ((uint64_t)n + kChunk - 1) / kChunk;
+    uint64_t blocks = (chunks + kWaves - 1) / kWaves;
     if (blocks > 16384u) blocks = 16384u;
-    hipLaunchKernelGGL(k_unpack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, bits, (uint64_t)n, pred);
+    const bool vec = ((uintptr_t)pred % 16u) == 0;
+    hipLaunchKernelGGL(k_unpack, dim3((uint32_t)blocks), dim3(kBlock), 0, s, bits, (uint64_t)n, pred, vec);
     return hipGetLastError();
 }
 
 // Plain device copy for measuring the stream-copy rate the step's kernels
 // are compared with: one-shot, 16 bytes per thread, non-temporal loads and
 // stores, workgroups in the same XCD-aware order as the dense pass.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kBlock) void k_copy_probe(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                        uint64_t n16) {

@@ -60,20 +60,33 @@ def test_gpu_generator_matches_host(name):
 # kernels one by one
 
 
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 1000, 100003, (1 << 20) + 17])
-def test_pack_unpack(n):
+# sizes around the 16-element lane and 1024-element wave chunks, and one with
+# more chunks than the grid covers in a trip; offset 0 takes the 16-byte
+# path, offsets 1 and 8 (pred not 16-byte aligned) the byte path
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 63, 64, 65, 1000, 1023, 1024, 1025, 100003, (1 << 20) + 17,
+                               (1 << 26) + 1043])
+@pytest.mark.parametrize("offset", [0, 1, 8])
+def test_pack_unpack(n, offset):
     import torch
     import sparse_communication_adam_amd as sc
-    rng = np.random.default_rng(n)
+    if offset and n > (1 << 21):
+        pytest.skip("the byte path is covered at the smaller sizes")
+    rng = np.random.default_rng(n + offset)
     pred = (rng.random(n) < 0.3).astype(np.uint8)
     pred[rng.integers(0, n, 3)] = 7  # any nonzero byte counts as set
-    d_pred = torch.from_numpy(pred).cuda()
+    pred[rng.integers(0, n, 3)] = 0x80
+    buf = torch.zeros(n + offset, dtype=torch.uint8, device="cuda")
+    d_pred = buf[offset:]
+    d_pred.copy_(torch.from_numpy(pred))
     bits = torch.full(((n + 63) // 64,), -1, dtype=torch.int64, device="cuda")
     sc.scape_pack(d_pred, bits)
     assert np.array_equal(u64(bits), oracle.pack(pred != 0))
-    back = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = torch.full((n + offset + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    back = out[offset:offset + n]
     sc.scape_unpack(bits, back)
     assert np.array_equal(to_np(back), (pred != 0).astype(np.uint8))
+    rest = to_np(out)
+    assert (rest[:offset] == 0xA5).all() and (rest[offset + n:] == 0xA5).all()  # nothing outside the range
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 8, 32])
