@@ -16,7 +16,7 @@
 // layout as the dense SCAPE pass: the W gradients averaged in worker order and
 // the AdamS update of x, m, v on every element.
 //
-// Sparse pass (k_reduce_update): one lane per masked position: the W-way mean
+// Sparse pass (k_reduce_update): eight masked positions per lane: the W-way mean
 // of the sparse buffers in worker order, the reconstruction of the averaged
 // gradient from that one buffer, the AdamS normaliser, and the m/v/x update.
 // The dense pass leaves m of every masked position in a compacted stash, so
@@ -32,11 +32,12 @@
 
 namespace scape {
 
-// Dense pass, one-shot layout: a wave handles one 64-element word and
-// exits; a workgroup is 4 consecutive words.  Work is dispatched in address
-// order, so the words in flight at any time are a compact window of every
-// array; on MI355X that sustains a higher HBM rate than long-lived
-// workgroups streaming separate tiles or striding over the grid.  Per word, a
+// Dense pass, one-shot layout: a wave handles a short run of consecutive
+// 64-element words (how many depends on W, below) and exits; a workgroup's
+// four waves take consecutive runs.  Work is dispatched in address order, so
+// the words in flight at any time are a compact window of every array; on
+// MI355X that sustains a higher HBM rate than long-lived workgroups streaming
+// separate tiles or striding over the grid.  Per word, a
 // 16-bit descriptor gives the owner worker (bits 8..13) and the number of
 // elements of the word inside its layer (bits 0..6, 1..64; 0 = padding).
 // Every worker's loads are issued before any store.
@@ -51,7 +52,7 @@ __device__ __forceinline__ T stream_load(const T* p) {
 #ifndef SCAPE_EF_BLOCK
 #define SCAPE_EF_BLOCK 256
 #endif
-constexpr int kEfBlock = SCAPE_EF_BLOCK;  // threads per workgroup of the dense pass (one word per wave)
+constexpr int kEfBlock = SCAPE_EF_BLOCK;  // threads per workgroup of the dense pass
 constexpr int kEfWaves = kEfBlock / 64;
 // Each XCD streams one contiguous eighth of the words (measured: the dense
 // pass 0.3-0.9 ms faster on the 1.75B workload, most where the process's
