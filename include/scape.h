@@ -279,11 +279,10 @@ int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream);
 
 /* Optional per-phase timing of scape_step with HIP events recorded on the
  * step's stream (and on the context's update stream).  The W-way reduction
- * and update run on the context's own stream, starting once the mask
- * selection is done, beside the mask index (they share no data the other
- * writes); the update and the selection are both measured from the end of
- * the dense pass, and the index phase includes waiting for the update.
- * Phases: */
+ * and update run on the context's own stream beside the mask selection's
+ * record passes (they share no data the other writes), starting once the key
+ * filter is done, so those two phases overlap: both are measured from the end
+ * of the dense pass.  Phases: */
 #define SCAPE_PHASE_EF_COMPACT 0    /* error feedback, candidates, compaction, statistic */
 #define SCAPE_PHASE_REDUCE_UPDATE 1 /* W-way reduction, reconstruction, v/m/x update     */
 #define SCAPE_PHASE_MASK_SELECT 2   /* per-layer top-k into bits                        */

@@ -268,11 +268,10 @@ hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t
 // Sparse pass: positions q of the current mask, kUpdatePer per thread (strided
 // by the workgroup size so that idx, the sparse buffers and the m stash are
 // read contiguously), every load issued before the arithmetic.  The pass runs
-// on another stream, after the mask selection and beside the mask index; its
-// grid is capped at two workgroups per CU, striding over the positions
-// (measured on the 0.35B, 0.55B and 1.75B workloads: 512 and no cap were
-// about equally fast, 256 and 128 starved the pass where it is long, W = 8
-// at keep 1/10).
+// beside the mask selection's record passes on another stream; its grid is
+// capped at two workgroups per CU, striding over the positions (measured on
+// the 0.35B, 0.55B and 1.75B workloads: 512 and no cap were equally fast,
+// 256 and 128 starved the pass where it is long, W = 8 at keep 1/10).
 #ifndef SCAPE_UPDATE_PER
 #define SCAPE_UPDATE_PER 8  // with few workgroups, more positions in flight per thread
 #endif

@@ -261,11 +261,10 @@ void prof_collect(scape_ctx* c, int slot) {
     ProfSlot& p = c->prof[slot];
     if (!p.pending) return;
     hipEventSynchronize(p.ev[SCAPE_PHASE_COUNT]);
-    // points: 0 start, 1 end of the dense pass, 2 end of the update, 3 end
-    // of the selection (where the update is forked), 4 end of the index and
-    // the join.  The update is measured from point 1 like the selection, so
-    // its phase covers the selection it waits for; the index phase includes
-    // waiting for the update.
+    // points: 0 start, 1 end of the dense pass (where the update and the
+    // selection fork), 2 end of the update, 3 end of the selection, 4 end of
+    // the index and the join.  The update and the selection run side by side,
+    // so both are measured from point 1.
     static const int from[SCAPE_PHASE_COUNT] = {0, 1, 1, 3};
     static const int to[SCAPE_PHASE_COUNT] = {1, 2, 3, 4};
     for (int i = 0; i < SCAPE_PHASE_COUNT; ++i) {
@@ -287,12 +286,17 @@ int prof_begin(scape_ctx* c) {
 
 // Mask selection over layers [la, la+nl) and tiles [ta, tb), from 16-bit keys
 // and the source of candidates' full keys, bits into `bits`.
+// `fork`, when given, is recorded on `s` once the key filter is queued (at
+// once if there is nothing to select): the step's update starts there.
 int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
-               const KeySource& ks, uint64_t* bits, hipStream_t s) {
+               const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork = nullptr) {
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
     const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
-    if (ns == 0) return SCAPE_OK;  // every layer in the range is empty: no bits to set
+    if (ns == 0) {  // every layer in the range is empty: no bits to set
+        if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
+        return SCAPE_OK;
+    }
     uint32_t* sample_count = c->d_counts;
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_fill + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
@@ -302,6 +306,7 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
                             c->d_seg_above),
               "filter");
+    if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
               "cand_scan");
     SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
@@ -493,17 +498,14 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     }
     prof_mark(ctx, slot, 1, s);
     // The update touches x, v, and m on the mask only; the selection reads
-    // the keys, m off the mask, the owner's residual and the sparse buffers,
-    // and the mask index reads only the new bits.  Nothing one writes is read
-    // by another, so the update could run beside any of them; it is forked
-    // once the selection is done and runs on its own stream beside the mask
-    // index, and `stream` waits for it at the end.  Its scattered traffic
-    // stretched the selection's latency-bound record passes when they ran
-    // together (measured on three workloads: forked here the time after the
-    // dense pass was as short or shorter, and varied least).
-    rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s);
+    // the keys, m off the mask, the owner's residual and the sparse buffers.
+    // Nothing one writes is read by the other, so the update runs on its own
+    // stream beside the selection, and `stream` waits for it at the end.  It
+    // starts after the key filter: the sampling and filter passes stream the
+    // keys and run best alone, while the record passes that follow are
+    // latency-bound and share the GPU well with the update.
+    rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s, ctx->ev_fork);
     if (rc) return rc;  // nothing was queued on the update's stream
-    SCAPE_HIP(hipEventRecord(ctx->ev_fork, s), "fork");
     SCAPE_HIP(hipStreamWaitEvent(ctx->s_upd, ctx->ev_fork, 0), "fork");
     SCAPE_HIP(launch_reduce_update(ctx->s_upd, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash,
                                    ctx->n_words, (uint32_t)ctx->lay.n_pad, k_cap),
