@@ -28,6 +28,8 @@ shard, beside the build over every layer.  `one_worker_step` times the step
 of the main workload with W = 1: one GPU's share when every worker has a GPU
 of its own (its residual and gradient, the whole model's x, m and v).
 `pack_unpack` times the standalone 1-bit pack and unpack over N elements.
+`graph_step` times the single-layer workload's step replayed from HIP graphs
+beside the same step launched eagerly.
 """
 from __future__ import annotations
 
@@ -367,6 +369,44 @@ def pack_unpack(n: int) -> dict:
     return out
 
 
+def graph_step(name: str, steps: int = 20, warmup: int = 2) -> dict:
+    """The step of a small workload replayed from HIP graphs (ScapeState.capture)
+    beside the same step launched eagerly, each timed with HIP events."""
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    from sparse_communication_adam_amd.state import ScapeState
+    wl = synth.WORKLOADS[name]
+    cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
+                         owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
+                         weight_decay=wl.weight_decay)
+    out = {"workload": name, "steps": steps, "warmup": warmup}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for mode in ("eager", "graph"):
+        st = ScapeState(cfg)
+        lay = st.layout
+        synth.params_flat_gpu(wl, lay.layer_offset, st.x)
+        gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
+        for i, g in enumerate(gs):
+            synth.grads_flat_gpu(wl, lay.layer_offset, g, 1, i)
+        if mode == "graph":
+            st.capture(gs)
+        run = st.step_graph if mode == "graph" else (lambda: st.step(gs, key_out=False))
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(steps):
+            run()
+        ev1.record()
+        torch.cuda.synchronize()
+        out[f"{mode}_ms_per_step"] = ev0.elapsed_time(ev1) / steps
+        st.destroy()
+        del st, gs
+    torch.cuda.empty_cache()
+    return out
+
+
 def spin_up(seconds: float) -> None:
     """Plain device-to-device copies for `seconds`: an idle GPU takes a while
     to reach its steady memory and fabric clocks."""
@@ -540,6 +580,11 @@ def main() -> int:
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
+    graphed = None
+    if not args.no_other_workloads:
+        graphed = graph_step("single-1024x1024")
+        log(f"single-1024x1024 step: eager {graphed['eager_ms_per_step']:.3f} ms, replayed from HIP graphs "
+            f"{graphed['graph_ms_per_step']:.3f} ms")
     one_worker = None
     if not args.no_other_workloads:
         one_worker = other_workload(wl.name, 5, 2, workers=1)
@@ -587,6 +632,8 @@ def main() -> int:
         result["workloads"] = others
     if one_worker is not None:
         result["one_worker_step"] = one_worker
+    if graphed is not None:
+        result["graph_step"] = graphed
     if shard_builds:
         result["shard_mask_build"] = shard_builds
     if pu is not None:

@@ -7,6 +7,11 @@ Usage, gist.science Technical Summary s.2): after each step the two mask
 slots swap roles.  The first step uses an all-zero mask.  With
 ``offload=True`` the residuals live in pinned host memory and each step calls
 ``scape_step_offload`` (Memory Optimization, same section).
+
+``capture`` records the step as HIP graphs, for small models whose step is
+bound by its ~30 kernel launches: ``step_graph`` then replays it with one
+launch.  scape_step never waits on the host, clears memory with kernels, and
+joins its second stream back with events, so it can be captured.
 """
 from __future__ import annotations
 
@@ -53,6 +58,32 @@ class ScapeState:
         fn = scape_step_offload if self.offload else scape_step
         fn(self.ctx, self.x, self.m, self.v, self.r, grads, self.cur_mask, self.next_mask, self.sparse,
            self.key if key_out else None, stream)
+        self._cur = 1 - self._cur
+        self.t += 1
+
+    def capture(self, grads: Sequence, key_out: bool = False) -> None:
+        """Capture the step as two HIP graphs, one for each assignment of the
+        two mask slots (they swap roles every step).  The graphs read the
+        gradients from `grads`, the W int16 tensors given here: before each
+        ``step_graph`` the caller writes that step's gradients into them.
+        Capturing runs nothing, so the state does not change."""
+        import torch
+        if self.offload:
+            raise ValueError("the offloaded step copies to and from host memory and is not captured")
+        self._graph_grads = list(grads)
+        graphs = []
+        for cur in (0, 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                scape_step(self.ctx, self.x, self.m, self.v, self.r, self._graph_grads, self.masks[cur],
+                           self.masks[1 - cur], self.sparse, self.key if key_out else None)
+            graphs.append(g)
+        self._graphs = graphs
+
+    def step_graph(self) -> None:
+        """One step replayed from the captured graphs on the current stream,
+        with this step's gradients already in the capture buffers."""
+        self._graphs[self._cur].replay()
         self._cur = 1 - self._cur
         self.t += 1
 
