@@ -256,9 +256,10 @@ int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits
 int scape_mask_index(scape_ctx* ctx, const scape_mask* mask, void* stream);
 
 /* Pack n bytes (nonzero = set) into ceil(n/64) words, LSB first; bits past n
- * are zero.  Unpack writes n bytes of 0/1.  pred needs no alignment, bits
- * 8-byte alignment.  n >= 0 (n = 0 enqueues nothing).  Errors: INVALID_ARG,
- * ALIGN, SHAPE (n >= 2^37), HIP. */
+ * are zero.  Unpack writes n bytes of 0/1 and nothing past them.  pred needs
+ * no alignment (a 16-byte aligned pred is read or written 16 bytes at a
+ * time), bits 8-byte alignment.  n >= 0 (n = 0 enqueues nothing).  Errors:
+ * INVALID_ARG, ALIGN, SHAPE (n >= 2^37), HIP. */
 int scape_pack(const uint8_t* pred, int64_t n, uint64_t* bits, void* stream);
 int scape_unpack(const uint64_t* bits, int64_t n, uint8_t* pred, void* stream);
 
