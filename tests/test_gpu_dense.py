@@ -61,3 +61,11 @@ FULL_SAMPLES = {
 def test_dense_step_full_size_sampled_layers(name):
     wl = synth.WORKLOADS[name]
     _assert_bitexact(run_dense_parity(wl, 2, sample=FULL_SAMPLES[name]))
+
+
+def test_dense_step_maximum_size():
+    """The largest layout the ABI takes (n_pad = 2^31 - 64, one worker); the
+    last layer, whose positions end 64 elements short of 2^31, against the
+    oracle."""
+    from test_gpu_parity import max_size_workload
+    _assert_bitexact(run_dense_parity(max_size_workload(), 2, sample=[31]))

@@ -453,6 +453,25 @@ def test_step_parity_full_size_sampled_layers(name):
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name]))
 
 
+def max_size_workload() -> "synth.Workload":
+    """The largest layout the ABI takes: n_pad = 2^31 - 64 (30 layers of 2^26
+    elements, one of 133,217,600, and a ragged last layer of 1,000,003 whose
+    positions end 64 elements short of 2^31), one worker."""
+    ts = [synth.configs.Tensor(f"big{i}", (1 << 26,)) for i in range(30)]
+    ts += [synth.configs.Tensor("big30", (133217600,)), synth.configs.Tensor("last", (1000003,))]
+    return synth.Workload(name="max-size", tensors=tuple(ts), W=1, keep_num=1, keep_den=100, steps=2,
+                          seed=1098, grad_kind="loguniform")
+
+
+def test_step_parity_maximum_size():
+    """Every layer's counts and the index at the largest positions the ABI
+    allows; the last layer against the oracle; candidates' keys recomputed
+    (the configuration bench.py times)."""
+    wl = max_size_workload()
+    assert sum((t.numel + 63) // 64 * 64 for t in wl.tensors) == (1 << 31) - 64
+    _assert_bitexact(run_parity(wl, wl.steps, sample=[31], key_out=False))
+
+
 # Without key_out the step keeps only 16-bit keys and recomputes each
 # candidate's full key from m, the owner's residual and its sparse buffer:
 # the configuration bench.py times.
