@@ -365,11 +365,12 @@ def test_step_parity_ragged_layout():
     _assert_bitexact(run_parity(synth.ragged(), 5))
 
 
-@pytest.mark.parametrize("W", [1, 2, 4])
+@pytest.mark.parametrize("W", [1, 2, 4, 5, 16])
 def test_step_parity_ragged_layout_worker_counts(W):
     """The dense pass takes 8 consecutive words per wave at W = 1 and 4 at
     W = 2..4: the ragged layout's word count leaves the last workgroup
-    partly past the end, and its layers end inside words."""
+    partly past the end, and its layers end inside words.  W = 5 runs the
+    kernels' instance for a worker count without its own, W = 16 its own."""
     _assert_bitexact(run_parity(synth.ragged(), 4, W=W))
 
 
