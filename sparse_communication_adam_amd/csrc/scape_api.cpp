@@ -502,8 +502,10 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     // Nothing one writes is read by the other, so the update runs on its own
     // stream beside the selection, and `stream` waits for it at the end.  It
     // starts after the key filter: the sampling and filter passes stream the
-    // keys and run best alone, while the record passes that follow are
-    // latency-bound and share the GPU well with the update.
+    // keys and run best alone.  The latency-bound record passes that follow
+    // are slowed by the update's scattered traffic, but forking the update
+    // only after the whole selection measured slower where the dense pass
+    // lands at its slow placement (and no faster elsewhere).
     rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s, ctx->ev_fork);
     if (rc) return rc;  // nothing was queued on the update's stream
     SCAPE_HIP(hipStreamWaitEvent(ctx->s_upd, ctx->ev_fork, 0), "fork");
