@@ -237,17 +237,26 @@ def _vals(s, dtype=np.float32):
     return np.array([float(Fraction(x)) for x in s.split(",")] if s else [], dtype)
 
 
-def test_golden_worked_step():
-    d = _parse_golden()
+@pytest.mark.parametrize("name", ["worked_step.txt", "worked_step_wd.txt"])
+def test_golden_worked_step(name):
+    """Hand-worked dyadic steps: the three-step example without weight decay,
+    and the one with decoupled weight decay (wd = 0.5) that starts from a full
+    mask, so that the decay term is exercised at masked positions and shown
+    absent off the mask."""
+    d = _parse_golden(name)
     n, W, P = int(d["layer_n"]), int(d["W"]), int(d["P"])
     num, den = [int(v) for v in d["keep"].split("/")]
     lay = oracle.layout([n], num, den, P)
     assert lay.owner.tolist() == [0] and lay.k.tolist() == [2]
-    hp = oracle.Hyper(float(d["beta1"]), float(d["beta2"]), float(d["lr"]), float(d["eps"]), 0.0)
+    hp = oracle.Hyper(float(d["beta1"]), float(d["beta2"]), float(d["lr"]), float(d["eps"]),
+                      float(d.get("wd", "0")))
     x = np.zeros(lay.n_pad, np.float32)
     x[:n] = _vals(d["x0"])
     st = oracle.State.zeros(lay.n_pad, W, x)
-    cur = np.zeros(lay.n_words, np.uint64)
+    pred = np.zeros(lay.n_pad, np.uint8)
+    if d.get("M1"):
+        pred[[int(v) for v in d["M1"].split(",")]] = 1
+    cur = oracle.pack(pred)
     for t in (1, 2, 3):
         gs = []
         for i in range(W):
@@ -266,6 +275,49 @@ def test_golden_worked_step():
         assert np.array_equal(st.v[:n], _vals(d[f"step{t}.v"])), t
         assert out.next_idx.tolist() == [int(v) for v in d[f"step{t}.next"].split(",")], t
         cur = out.next_words
+
+
+def round_to_f32(q: Fraction) -> np.float32:
+    """Exact round-to-nearest-even of a rational to fp32 (normal range), by
+    integer arithmetic on the significand."""
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while q * Fraction(2) ** (23 - e) >= 2 ** 24:
+        e += 1
+    while q * Fraction(2) ** (23 - e) < 2 ** 23:
+        e -= 1
+    t = q * Fraction(2) ** (23 - e)
+    n = t.numerator // t.denominator
+    rest = t - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(Fraction(n) * Fraction(2) ** (e - 23)))
+
+
+@pytest.mark.parametrize("W", [3, 5, 6, 7])
+def test_reduce_mean_is_one_correctly_rounded_division(W):
+    """The mean is the fp32 sum in worker order followed by one correctly
+    rounded division by W (the reading of "averaged" in the Single-Buffer
+    Second-Moment Reconstruction paragraph).  At worker counts that are not
+    powers of two, multiplying by the rounded reciprocal 1/W gives a different
+    fp32 value for about a third of the sums; the expected values here are
+    the exact quotients rounded by integer arithmetic."""
+    rng = np.random.default_rng(W)
+    k = 600
+    bufs = [(rng.standard_normal(k) * 10.0 ** rng.integers(-3, 3, k)).astype(np.float32) for _ in range(W)]
+    got = oracle.reduce(bufs)
+    recip_differs = 0
+    for q in range(k):
+        s = Fraction(float(bufs[0][q]))
+        for i in range(1, W):  # each fp32 addition rounds once
+            s = Fraction(float(round_to_f32(s + Fraction(float(bufs[i][q])))))
+        exp = round_to_f32(s / W)
+        assert got[q].view(np.uint32) == exp.view(np.uint32), (q, got[q], exp)
+        recip_differs += round_to_f32(s * Fraction(float(np.float32(1.0) / np.float32(W)))) != exp
+    assert recip_differs > k // 10  # the cases do tell the two forms apart
 
 
 def _run(lay, W, T, hp, grads_fn, cur=None, x=None, owner_map=None):
