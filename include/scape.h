@@ -174,6 +174,25 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
                void* stream);
 
 /*
+ * scape_step with the W workers' residuals and gradients in the
+ * worker-interleaved layout: one array each, in which every 64-element word
+ * of the flat layout holds worker 0's 64 values, then worker 1's, ..., then
+ * worker W-1's.  Element j = 64*w + l (0 <= l < 64) of worker i is
+ *   r_il[(w*W + i)*64 + l]   and   g_il[(w*W + i)*64 + l].
+ * The dense pass then streams two worker arrays instead of 2W (measured on
+ * the 1.75B-shaped workload at W = 4: 14.3 against 15.3 ms for the pass).
+ * Same computation and results as scape_step, bit for bit.
+ * Arguments as scape_step, except:
+ *   r_il  fp32 device array of n_pad*W elements, updated in place;
+ *   g_il  bfloat16 bits (uint16) device array of n_pad*W elements, read only;
+ * both 16-byte aligned.
+ * Errors: as scape_step.
+ */
+int scape_step_interleaved(scape_ctx* ctx, float* x, float* m, float* v, float* r_il, const uint16_t* g_il,
+                           const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs,
+                           uint32_t* key_out, void* stream);
+
+/*
  * scape_step with the W residuals in pinned host memory: CPU offloading of
  * the residual buffers with double buffering ([TS-2] Memory Optimization).
  * Same computation and results as scape_step, bit for bit.  The residuals
@@ -218,6 +237,11 @@ int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* cons
  * Errors: INVALID_ARG, ALIGN, HIP.
  */
 int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream);
+
+/* scape_dense_step with the W gradients in the worker-interleaved layout of
+ * scape_step_interleaved (g_il: n_pad*W bfloat16 bits, 16-byte aligned).
+ * Errors: as scape_dense_step. */
+int scape_dense_step_interleaved(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* g_il, void* stream);
 
 /*
  * Mask build alone, from first-moment statistics mtilde (fp32, n_pad): per

@@ -63,7 +63,9 @@ def lib() -> ctypes.CDLL:
             "scape_destroy": [vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
+            "scape_step_interleaved": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_dense_step": [vp, vp, vp, vp, vp, vp],
+            "scape_dense_step_interleaved": [vp, vp, vp, vp, vp, vp],
             "scape_mask_union_add": [vp, vp, vp, vp],
             "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
             "scape_mask_index": [vp, maskp, vp],
@@ -169,18 +171,25 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _dev(t, dtype, numel: Optional[int], name: str) -> int:
+def _shape(t, dtype, numel: Optional[int], name: str) -> None:
+    """Check a tensor's type, dtype, layout and length."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on the GPU (got {t.device})")
     if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+
+
+def _dev(t, dtype, numel: Optional[int], name: str) -> int:
+    """Device pointer of a torch tensor, after checking its type, dtype,
+    layout, length and device (all before anything reaches the library)."""
+    _shape(t, dtype, numel, name)
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
     return t.data_ptr()
 
 
@@ -212,13 +221,22 @@ class Mask:
     def __init__(self, bits, idx, block_prefix):
         self.bits, self.idx, self.block_prefix = bits, idx, block_prefix
 
-    def _c(self) -> _Mask:
+    def _c(self, layout: "Layout", need_index: bool = True) -> _Mask:
+        """The C struct, after checking each array against `layout`: bits
+        needs n_pad/64 words, idx k_total entries and block_prefix
+        n_pad/64 + 1 (idx and block_prefix only when the entry point uses
+        them).  Every length is checked before any device check."""
         import torch
-        ints = (torch.int64,)
-        b = _dev(self.bits, ints, None, "mask.bits")
-        i = _dev(self.idx, (torch.int32,), None, "mask.idx") if self.idx is not None else None
-        p = _dev(self.block_prefix, (torch.int32,), None, "mask.block_prefix") if self.block_prefix is not None else None
-        return _Mask(b, i, p)
+        nw = layout.n_words
+        arrs = [(self.bits, (torch.int64,), nw, "mask.bits")]
+        if need_index or self.idx is not None:
+            arrs.append((self.idx, (torch.int32,), max(layout.k_total, 1), "mask.idx"))
+        if need_index or self.block_prefix is not None:
+            arrs.append((self.block_prefix, (torch.int32,), nw + 1, "mask.block_prefix"))
+        for a in arrs:
+            _shape(*a)
+        ptrs = {name: _dev(*a[:3], name) for *a, name in arrs}
+        return _Mask(ptrs["mask.bits"], ptrs.get("mask.idx"), ptrs.get("mask.block_prefix"))
 
     def clear(self):
         self.bits.zero_()
@@ -287,9 +305,30 @@ def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next:
     gp = _ptr_array([_dev(t, (torch.int16, torch.bfloat16, torch.uint16), n, f"g[{i}]") for i, t in enumerate(g)])
     bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
     kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
-    c, nx = cur._c(), next._c()
+    c, nx = cur._c(ctx.layout), next._c(ctx.layout)
     _check(lib().scape_step(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
                             _stream(stream)))
+
+
+def scape_step_interleaved(ctx: Context, x, m, v, r_il, g_il, cur: Mask, next: Mask, sparse_bufs: Sequence,
+                           key_out=None, stream=None) -> None:
+    """scape_step with the residuals and gradients in the worker-interleaved
+    layout: r_il (fp32) and g_il (bf16 bits) of n_pad*W elements, word w of
+    worker i at [(w*W + i)*64, (w*W + i)*64 + 64)."""
+    import torch
+    n, W, k = ctx.layout.n_pad, ctx.cfg.workers, ctx.layout.k_total
+    if len(sparse_bufs) != W:
+        raise ValueError(f"sparse_bufs needs {W} entries")
+    xp = _dev(x, torch.float32, n, "x")
+    mp = _dev(m, torch.float32, n, "m")
+    vp = _dev(v, torch.float32, n, "v")
+    rp = _dev(r_il, torch.float32, n * W, "r_il")
+    gp = _dev(g_il, (torch.int16, torch.bfloat16, torch.uint16), n * W, "g_il")
+    bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
+    kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
+    c, nx = cur._c(ctx.layout), next._c(ctx.layout)
+    _check(lib().scape_step_interleaved(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
+                                        _stream(stream)))
 
 
 def scape_step_offload(ctx: Context, x, m, v, r_host: Sequence, g: Sequence, cur: Mask, next: Mask,
@@ -306,7 +345,7 @@ def scape_step_offload(ctx: Context, x, m, v, r_host: Sequence, g: Sequence, cur
     gp = _ptr_array([_dev(t, (torch.int16, torch.bfloat16, torch.uint16), n, f"g[{i}]") for i, t in enumerate(g)])
     bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
     kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
-    c, nx = cur._c(), next._c()
+    c, nx = cur._c(ctx.layout), next._c(ctx.layout)
     _check(lib().scape_step_offload(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
                                     _stream(stream)))
 
@@ -323,10 +362,27 @@ def scape_dense_step(ctx: Context, x, m, v, g: Sequence, stream=None) -> None:
     _check(lib().scape_dense_step(ctx.handle, xp, mp, vp, gp, _stream(stream)))
 
 
+def scape_dense_step_interleaved(ctx: Context, x, m, v, g_il, stream=None) -> None:
+    """scape_dense_step with the gradients in the worker-interleaved layout."""
+    import torch
+    n, W = ctx.layout.n_pad, ctx.cfg.workers
+    xp = _dev(x, torch.float32, n, "x")
+    mp = _dev(m, torch.float32, n, "m")
+    vp = _dev(v, torch.float32, n, "v")
+    gp = _dev(g_il, (torch.int16, torch.bfloat16, torch.uint16), n * W, "g_il")
+    _check(lib().scape_dense_step_interleaved(ctx.handle, xp, mp, vp, gp, _stream(stream)))
+
+
+def interleaved_view(t, W: int):
+    """Worker i's elements of a worker-interleaved array `t` (n_pad*W) as a
+    strided (n_pad/64, 64) view; .reshape(-1) copies them out flat."""
+    return t.view(-1, W, 64)
+
+
 def scape_mask_build(ctx: Context, mtilde, out: Mask, num_shards: int = 0, shard: int = -1, stream=None) -> None:
     import torch
     mp = _dev(mtilde, torch.float32, ctx.layout.n_pad, "mtilde")
-    o = out._c()
+    o = out._c(ctx.layout, need_index=num_shards <= 0 or shard < 0)
     _check(lib().scape_mask_build(ctx.handle, mp, num_shards, shard, ctypes.byref(o), _stream(stream)))
 
 
@@ -338,7 +394,7 @@ def scape_mask_union_add(ctx: Context, mtilde, acc_bits, stream=None) -> None:
 
 
 def scape_mask_index(ctx: Context, mask: Mask, stream=None) -> None:
-    c = mask._c()
+    c = mask._c(ctx.layout)
     _check(lib().scape_mask_index(ctx.handle, ctypes.byref(c), _stream(stream)))
 
 

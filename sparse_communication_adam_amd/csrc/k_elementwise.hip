@@ -62,24 +62,19 @@ constexpr int kEfWaves = kEfBlock / 64;
 #endif
 constexpr bool kEfXcd = SCAPE_EF_XCD != 0;
 
-// Consecutive words per wave: a one-shot wave must keep enough bytes in
-// flight.  Measured on the 1.75B shape: at W = 1 (640 bytes per word) the pass
-// took 7.0-7.4 ms with one word per wave, 5.2 with four and 5.0 with eight; at
-// W = 2, 9.4-9.7 against 7.5-8.1 with four; at W = 4 (1.8 KB per word) one,
-// two and four words were within the run-to-run spread (13.1-13.5 ms).  At
-// larger W one word already holds enough.
+// Consecutive words per wave.  Measured on the 1.75B shape in both
+// residual/gradient layouts: at W = 4 one word per wave took 15.3 ms (one
+// array per worker) and 14.3 ms (worker-interleaved) where two took 15.4 and
+// 14.7 and four 15.5 and 15.1; at W = 8 (0.35B shape) one word 6.04 / 5.67 ms
+// against 6.08 / 5.81 with two; at W = 1 (640 bytes per word) two words
+// 4.94 ms against 5.14 with eight.  At W = 32 one and two words were within
+// 1% of each other.
 #ifndef SCAPE_EF_W1
-#define SCAPE_EF_W1 8
-#endif
-#ifndef SCAPE_EF_W2
-#define SCAPE_EF_W2 4
-#endif
-#ifndef SCAPE_EF_W4
-#define SCAPE_EF_W4 4
+#define SCAPE_EF_W1 2
 #endif
 template <int WT>
 constexpr uint32_t ef_words() {
-    return WT == 1 ? SCAPE_EF_W1 : WT == 2 ? SCAPE_EF_W2 : (WT == 3 || WT == 4) ? SCAPE_EF_W4 : 1;
+    return WT == 1 ? SCAPE_EF_W1 : 1;
 }
 
 template <int WT, bool K32>
@@ -105,20 +100,21 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
     uint16_t gv[kWords][WMAX];
 #pragma unroll
     for (uint32_t e = 0; e < kWords; ++e) {
-        const size_t j = (size_t)min(w0 + e, n_words - 1u) * 64u + lane;
+        const size_t wc = min(w0 + e, n_words - 1u);
+        const size_t j = wc * 64u + lane, jw = wc * wp.ws + lane;
         mo[e] = stream_load(&m[j]);
 #pragma unroll
         for (int i = 0; i < WMAX; ++i) {
             if (i >= W) break;
-            rv[e][i] = stream_load(&wp.r[i][j]);
-            gv[e][i] = stream_load(&wp.g[i][j]);
+            rv[e][i] = stream_load(&wp.r[i][jw]);
+            gv[e][i] = stream_load(&wp.g[i][jw]);
         }
     }
 #pragma unroll
     for (uint32_t e = 0; e < kWords; ++e) {
         const uint32_t w = w0 + e;
         if (w >= n_words) break;
-        const size_t j = (size_t)w * 64u + lane;
+        const size_t j = (size_t)w * 64u + lane, jw = (size_t)w * wp.ws + lane;
         const uint32_t info = word_info[w];
         const uint64_t word = cur_bits[w];
         const uint32_t pre = cur_prefix[w];
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
             const float a = rv[e][i] + bf16_bits_to_f32(gv[e][i]);
             const float mt = bm + sc.c1 * a;
             if (i == owner) kk = magnitude_key(mt);
-            wp.r[i][j] = msk ? 0.0f : a;
+            wp.r[i][jw] = msk ? 0.0f : a;
             if (msk) wp.b[i][rank] = mt;
         }
         // the selection reads the top 16 bits; candidates get their full key
@@ -207,13 +203,14 @@ __global__ __launch_bounds__(kBlock) void k_dense_adams(const uint16_t* __restri
     uint16_t gv[kDaWords][WMAX];
 #pragma unroll
     for (uint32_t e = 0; e < kDaWords; ++e) {
-        const size_t j = (size_t)min(w0 + e, n_words - 1u) * 64u + lane;
+        const size_t wc = min(w0 + e, n_words - 1u);
+        const size_t j = wc * 64u + lane, jw = wc * wp.ws + lane;
         mo[e] = stream_load(&m[j]);
         xo[e] = stream_load(&x[j]);
 #pragma unroll
         for (int i = 0; i < WMAX; ++i) {
             if (i >= W) break;
-            gv[e][i] = stream_load(&wp.g[i][j]);
+            gv[e][i] = stream_load(&wp.g[i][jw]);
         }
     }
 #pragma unroll

@@ -336,36 +336,39 @@ __device__ __forceinline__ void candidate_keys(const KeySource& ks, const LayerD
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) kk[u] = ks.key32[jj[u]];
     } else {
+        // first the mask word, prefix and owner's residual of each record;
+        // then one load per record from the array its mask bit selects: the
+        // owner's sparse buffer on the current mask, m off it.  m is never
+        // read at a masked position, where the update pass, running beside
+        // the selection, writes it.
         const float* r = ks.r[L.owner];
+        const float* b = ks.b[L.owner];
         uint64_t word[kFetch];
         uint32_t pre[kFetch];
-        float rv[kFetch], mv[kFetch];
+        float rv[kFetch];
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) {
             word[u] = ks.cur_bits[jj[u] >> 6];
             pre[u] = ks.cur_prefix[jj[u] >> 6];
-            rv[u] = r[jj[u]];
-            mv[u] = ks.m[jj[u]];
+            rv[u] = r[(size_t)(jj[u] >> 6) * ks.ws + (jj[u] & 63u)];
         }
         bool on[kFetch];
-        float bv[kFetch] = {};
-        uint32_t rk[kFetch];
+        const float* src[kFetch];
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) {
             const uint32_t bit = jj[u] & 63u;
             const uint32_t rank = pre[u] + (uint32_t)__popcll(word[u] & ((1ull << bit) - 1ull));
+            // with no buffer (k_cap == 0) no position counts as masked
             on[u] = ((word[u] >> bit) & 1ull) && rank < ks.k_cap;
-            rk[u] = on[u] ? rank : 0u;
+            src[u] = on[u] ? b + rank : ks.m + jj[u];
         }
-        if (ks.k_cap) {  // uniform: with no buffer there is no mask to read from
-            const float* b = ks.b[L.owner];
+        float val[kFetch];
 #pragma unroll
-            for (int u = 0; u < kFetch; ++u) bv[u] = b[rk[u]];
-        }
+        for (int u = 0; u < kFetch; ++u) val[u] = *src[u];
 #pragma unroll
         for (int u = 0; u < kFetch; ++u) {
-            const float bm = ks.beta1 * mv[u];
-            kk[u] = on[u] ? magnitude_key(bv[u]) : magnitude_key(bm + ks.c1 * rv[u]);
+            const float bm = ks.beta1 * val[u];
+            kk[u] = on[u] ? magnitude_key(val[u]) : magnitude_key(bm + ks.c1 * rv[u]);
         }
     }
 #pragma unroll

@@ -373,7 +373,7 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
                       "offload copy in");
         SCAPE_HIP(hipEventRecord(c->ev_in[b], c->s_in[b]), "offload event");
         SCAPE_HIP(hipStreamWaitEvent(s, c->ev_in[b], 0), "offload wait");
-        WorkerPtrs cp = wp;
+        WorkerPtrs cp = wp;  // one array per worker (word stride 64)
         for (int i = 0; i < W; ++i) {
             cp.r[i] = stage + (size_t)i * slot_elems;
             cp.g[i] = wp.g[i] + j0;
@@ -423,9 +423,17 @@ int ensure_offload(scape_ctx* c) {
     return SCAPE_OK;
 }
 
+// Where the W residuals and gradients are: one device array per worker, one
+// pinned host array per worker (residuals; the offloaded step), or one device
+// array each holding the W workers' 64 values of every word in turn (the
+// worker-interleaved layout: r[0] and g[0] are its base pointers).
+enum class WorkerLayout { kSeparate, kHostResiduals, kInterleaved };
+
 int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
                 const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
-                void* stream, bool r_on_host) {
+                void* stream, WorkerLayout wl) {
+    const bool r_on_host = wl == WorkerLayout::kHostResiduals;
+    const bool il = wl == WorkerLayout::kInterleaved;
     if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
     if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
     if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
@@ -433,9 +441,11 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     if (!r || !g || !sparse_bufs) return fail(SCAPE_ERR_INVALID_ARG, "r, g and sparse_bufs must not be NULL");
     const int W = ctx->cfg.workers;
     for (int i = 0; i < W; ++i) {
-        if (!r[i] || !g[i]) return fail(SCAPE_ERR_INVALID_ARG, "r[%d] or g[%d] is NULL", i, i);
-        if (!aligned(r[i], 16) || !aligned(g[i], 16))
-            return fail(SCAPE_ERR_ALIGN, "r[%d] and g[%d] must be 16-byte aligned", i, i);
+        if (!il || i == 0) {
+            if (!r[i] || !g[i]) return fail(SCAPE_ERR_INVALID_ARG, "r[%d] or g[%d] is NULL", i, i);
+            if (!aligned(r[i], 16) || !aligned(g[i], 16))
+                return fail(SCAPE_ERR_ALIGN, "r[%d] and g[%d] must be 16-byte aligned", i, i);
+        }
         if (ctx->lay.k_total > 0) {
             if (!sparse_bufs[i]) return fail(SCAPE_ERR_INVALID_ARG, "sparse_bufs[%d] is NULL", i);
             if (!aligned(sparse_bufs[i], 4)) return fail(SCAPE_ERR_ALIGN, "sparse_bufs[%d] must be 4-byte aligned", i);
@@ -451,9 +461,10 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
 
     hipStream_t s = (hipStream_t)stream;
     WorkerPtrs wp{};
+    wp.ws = il ? 64u * (uint32_t)W : 64u;
     for (int i = 0; i < W; ++i) {
-        wp.r[i] = r_on_host ? nullptr : r[i];
-        wp.g[i] = g[i];
+        wp.r[i] = r_on_host ? nullptr : il ? r[0] + 64 * i : r[i];
+        wp.g[i] = il ? g[0] + 64 * i : g[i];
         wp.b[i] = ctx->lay.k_total > 0 ? sparse_bufs[i] : nullptr;
     }
     StepScalars sc;
@@ -473,8 +484,9 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     KeySource ks{};
     ks.key32 = key32;
     ks.m = m;
+    ks.ws = wp.ws;
     for (int i = 0; i < W; ++i) {
-        ks.r[i] = r_on_host ? nullptr : r[i];
+        ks.r[i] = wp.r[i];
         ks.b[i] = wp.b[i];
     }
     ks.cur_bits = cur->bits;
@@ -528,6 +540,37 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
         for (int b = 0; b < kOffloadSlots; ++b) SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[b], 0), "offload wait");
     }
     prof_mark(ctx, slot, 4, s);
+    return SCAPE_OK;
+}
+
+int dense_common(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream, bool il) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
+    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
+        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    if (!g) return fail(SCAPE_ERR_INVALID_ARG, "g must not be NULL");
+    const int W = ctx->cfg.workers;
+    WorkerPtrs wp{};
+    wp.ws = il ? 64u * (uint32_t)W : 64u;
+    for (int i = 0; i < W; ++i) {
+        const uint16_t* gi = il ? g[0] : g[i];
+        if (!gi) return fail(SCAPE_ERR_INVALID_ARG, "g[%d] is NULL", il ? 0 : i);
+        if (!aligned(gi, 16)) return fail(SCAPE_ERR_ALIGN, "g[%d] must be 16-byte aligned", il ? 0 : i);
+        wp.g[i] = il ? gi + 64 * i : gi;
+    }
+    int rc;
+    if ((rc = check_device(ctx))) return rc;
+    StepScalars sc;
+    sc.beta1 = ctx->cfg.beta1;
+    sc.beta2 = ctx->cfg.beta2;
+    sc.c1 = 1.0f - ctx->cfg.beta1;
+    sc.c2 = 1.0f - ctx->cfg.beta2;
+    sc.lr = ctx->cfg.lr;
+    sc.eps = ctx->cfg.eps;
+    sc.wd = ctx->cfg.weight_decay;
+    sc.W = W;
+    SCAPE_HIP(launch_dense_adams((hipStream_t)stream, ctx->d_word_info, ctx->n_words, wp, sc, x, m, v),
+              "dense_adams");
     return SCAPE_OK;
 }
 
@@ -706,42 +749,30 @@ int scape_destroy(scape_ctx* ctx) {
 int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
                const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
                void* stream) {
-    return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, false);
+    return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kSeparate);
+}
+
+int scape_step_interleaved(scape_ctx* ctx, float* x, float* m, float* v, float* r_il, const uint16_t* g_il,
+                           const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
+                           void* stream) {
+    float* r[1] = {r_il};
+    const uint16_t* g[1] = {g_il};
+    return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kInterleaved);
 }
 
 int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* const* r_host, const uint16_t* const* g,
                        const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
                        void* stream) {
-    return step_common(ctx, x, m, v, r_host, g, cur, next, sparse_bufs, key_out, stream, true);
+    return step_common(ctx, x, m, v, r_host, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kHostResiduals);
 }
 
 int scape_dense_step(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* const* g, void* stream) {
-    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
-    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
-    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
-        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
-    if (!g) return fail(SCAPE_ERR_INVALID_ARG, "g must not be NULL");
-    const int W = ctx->cfg.workers;
-    WorkerPtrs wp{};
-    for (int i = 0; i < W; ++i) {
-        if (!g[i]) return fail(SCAPE_ERR_INVALID_ARG, "g[%d] is NULL", i);
-        if (!aligned(g[i], 16)) return fail(SCAPE_ERR_ALIGN, "g[%d] must be 16-byte aligned", i);
-        wp.g[i] = g[i];
-    }
-    int rc;
-    if ((rc = check_device(ctx))) return rc;
-    StepScalars sc;
-    sc.beta1 = ctx->cfg.beta1;
-    sc.beta2 = ctx->cfg.beta2;
-    sc.c1 = 1.0f - ctx->cfg.beta1;
-    sc.c2 = 1.0f - ctx->cfg.beta2;
-    sc.lr = ctx->cfg.lr;
-    sc.eps = ctx->cfg.eps;
-    sc.wd = ctx->cfg.weight_decay;
-    sc.W = W;
-    SCAPE_HIP(launch_dense_adams((hipStream_t)stream, ctx->d_word_info, ctx->n_words, wp, sc, x, m, v),
-              "dense_adams");
-    return SCAPE_OK;
+    return dense_common(ctx, x, m, v, g, stream, false);
+}
+
+int scape_dense_step_interleaved(scape_ctx* ctx, float* x, float* m, float* v, const uint16_t* g_il, void* stream) {
+    const uint16_t* g[1] = {g_il};
+    return dense_common(ctx, x, m, v, g, stream, true);
 }
 
 int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, int32_t shard, const scape_mask* out,

@@ -97,10 +97,15 @@ struct VblockDesc {
     int32_t layer;
 };
 
+// Worker i's residual and gradient of element j = 64 w + l (l < 64) are
+// r[i][w * ws + l] and g[i][w * ws + l]: ws = 64 for one array per worker,
+// ws = 64 W for the worker-interleaved layout, where each 64-element word
+// holds the W workers' 64 values one after another (r[i] = base + 64 i).
 struct WorkerPtrs {
     float* r[SCAPE_MAX_WORKERS];
     const uint16_t* g[SCAPE_MAX_WORKERS];
     float* b[SCAPE_MAX_WORKERS];
+    uint32_t ws;
 };
 
 // Where the selection finds the full 31-bit key of a candidate (the stored
@@ -115,7 +120,8 @@ struct KeySource {
     const float* mtilde;
     const uint32_t* key32;
     const float* m;
-    const float* r[SCAPE_MAX_WORKERS];
+    const float* r[SCAPE_MAX_WORKERS];  // word stride ws, as in WorkerPtrs
+    uint32_t ws;
     const float* b[SCAPE_MAX_WORKERS];
     const uint64_t* cur_bits;
     const uint32_t* cur_prefix;

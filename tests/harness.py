@@ -95,6 +95,7 @@ class GpuRun:
     grad_override: Optional[object] = None  # callable(step, worker, tensor) -> np.uint16 array
     offload: bool = False  # residuals in pinned host memory (scape_step_offload)
     key_out: bool = True  # ask the step for the full statistic keys (else candidates' keys are recomputed)
+    interleaved: bool = False  # residuals and gradients in the worker-interleaved layout
     state: object = None
     grads: List[object] = field(default_factory=list)
 
@@ -102,12 +103,13 @@ class GpuRun:
         import torch
         from sparse_communication_adam_amd.state import ScapeState
         cfg = scape_config(self.wl, self.keep, self.W)
-        self.state = ScapeState(cfg, offload=self.offload)
+        self.state = ScapeState(cfg, offload=self.offload, interleaved=self.interleaved)
         self.layout = self.state.layout
         n = self.layout.n_pad
         if not self.x_zero:
             synth.params_flat_gpu(self.wl, self.layout.layer_offset, self.state.x)
         self.grads = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(cfg.workers)]
+        self.g_il = torch.zeros(n * cfg.workers, dtype=torch.int16, device="cuda") if self.interleaved else None
         if self.init_mask_all:
             import sparse_communication_adam_amd as sc
             pred = torch.zeros(n, dtype=torch.uint8, device="cuda")
@@ -128,10 +130,27 @@ class GpuRun:
                 g.copy_(torch.from_numpy(host.view(np.int16)))
             else:
                 synth.grads_flat_gpu(self.wl, self.layout.layer_offset, g, step, i)
+        if self.interleaved:
+            import sparse_communication_adam_amd as sc
+            view = sc.interleaved_view(self.g_il, len(self.grads))
+            for i, g in enumerate(self.grads):
+                view[:, i, :].copy_(g.view(-1, 64))
 
     def step(self, t: int) -> None:
         self.gen(t)
-        self.state.step(self.grads, key_out=self.key_out)
+        self.state.step(self.g_il if self.interleaved else self.grads, key_out=self.key_out)
+
+
+def worker_slice(st, i: int, fs: slice):
+    """Elements fs (a slice starting on a 64-element word) of worker i's
+    residual, in either residual layout."""
+    if not st.interleaved:
+        return st.r[i][fs]
+    import sparse_communication_adam_amd as sc
+    a, b = fs.start, fs.stop
+    assert a % 64 == 0
+    v = sc.interleaved_view(st.r_il, st.cfg.workers)[a // 64:(b + 63) // 64, i, :]
+    return v.reshape(-1)[:b - a]
 
 
 def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int], step: int, W: int,
@@ -151,7 +170,7 @@ def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int]
 
 def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, keep=None, W=None,
                init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True,
-               offload=False, key_out=True) -> Dict[str, int]:
+               offload=False, key_out=True, interleaved=False) -> Dict[str, int]:
     """Run `steps` steps on the GPU (all layers) and the oracle (all layers, or
     the sampled ones) and compare every output of every step."""
     import torch
@@ -161,8 +180,8 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
     lay = full if sample is None else oracle.sub_layout(full, tensors)
     log(f"{wl.name}: W={W} L={full.L} n_pad={full.n_pad} k_total={full.k_total} steps={steps} "
         f"oracle layers={len(tensors)} ({lay.n_pad} elements){' residuals on the host' if offload else ''}"
-        f"{'' if key_out else ', candidate keys recomputed'}")
-    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out)
+        f"{'' if key_out else ', candidate keys recomputed'}{', worker-interleaved layout' if interleaved else ''}")
+    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total
     assert list(glay.layer_offset) == full.off.tolist() and list(glay.layer_k) == full.k.tolist()
@@ -218,7 +237,7 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
             check_float(f"{tag} m", to_np(st.m[fs]), ost.m[os_], stats)
             check_float(f"{tag} v", to_np(st.v[fs]), ost.v[os_], stats)
             for i in range(W):
-                check_float(f"{tag} r[{i}]", to_np(st.r[i][fs]), ost.r[i][os_], stats)
+                check_float(f"{tag} r[{i}]", to_np(worker_slice(st, i, fs)), ost.r[i][os_], stats)
             if check_buffers and out.count:
                 # this layer's segment of every worker's sparse buffer
                 oa = np.searchsorted(o_pos, lay.off[a])
@@ -241,13 +260,14 @@ def release(run) -> None:
     run.state.destroy()
     run.state = None
     run.grads = []
+    run.g_il = None
     gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
 
 def run_dense_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, W=None,
-                     weight_decay=None) -> Dict[str, int]:
+                     weight_decay=None, interleaved=False) -> Dict[str, int]:
     """The dense AdamS step through the C ABI against the oracle's, on every
     layer or on the sampled ones, for every step: x, m and v within the parity
     bar (bit-exact expected), padding untouched."""
@@ -272,6 +292,7 @@ def run_dense_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[i
     v = torch.zeros_like(x)
     x_pad0 = x.clone()
     grads = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(W)]
+    g_il = torch.zeros(n * W, dtype=torch.int16, device="cuda") if interleaved else None
     ox = synth.params_flat(wl, lay.off, lay.n_pad, tensors)
     om, ov = np.zeros(lay.n_pad, np.float32), np.zeros(lay.n_pad, np.float32)
     hp = hyper(wl)
@@ -279,7 +300,13 @@ def run_dense_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[i
     for t in range(1, steps + 1):
         for i, g in enumerate(grads):
             synth.grads_flat_gpu(wl, offs, g, t, i)
-        sc.scape_dense_step(ctx, x, m, v, grads)
+        if interleaved:
+            view = sc.interleaved_view(g_il, W)
+            for i, g in enumerate(grads):
+                view[:, i, :].copy_(g.view(-1, 64))
+            sc.scape_dense_step_interleaved(ctx, x, m, v, g_il)
+        else:
+            sc.scape_dense_step(ctx, x, m, v, grads)
         oracle.dense_step(lay, hp, ox, om, ov, oracle_inputs(wl, lay, tensors, t, W))
         torch.cuda.synchronize()
         for a, l in enumerate(tensors):
@@ -295,7 +322,7 @@ def run_dense_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[i
         log(f"dense step {t}: sampled ok (float values so far {stats['float_values']}, "
             f"not bit-exact {stats['float_not_bitexact']})")
     ctx.destroy()
-    del x, m, v, grads, x_pad0
+    del x, m, v, grads, x_pad0, g_il
     import gc
     gc.collect()
     torch.cuda.synchronize()

@@ -156,3 +156,26 @@ def test_binding_requires_pinned_host_residuals(sc):
         _host(torch.zeros(16, dtype=torch.float64), torch.float32, 16, "r_host[0]")
     with pytest.raises(TypeError):
         _host(np.zeros(16, np.float32), torch.float32, 16, "r_host[0]")
+
+
+def test_binding_checks_mask_lengths_against_the_layout(sc):
+    """A mask array shorter than the layout needs is refused before anything
+    reaches the library: bits n_pad/64 words, idx k_total, block_prefix
+    n_pad/64 + 1 (length is checked before the device, so this runs on the
+    host)."""
+    import torch
+    lay = sc.scape_layout(_cfg(sc, synth.ragged()))
+    nw, k = lay.n_words, lay.k_total
+    ok = dict(bits=torch.zeros(nw, dtype=torch.int64), idx=torch.zeros(k, dtype=torch.int32),
+              block_prefix=torch.zeros(nw + 1, dtype=torch.int32))
+    for name, short in [("bits", torch.zeros(nw - 1, dtype=torch.int64)), ("idx", torch.zeros(k - 1, dtype=torch.int32)),
+                        ("block_prefix", torch.zeros(nw, dtype=torch.int32))]:
+        m = sc.Mask(**{**ok, name: short})
+        with pytest.raises(ValueError, match=f"mask.{name} has"):
+            m._c(lay)
+    # a shard build needs only the bits
+    with pytest.raises(ValueError, match="mask.bits has"):
+        sc.Mask(torch.zeros(nw - 1, dtype=torch.int64), None, None)._c(lay, need_index=False)
+    # right lengths: the next check is the device (these are host tensors)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        sc.Mask(**ok)._c(lay)

@@ -69,3 +69,15 @@ def test_dense_step_maximum_size():
     oracle."""
     from test_gpu_parity import max_size_workload
     _assert_bitexact(run_dense_parity(max_size_workload(), 2, sample=[31]))
+
+
+@pytest.mark.parametrize("W", [1, 3, 4, 8, 32])
+def test_dense_step_interleaved_gradients(W):
+    """scape_dense_step_interleaved: the W gradients in one worker-interleaved
+    array (word stride 64 W)."""
+    _assert_bitexact(run_dense_parity(synth.ragged(), 3, W=W, interleaved=True))
+
+
+def test_dense_step_interleaved_full_size_sampled_layers():
+    wl = synth.WORKLOADS["llama-1.75b"]
+    _assert_bitexact(run_dense_parity(wl, 2, sample=FULL_SAMPLES["llama-1.75b"], interleaved=True))

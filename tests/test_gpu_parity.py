@@ -5,6 +5,7 @@ bit-exact; fp32 state within rel 1e-5 / abs 1e-7 of the oracle (the harness
 also counts positions that are not bit-exact; the fp32 operation order is the
 same on both sides, so the expected count is zero and the tests assert it).
 """
+import dataclasses
 import gc
 
 import numpy as np
@@ -374,6 +375,18 @@ def test_step_parity_ragged_layout_worker_counts(W):
     _assert_bitexact(run_parity(synth.ragged(), 4, W=W))
 
 
+@pytest.mark.parametrize("W", [3, 5])
+@pytest.mark.parametrize("key_out", [True, False])
+def test_step_parity_weight_decay(W, key_out):
+    """Decoupled weight decay (wd = 0.1) on the ragged layout, at worker counts
+    that are not powers of two (so the mean's division by W rounds): from an
+    empty first mask and from a full one, so the decay term is applied at
+    masked positions from the first step; off the mask x must not change."""
+    wl = dataclasses.replace(synth.ragged(), weight_decay=0.1)
+    _assert_bitexact(run_parity(wl, 4, W=W, key_out=key_out))
+    _assert_bitexact(run_parity(wl, 3, W=W, key_out=key_out, keep=(1, 1), init_mask_all=True))
+
+
 def test_step_keep_all_is_dense_from_full_mask():
     wl = synth.ragged()
     _assert_bitexact(run_parity(wl, 4, keep=(1, 1), init_mask_all=True))
@@ -452,6 +465,90 @@ FULL_SAMPLES = {
 def test_step_parity_full_size_sampled_layers(name):
     wl = synth.WORKLOADS[name]
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name]))
+
+
+# The largest tensor of each workload (and the 1.75B shape's fused gate_up),
+# compared against the oracle at full size: their selections keep 131,072 to
+# 655,360 positions, and their tie positions reach past 2^25 inside the layer.
+FULL_LARGEST = {
+    "gpt-345m": [0],              # word_emb, 51.5M elements, keep 1/10
+    "llama-0.55b": [0, 98],       # emb and lm_head, 49.2M each
+    "llama-1.75b": [0, 5, 194],   # emb, l0.gate_up, lm_head (65.5M, 22.5M, 65.5M)
+    "adversarial-ties": [0],      # emb, 131M elements, quantised to 16 levels, W = 32
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(FULL_LARGEST))
+def test_step_parity_full_size_largest_layers(name):
+    """Three full-size steps in the configuration bench.py times
+    (worker-interleaved residuals and gradients, candidates' keys
+    recomputed), every output of the largest layers against the oracle."""
+    wl = synth.WORKLOADS[name]
+    _assert_bitexact(run_parity(wl, 3, sample=FULL_LARGEST[name], key_out=False, interleaved=True))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("keep", [(1, 2), (1, 100)])
+def test_mask_build_largest_layer_sixteen_levels(keep):
+    """One layer of 67,108,927 elements (2^26 + 63, a ragged last word) holding
+    16 levels: at keep 1/2 the threshold level is tied over millions of
+    positions spread to about 2^25, so every position digit is decided at
+    large in-layer positions; at 1/100 the cut lies inside the top level."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(keep[1])
+    sizes = [(1 << 26) + 63, 1000]
+    ctx = _ctx(sizes, W=2, keep=keep)
+    lay = oracle.layout(sizes, keep[0], keep[1], 2)
+    mt = (rng.integers(-8, 8, lay.n_pad) * 2.0 ** -12).astype(np.float32)
+    log(f"mask build: layer of {sizes[0]} elements, 16 levels, keep {keep}")
+    out = sc.alloc_mask(ctx.layout)
+    sc.scape_mask_build(ctx, torch.from_numpy(mt).cuda(), out)
+    exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+    got = u64(out.bits)
+    if not np.array_equal(got, exp):
+        d = np.flatnonzero(got != exp)
+        raise AssertionError(f"{d.size} mask words differ, first word {d[0]}")
+    idx, pre, cnt = oracle.mask_index(exp)
+    assert cnt == lay.k_total
+    assert np.array_equal(u32(out.idx)[:cnt], idx) and np.array_equal(u32(out.block_prefix), pre)
+    ctx.destroy()
+
+
+# The worker-interleaved layout (scape_step_interleaved): one residual array
+# and one gradient array, each 64-element word holding the W workers' values
+# in turn.  bench.py times the step in this layout.
+
+
+@pytest.mark.parametrize("name", ["single-1024x1024", "gpt-345m", "llama-0.55b", "llama-1.75b", "adversarial-ties"])
+def test_step_interleaved_oracle_sized(name):
+    wl = synth.WORKLOADS[name]
+    small = wl if name == "single-1024x1024" else synth.reduced(wl)
+    _assert_bitexact(run_parity(small, wl.steps, key_out=False, interleaved=True))
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 16, 32])
+def test_step_interleaved_ragged_worker_counts(W):
+    """Every worker count with its own kernel instance, and 3 and 5 without:
+    the word stride of the interleaved arrays is 64 W."""
+    _assert_bitexact(run_parity(synth.ragged(), 4, W=W, key_out=False, interleaved=True))
+
+
+def test_step_interleaved_edge_cases():
+    wl = synth.ragged()
+    _assert_bitexact(run_parity(wl, 3, key_out=True, interleaved=True))
+    _assert_bitexact(run_parity(wl, 3, keep=(1, 1), init_mask_all=True, key_out=False, interleaved=True))
+    _assert_bitexact(run_parity(dataclasses.replace(wl, weight_decay=0.1), 3, W=5, key_out=False, interleaved=True))
+    _assert_bitexact(run_parity(wl, 4, grad_override=_special_grads(wl), key_out=False, interleaved=True))
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_step_interleaved_full_size_sampled_layers(name):
+    """Full size, in the configuration bench.py times: worker-interleaved
+    residuals and gradients, candidates' keys recomputed."""
+    wl = synth.WORKLOADS[name]
+    _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name], key_out=False, interleaved=True))
 
 
 def max_size_workload() -> "synth.Workload":
