@@ -54,7 +54,7 @@ CPU_SAMPLE = {
     "single-1024x1024": [0],
     "gpt-345m": list(range(2, 2 + 12 * 6)),        # six blocks, 75.6M params, W = 8
     "llama-0.55b": list(range(1, 1 + 6 * 3)),      # three blocks, 84.9M params, W = 8
-    "llama-1.75b": list(range(1, 1 + 6 * 3)),      # three blocks, 151.8M params, W = 4
+    "llama-1.75b": list(range(1, 1 + 6 * 8)),      # eight blocks, 404.8M params, W = 4
     "adversarial-ties": list(range(1, 1 + 17 * 4)),  # four blocks, 16.8M params, W = 32
 }
 
@@ -105,7 +105,20 @@ def counter_traffic(workload: str):
     return float(val.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, steps_needed: int = 2):
+    """The oracle (plain C, OpenMP over layers and positions, no parallel
+    floating-point sum) on a contiguous run of the workload's tensors, timing
+    the step after the first (which has a built mask)."""
     import numpy as np
     import oracle
     import synth
@@ -125,10 +138,35 @@ def cpu_baseline(wl, steps_needed: int = 2):
         log(f"cpu baseline step {t}: {times[-1]:.2f} s on {int(lay.sizes.sum())} params")
     n = int(lay.sizes.sum())
     names = [wl.tensors[t].name for t in tensors]
-    return {"value": n / times[-1], "unit": "params/s", "cores": 1, "kind": "oracle",
+    threads = oracle.threads()
+    return {"value": n / times[-1], "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(tensors)} tensors ({names[0]}..{names[-1]}, {n} params, W={wl.W}) of {wl.name}; "
-                      f"step {steps_needed} timed (mask built by step {steps_needed - 1}); single-threaded C oracle",
-            "seconds": times[-1]}
+                      f"step {steps_needed} timed (mask built by step {steps_needed - 1}); C oracle, OpenMP over "
+                      f"layers and positions with {threads} threads",
+            "seconds": times[-1], "threads": threads, "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def grad_set(wl, layer_offset, n_pad: int, step: int, interleaved: bool):
+    """One batch of the W workers' bf16 gradients (as int16), generated on
+    the GPU: a list of W flat tensors, or one worker-interleaved tensor of
+    n_pad*W elements (each 64-element word holding the W workers' values)."""
+    import torch
+    import synth
+    import sparse_communication_adam_amd as sc
+    W = wl.W
+    if not interleaved:
+        gs = [torch.zeros(n_pad, dtype=torch.int16, device="cuda") for _ in range(W)]
+        for i, g in enumerate(gs):
+            synth.grads_flat_gpu(wl, layer_offset, g, step, i)
+        return gs
+    g_il = torch.zeros(n_pad * W, dtype=torch.int16, device="cuda")
+    view = sc.interleaved_view(g_il, W)
+    tmp = torch.zeros(n_pad, dtype=torch.int16, device="cuda")
+    for i in range(W):
+        synth.grads_flat_gpu(wl, layer_offset, tmp, step, i)
+        view[:, i, :].copy_(tmp.view(-1, 64))
+    del tmp
+    return g_il
 
 
 def dense_alg_bytes(N: int, W: int) -> float:
@@ -137,7 +175,7 @@ def dense_alg_bytes(N: int, W: int) -> float:
     return N * (2 * W + 20)
 
 
-def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> dict:
+def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int, interleaved: bool) -> dict:
     import torch
     import synth
     import sparse_communication_adam_amd as sc
@@ -148,13 +186,14 @@ def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> 
     x = torch.zeros(n_pad, dtype=torch.float32, device="cuda")
     synth.params_flat_gpu(wl, layer_offset, x)
     m, v = torch.zeros_like(x), torch.zeros_like(x)
+    step = sc.scape_dense_step_interleaved if interleaved else sc.scape_dense_step
     for s in range(warmup):
-        sc.scape_dense_step(ctx, x, m, v, sets[s % len(sets)])
+        step(ctx, x, m, v, sets[s % len(sets)])
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for s in range(steps):
-        sc.scape_dense_step(ctx, x, m, v, sets[(warmup + s) % len(sets)])
+        step(ctx, x, m, v, sets[(warmup + s) % len(sets)])
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
@@ -163,19 +202,21 @@ def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int) -> 
     torch.cuda.empty_cache()
     N = wl.numel
     gbps = dense_alg_bytes(N, wl.W) / (ms * 1e-3) / 1e9
-    return {"kernel": "scape_k_dense_adams", "ms_per_step": ms, "params_per_s": N / (ms * 1e-3),
+    return {"kernel": "scape_k_dense_adams", "gradient_layout": "worker-interleaved" if interleaved else "per worker",
+            "ms_per_step": ms, "params_per_s": N / (ms * 1e-3),
             "alg_bytes_per_step": dense_alg_bytes(N, wl.W), "alg_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
-def offload_step(cfg, wl, sets, steps: int, warmup: int) -> dict:
+def offload_step(cfg, wl, steps: int, warmup: int) -> dict:
     """The step with the residuals in pinned host memory: W*N*4 bytes copied
-    in and out over PCIe per step."""
+    in and out over PCIe per step (one gradient batch, per-worker arrays)."""
     import torch
     import synth
     from sparse_communication_adam_amd.state import ScapeState
     state = ScapeState(cfg, offload=True)
     lay = state.layout
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
+    sets = [grad_set(wl, lay.layer_offset, lay.n_pad, 1, False)]
     torch.cuda.synchronize()
     for s in range(warmup):
         state.step(sets[s % len(sets)], key_out=False)
@@ -186,7 +227,7 @@ def offload_step(cfg, wl, sets, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     state.destroy()
-    del state
+    del state, sets
     torch.cuda.empty_cache()
     pcie = 2 * wl.W * lay.n_pad * 4
     return {"ms_per_step": ms, "params_per_s": wl.numel / (ms * 1e-3), "residuals_on_host_GB": pcie / 2 / 1e9,
@@ -232,7 +273,7 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
             "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
 
 
-def other_workload(name: str, steps: int, warmup: int, workers: int = 0) -> dict:
+def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interleaved: bool = True) -> dict:
     """The fused step on another workload shape (with `workers` workers instead
     of the workload's own W when given): state and two gradient batches
     resident, `warmup` untimed steps, then `steps` timed ones."""
@@ -247,15 +288,10 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0) -> dict
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
-    state = ScapeState(cfg)
+    state = ScapeState(cfg, interleaved=interleaved)
     lay = state.layout
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
-    sets = []
-    for s in range(2):
-        gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
-        for i, g in enumerate(gs):
-            synth.grads_flat_gpu(wl, lay.layer_offset, g, s + 1, i)
-        sets.append(gs)
+    sets = [grad_set(wl, lay.layer_offset, lay.n_pad, s + 1, interleaved) for s in range(2)]
     for s in range(warmup):
         state.step(sets[s % 2], key_out=False)
     torch.cuda.synchronize()
@@ -274,7 +310,8 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0) -> dict
     torch.cuda.empty_cache()
     dense_b, step_b = alg_bytes(N, wl.W, ksum)
     ef_ms = phase_ms["ef_compact"] / nrec
-    return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}", "steps": steps, "warmup": warmup,
+    return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}",
+            "layout": "worker-interleaved" if interleaved else "per worker", "steps": steps, "warmup": warmup,
             "ms_per_step": ms, "params_per_s": N / (ms * 1e-3), "worker_elements_per_s": wl.W * N / (ms * 1e-3),
             "step_alg_GBps": step_b / (ms * 1e-3) / 1e9, "step_hbm_frac": step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "dense_pass_ms": ef_ms, "dense_pass_GBps": dense_b / (ef_ms * 1e-3) / 1e9,
@@ -468,6 +505,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(CPU_SAMPLE))
     ap.add_argument("--grad-sets", type=int, default=2, help="distinct gradient batches cycled over the steps")
+    ap.add_argument("--layout", choices=("interleaved", "separate"), default="interleaved",
+                    help="residuals and gradients worker-interleaved (scape_step_interleaved) or one array per "
+                         "worker (scape_step)")
+    ap.add_argument("--no-other-layout", action="store_true",
+                    help="skip timing the main workload in the other residual/gradient layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense AdamS comparison step")
     ap.add_argument("--no-fill-in", action="store_true", help="skip the fill-in union measurement")
@@ -503,17 +545,15 @@ def main() -> int:
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
-    log(f"workload {wl.name}: {len(wl.tensors)} tensors, N={wl.numel}, W={wl.W}, keep={wl.keep_num}/{wl.keep_den}")
-    state = ScapeState(cfg)
+    il = args.layout == "interleaved"
+    log(f"workload {wl.name}: {len(wl.tensors)} tensors, N={wl.numel}, W={wl.W}, keep={wl.keep_num}/{wl.keep_den}, "
+        f"{'worker-interleaved' if il else 'per-worker'} residuals and gradients")
+    state = ScapeState(cfg, interleaved=il)
     lay = state.layout
     N, W, ksum = wl.numel, wl.W, lay.k_total
+    workspace = sc.scape_workspace_bytes(state.ctx)
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
-    sets = []
-    for s in range(args.grad_sets):
-        gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(W)]
-        for i, g in enumerate(gs):
-            synth.grads_flat_gpu(wl, lay.layer_offset, g, s + 1, i)
-        sets.append(gs)
+    sets = [grad_set(wl, lay.layer_offset, lay.n_pad, s + 1, il) for s in range(args.grad_sets)]
     torch.cuda.synchronize()
     log(f"state and {args.grad_sets} gradient batches resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
 
@@ -558,15 +598,20 @@ def main() -> int:
     torch.cuda.empty_cache()
     dense = None
     if not args.no_dense:
-        dense = dense_adams(wl, offsets, n_pad, sets, args.steps, args.warmup)
+        dense = dense_adams(wl, offsets, n_pad, sets, args.steps, args.warmup, il)
         dense["scape_step_over_dense"] = ms / dense["ms_per_step"]
         log(f"dense AdamS step: {dense['ms_per_step']:.3f} ms ({dense['alg_GBps']:.0f} GB/s algorithmic)")
-    offload = None
-    if not args.no_offload:
-        offload = offload_step(cfg, wl, sets, 3, 2)
-        log(f"offloaded-residual step: {offload['ms_per_step']:.1f} ms ({offload['pcie_GBps']:.1f} GB/s over PCIe)")
     del sets
     torch.cuda.empty_cache()
+    other_layout = None
+    if not args.no_other_layout:
+        other_layout = other_workload(wl.name, args.steps, args.warmup, interleaved=not il)
+        log(f"{wl.name} with {other_layout['layout']} residuals and gradients: {other_layout['ms_per_step']:.3f} ms/step, "
+            f"dense pass {other_layout['dense_pass_ms']:.3f} ms ({other_layout['dense_pass_GBps']:.0f} GB/s)")
+    offload = None
+    if not args.no_offload:
+        offload = offload_step(cfg, wl, 3, 2)
+        log(f"offloaded-residual step: {offload['ms_per_step']:.1f} ms ({offload['pcie_GBps']:.1f} GB/s over PCIe)")
     fill = None
     if not args.no_fill_in:
         fill = fill_in(wl, cfg, offsets, n_pad)
@@ -576,7 +621,7 @@ def main() -> int:
         for name in sorted(synth.WORKLOADS):
             if name == wl.name:
                 continue
-            others[name] = other_workload(name, 5, 2)
+            others[name] = other_workload(name, 5, 2, interleaved=il)
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
@@ -587,7 +632,7 @@ def main() -> int:
             f"{graphed['graph_ms_per_step']:.3f} ms")
     one_worker = None
     if not args.no_other_workloads:
-        one_worker = other_workload(wl.name, 5, 2, workers=1)
+        one_worker = other_workload(wl.name, 5, 2, workers=1, interleaved=il)
         log(f"one worker (W = 1) on {wl.name}: {one_worker['ms_per_step']:.3f} ms/step, dense pass "
             f"{one_worker['dense_pass_GBps']:.0f} GB/s")
     pu = None
@@ -611,7 +656,10 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "params": N, "tensors": len(wl.tensors), "workers": W,
                    "keep": f"{wl.keep_num}/{wl.keep_den}", "kept_total": ksum, "grad_dtype": "bf16",
-                   "gradient_batches": args.grad_sets},
+                   "gradient_batches": args.grad_sets,
+                   "layout": "worker-interleaved residuals and gradients" if il else "one residual and gradient "
+                             "array per worker"},
+        "context_workspace_bytes": workspace,
         "step_ms_median": step_ms[len(step_ms) // 2], "step_ms_min": step_ms[0],
         "worker_elements_per_s": W * N / (ms * 1e-3),
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
@@ -622,6 +670,8 @@ def main() -> int:
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
                      "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps},
     }
+    if other_layout is not None:
+        result["other_layout_step"] = other_layout
     if dense is not None:
         result["dense_adams"] = dense
     if fill is not None:

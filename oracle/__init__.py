@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-BUILD_CMD = ["gcc", "-O2", "-fPIC", "-shared", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math",
+BUILD_CMD = ["gcc", "-O2", "-fPIC", "-shared", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
              os.path.join(_HERE, "scape_oracle.c"), "-o", LIB_PATH + ".tmp", "-lm"]
 
 
@@ -45,6 +45,8 @@ def lib():
             build()
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = i32
         L.oracle_keep_count.argtypes = [i64, u32, u32]
         L.oracle_keep_count.restype = i64
         L.oracle_owner.argtypes = [i64, i64, i64, i32]
@@ -74,6 +76,11 @@ def lib():
         L.oracle_union_mask.restype = None
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops use (OMP_NUM_THREADS)."""
+    return int(lib().oracle_threads())
 
 
 def _p(a: np.ndarray) -> int:

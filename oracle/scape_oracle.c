@@ -44,6 +44,12 @@
  *                 and that average drives the same AdamS update as
  *                 R-normaliser, with no residual and no mask.
  *
+ * Threads: built with OpenMP, the loops run in parallel over layers (each
+ * layer's elements in order, its first compaction slot counted beforehand)
+ * and over positions of the sparse buffers.  Every iteration writes its own
+ * outputs and no floating-point sum is split across threads, so the results
+ * do not depend on the thread count.
+ *
  * Precision: every floating-point value is fp32, every operation rounds to
  * nearest even, and nothing is contracted into a fused multiply-add (the file
  * is compiled with -ffp-contract=off, no fast-math).  fp32 is the state
@@ -61,9 +67,13 @@
  * not fix: parity unpinned for that form beyond its algebraic special cases.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the parallel loops use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* Layout, kept counts, ownership                                           */
@@ -179,6 +189,8 @@ static uint32_t magnitude_key(float v) {
  * when shard >= 0; other words are left untouched. */
 void oracle_mask_from_keys(int32_t L, const int64_t* off, const int64_t* n, const int64_t* k,
                            const int32_t* owner, int32_t shard, const uint32_t* key, uint64_t* words) {
+    /* layers own disjoint words (each starts on a 64-element boundary) */
+#pragma omp parallel for schedule(dynamic, 1)
     for (int32_t l = 0; l < L; ++l) {
         if (shard >= 0 && owner[l] != shard) continue;
         uint8_t* sel = (uint8_t*)malloc((size_t)(n[l] > 0 ? n[l] : 1));
@@ -197,8 +209,9 @@ void oracle_mask_from_keys(int32_t L, const int64_t* off, const int64_t* n, cons
  * worker builds a mask for every layer, the union fills in as W grows. */
 void oracle_union_mask(int32_t L, const int64_t* off, const int64_t* n, const int64_t* k, int32_t W,
                        const uint32_t* const* keys, uint64_t* words) {
-    for (int32_t i = 0; i < W; ++i) {
-        for (int32_t l = 0; l < L; ++l) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t l = 0; l < L; ++l) {
+        for (int32_t i = 0; i < W; ++i) {
             uint8_t* sel = (uint8_t*)malloc((size_t)(n[l] > 0 ? n[l] : 1));
             oracle_topk(keys[i] + off[l], n[l], k[l], sel);
             for (int64_t j = 0; j < n[l]; ++j)
@@ -220,6 +233,7 @@ void oracle_keys_of(const float* mtilde, int64_t n, uint32_t* key) {
 /* R-mean (Single-Buffer Second-Moment Reconstruction, TS-2: one synchronized
  * sparse buffer b-bar).  out[q] = ((b_0[q] + b_1[q]) + ... + b_{W-1}[q]) / W. */
 void oracle_reduce(const float* const* bufs, int32_t W, int64_t k, float* out) {
+#pragma omp parallel for schedule(static)
     for (int64_t q = 0; q < k; ++q) {
         float s = bufs[0][q];
         for (int32_t i = 1; i < W; ++i) s = s + bufs[i][q];
@@ -285,10 +299,35 @@ int64_t oracle_step(const oracle_problem* P, float* x, float* m, float* v, float
      *     go into the worker's sparse buffer and the residual is cleared; off
      *     the mask the residual keeps a_i (R-buffer).  The owner's candidate
      *     gives the mask statistic (R-statistic). */
-    int64_t q = 0;
-    for (int32_t l = 0; l < P->L; ++l) {
-        for (int64_t e = 0; e < P->n[l]; ++e) {
-            const int64_t j = P->off[l] + e;
+    /* The layers are cut into runs of at most 2^20 elements, and the first
+     * compaction slot of each run (the masked positions before it) is
+     * counted beforehand, so that the runs can be processed independently;
+     * inside a run, elements go in order. */
+    const int64_t run_len = (int64_t)1 << 20;
+    int64_t n_runs = 0;
+    for (int32_t l = 0; l < P->L; ++l) n_runs += (P->n[l] + run_len - 1) / run_len;
+    int64_t* run_j0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_runs > 0 ? n_runs : 1));
+    int64_t* run_j1 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_runs > 0 ? n_runs : 1));
+    int32_t* run_l = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_runs > 0 ? n_runs : 1));
+    int64_t* q0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_runs > 0 ? n_runs : 1));
+    {
+        int64_t r = 0, c = 0;
+        for (int32_t l = 0; l < P->L; ++l) {
+            for (int64_t e0 = 0; e0 < P->n[l]; e0 += run_len, ++r) {
+                const int64_t e1 = e0 + run_len < P->n[l] ? e0 + run_len : P->n[l];
+                run_l[r] = l;
+                run_j0[r] = P->off[l] + e0;
+                run_j1[r] = P->off[l] + e1;
+                q0[r] = c;
+                for (int64_t j = run_j0[r]; j < run_j1[r]; ++j) c += bit_at(cur_words, j);
+            }
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rr = 0; rr < n_runs; ++rr) {
+        const int32_t l = run_l[rr];
+        int64_t q = q0[rr];
+        for (int64_t j = run_j0[rr]; j < run_j1[rr]; ++j) {
             const float mo = m[j];
             const float bm = b1 * mo;
             const int masked = bit_at(cur_words, j);
@@ -307,6 +346,11 @@ int64_t oracle_step(const oracle_problem* P, float* x, float* m, float* v, float
         }
     }
 
+    free(q0);
+    free(run_j0);
+    free(run_j1);
+    free(run_l);
+
     /* (4) The single synchronized sparse buffer: mean over workers (R-mean). */
     oracle_reduce((const float* const*)sent, W, cnt, bbar);
 
@@ -315,6 +359,7 @@ int64_t oracle_step(const oracle_problem* P, float* x, float* m, float* v, float
      *     error-compensated gradient; then the AdamS normaliser
      *     (R-normaliser), m = b-bar, and the parameter update.  Off-mask
      *     coordinates are untouched (R-offmask). */
+#pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < cnt; ++s) {
         const int64_t j = pos[s];
         const float mo = m[j];
@@ -355,6 +400,7 @@ void oracle_dense_step(const oracle_problem* P, float* x, float* m, float* v, co
     const float b1 = P->beta1, b2 = P->beta2;
     const float c1 = 1.0f - b1;
     const float c2 = 1.0f - b2;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int32_t l = 0; l < P->L; ++l) {
         for (int64_t e = 0; e < P->n[l]; ++e) {
             const int64_t j = P->off[l] + e;

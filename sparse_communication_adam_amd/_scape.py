@@ -61,9 +61,10 @@ def lib() -> ctypes.CDLL:
             "scape_owner_map": [cfgp, i32, vp],
             "scape_init": [cfgp, ctypes.POINTER(vp)],
             "scape_destroy": [vp],
+            "scape_workspace_bytes": [vp, vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
-            "scape_step_interleaved": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
+            "scape_step_interleaved": [vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_dense_step": [vp, vp, vp, vp, vp, vp],
             "scape_dense_step_interleaved": [vp, vp, vp, vp, vp, vp],
             "scape_mask_union_add": [vp, vp, vp, vp],
@@ -292,6 +293,13 @@ def scape_destroy(ctx: Context) -> None:
     ctx.destroy()
 
 
+def scape_workspace_bytes(ctx: Context) -> int:
+    """Device memory the context's workspaces hold, in bytes."""
+    b = ctypes.c_int64()
+    _check(lib().scape_workspace_bytes(ctx.handle, ctypes.byref(b)))
+    return b.value
+
+
 def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next: Mask, sparse_bufs: Sequence,
                key_out=None, stream=None) -> None:
     import torch
@@ -310,24 +318,23 @@ def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next:
                             _stream(stream)))
 
 
-def scape_step_interleaved(ctx: Context, x, m, v, r_il, g_il, cur: Mask, next: Mask, sparse_bufs: Sequence,
+def scape_step_interleaved(ctx: Context, xv, m, r_il, g_il, cur: Mask, next: Mask, sparse_bufs: Sequence,
                            key_out=None, stream=None) -> None:
-    """scape_step with the residuals and gradients in the worker-interleaved
-    layout: r_il (fp32) and g_il (bf16 bits) of n_pad*W elements, word w of
+    """scape_step in the interleaved layout: xv holds (x, v) pairs (2*n_pad
+    fp32), r_il (fp32) and g_il (bf16 bits) n_pad*W elements each, word w of
     worker i at [(w*W + i)*64, (w*W + i)*64 + 64)."""
     import torch
     n, W, k = ctx.layout.n_pad, ctx.cfg.workers, ctx.layout.k_total
     if len(sparse_bufs) != W:
         raise ValueError(f"sparse_bufs needs {W} entries")
-    xp = _dev(x, torch.float32, n, "x")
+    xp = _dev(xv, torch.float32, 2 * n, "xv")
     mp = _dev(m, torch.float32, n, "m")
-    vp = _dev(v, torch.float32, n, "v")
     rp = _dev(r_il, torch.float32, n * W, "r_il")
     gp = _dev(g_il, (torch.int16, torch.bfloat16, torch.uint16), n * W, "g_il")
     bp = _ptr_array([_dev(t, torch.float32, k, f"sparse_bufs[{i}]") for i, t in enumerate(sparse_bufs)])
     kp = _dev(key_out, torch.int32, n, "key_out") if key_out is not None else None
     c, nx = cur._c(ctx.layout), next._c(ctx.layout)
-    _check(lib().scape_step_interleaved(ctx.handle, xp, mp, vp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
+    _check(lib().scape_step_interleaved(ctx.handle, xp, mp, rp, gp, ctypes.byref(c), ctypes.byref(nx), bp, kp,
                                         _stream(stream)))
 
 

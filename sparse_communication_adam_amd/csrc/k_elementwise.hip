@@ -66,11 +66,12 @@ constexpr bool kEfXcd = SCAPE_EF_XCD != 0;
 // residual/gradient layouts: at W = 4 one word per wave took 15.3 ms (one
 // array per worker) and 14.3 ms (worker-interleaved) where two took 15.4 and
 // 14.7 and four 15.5 and 15.1; at W = 8 (0.35B shape) one word 6.04 / 5.67 ms
-// against 6.08 / 5.81 with two; at W = 1 (640 bytes per word) two words
-// 4.94 ms against 5.14 with eight.  At W = 32 one and two words were within
-// 1% of each other.
+// against 6.08 / 5.81 with two.  At W = 32 one and two words were within 1%
+// of each other.  At W = 1 (640 bytes per word) the per-word descriptor, mask
+// word and prefix loads weigh more: eight words per wave took 5.0 ms, two
+// 5.9 ms.
 #ifndef SCAPE_EF_W1
-#define SCAPE_EF_W1 2
+#define SCAPE_EF_W1 8
 #endif
 template <int WT>
 constexpr uint32_t ef_words() {
@@ -280,18 +281,24 @@ constexpr int kUpdatePer = SCAPE_UPDATE_PER;
 
 constexpr uint32_t kUpdateGrid = SCAPE_UPDATE_GRID;  // workgroups at most (0: one per chunk)
 
-template <int WT>
+// With XV the parameters and the second moment are one array of (x, v)
+// pairs, 8 bytes per element: the pass gathers and stores a position's pair
+// with one access each instead of touching two arrays (measured on 17.5M
+// positions at 1% density: 1.4-1.7 ms against 2.1-2.5 ms with x and v apart).
+template <int WT, bool XV>
 __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepScalars sc, float* __restrict__ x,
                                                           float* __restrict__ m, float* __restrict__ v,
                                                           const uint32_t* __restrict__ idx,
                                                           const uint32_t* __restrict__ prefix,
                                                           const float* __restrict__ m_stash, uint32_t n_words,
                                                           uint32_t n_pad, uint32_t k_cap) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     const uint32_t total = prefix[n_words];
     const uint32_t cnt = total < k_cap ? total : k_cap;
     const int W = WT > 0 ? WT : sc.W;
     const float fW = (float)W;
+    f32x2* __restrict__ xv = reinterpret_cast<f32x2*>(x);
     constexpr uint32_t chunk = kBlock * kUpdatePer;
     for (uint32_t base = blockIdx.x * chunk; base < cnt; base += gridDim.x * chunk) {
     const uint32_t q0 = base + threadIdx.x;
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
     // compiles to a branch and a wait for all outstanding loads, which
     // serialized the positions.  Only the stores are guarded.
     uint32_t qc[kUpdatePer], jj[kUpdatePer];
-    float mo[kUpdatePer], xv[kUpdatePer], s[kUpdatePer];
+    float mo[kUpdatePer], xv0[kUpdatePer], s[kUpdatePer];
     bool ok[kUpdatePer];
 #pragma unroll
     for (int u = 0; u < kUpdatePer; ++u) {
@@ -313,7 +320,9 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
 #pragma unroll
     for (int u = 0; u < kUpdatePer; ++u) {
         mo[u] = m_stash[qc[u]];
-        xv[u] = x[jj[u] < n_pad ? jj[u] : 0u];  // cached: the store below merges into the line in L2
+        const uint32_t jc = jj[u] < n_pad ? jj[u] : 0u;
+        // cached: the store below merges into the line in L2
+        xv0[u] = XV ? xv[jc].x : x[jc];
         s[u] = wp.b[0][qc[u]];
     }
 #pragma unroll
@@ -329,27 +338,38 @@ __global__ __launch_bounds__(kBlock) void k_reduce_update(WorkerPtrs wp, StepSca
         const float ghat = (bb - sc.beta1 * mo[u]) / sc.c1;
         const float vv = sc.beta2 * (mo[u] * mo[u]) + sc.c2 * (ghat * ghat);
         float upd = bb / (sqrtf(vv) + sc.eps);
-        if (sc.wd != 0.0f) upd = upd + sc.wd * xv[u];
-        // m and v are stored non-temporally; x goes through L2, where its
-        // line is already held by the gather (both measured faster)
-        __builtin_nontemporal_store(vv, &v[jj[u]]);
+        if (sc.wd != 0.0f) upd = upd + sc.wd * xv0[u];
+        // m (and v when apart) are stored non-temporally; x, or the (x, v)
+        // pair, goes through L2, where its line is already held by the gather
+        // (both measured faster)
         __builtin_nontemporal_store(bb, &m[jj[u]]);
-        x[jj[u]] = xv[u] - sc.lr * upd;
+        if (XV) {
+            f32x2 p;
+            p.x = xv0[u] - sc.lr * upd;
+            p.y = vv;
+            xv[jj[u]] = p;
+        } else {
+            __builtin_nontemporal_store(vv, &v[jj[u]]);
+            x[jj[u]] = xv0[u] - sc.lr * upd;
+        }
     }
     }
 }
 
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
-                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
-                                uint32_t n_words, uint32_t n_pad, uint32_t k_cap) {
+                                float* v, bool xv_pairs, const uint32_t* cur_idx, const uint32_t* cur_prefix,
+                                const float* m_stash, uint32_t n_words, uint32_t n_pad, uint32_t k_cap) {
     if (k_cap == 0) return hipSuccess;
     uint32_t blocks = (k_cap + kBlock * kUpdatePer - 1) / (kBlock * kUpdatePer);
     if (kUpdateGrid > 0 && blocks > kUpdateGrid) blocks = kUpdateGrid;
     const dim3 grid(blocks);
-#define SCAPE_RU_CASE(WV)                                                                                     \
-    case WV:                                                                                                  \
-        hipLaunchKernelGGL(k_reduce_update<WV>, grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix, \
-                           m_stash, n_words, n_pad, k_cap);                                                   \
+#define SCAPE_RU_LAUNCH(WV, XVV)                                                                                \
+    hipLaunchKernelGGL((k_reduce_update<WV, XVV>), grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix, \
+                       m_stash, n_words, n_pad, k_cap)
+#define SCAPE_RU_CASE(WV)                        \
+    case WV:                                     \
+        if (xv_pairs) SCAPE_RU_LAUNCH(WV, true); \
+        else SCAPE_RU_LAUNCH(WV, false);         \
         break;
     switch (sc.W) {
         SCAPE_RU_CASE(1)
@@ -360,9 +380,10 @@ hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepS
         SCAPE_RU_CASE(16)
         SCAPE_RU_CASE(32)
         default:
-            hipLaunchKernelGGL(k_reduce_update<0>, grid, dim3(kBlock), 0, s, wp, sc, x, m, v, cur_idx, cur_prefix,
-                               m_stash, n_words, n_pad, k_cap);
+            if (xv_pairs) SCAPE_RU_LAUNCH(0, true);
+            else SCAPE_RU_LAUNCH(0, false);
     }
+#undef SCAPE_RU_LAUNCH
 #undef SCAPE_RU_CASE
     return hipGetLastError();
 }

@@ -181,6 +181,7 @@ struct scape_ctx {
     int prof_next = 0;
     double prof_ms[SCAPE_PHASE_COUNT] = {0, 0, 0, 0};
     int64_t prof_steps = 0;
+    size_t ws_bytes = 0;  // device memory the context holds
 };
 
 namespace {
@@ -224,11 +225,12 @@ void free_ctx(scape_ctx* c) {
 }
 
 template <typename T>
-int dev_alloc(T** p, size_t count, const char* what) {
+int dev_alloc(scape_ctx* c, T** p, size_t count, const char* what) {
     const size_t bytes = count * sizeof(T) > 0 ? count * sizeof(T) : 16;
     hipError_t e = hipMalloc((void**)p, bytes);
     if (e == hipErrorOutOfMemory) return fail(SCAPE_ERR_OOM, "out of device memory allocating %s (%zu bytes)", what, bytes);
     if (e != hipSuccess) return hip_fail(e, what);
+    c->ws_bytes += bytes;
     return SCAPE_OK;
 }
 
@@ -400,11 +402,11 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
 int ensure_offload(scape_ctx* c) {
     if (c->offload_ready || c->n_words == 0) return SCAPE_OK;
     int rc;
-    if (!c->d_key32 && (rc = dev_alloc(&c->d_key32, (size_t)c->lay.n_pad, "full statistic keys"))) return rc;
+    if (!c->d_key32 && (rc = dev_alloc(c, &c->d_key32, (size_t)c->lay.n_pad, "full statistic keys"))) return rc;
     c->chunk_words = std::min<uint32_t>(
         c->n_words, std::max<uint32_t>(kOffloadMinChunkWords, (uint32_t)(kOffloadSlotBytes / ((size_t)c->cfg.workers *
                                                                                              64 * sizeof(float)))));
-    if (!c->d_stage && (rc = dev_alloc(&c->d_stage, (size_t)kOffloadSlots * c->cfg.workers * c->chunk_words * 64,
+    if (!c->d_stage && (rc = dev_alloc(c, &c->d_stage, (size_t)kOffloadSlots * c->cfg.workers * c->chunk_words * 64,
                                        "offload staging")))
         return rc;
     hipError_t e = hipSuccess;
@@ -426,7 +428,8 @@ int ensure_offload(scape_ctx* c) {
 // Where the W residuals and gradients are: one device array per worker, one
 // pinned host array per worker (residuals; the offloaded step), or one device
 // array each holding the W workers' 64 values of every word in turn (the
-// worker-interleaved layout: r[0] and g[0] are its base pointers).
+// interleaved layout: r[0] and g[0] are its base pointers; x then holds the
+// (x, v) pairs and v is not used).
 enum class WorkerLayout { kSeparate, kHostResiduals, kInterleaved };
 
 int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, const uint16_t* const* g,
@@ -435,9 +438,14 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     const bool r_on_host = wl == WorkerLayout::kHostResiduals;
     const bool il = wl == WorkerLayout::kInterleaved;
     if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
-    if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
-    if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
-        return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    if (il) {  // x holds the (x, v) pairs; there is no separate v
+        if (!x || !m) return fail(SCAPE_ERR_INVALID_ARG, "xv and m must not be NULL");
+        if (!aligned(x, 16) || !aligned(m, 16)) return fail(SCAPE_ERR_ALIGN, "xv and m must be 16-byte aligned");
+    } else {
+        if (!x || !m || !v) return fail(SCAPE_ERR_INVALID_ARG, "x, m and v must not be NULL");
+        if (!aligned(x, 16) || !aligned(m, 16) || !aligned(v, 16))
+            return fail(SCAPE_ERR_ALIGN, "x, m and v must be 16-byte aligned");
+    }
     if (!r || !g || !sparse_bufs) return fail(SCAPE_ERR_INVALID_ARG, "r, g and sparse_bufs must not be NULL");
     const int W = ctx->cfg.workers;
     for (int i = 0; i < W; ++i) {
@@ -521,7 +529,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s, ctx->ev_fork);
     if (rc) return rc;  // nothing was queued on the update's stream
     SCAPE_HIP(hipStreamWaitEvent(ctx->s_upd, ctx->ev_fork, 0), "fork");
-    SCAPE_HIP(launch_reduce_update(ctx->s_upd, wp, sc, x, m, v, cur->idx, cur->block_prefix, ctx->d_m_stash,
+    SCAPE_HIP(launch_reduce_update(ctx->s_upd, wp, sc, x, m, v, il, cur->idx, cur->block_prefix, ctx->d_m_stash,
                                    ctx->n_words, (uint32_t)ctx->lay.n_pad, k_cap),
               "reduce_update");
     prof_mark(ctx, slot, 2, ctx->s_upd);
@@ -685,22 +693,22 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     }
     c->device = dev;
     const size_t L = (size_t)c->lay.L;
-    if ((rc = dev_alloc(&c->d_layers, L, "layer table")) || (rc = dev_alloc(&c->d_tiles, c->tiles.size(), "tile table")) ||
-        (rc = dev_alloc(&c->d_hist, L * kHistBins, "histograms")) || (rc = dev_alloc(&c->d_sel, L, "selection state")) ||
-        (rc = dev_alloc(&c->d_segs, n_segs, "segment table")) ||
-        (rc = dev_alloc(&c->d_layer_seg0, L + 1, "layer segment table")) ||
-        (rc = dev_alloc(&c->d_seg_fill, n_segs, "segment record counters")) ||
-        (rc = dev_alloc(&c->d_seg_above, n_segs, "segment bit counters")) ||
-        (rc = dev_alloc(&c->d_vb, c->vb_cap, "record blocks")) ||
-        (rc = dev_alloc(&c->d_vb_count, c->vb_cap, "record block counts")) ||
-        (rc = dev_alloc(&c->d_totals, 4, "totals")) || (rc = dev_alloc(&c->d_miss, 1, "miss flag")) ||
-        (rc = dev_alloc(&c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
-        (rc = dev_alloc(&c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
-        (rc = dev_alloc(&c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
-        (rc = dev_alloc(&c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
-        (rc = dev_alloc(&c->d_counts, L, "per-layer counters")) ||
-        (rc = dev_alloc(&c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
-        (rc = dev_alloc(&c->d_union_bits, (size_t)c->n_words, "union staging bits"))) {
+    if ((rc = dev_alloc(c, &c->d_layers, L, "layer table")) || (rc = dev_alloc(c, &c->d_tiles, c->tiles.size(), "tile table")) ||
+        (rc = dev_alloc(c, &c->d_hist, L * kHistBins, "histograms")) || (rc = dev_alloc(c, &c->d_sel, L, "selection state")) ||
+        (rc = dev_alloc(c, &c->d_segs, n_segs, "segment table")) ||
+        (rc = dev_alloc(c, &c->d_layer_seg0, L + 1, "layer segment table")) ||
+        (rc = dev_alloc(c, &c->d_seg_fill, n_segs, "segment record counters")) ||
+        (rc = dev_alloc(c, &c->d_seg_above, n_segs, "segment bit counters")) ||
+        (rc = dev_alloc(c, &c->d_vb, c->vb_cap, "record blocks")) ||
+        (rc = dev_alloc(c, &c->d_vb_count, c->vb_cap, "record block counts")) ||
+        (rc = dev_alloc(c, &c->d_totals, 4, "totals")) || (rc = dev_alloc(c, &c->d_miss, 1, "miss flag")) ||
+        (rc = dev_alloc(c, &c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
+        (rc = dev_alloc(c, &c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
+        (rc = dev_alloc(c, &c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
+        (rc = dev_alloc(c, &c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
+        (rc = dev_alloc(c, &c->d_counts, L, "per-layer counters")) ||
+        (rc = dev_alloc(c, &c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
+        (rc = dev_alloc(c, &c->d_union_bits, (size_t)c->n_words, "union staging bits"))) {
         free_ctx(c);
         return rc;
     }
@@ -733,6 +741,12 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     return SCAPE_OK;
 }
 
+int scape_workspace_bytes(const scape_ctx* ctx, int64_t* bytes) {
+    if (!ctx || !bytes) return fail(SCAPE_ERR_INVALID_ARG, "NULL argument");
+    *bytes = (int64_t)ctx->ws_bytes;
+    return SCAPE_OK;
+}
+
 int scape_destroy(scape_ctx* ctx) {
     if (!ctx) return SCAPE_OK;
     // wait for the context's own device, free its workspaces there, and leave
@@ -752,12 +766,12 @@ int scape_step(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, co
     return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kSeparate);
 }
 
-int scape_step_interleaved(scape_ctx* ctx, float* x, float* m, float* v, float* r_il, const uint16_t* g_il,
+int scape_step_interleaved(scape_ctx* ctx, float* xv, float* m, float* r_il, const uint16_t* g_il,
                            const scape_mask* cur, const scape_mask* next, float* const* sparse_bufs, uint32_t* key_out,
                            void* stream) {
     float* r[1] = {r_il};
     const uint16_t* g[1] = {g_il};
-    return step_common(ctx, x, m, v, r, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kInterleaved);
+    return step_common(ctx, xv, m, nullptr, r, g, cur, next, sparse_bufs, key_out, stream, WorkerLayout::kInterleaved);
 }
 
 int scape_step_offload(scape_ctx* ctx, float* x, float* m, float* v, float* const* r_host, const uint16_t* const* g,

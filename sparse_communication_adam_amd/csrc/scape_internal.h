@@ -143,9 +143,11 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
                              float* m_stash);
+// xv_pairs: x is an array of (x, v) pairs (x at 2j, v at 2j + 1) and v is
+// not used.
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
-                                float* v, const uint32_t* cur_idx, const uint32_t* cur_prefix, const float* m_stash,
-                                uint32_t n_words, uint32_t n_pad, uint32_t k_cap);
+                                float* v, bool xv_pairs, const uint32_t* cur_idx, const uint32_t* cur_prefix,
+                                const float* m_stash, uint32_t n_words, uint32_t n_pad, uint32_t k_cap);
 hipError_t launch_dense_adams(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                               const StepScalars& sc, float* x, float* m, float* v);
 hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uint32_t w_begin, uint32_t w_end,

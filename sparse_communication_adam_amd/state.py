@@ -8,10 +8,12 @@ slots swap roles.  The first step uses an all-zero mask.  With
 ``offload=True`` the residuals live in pinned host memory and each step calls
 ``scape_step_offload`` (Memory Optimization, same section).
 
-With ``interleaved=True`` the W residuals are one array in the
-worker-interleaved layout (``scape_step_interleaved``): each 64-element word
-holds the W workers' values in turn, and each step takes the gradients in the
-same layout, one int16 tensor of n_pad*W elements.
+With ``interleaved=True`` the state is in the interleaved layout of
+``scape_step_interleaved``: the W residuals are one array in which each
+64-element word holds the W workers' values in turn (each step takes the
+gradients in the same layout, one int16 tensor of n_pad*W elements), and x
+and v are one array of (x, v) pairs, ``xv``; ``x`` and ``v`` are then strided
+views of it.
 
 ``capture`` records the step as HIP graphs, for small models whose step is
 bound by its ~30 kernel launches: ``step_graph`` then replays it with one
@@ -35,9 +37,17 @@ class ScapeState:
         self.layout = self.ctx.layout
         n, W, k = self.layout.n_pad, cfg.workers, self.layout.k_total
         f32 = dict(dtype=torch.float32, device=device)
-        self.x = torch.zeros(n, **f32) if x is None else x
+        self.xv = None
+        if interleaved:
+            self.xv = torch.zeros(2 * n, **f32)
+            self.x = self.xv.view(-1, 2)[:, 0]
+            self.v = self.xv.view(-1, 2)[:, 1]
+            if x is not None:
+                self.x.copy_(x)
+        else:
+            self.x = torch.zeros(n, **f32) if x is None else x
+            self.v = torch.zeros(n, **f32)
         self.m = torch.zeros(n, **f32)
-        self.v = torch.zeros(n, **f32)
         if offload and interleaved:
             raise ValueError("the offloaded step takes one residual array per worker")
         self.offload = offload
@@ -65,6 +75,10 @@ class ScapeState:
     def next_mask(self) -> Mask:
         return self.masks[1 - self._cur]
 
+    def set_params(self, flat) -> None:
+        """Copy n_pad parameters into x (whatever its layout)."""
+        self.x.copy_(flat)
+
     def residual(self, i: int):
         """Worker i's residual as a flat n_pad tensor (a copy in the
         interleaved layout)."""
@@ -80,7 +94,7 @@ class ScapeState:
         it."""
         key = self.key if key_out else None
         if self.interleaved:
-            scape_step_interleaved(self.ctx, self.x, self.m, self.v, self.r_il, grads, self.cur_mask, self.next_mask,
+            scape_step_interleaved(self.ctx, self.xv, self.m, self.r_il, grads, self.cur_mask, self.next_mask,
                                    self.sparse, key, stream)
         else:
             fn = scape_step_offload if self.offload else scape_step
@@ -104,7 +118,7 @@ class ScapeState:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 if self.interleaved:
-                    scape_step_interleaved(self.ctx, self.x, self.m, self.v, self.r_il, self._graph_grads,
+                    scape_step_interleaved(self.ctx, self.xv, self.m, self.r_il, self._graph_grads,
                                            self.masks[cur], self.masks[1 - cur], self.sparse,
                                            self.key if key_out else None)
                 else:
@@ -133,7 +147,7 @@ class ScapeState:
         buffers and statistic keys are outputs of a step, not state."""
         import torch
         torch.cuda.synchronize()
-        cpu = lambda t: t.detach().to("cpu", copy=True)  # noqa: E731
+        cpu = lambda t: t.detach().to("cpu", copy=True).contiguous()  # noqa: E731
         lay = self.layout
         return {
             "n_pad": lay.n_pad, "k_total": lay.k_total, "workers": self.cfg.workers,

@@ -196,6 +196,8 @@ def grads_flat_gpu(wl: Workload, offsets: Sequence[int], out, step: int, worker:
     is left as it is."""
     if tensors is None:
         tensors = range(len(wl.tensors))
+    if not out.is_contiguous():
+        raise ValueError("the generator writes a contiguous flat tensor")
     base = out.data_ptr()
     st = _gpu_stream(stream)
     for off, t in zip(offsets, tensors):
@@ -211,6 +213,11 @@ def params_flat_gpu(wl: Workload, offsets: Sequence[int], out, tensors: Optional
                     stream=None) -> None:
     if tensors is None:
         tensors = range(len(wl.tensors))
+    if not out.is_contiguous():  # a strided view (x inside (x, v) pairs): through a contiguous copy
+        tmp = out.contiguous()
+        params_flat_gpu(wl, offsets, tmp, tensors, stream)
+        out.copy_(tmp)
+        return
     base = out.data_ptr()
     st = _gpu_stream(stream)
     scale = lib().synth_normal_scale(wl.param_sigma)

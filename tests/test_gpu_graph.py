@@ -20,21 +20,24 @@ def gpu():
     yield
 
 
-def _state(wl):
+def _state(wl, interleaved=False):
     import sparse_communication_adam_amd as sc
     from sparse_communication_adam_amd.state import ScapeState
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
-    st = ScapeState(cfg)
+    st = ScapeState(cfg, interleaved=interleaved)
     synth.params_flat_gpu(wl, st.layout.layer_offset, st.x)
     return st
 
 
 def _arrays(st):
-    out = {"x": st.x, "m": st.m, "v": st.v}
-    for i, r in enumerate(st.r):
-        out[f"r{i}"] = r
+    if st.interleaved:
+        out = {"xv": st.xv, "m": st.m, "r_il": st.r_il}
+    else:
+        out = {"x": st.x, "m": st.m, "v": st.v}
+        for i, r in enumerate(st.r):
+            out[f"r{i}"] = r
     for s, mk in enumerate(st.masks):
         out[f"bits{s}"] = mk.bits
         out[f"idx{s}"] = mk.idx
@@ -42,14 +45,17 @@ def _arrays(st):
     return {k: v.view(-1).cpu().numpy().view(np.uint8) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("name", ["ragged", "single-1024x1024"])
-def test_graph_replays_match_eager_steps(name):
+@pytest.mark.parametrize("name,interleaved", [("ragged", False), ("single-1024x1024", False),
+                                             ("ragged", True), ("single-1024x1024", True)])
+def test_graph_replays_match_eager_steps(name, interleaved):
     import torch
+    import sparse_communication_adam_amd as sc
     wl = synth.ragged() if name == "ragged" else synth.WORKLOADS[name]
-    eager, graphed = _state(wl), _state(wl)
+    eager, graphed = _state(wl, interleaved), _state(wl, interleaved)
     lay = eager.layout
     bufs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
-    graphed.capture(bufs)
+    g_il = torch.zeros(lay.n_pad * wl.W, dtype=torch.int16, device="cuda")
+    graphed.capture(g_il if interleaved else bufs)
     torch.cuda.synchronize()
     assert all(np.array_equal(a, b) for a, b in zip(_arrays(eager).values(), _arrays(graphed).values()))
     side = torch.randn(1 << 20, device="cuda")
@@ -57,9 +63,15 @@ def test_graph_replays_match_eager_steps(name):
         gs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
         for i, g in enumerate(gs):
             synth.grads_flat_gpu(wl, lay.layer_offset, g, t, i)
-        eager.step(gs, key_out=False)
-        for b, g in zip(bufs, gs):
-            b.copy_(g)
+        if interleaved:
+            view = sc.interleaved_view(g_il, wl.W)
+            for i, g in enumerate(gs):
+                view[:, i, :].copy_(g.view(-1, 64))
+            eager.step(g_il.clone(), key_out=False)
+        else:
+            eager.step(gs, key_out=False)
+            for b, g in zip(bufs, gs):
+                b.copy_(g)
         graphed.step_graph()
         side.mul_(1.0001).sum()  # eager work of the program's own between replays
         torch.cuda.synchronize()

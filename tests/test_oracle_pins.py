@@ -777,3 +777,39 @@ def test_union_of_disjoint_and_of_identical_workers():
     one = oracle.union_mask(lay, keys[:1])
     assert np.array_equal(oracle.union_mask(lay, [keys[0]] * W), one)
     assert np.array_equal(one, oracle.mask_from_keys(lay, keys[0]))
+
+
+_THREAD_PROBE = r"""
+import hashlib, sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import oracle, synth
+wl = synth.reduced(synth.GPT345M)
+lay = oracle.layout(wl.layer_sizes, wl.keep_num, wl.keep_den, wl.W)
+st = oracle.State.zeros(lay.n_pad, wl.W, synth.params_flat(wl, lay.off, lay.n_pad))
+cur = np.zeros(lay.n_words, np.uint64)
+h = hashlib.sha256()
+for t in (1, 2, 3):
+    out = oracle.step(lay, oracle.Hyper(wl.beta1, wl.beta2, wl.lr, wl.eps, 0.01), st,
+                      [synth.grads_flat(wl, lay.off, lay.n_pad, t, i) for i in range(wl.W)], cur)
+    cur = out.next_words
+    for a in [st.x, st.m, st.v, cur, out.bbar] + st.r + out.sent:
+        h.update(a.tobytes())
+print(oracle.threads(), h.hexdigest())
+"""
+
+
+def test_oracle_results_do_not_depend_on_thread_count():
+    """The oracle's loops run in parallel over layers and positions, never
+    splitting a floating-point sum: one thread and several give the same bits."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = []
+    for n in ("1", "4"):
+        env = dict(os.environ, OMP_NUM_THREADS=n)
+        r = subprocess.run([sys.executable, "-c", _THREAD_PROBE, root], env=env, capture_output=True, text=True,
+                           check=True)
+        outs.append(r.stdout.split())
+    assert outs[0][0] == "1" and outs[1][0] == "4"
+    assert outs[0][1] == outs[1][1]
