@@ -295,6 +295,27 @@ int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits
  * Errors: INVALID_ARG, ALIGN, HIP. */
 int scape_mask_index(scape_ctx* ctx, const scape_mask* mask, void* stream);
 
+/*
+ * scape_mask_index without a context and without allocating: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same result as scape_mask_index
+ * on a mask of n_words words with at most k_cap positions stored: idx (the
+ * set positions in ascending order, the first k_cap of them) and
+ * block_prefix[n_words+1] (set bits before each word; the last entry counts
+ * every set bit).  Its partial sums live in a static device array of the
+ * library (about 64 KB, held by every GPU the library runs on until the
+ * process ends), so n_words is limited to 2^25 (every layout scape_init
+ * takes).  Every entry a call reads is written earlier in the same call;
+ * calls that overlap on one GPU share that array and race.  It calls no
+ * allocating routine.
+ * Arguments: bits device (n_words words, 8-byte aligned), idx device (k_cap
+ * entries, 4-byte aligned; may be NULL when k_cap = 0), block_prefix device
+ * (n_words+1 entries, 4-byte aligned).
+ * Errors: INVALID_ARG, ALIGN, SHAPE (n_words > 2^25), HIP.
+ */
+int scape_mask_index_static(const uint64_t* bits, int64_t n_words, uint32_t* idx, int64_t k_cap,
+                            uint32_t* block_prefix, void* stream);
+
 /* Pack n bytes (nonzero = set) into ceil(n/64) words, LSB first; bits past n
  * are zero.  Unpack writes n bytes of 0/1 and nothing past them.  pred needs
  * no alignment (a 16-byte aligned pred is read or written 16 bytes at a

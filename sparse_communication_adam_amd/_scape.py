@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "scape_mask_union_add": [vp, vp, vp, vp],
             "scape_mask_build": [vp, vp, i32, i32, maskp, vp],
             "scape_mask_index": [vp, maskp, vp],
+            "scape_mask_index_static": [vp, i64, vp, i64, vp, vp],
             "scape_pack": [vp, i64, vp, vp],
             "scape_unpack": [vp, i64, vp, vp],
             "scape_reduce_sparse": [vp, i32, i64, vp, vp],
@@ -403,6 +404,19 @@ def scape_mask_union_add(ctx: Context, mtilde, acc_bits, stream=None) -> None:
 def scape_mask_index(ctx: Context, mask: Mask, stream=None) -> None:
     c = mask._c(ctx.layout)
     _check(lib().scape_mask_index(ctx.handle, ctypes.byref(c), _stream(stream)))
+
+
+def scape_mask_index_static(bits, idx, block_prefix, n_words: Optional[int] = None, k_cap: Optional[int] = None,
+                            stream=None) -> None:
+    """idx and block_prefix of the mask in `bits` without a context or any
+    allocation (the library's static scratch)."""
+    import torch
+    n_words = bits.numel() if n_words is None else int(n_words)
+    k_cap = (idx.numel() if idx is not None else 0) if k_cap is None else int(k_cap)
+    bp = _dev(bits, torch.int64, n_words, "bits")
+    ip = _dev(idx, torch.int32, k_cap, "idx") if idx is not None else None
+    pp = _dev(block_prefix, torch.int32, n_words + 1, "block_prefix")
+    _check(lib().scape_mask_index_static(bp, n_words, ip, k_cap, pp, _stream(stream)))
 
 
 def scape_pack(pred, bits, n: Optional[int] = None, stream=None) -> None:

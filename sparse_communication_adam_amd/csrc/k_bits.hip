@@ -10,6 +10,8 @@
 // The index is built in three passes over the bits (N/8 bytes each):
 // per-workgroup popcounts, one scan of those partial sums, then an emit pass
 // that writes block_prefix for every word and the set positions into idx.
+#include <mutex>
+
 #include "scape_device.h"
 
 namespace scape {
@@ -140,6 +142,37 @@ hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_wor
     if (nb == 0) return hipSuccess;
     hipLaunchKernelGGL(k_index_emit, dim3(nb), dim3(kBlock), 0, s, bits, n_words, block_offs, idx, k_cap, prefix);
     return hipGetLastError();
+}
+
+// The index without a context: the per-workgroup partial sums live in a
+// file-scope device array instead of a context workspace, for callers that
+// cannot allocate.  Every entry a call reads is written earlier in that call
+// (count, then scan), so nothing needs clearing between calls; calls that
+// overlap on one GPU share the array and race.
+__device__ __align__(256) uint32_t g_index_scratch[kIndexScratchEntries];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t index_scratch(uint32_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // the array's name is a host-side stand-in: its device address on
+        // this device (each device holds its own copy) comes from the runtime
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_index_scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // acc |= src over n_words words (the fill-in union of per-worker masks).

@@ -855,6 +855,32 @@ int scape_mask_index(scape_ctx* ctx, const scape_mask* mask, void* stream) {
     return run_index(ctx, mask, (hipStream_t)stream);
 }
 
+int scape_mask_index_static(const uint64_t* bits, int64_t n_words, uint32_t* idx, int64_t k_cap,
+                            uint32_t* block_prefix, void* stream) {
+    if (n_words < 0) return fail(SCAPE_ERR_INVALID_ARG, "n_words must be >= 0");
+    if (n_words > kIndexStaticMaxWords)
+        return fail(SCAPE_ERR_SHAPE, "n_words %lld exceeds the static scratch's maximum of %lld words",
+                    (long long)n_words, (long long)kIndexStaticMaxWords);
+    if (k_cap < 0 || k_cap > (int64_t)0xFFFFFFFFu) return fail(SCAPE_ERR_INVALID_ARG, "k_cap must be in 0..2^32-1");
+    if (!bits || !block_prefix || (k_cap > 0 && !idx))
+        return fail(SCAPE_ERR_INVALID_ARG, "bits, block_prefix and (for k_cap > 0) idx must not be NULL");
+    if (!aligned(bits, 8)) return fail(SCAPE_ERR_ALIGN, "bits must be 8-byte aligned");
+    if (!aligned(block_prefix, 4) || (idx && !aligned(idx, 4)))
+        return fail(SCAPE_ERR_ALIGN, "idx and block_prefix must be 4-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t nw = (uint32_t)n_words;
+    if (nw == 0) {  // an empty mask: the prefix is the one total, 0
+        SCAPE_HIP(launch_fill_u32(s, block_prefix, 1, 0u), "fill");
+        return SCAPE_OK;
+    }
+    uint32_t* scratch = nullptr;
+    SCAPE_HIP(index_scratch(&scratch), "index scratch address");
+    SCAPE_HIP(launch_index_count(s, bits, nw, scratch), "index_count");
+    SCAPE_HIP(launch_index_scan(s, scratch, (nw + kIndexWordsPerBlock - 1) / kIndexWordsPerBlock), "index_scan");
+    SCAPE_HIP(launch_index_emit(s, bits, nw, scratch, idx, (uint32_t)k_cap, block_prefix), "index_emit");
+    return SCAPE_OK;
+}
+
 int scape_pack(const uint8_t* pred, int64_t n, uint64_t* bits, void* stream) {
     if (n < 0) return fail(SCAPE_ERR_INVALID_ARG, "n must be >= 0");
     if (n >= (int64_t(1) << 37)) return fail(SCAPE_ERR_SHAPE, "n too large");

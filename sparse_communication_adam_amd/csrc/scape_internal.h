@@ -33,6 +33,11 @@ constexpr int kKey3Bits = 9;                                // bits 14..6
 constexpr int kKey4Bits = kKeyShift - kKey3Bits;            // 6: bits 5..0
 constexpr int kHistBins = kDigit1Bins;          // histogram row per layer (>= every digit's bins)
 constexpr int kIndexWordsPerBlock = 2048;  // words per workgroup in the index passes
+// Largest word count of the context-free index (every layout the ABI takes:
+// n_pad < 2^31 elements), and the entries of its static partial-sum array
+// (one per index workgroup, plus the total).
+constexpr int64_t kIndexStaticMaxWords = int64_t(1) << 25;
+constexpr int kIndexScratchEntries = (int)(kIndexStaticMaxWords / kIndexWordsPerBlock) + 2;
 constexpr int kCandChunk = 8192;        // candidate records per virtual block
 constexpr int kSegTiles = 16;           // tiles per record segment
 
@@ -189,6 +194,9 @@ hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_wo
 hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blocks);
 hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,
                              uint32_t* idx, uint32_t k_cap, uint32_t* prefix);
+// Device address (on the current device) of the index's file-scope
+// partial-sum array, looked up once per device.
+hipError_t index_scratch(uint32_t** out);
 hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, uint32_t n_words);
 hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits);
 hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred);
