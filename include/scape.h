@@ -122,6 +122,17 @@ int scape_destroy(scape_ctx* ctx);
  * Errors: INVALID_ARG. */
 int scape_workspace_bytes(const scape_ctx* ctx, int64_t* bytes);
 
+/* Which exact fallbacks the context's last mask selection took (a
+ * diagnostic; waits for the device): bit 0 = some layer's threshold fell
+ * outside its sampled window or its window held more records than its
+ * record space, and was redone from an exact histogram of its keys; bit 1 =
+ * some layer's exact threshold bucket still did not fit its record space and
+ * was decided by passes over its keys.  Either way the mask is the exact one.
+ * Errors: INVALID_ARG, STATE, HIP. */
+#define SCAPE_SELECT_EXACT_HISTOGRAM 1u
+#define SCAPE_SELECT_KEY_PASSES 2u
+int scape_selection_flags(scape_ctx* ctx, uint32_t* flags);
+
 /*
  * One SCAPE step on W simulated workers, all resident on this GPU.
  *

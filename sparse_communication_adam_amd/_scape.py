@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "scape_init": [cfgp, ctypes.POINTER(vp)],
             "scape_destroy": [vp],
             "scape_workspace_bytes": [vp, vp],
+            "scape_selection_flags": [vp, vp],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_interleaved": [vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
@@ -299,6 +300,18 @@ def scape_workspace_bytes(ctx: Context) -> int:
     b = ctypes.c_int64()
     _check(lib().scape_workspace_bytes(ctx.handle, ctypes.byref(b)))
     return b.value
+
+
+SELECT_EXACT_HISTOGRAM = 1
+SELECT_KEY_PASSES = 2
+
+
+def scape_selection_flags(ctx: Context) -> int:
+    """Fallbacks the last mask selection took (waits for the device): bit 0
+    exact histogram, bit 1 passes over the keys (SELECT_* constants)."""
+    f = ctypes.c_uint32()
+    _check(lib().scape_selection_flags(ctx.handle, ctypes.byref(f)))
+    return f.value
 
 
 def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next: Mask, sparse_bufs: Sequence,

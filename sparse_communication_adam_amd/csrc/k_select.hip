@@ -86,7 +86,10 @@ constexpr uint32_t kSampleShift = 4;            // 1 word in 16
 constexpr uint32_t kFullSampleWords = 4096;     // layers up to 262144 elements are taken whole
 constexpr float kZ = 6.0f;                      // sampling margin in standard deviations
 
-enum SelMode : uint32_t { kModeWindow = 0, kModeFullHist = 2, kModeReclassify = 1 };
+// kModeNoRecords: the layer's records did not fit its record space even for
+// the exact threshold bucket; its remaining digits are decided by passes over
+// the layer's keys themselves (k_layer_pass) instead of records.
+enum SelMode : uint32_t { kModeWindow = 0, kModeFullHist = 2, kModeReclassify = 1, kModeNoRecords = 3 };
 
 __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
     uint32_t h = w * 0x9E3779B1u;
@@ -553,6 +556,7 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
                                                          uint32_t* __restrict__ hist, SelState* __restrict__ st,
                                                          const uint32_t* __restrict__ seg_above,
                                                          uint32_t* __restrict__ seg_fill,
+                                                         const uint32_t* __restrict__ ovf,
                                                          uint32_t* __restrict__ miss) {
     __shared__ uint32_t scratch[kWaves];
     __shared__ uint32_t s_bucket, s_before, s_count, s_above;
@@ -583,8 +587,9 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
         S.phase = kPhaseDone;
         S.J = 0xFFFFFFFFu;
         S.mode = kModeWindow;
-    } else if (first_pass && (!win || a >= k || s_bucket == kNone)) {
-        // outside the window (or no window): count every key of the layer
+    } else if (first_pass && (!win || a >= k || s_bucket == kNone || ovf[l])) {
+        // outside the window (or no window, or more records than the layer's
+        // record space holds): count every key of the layer
         S.mode = kModeFullHist;
         S.none = 1;  // provisional; the second pass decides
         S.phase = kPhaseDone;
@@ -603,10 +608,10 @@ __global__ __launch_bounds__(kBlock) void k_select_first(int32_t layer0, bool fi
 
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
-                               const uint32_t* seg_above, uint32_t* seg_fill, uint32_t* miss) {
+                               const uint32_t* seg_above, uint32_t* seg_fill, const uint32_t* ovf, uint32_t* miss) {
     if (n_layers <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_select_first, dim3(n_layers), dim3(kBlock), 0, s, layer0, first_pass, layers, layer_seg0,
-                       hist, st, seg_above, seg_fill, miss);
+                       hist, st, seg_above, seg_fill, ovf, miss);
     return hipGetLastError();
 }
 
@@ -693,18 +698,35 @@ hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_
 // One workgroup of 1024 threads numbers the blocks of the segments
 // [seg0, seg0 + n_segs), each thread owning a contiguous run of segments, and
 // writes every block's descriptor and initial count.
+// A segment whose fill counter passed its record space (G.size) lost records:
+// after the key filter (`second` false) its layer is flagged in ovf, and
+// k_select_first sends it down the exact path; after the exact filter
+// (`second` true) the layer switches to kModeNoRecords (bit 1 of *miss tells
+// k_layer_pass there is work).
 __global__ __launch_bounds__(1024) void k_cand_scan(uint32_t seg0, uint32_t n_segs,
                                                     const SegDesc* __restrict__ segs,
                                                     const uint32_t* __restrict__ seg_fill,
                                                     VblockDesc* __restrict__ vb, uint32_t* __restrict__ vb_count,
-                                                    uint32_t* __restrict__ totals) {
+                                                    uint32_t* __restrict__ totals, bool second,
+                                                    uint32_t* __restrict__ ovf, SelState* __restrict__ st,
+                                                    uint32_t* __restrict__ miss) {
     __shared__ uint32_t sv[1024];
     const uint32_t per = (n_segs + 1023) / 1024;
     const uint32_t a = threadIdx.x * per;
     const uint32_t b = min(a + per, n_segs);
     uint32_t v = 0;
     for (uint32_t i = a; i < b; ++i) {
-        const uint32_t n = min(seg_fill[seg0 + i], segs[seg0 + i].size);
+        const SegDesc G = segs[seg0 + i];
+        const uint32_t f = seg_fill[seg0 + i];
+        if (f > G.size) {  // records were dropped
+            if (second) {
+                st[G.layer].mode = kModeNoRecords;
+                atomicOr(miss, 2u);
+            } else {
+                ovf[G.layer] = 1u;
+            }
+        }
+        const uint32_t n = min(f, G.size);
         v += (n + kCandChunk - 1) / kCandChunk;
     }
     sv[threadIdx.x] = v;
@@ -728,9 +750,11 @@ __global__ __launch_bounds__(1024) void k_cand_scan(uint32_t seg0, uint32_t n_se
 }
 
 hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
-                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals) {
+                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals,
+                            bool second, uint32_t* ovf, SelState* st, uint32_t* miss) {
     if (n_segs == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, seg0, n_segs, segs, seg_fill, vb, vb_count, totals);
+    hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(1024), 0, s, seg0, n_segs, segs, seg_fill, vb, vb_count, totals,
+                       second, ovf, st, miss);
     return hipGetLastError();
 }
 
@@ -832,7 +856,7 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
         const VblockDesc D = vb[v];
         const int l = D.layer;
         const SelState S = st[l];
-        if (!hist_only && S.none) {
+        if (!hist_only && (S.none || S.mode == kModeNoRecords)) {  // nothing here, or decided without records
             if (threadIdx.x == 0) vb_count[v] = 0;
             continue;
         }
@@ -943,6 +967,77 @@ hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb,
                             const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits) {
     hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kPassBlock), 0, s, phase, vb, vb_count, totals, layers, st, ks, cand,
                        hist, bits);
+    return hipGetLastError();
+}
+
+// A pass over the keys of the layers in kModeNoRecords, standing in for a
+// record pass: every element of the layer's exact threshold bucket d1 is
+// classified by the same rule a record of it would be (classify, plus the
+// key test that the record passes leave to compaction), with its full key
+// fetched only where its stored 16 bits equal the threshold prefix
+// (elsewhere those 16 bits decide).  Intermediate phases only histogram the
+// undecided elements; the final pass (kPhaseDone) marks every element the
+// final rule selects (keys above the bucket were set by the exact filter).
+// Normally no layer needs it: the grid walks the tile table and returns at
+// once while bit 1 of *miss is clear.
+__global__ __launch_bounds__(kBlock) void k_layer_pass(uint32_t phase, const TileDesc* __restrict__ tiles,
+                                                       uint32_t n_tiles, const LayerDesc* __restrict__ layers,
+                                                       const SelState* __restrict__ st,
+                                                       const uint16_t* __restrict__ key, KeySource ks,
+                                                       uint32_t* __restrict__ hist, uint64_t* __restrict__ bits,
+                                                       const uint32_t* __restrict__ miss) {
+    __shared__ uint32_t h[kPassBins];
+    if ((*miss & 2u) == 0) return;
+    const uint32_t lane = lane_id();
+    const bool final_pass = phase == kPhaseDone;
+    const int nb = final_pass ? 0 : phase_bins(phase);
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+        const TileDesc t = tiles[ti];
+        const SelState S = st[t.layer];
+        // uniform per workgroup: only this kind of layer, in this phase
+        if (S.mode != kModeNoRecords || S.none || S.phase != phase) continue;
+        const LayerDesc L = layers[t.layer];
+        for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
+        __syncthreads();
+        // top 16 bits of the threshold prefix decided so far
+        const uint32_t p16 = phase == kPhaseKey3   ? S.kprefix
+                             : phase == kPhaseKey4 ? S.kprefix >> kKey3Bits
+                                                   : S.T >> kKeyShift;
+        const uint32_t lend = L.off + L.n;
+        for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kWaves) {
+            const uint32_t j = w * 64u + lane;
+            const bool inl = j < lend;
+            const uint32_t kv16 = key[inl ? j : L.off];
+            const bool cand = inl && (kv16 >> kDigit1FromKey16) == S.d1;
+            const bool need = cand && phase != kPhaseKey2 && kv16 == p16;
+            uint64_t rec[kFetch] = {(uint64_t)(kv16 << kKeyShift) << 32 | (j - L.off), 0, 0, 0};
+            if (wave_ballot(need)) candidate_keys(ks, L, rec, need ? 1u : 0u);
+            const uint32_t kv = (uint32_t)(rec[0] >> 32);
+            uint32_t digit = 0;
+            uint32_t c = cand ? classify(phase, S, kv, j - L.off, &digit) : 0u;
+            // the rules of the later position digits assume the set they split
+            // holds only keys equal to T, as a layer's records do by then;
+            // here every element of the bucket is seen again
+            if ((phase == kPhasePos2 || phase == kPhasePos3) && cand && kv != S.T) c = kv > S.T ? 1u : 0u;
+            if (final_pass) {
+                if (c == 1u) atomicOr((unsigned long long*)&bits[j >> 6], 1ull << (j & 63u));
+            } else {
+                if (phase == kPhaseKey3) digit = (kv >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
+                hist_add_wave(h, digit, c == 2u);
+            }
+        }
+        __syncthreads();
+        if (!final_pass) hist_flush(h, hist + (size_t)t.layer * kHistBins, nb);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_layer_pass(hipStream_t s, uint32_t phase, const TileDesc* tiles, uint32_t n_tiles,
+                             const LayerDesc* layers, const SelState* st, const uint16_t* key, const KeySource& ks,
+                             uint32_t* hist, uint64_t* bits, const uint32_t* miss) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_layer_pass, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, phase, tiles, n_tiles,
+                       layers, st, key, ks, hist, bits, miss);
     return hipGetLastError();
 }
 

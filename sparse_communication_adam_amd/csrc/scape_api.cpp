@@ -163,6 +163,7 @@ struct scape_ctx {
     uint32_t* d_block_sums = nullptr;
     uint16_t* d_word_info = nullptr;  // per word: owner << 8 | elements inside the layer
     uint32_t* d_counts = nullptr;     // per layer: sampled keys
+    uint32_t* d_ovf = nullptr;        // per layer: records lost to the record space in the key filter
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
@@ -206,6 +207,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_block_sums);
     hipFree(c->d_word_info);
     hipFree(c->d_counts);
+    hipFree(c->d_ovf);
     hipFree(c->d_m_stash);
     hipFree(c->d_stage);
     for (int b = 0; b < kOffloadSlots; ++b) {
@@ -303,40 +305,50 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_fill + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
     SCAPE_HIP(launch_fill_u32(s, sample_count + la, (uint64_t)nl, 0u), "fill");
+    SCAPE_HIP(launch_fill_u32(s, c->d_ovf + la, (uint64_t)nl, 0u), "fill");
     SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
     SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel, c->d_miss), "estimate");
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
                             c->d_seg_above),
               "filter");
     if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
-    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
+    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals, false,
+                               c->d_ovf, c->d_sel, c->d_miss),
               "cand_scan");
     SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                c->d_hist, bits),
               "cand_pass");
     SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
-                                  c->d_seg_above, c->d_seg_fill, c->d_miss),
+                                  c->d_seg_above, c->d_seg_fill, c->d_ovf, c->d_miss),
               "select_first");
-    // sampling misses: full histogram, exact bucket, reclassification
+    // sampling misses and lost records: full histogram, exact bucket,
+    // reclassification
     SCAPE_HIP(launch_hist_full(s, tiles, nt, c->d_layers, c->d_sel, key, c->d_hist, c->d_miss), "hist_full");
     SCAPE_HIP(launch_select_first(s, la, nl, false, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
-                                  c->d_seg_above, c->d_seg_fill, c->d_miss),
+                                  c->d_seg_above, c->d_seg_fill, c->d_ovf, c->d_miss),
               "select_first");
     SCAPE_HIP(launch_filter_exact(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill,
                                   c->d_cand, c->d_seg_above, c->d_miss),
               "filter_exact");
-    // radix passes with shrinking record sets, then the final marking
-    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals),
+    // radix passes with shrinking record sets, then the final marking; a layer
+    // whose exact bucket still did not fit its record space is decided by
+    // passes over its keys instead
+    SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals, true,
+                               c->d_ovf, c->d_sel, c->d_miss),
               "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
         SCAPE_HIP(launch_cand_pass(s, phase, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                    c->d_hist, bits),
                   "cand_pass");
+        SCAPE_HIP(launch_layer_pass(s, phase, tiles, nt, c->d_layers, c->d_sel, key, ks, c->d_hist, bits, c->d_miss),
+                  "layer_pass");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
     SCAPE_HIP(launch_cand_pass(s, kPhaseDone, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
                                c->d_hist, bits),
               "cand_pass");
+    SCAPE_HIP(launch_layer_pass(s, kPhaseDone, tiles, nt, c->d_layers, c->d_sel, key, ks, c->d_hist, bits, c->d_miss),
+              "layer_pass");
     return SCAPE_OK;
 }
 
@@ -635,7 +647,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     owner_map(c->lay, c->P, c->owner.data());
     c->n_words = (uint32_t)(c->lay.n_pad / 64);
     c->n_index_blocks = (c->n_words + kIndexWordsPerBlock - 1) / kIndexWordsPerBlock;
-    c->cand_cap = (uint32_t)c->lay.n_pad;
+
 
     std::vector<LayerDesc> ld(c->lay.L);
     c->layer_tile0.assign(c->lay.L + 1, 0);
@@ -659,23 +671,27 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     c->layer_tile0[c->lay.L] = (uint32_t)c->tiles.size();
     // record segments: runs of kSegTiles tiles inside each layer
     c->layer_seg0.assign(c->lay.L + 1, 0);
+    uint64_t rec_total = 0;
     for (int32_t l = 0; l < c->lay.L; ++l) {
         c->layer_seg0[l] = (uint32_t)c->segs.size();
         for (uint32_t t0 = c->layer_tile0[l]; t0 < c->layer_tile0[l + 1]; t0 += kSegTiles) {
             const uint32_t t1 = std::min<uint32_t>(t0 + kSegTiles, c->layer_tile0[l + 1]);
+            const uint32_t elems = (c->tiles[t1 - 1].w1 - c->tiles[t0].w0) * 64u;
             SegDesc g;
             g.layer = l;
-            g.base = c->tiles[t0].w0 * 64u;
-            g.size = (c->tiles[t1 - 1].w1 - c->tiles[t0].w0) * 64u;
+            g.base = (uint32_t)rec_total;  // below n_pad < 2^31: each space is at most its elements
+            g.size = std::min<uint32_t>(elems, (elems >> kRecordShift) + kRecordSlack);
             g.pad = 0;
+            rec_total += g.size;
             for (uint32_t t = t0; t < t1; ++t) c->tiles[t].seg = (uint32_t)c->segs.size();
             c->segs.push_back(g);
         }
     }
     c->layer_seg0[c->lay.L] = (uint32_t)c->segs.size();
     const size_t n_segs = c->segs.size();
+    c->cand_cap = (uint32_t)rec_total;
     // a segment of s records makes ceil(s / kCandChunk) blocks
-    c->vb_cap = (size_t)(c->lay.n_pad / kCandChunk) + n_segs + 1;
+    c->vb_cap = (size_t)(rec_total / kCandChunk) + n_segs + 1;
     std::vector<uint16_t> winfo(c->n_words, 0);
     for (int32_t l = 0; l < c->lay.L; ++l) {
         const int64_t off = c->lay.off[l], n = c->lay.n[l];
@@ -707,6 +723,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(c, &c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
         (rc = dev_alloc(c, &c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(c, &c->d_counts, L, "per-layer counters")) ||
+        (rc = dev_alloc(c, &c->d_ovf, L, "per-layer record overflow flags")) ||
         (rc = dev_alloc(c, &c->d_m_stash, (size_t)c->lay.k_total, "m stash")) ||
         (rc = dev_alloc(c, &c->d_union_bits, (size_t)c->n_words, "union staging bits"))) {
         free_ctx(c);
@@ -744,6 +761,16 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
 int scape_workspace_bytes(const scape_ctx* ctx, int64_t* bytes) {
     if (!ctx || !bytes) return fail(SCAPE_ERR_INVALID_ARG, "NULL argument");
     *bytes = (int64_t)ctx->ws_bytes;
+    return SCAPE_OK;
+}
+
+int scape_selection_flags(scape_ctx* ctx, uint32_t* flags) {
+    if (!ctx || !flags) return fail(SCAPE_ERR_INVALID_ARG, "NULL argument");
+    int rc;
+    if ((rc = check_device(ctx))) return rc;
+    uint32_t f = 0;
+    SCAPE_HIP(hipMemcpy(&f, ctx->d_miss, sizeof(f), hipMemcpyDeviceToHost), "reading the selection flags");
+    *flags = f;
     return SCAPE_OK;
 }
 

@@ -49,16 +49,22 @@ struct TileDesc {
 };
 
 // A record segment: up to kSegTiles consecutive tiles of one layer.  Their
-// candidate records are stored in the segment's own element range of the
-// record buffer, [base, base + size), so a segment can never overflow, and
-// the workgroups in flight at one time reserve space on many different
-// counters instead of one per layer.
+// candidate records go to the segment's own range of the record buffer,
+// [base, base + size): the workgroups in flight at one time reserve space on
+// many different counters instead of one per layer.  The range holds a
+// fraction of the segment's elements (the record space); records past it are
+// dropped and counted, and the layer is then redone exactly.
 struct SegDesc {
     int32_t layer;
-    uint32_t base;  // first element of the first tile
-    uint32_t size;  // elements covered by the segment's tiles
+    uint32_t base;  // first record slot
+    uint32_t size;  // record slots
     uint32_t pad;
 };
+// Record space of a segment of e elements: e / 2^kRecordShift + kRecordSlack
+// slots (at most e).  Windows from the sampled histogram hold 1-3% of a
+// layer's keys on the workloads measured.
+constexpr int kRecordShift = 4;
+constexpr uint32_t kRecordSlack = 1024;
 
 struct LayerDesc {
     uint32_t off;    // first element (multiple of 64)
@@ -173,16 +179,21 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                          const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                          uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
+// ovf[l] != 0: layer l lost records to its record space in the key filter.
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
-                               const uint32_t* seg_above, uint32_t* seg_fill, uint32_t* miss);
+                               const uint32_t* seg_above, uint32_t* seg_fill, const uint32_t* ovf, uint32_t* miss);
 hipError_t launch_hist_full(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                             const SelState* st, const uint16_t* key, uint32_t* hist, const uint32_t* miss);
 hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                                const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
                                uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above, const uint32_t* miss);
 hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
-                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals);
+                            const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals,
+                            bool second, uint32_t* ovf, SelState* st, uint32_t* miss);
+hipError_t launch_layer_pass(hipStream_t s, uint32_t phase, const TileDesc* tiles, uint32_t n_tiles,
+                             const LayerDesc* layers, const SelState* st, const uint16_t* key, const KeySource& ks,
+                             uint32_t* hist, uint64_t* bits, const uint32_t* miss);
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
                             const uint32_t* totals, const LayerDesc* layers, const SelState* st,
                             const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits);

@@ -172,6 +172,38 @@ def test_mask_build_heavy_ties_across_many_candidate_blocks():
         ctx.destroy()
 
 
+@pytest.mark.parametrize("case,keep,want_flags", [
+    ("normal", (1, 100), 0),          # records fit: no fallback
+    ("levels16", (1, 2), 3),          # window and exact bucket both beyond the record space
+    ("all_equal", (1, 10), 3),        # one bucket holds every key
+    ("zeros", (37, 1000), 3),
+])
+def test_mask_build_record_space_overflow(case, keep, want_flags):
+    """A record segment holds 1/16 of its elements plus 1024 records.  When a
+    layer's window holds more, the layer is redone from an exact histogram;
+    when even its exact threshold bucket does not fit, the remaining digits
+    are decided by passes over its keys.  The mask is the oracle's either
+    way, and scape_selection_flags reports which path ran."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    sizes = [2_000_000, 300_001, 5000]
+    ctx = _ctx(sizes, W=2, keep=keep)
+    lay = oracle.layout(sizes, keep[0], keep[1], 2)
+    gen = _mtilde_cases()[case]
+    mt = np.zeros(lay.n_pad, np.float32)
+    for off, n in zip(lay.off, lay.sizes):
+        mt[off:off + n] = gen(int(n))
+    out = sc.alloc_mask(ctx.layout)
+    sc.scape_mask_build(ctx, torch.from_numpy(mt).cuda(), out)
+    flags = sc.scape_selection_flags(ctx)
+    exp = oracle.mask_from_keys(lay, oracle.keys_of(mt))
+    assert np.array_equal(u64(out.bits), exp), (case, keep, flags)
+    idx, pre, cnt = oracle.mask_index(exp)
+    assert np.array_equal(u32(out.idx)[:cnt], idx) and np.array_equal(u32(out.block_prefix), pre)
+    assert flags == want_flags, (case, keep, flags)
+    ctx.destroy()
+
+
 def test_mask_build_more_segments_than_lds_map():
     """Over 4096 record segments (one per tiny layer): the record passes look
     segments up in global memory instead of their LDS copy."""
