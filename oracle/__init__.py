@@ -17,18 +17,27 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SCAPE_ORACLE_LIB selects another build of the same source (the sanitizer
+# build the CPU suite runs once under AddressSanitizer and UBSan).
+LIB_PATH = os.environ.get("SCAPE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-BUILD_CMD = ["gcc", "-O2", "-fPIC", "-shared", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-             os.path.join(_HERE, "scape_oracle.c"), "-o", LIB_PATH + ".tmp", "-lm"]
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
 
 
-def build(force: bool = True) -> str:
-    if force or not os.path.exists(LIB_PATH):
-        subprocess.run(BUILD_CMD, check=True)
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+def build_cmd(out: str, sanitize: bool = False) -> list:
+    return (["gcc", "-O2", "-fPIC", "-shared", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math"]
+            + (SANITIZE_FLAGS if sanitize else []) + [os.path.join(_HERE, "scape_oracle.c"), "-o", out, "-lm"])
+
+
+def build(force: bool = True, sanitize: bool = False, out: str = None) -> str:
+    """Compile the oracle (gcc, OpenMP); with sanitize, an AddressSanitizer
+    and UBSan build to `out` (load it with the gcc ASan runtime preloaded)."""
+    out = out or LIB_PATH
+    if force or not os.path.exists(out):
+        subprocess.run(build_cmd(out + ".tmp", sanitize), check=True)
+        os.replace(out + ".tmp", out)
+    return out
 
 
 class _Problem(ctypes.Structure):

@@ -13,7 +13,9 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libscape.so")
+# SCAPE_LIB selects another build of the library (the host-sanitizer build
+# the CPU suite checks its host paths with).
+LIB_PATH = os.environ.get("SCAPE_LIB") or os.path.join(HERE, "libscape.so")
 
 SCAPE_OK = 0
 SCAPE_ERR_INVALID_ARG = -1
