@@ -88,7 +88,8 @@ constexpr float kZ = 6.0f;                      // sampling margin in standard d
 
 // kModeNoRecords: the layer's records did not fit its record space even for
 // the exact threshold bucket; its remaining digits are decided by passes over
-// the layer's keys themselves (k_layer_pass) instead of records.
+// the layer's keys themselves (key_passes, run by the record passes)
+// instead of records.
 enum SelMode : uint32_t { kModeWindow = 0, kModeFullHist = 2, kModeReclassify = 1, kModeNoRecords = 3 };
 
 __device__ __forceinline__ uint32_t word_hash(uint32_t w) {
@@ -391,25 +392,36 @@ __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, ui
 // Keys of a tile: first digit d >= sel_from -> mask bit; cand_lo <= d <=
 // cand_hi -> record, holding the 16 stored key bits (the low 15 bits zero;
 // the pass over key bits 17..9 fetches the full key of the records it still
-// needs).  Every word of the tile is written.  The waves work
+// needs).  With kHist the records' first digits are also counted into the
+// layer's histogram row (bins cand_lo..cand_hi), which the threshold-bucket
+// search reads next.  Every word of the tile is written.  The waves work
 // alone until the end of the tile, where one reservation on the segment's
 // counter places all of the workgroup's records (a wave whose staging fills
 // up mid-tile reserves on its own), and the count of bits set is added to the
 // segment's total.  Must be called by every thread of the workgroup.
 // LDS of the key pass: each wave's staged records, and the workgroup's
 // record and bit counts.
+constexpr int kFilterHistBins = 512;  // LDS bins of the records' first digits (wider windows count in global memory)
 struct KeyPassLds {
     uint64_t rec[kWaves][kWaveStage];
+    uint32_t hist[kFilterHistBins];
     uint32_t n[kWaves], ab[kWaves], base;
 };
 
-template <bool kRecords>
+template <bool kRecords, bool kHist = false>
 __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
                                          uint32_t sel_from, uint32_t cand_lo, uint32_t cand_hi,
                                          const uint16_t* __restrict__ key, uint64_t* __restrict__ bits,
                                          uint32_t* __restrict__ seg_fill, uint64_t* __restrict__ cand,
-                                         uint32_t* __restrict__ seg_above) {
+                                         uint32_t* __restrict__ seg_above, uint32_t* __restrict__ hist_row = nullptr) {
     const uint32_t lend = L.off + L.n;
+    // histogram bins of the window's first digits: in LDS when they fit
+    const uint32_t width = kHist ? cand_hi - cand_lo + 1u : 0u;
+    const bool lds_hist = kHist && width <= (uint32_t)kFilterHistBins;
+    if (kHist) {
+        for (uint32_t b = threadIdx.x; b < (lds_hist ? width : 0u); b += kBlock) lds.hist[b] = 0;
+        __syncthreads();
+    }
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     uint64_t* stage = lds.rec[wave];
@@ -448,9 +460,15 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
                     wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
                     n_st = 0;
                 }
-                if (in_range && (!decltype(partial)::value || lane < left))
+                const bool rec = in_range && (!decltype(partial)::value || lane < left);
+                if (rec)
                     stage[n_st + lanes_below(cb)] = ((uint64_t)(kw << kKeyShift) << 32) | (uint64_t)(w * 64u + lane - L.off);
                 n_st += (uint32_t)__popcll(cb);
+                if (kHist) {
+                    const uint32_t bin = (kw >> kDigit1FromKey16) - cand_lo;
+                    if (lds_hist) hist_add_wave(lds.hist, bin, rec);
+                    else if (rec) atomicAdd(&hist_row[cand_lo + bin], 1u);
+                }
             }
         }
     };
@@ -485,6 +503,7 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
         lds.ab[wave] = n_above;
     }
     __syncthreads();
+    if (lds_hist) hist_flush(lds.hist, hist_row + cand_lo, (int)width);
     if (threadIdx.x == 0) {
         uint32_t tot = 0, ab = 0;
         for (int q = 0; q < kWaves; ++q) {
@@ -505,7 +524,8 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
                                                    const SegDesc* __restrict__ segs,
                                                    const SelState* __restrict__ st, const uint16_t* __restrict__ key,
                                                    uint64_t* __restrict__ bits, uint32_t* __restrict__ seg_fill,
-                                                   uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above) {
+                                                   uint64_t* __restrict__ cand, uint32_t* __restrict__ seg_above,
+                                                   uint32_t* __restrict__ hist) {
     const TileDesc t = tiles[blockIdx.x];
     const LayerDesc L = layers[t.layer];
     const SegDesc G = segs[t.seg];
@@ -514,17 +534,18 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
     __shared__ KeyPassLds lds;
     // no window (nothing to select, or an empty sample): no bits, no records
     if (win)
-        key_pass<true>(lds, t, L, G, S.n_hi + 1, S.n_lo, S.n_hi, key, bits, seg_fill, cand, seg_above);
+        key_pass<true, true>(lds, t, L, G, S.n_hi + 1, S.n_lo, S.n_hi, key, bits, seg_fill, cand, seg_above,
+                             hist + (size_t)t.layer * kHistBins);
     else  // no window (nothing to select, or an empty sample): no bits, no records
         key_pass<false>(lds, t, L, G, (uint32_t)kDigit1Bins, 1u, 0u, key, bits, seg_fill, cand, seg_above);
 }
 
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                          const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
-                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above) {
+                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above, uint32_t* hist) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_filter, dim3(n_tiles), dim3(kBlock), 0, s, tiles, layers, segs, st, key, bits, seg_fill,
-                       cand, seg_above);
+                       cand, seg_above, hist);
     return hipGetLastError();
 }
 
@@ -699,10 +720,10 @@ hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_
 // [seg0, seg0 + n_segs), each thread owning a contiguous run of segments, and
 // writes every block's descriptor and initial count.
 // A segment whose fill counter passed its record space (G.size) lost records:
-// after the key filter (`second` false) its layer is flagged in ovf, and
-// k_select_first sends it down the exact path; after the exact filter
-// (`second` true) the layer switches to kModeNoRecords (bit 1 of *miss tells
-// k_layer_pass there is work).
+// after the key filter (`second` false; no blocks are made then) its layer is
+// flagged in ovf, and k_select_first sends it down the exact path; after the
+// exact filter (`second` true) the layer switches to kModeNoRecords (bit 1 of
+// *miss tells the record passes to run key_passes).
 __global__ __launch_bounds__(1024) void k_cand_scan(uint32_t seg0, uint32_t n_segs,
                                                     const SegDesc* __restrict__ segs,
                                                     const uint32_t* __restrict__ seg_fill,
@@ -729,6 +750,7 @@ __global__ __launch_bounds__(1024) void k_cand_scan(uint32_t seg0, uint32_t n_se
         const uint32_t n = min(f, G.size);
         v += (n + kCandChunk - 1) / kCandChunk;
     }
+    if (!second) return;  // after the key filter only the overflow flags are needed
     sv[threadIdx.x] = v;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
@@ -778,9 +800,6 @@ __device__ __forceinline__ int phase_bins(uint32_t phase) {
 __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, uint32_t kv, uint32_t jl,
                                              uint32_t* digit) {
     switch (phase) {
-        case kPhaseKey1:
-            *digit = kv >> kDigit1Shift;
-            return 2;
         case kPhaseKey2: {  // stored bits suffice
             const uint32_t d = kv >> kDigit1Shift;
             *digit = (kv >> kKeyShift) & ((1u << kKey2Bits) - 1u);
@@ -815,6 +834,67 @@ __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, 
     }
 }
 
+// Passes over the keys of the layers in kModeNoRecords, standing in for the
+// record passes: every element of the layer's exact threshold bucket d1 is
+// classified by the same rule a record of it would be (classify, plus the
+// key test that the record passes leave to compaction), with its full key
+// fetched only where its stored 16 bits equal the threshold prefix
+// (elsewhere those 16 bits decide).  Intermediate phases only histogram the
+// undecided elements; the final pass (kPhaseDone) marks every element the
+// final rule selects (keys above the bucket were set by the exact filter).
+// Run by the record pass's workgroups after their record blocks, walking the
+// tile table; normally no layer needs it (bit 1 of *miss clear).  h is the
+// workgroup's LDS histogram, free on entry; every thread must call it.
+template <int kThreads>
+__device__ void key_passes(uint32_t phase, const TileDesc* __restrict__ tiles, uint32_t n_tiles,
+                           const LayerDesc* __restrict__ layers, const SelState* __restrict__ st,
+                           const uint16_t* __restrict__ key, const KeySource& ks, uint32_t* __restrict__ hist,
+                           uint64_t* __restrict__ bits, uint32_t* h) {
+    constexpr uint32_t kW = kThreads / 64;
+    const uint32_t lane = lane_id();
+    const bool final_pass = phase == kPhaseDone;
+    const int nb = final_pass ? 0 : phase_bins(phase);
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+        const TileDesc t = tiles[ti];
+        const SelState S = st[t.layer];
+        // uniform per workgroup: only this kind of layer, in this phase
+        if (S.mode != kModeNoRecords || S.none || S.phase != phase) continue;
+        const LayerDesc L = layers[t.layer];
+        for (int b = threadIdx.x; b < nb; b += kThreads) h[b] = 0;
+        __syncthreads();
+        // top 16 bits of the threshold prefix decided so far
+        const uint32_t p16 = phase == kPhaseKey3   ? S.kprefix
+                             : phase == kPhaseKey4 ? S.kprefix >> kKey3Bits
+                                                   : S.T >> kKeyShift;
+        const uint32_t lend = L.off + L.n;
+        for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kW) {
+            const uint32_t j = w * 64u + lane;
+            const bool inl = j < lend;
+            const uint32_t kv16 = key[inl ? j : L.off];
+            const bool cand = inl && (kv16 >> kDigit1FromKey16) == S.d1;
+            const bool need = cand && phase != kPhaseKey2 && kv16 == p16;
+            uint64_t rec[kFetch] = {(uint64_t)(kv16 << kKeyShift) << 32 | (j - L.off), 0, 0, 0};
+            if (wave_ballot(need)) candidate_keys(ks, L, rec, need ? 1u : 0u);
+            const uint32_t kv = (uint32_t)(rec[0] >> 32);
+            uint32_t digit = 0;
+            uint32_t c = cand ? classify(phase, S, kv, j - L.off, &digit) : 0u;
+            // the rules of the later position digits assume the set they split
+            // holds only keys equal to T, as a layer's records do by then;
+            // here every element of the bucket is seen again
+            if ((phase == kPhasePos2 || phase == kPhasePos3) && cand && kv != S.T) c = kv > S.T ? 1u : 0u;
+            if (final_pass) {
+                if (c == 1u) atomicOr((unsigned long long*)&bits[j >> 6], 1ull << (j & 63u));
+            } else {
+                if (phase == kPhaseKey3) digit = (kv >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
+                hist_add_wave(h, digit, c == 2u);
+            }
+        }
+        __syncthreads();
+        if (!final_pass) hist_flush(h, hist + (size_t)t.layer * kHistBins, nb, kThreads);
+        __syncthreads();
+    }
+}
+
 constexpr int kPassBlock = 512;                          // threads per workgroup of a record pass
 constexpr int kPassWaves = kPassBlock / 64;
 constexpr int kRecPerThread = kCandChunk / kPassBlock;  // 16 records held in registers per thread
@@ -823,11 +903,9 @@ constexpr int kRecPerThread = kCandChunk / kPassBlock;  // 16 records held in re
 // decided on the stored bits (T a multiple of 2^15, J = all positions), so
 // the final rule holds on the filter's partial keys too.
 //
-// One pass over the record blocks.  phase == kPhaseKey1: histogram of every
-// record's first digit, nothing else; the digits of a layer's records lie in
-// its window [n_lo, n_hi], so the LDS bins are relative to n_lo (a window
-// wider than kPassBins buckets counts straight into the global row).  Otherwise, for each block, by the
-// state of its layer: a layer in `phase` has its selected records marked,
+// One pass over the record blocks (the records' first digits were counted by
+// the key filter).  For each block, by the state of its layer: a layer in
+// `phase` has its selected records marked,
 // its undecided ones histogrammed and compacted to the front of the block,
 // the rest dropped; a layer already done has its selected records marked and
 // the block emptied.  Each workgroup takes a contiguous range of blocks and
@@ -838,17 +916,18 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
                                                       const LayerDesc* __restrict__ layers,
                                                       const SelState* __restrict__ st, KeySource ks,
                                                       uint64_t* __restrict__ cand, uint32_t* __restrict__ hist,
-                                                      uint64_t* __restrict__ bits) {
+                                                      uint64_t* __restrict__ bits, const TileDesc* __restrict__ tiles,
+                                                      uint32_t n_tiles, const uint16_t* __restrict__ key,
+                                                      const uint32_t* __restrict__ miss) {
     __shared__ uint32_t h[kPassBins];
     __shared__ uint32_t s_wsum[kPassWaves];
     const uint32_t nv = totals[1];
     const uint32_t per = (nv + gridDim.x - 1) / gridDim.x;
     const uint32_t v0 = blockIdx.x * per, v1 = min(v0 + per, nv);
-    const bool hist_only = phase == kPhaseKey1;
     const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
     int cur = -1;
     uint32_t* cur_row = nullptr;  // global bins of the LDS row (first bin)
-    int cur_nb = 0;               // bins to flush; 0 when counting straight into the row
+    int cur_nb = 0;               // bins to flush
     for (int b = threadIdx.x; b < kPassBins; b += kPassBlock) h[b] = 0;
     for (uint32_t v = v0; v < v1; ++v) {
         const uint32_t cnt = vb_count[v];
@@ -856,20 +935,14 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
         const VblockDesc D = vb[v];
         const int l = D.layer;
         const SelState S = st[l];
-        if (!hist_only && (S.none || S.mode == kModeNoRecords)) {  // nothing here, or decided without records
+        if (S.none || S.mode == kModeNoRecords) {  // nothing here, or decided without records
             if (threadIdx.x == 0) vb_count[v] = 0;
             continue;
         }
-        const uint32_t cph = hist_only ? kPhaseKey1 : S.phase;
+        const uint32_t cph = S.phase;
         if (cph != phase && cph != kPhaseDone) continue;  // not reached: a layer is in this phase or done
         const bool hist_on = cph != kPhaseDone;
-        uint32_t lo = 0;  // first digit histogrammed
-        int nbl = hist_on ? phase_bins(cph) : 0;
-        if (hist_only) {
-            lo = S.n_lo;
-            const uint32_t width = S.n_hi - S.n_lo + 1u;
-            nbl = width <= (uint32_t)kPassBins ? (int)width : 0;
-        }
+        const int nbl = hist_on ? phase_bins(cph) : 0;
         if (hist_on && l != cur) {
             if (cur >= 0) {
                 __syncthreads();
@@ -878,7 +951,7 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
                 for (int b = threadIdx.x; b < kPassBins; b += kPassBlock) h[b] = 0;
             }
             cur = l;
-            cur_row = hist + (size_t)l * kHistBins + lo;
+            cur_row = hist + (size_t)l * kHistBins;
             cur_nb = nbl;
             __syncthreads();
         }
@@ -911,10 +984,7 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
                 const uint32_t jj = off + jl;
                 atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
             }
-            if (hist_on && !fetch) {
-                if (cur_nb) hist_add_wave(h, digit - lo, c == 2u);
-                else if (c == 2u) atomicAdd(&cur_row[digit - lo], 1u);  // wide first-digit window
-            }
+            if (hist_on && !fetch) hist_add_wave(h, digit, c == 2u);
             if (c == 2u) und |= 1u << i;
         }
         if (fetch) {
@@ -931,7 +1001,7 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
                 hist_add_wave(h, digit, (und >> i) & 1u);
             }
         }
-        if (!hist_only) {
+        {
             // compaction in place: every record of the block is in registers
             // once the barrier is passed, so the writes cannot clobber a
             // record not yet read
@@ -960,84 +1030,18 @@ __global__ __launch_bounds__(kPassBlock) void k_cand_pass(uint32_t phase, const 
         __syncthreads();
         if (cur_nb) hist_flush(h, cur_row, cur_nb, kPassBlock);
     }
+    if (*miss & 2u) {  // layers decided without records: the same phase over their keys
+        __syncthreads();
+        key_passes<kPassBlock>(phase, tiles, n_tiles, layers, st, key, ks, hist, bits, h);
+    }
 }
 
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
                             const uint32_t* totals, const LayerDesc* layers, const SelState* st,
-                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits) {
+                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits,
+                            const TileDesc* tiles, uint32_t n_tiles, const uint16_t* key, const uint32_t* miss) {
     hipLaunchKernelGGL(k_cand_pass, dim3(1024), dim3(kPassBlock), 0, s, phase, vb, vb_count, totals, layers, st, ks, cand,
-                       hist, bits);
-    return hipGetLastError();
-}
-
-// A pass over the keys of the layers in kModeNoRecords, standing in for a
-// record pass: every element of the layer's exact threshold bucket d1 is
-// classified by the same rule a record of it would be (classify, plus the
-// key test that the record passes leave to compaction), with its full key
-// fetched only where its stored 16 bits equal the threshold prefix
-// (elsewhere those 16 bits decide).  Intermediate phases only histogram the
-// undecided elements; the final pass (kPhaseDone) marks every element the
-// final rule selects (keys above the bucket were set by the exact filter).
-// Normally no layer needs it: the grid walks the tile table and returns at
-// once while bit 1 of *miss is clear.
-__global__ __launch_bounds__(kBlock) void k_layer_pass(uint32_t phase, const TileDesc* __restrict__ tiles,
-                                                       uint32_t n_tiles, const LayerDesc* __restrict__ layers,
-                                                       const SelState* __restrict__ st,
-                                                       const uint16_t* __restrict__ key, KeySource ks,
-                                                       uint32_t* __restrict__ hist, uint64_t* __restrict__ bits,
-                                                       const uint32_t* __restrict__ miss) {
-    __shared__ uint32_t h[kPassBins];
-    if ((*miss & 2u) == 0) return;
-    const uint32_t lane = lane_id();
-    const bool final_pass = phase == kPhaseDone;
-    const int nb = final_pass ? 0 : phase_bins(phase);
-    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
-        const TileDesc t = tiles[ti];
-        const SelState S = st[t.layer];
-        // uniform per workgroup: only this kind of layer, in this phase
-        if (S.mode != kModeNoRecords || S.none || S.phase != phase) continue;
-        const LayerDesc L = layers[t.layer];
-        for (int b = threadIdx.x; b < nb; b += kBlock) h[b] = 0;
-        __syncthreads();
-        // top 16 bits of the threshold prefix decided so far
-        const uint32_t p16 = phase == kPhaseKey3   ? S.kprefix
-                             : phase == kPhaseKey4 ? S.kprefix >> kKey3Bits
-                                                   : S.T >> kKeyShift;
-        const uint32_t lend = L.off + L.n;
-        for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kWaves) {
-            const uint32_t j = w * 64u + lane;
-            const bool inl = j < lend;
-            const uint32_t kv16 = key[inl ? j : L.off];
-            const bool cand = inl && (kv16 >> kDigit1FromKey16) == S.d1;
-            const bool need = cand && phase != kPhaseKey2 && kv16 == p16;
-            uint64_t rec[kFetch] = {(uint64_t)(kv16 << kKeyShift) << 32 | (j - L.off), 0, 0, 0};
-            if (wave_ballot(need)) candidate_keys(ks, L, rec, need ? 1u : 0u);
-            const uint32_t kv = (uint32_t)(rec[0] >> 32);
-            uint32_t digit = 0;
-            uint32_t c = cand ? classify(phase, S, kv, j - L.off, &digit) : 0u;
-            // the rules of the later position digits assume the set they split
-            // holds only keys equal to T, as a layer's records do by then;
-            // here every element of the bucket is seen again
-            if ((phase == kPhasePos2 || phase == kPhasePos3) && cand && kv != S.T) c = kv > S.T ? 1u : 0u;
-            if (final_pass) {
-                if (c == 1u) atomicOr((unsigned long long*)&bits[j >> 6], 1ull << (j & 63u));
-            } else {
-                if (phase == kPhaseKey3) digit = (kv >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
-                hist_add_wave(h, digit, c == 2u);
-            }
-        }
-        __syncthreads();
-        if (!final_pass) hist_flush(h, hist + (size_t)t.layer * kHistBins, nb);
-        __syncthreads();
-    }
-}
-
-hipError_t launch_layer_pass(hipStream_t s, uint32_t phase, const TileDesc* tiles, uint32_t n_tiles,
-                             const LayerDesc* layers, const SelState* st, const uint16_t* key, const KeySource& ks,
-                             uint32_t* hist, uint64_t* bits, const uint32_t* miss) {
-    if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_layer_pass, dim3(min(n_tiles, kFallbackGrid)), dim3(kBlock), 0, s, phase, tiles, n_tiles,
-                       layers, st, key, ks, hist, bits, miss);
+                       hist, bits, tiles, n_tiles, key, miss);
     return hipGetLastError();
 }
 

@@ -309,15 +309,14 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
     SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
     SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel, c->d_miss), "estimate");
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
-                            c->d_seg_above),
+                            c->d_seg_above, c->d_hist),
               "filter");
     if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
+    // the filter counted the records' first digits; overflowed record spaces
+    // are flagged here, and the threshold bucket of each layer found next
     SCAPE_HIP(launch_cand_scan(s, sa, ns, c->d_segs, c->d_seg_fill, c->d_vb, c->d_vb_count, c->d_totals, false,
                                c->d_ovf, c->d_sel, c->d_miss),
               "cand_scan");
-    SCAPE_HIP(launch_cand_pass(s, kPhaseKey1, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
-                               c->d_hist, bits),
-              "cand_pass");
     SCAPE_HIP(launch_select_first(s, la, nl, true, c->d_layers, c->d_layer_seg0, c->d_hist, c->d_sel,
                                   c->d_seg_above, c->d_seg_fill, c->d_ovf, c->d_miss),
               "select_first");
@@ -338,17 +337,13 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
               "cand_scan");
     for (uint32_t phase = kPhaseKey2; phase <= kPhasePos3; ++phase) {
         SCAPE_HIP(launch_cand_pass(s, phase, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
-                                   c->d_hist, bits),
+                                   c->d_hist, bits, tiles, nt, key, c->d_miss),
                   "cand_pass");
-        SCAPE_HIP(launch_layer_pass(s, phase, tiles, nt, c->d_layers, c->d_sel, key, ks, c->d_hist, bits, c->d_miss),
-                  "layer_pass");
         SCAPE_HIP(launch_select_next(s, phase, la, nl, c->d_hist, c->d_sel), "select_next");
     }
     SCAPE_HIP(launch_cand_pass(s, kPhaseDone, c->d_vb, c->d_vb_count, c->d_totals, c->d_layers, c->d_sel, ks, c->d_cand,
-                               c->d_hist, bits),
+                               c->d_hist, bits, tiles, nt, key, c->d_miss),
               "cand_pass");
-    SCAPE_HIP(launch_layer_pass(s, kPhaseDone, tiles, nt, c->d_layers, c->d_sel, key, ks, c->d_hist, bits, c->d_miss),
-              "layer_pass");
     return SCAPE_OK;
 }
 

@@ -84,7 +84,6 @@ enum SelPhase : uint32_t {
     kPhasePos1 = 4,   // tie position bits 30..20 pending
     kPhasePos2 = 5,   // tie position bits 19..10 pending
     kPhasePos3 = 6,   // tie position bits 9..0 pending
-    kPhaseKey1 = 7,   // first key digit of the records (threshold bucket) pending
 };
 
 struct SelState {
@@ -176,9 +175,11 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 // (k_hist_full, k_filter_exact) return at once while it is clear.
 // Record segments: `segs`, `seg_fill` (records per segment) and `seg_above`
 // (keys above the window per segment) are indexed by global segment number.
+// The filter also counts its records' first digits into each layer's
+// histogram row (hist, kHistBins per layer), for k_select_first.
 hipError_t launch_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
                          const SegDesc* segs, const SelState* st, const uint16_t* key, uint64_t* bits,
-                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above);
+                         uint32_t* seg_fill, uint64_t* cand, uint32_t* seg_above, uint32_t* hist);
 // ovf[l] != 0: layer l lost records to its record space in the key filter.
 hipError_t launch_select_first(hipStream_t s, int32_t layer0, int32_t n_layers, bool first_pass,
                                const LayerDesc* layers, const uint32_t* layer_seg0, uint32_t* hist, SelState* st,
@@ -191,12 +192,13 @@ hipError_t launch_filter_exact(hipStream_t s, const TileDesc* tiles, uint32_t n_
 hipError_t launch_cand_scan(hipStream_t s, uint32_t seg0, uint32_t n_segs, const SegDesc* segs,
                             const uint32_t* seg_fill, VblockDesc* vb, uint32_t* vb_count, uint32_t* totals,
                             bool second, uint32_t* ovf, SelState* st, uint32_t* miss);
-hipError_t launch_layer_pass(hipStream_t s, uint32_t phase, const TileDesc* tiles, uint32_t n_tiles,
-                             const LayerDesc* layers, const SelState* st, const uint16_t* key, const KeySource& ks,
-                             uint32_t* hist, uint64_t* bits, const uint32_t* miss);
+
+// A record pass also runs the same phase over the keys of the layers that
+// lost records even in their exact bucket (bit 1 of *miss), walking tiles.
 hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb, uint32_t* vb_count,
                             const uint32_t* totals, const LayerDesc* layers, const SelState* st,
-                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits);
+                            const KeySource& ks, uint64_t* cand, uint32_t* hist, uint64_t* bits,
+                            const TileDesc* tiles, uint32_t n_tiles, const uint16_t* key, const uint32_t* miss);
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
 
