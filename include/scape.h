@@ -133,6 +133,22 @@ int scape_workspace_bytes(const scape_ctx* ctx, int64_t* bytes);
 #define SCAPE_SELECT_KEY_PASSES 2u
 int scape_selection_flags(scape_ctx* ctx, uint32_t* flags);
 
+/* How the context selects a mask (per-layer top-k; the mask is the same
+ * either way).  SAMPLED: a sampled histogram windows each layer's threshold,
+ * one pass over the keys marks what lies above the window and records what
+ * lies in it, and multi-workgroup passes over the records resolve the
+ * remaining digits (about 20 launches; built for large layers).  COMPACT: an
+ * exact histogram pass, then one pass that marks and records the threshold
+ * bucket, whose records one workgroup per layer resolves (2 launches; built
+ * for layers of up to a few million elements, where launches dominate).
+ * AUTO (the default): COMPACT for a layer range whose layers all have at
+ * most 2^22 elements, else SAMPLED.  Host only, takes effect from the next
+ * call.  Errors: INVALID_ARG. */
+#define SCAPE_SELECT_PATH_AUTO 0
+#define SCAPE_SELECT_PATH_SAMPLED 1
+#define SCAPE_SELECT_PATH_COMPACT 2
+int scape_set_select_path(scape_ctx* ctx, int32_t path);
+
 /*
  * One SCAPE step on W simulated workers, all resident on this GPU.
  *

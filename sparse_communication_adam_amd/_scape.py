@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "scape_destroy": [vp],
             "scape_workspace_bytes": [vp, vp],
             "scape_selection_flags": [vp, vp],
+            "scape_set_select_path": [vp, i32],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_interleaved": [vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
@@ -314,6 +315,18 @@ def scape_selection_flags(ctx: Context) -> int:
     f = ctypes.c_uint32()
     _check(lib().scape_selection_flags(ctx.handle, ctypes.byref(f)))
     return f.value
+
+
+SELECT_PATH_AUTO = 0
+SELECT_PATH_SAMPLED = 1
+SELECT_PATH_COMPACT = 2
+
+
+def scape_set_select_path(ctx: Context, path: int) -> None:
+    """How the context selects masks from the next call on (SELECT_PATH_*):
+    the sampled multi-pass path, the two-launch compact path, or AUTO (compact
+    where every layer of the range has at most 2^22 elements)."""
+    _check(lib().scape_set_select_path(ctx.handle, int(path)))
 
 
 def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next: Mask, sparse_bufs: Sequence,

@@ -144,6 +144,57 @@ hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_wor
     return hipGetLastError();
 }
 
+// The index of a mask of at most kIndexSmallMaxWords words in two launches
+// instead of three, with one word per thread: k_index_count_small counts each
+// workgroup's kBlock words, and each workgroup of k_index_emit_small adds up
+// the counts of the workgroups before it itself (there are at most kBlock)
+// before it emits its words.  For small masks the launches, not the bits,
+// take the time.
+__global__ __launch_bounds__(kBlock) void k_index_count_small(const uint64_t* __restrict__ bits, uint32_t n_words,
+                                                              uint32_t* __restrict__ block_sums) {
+    __shared__ uint32_t scratch[kWaves];
+    const uint32_t w = blockIdx.x * kBlock + threadIdx.x;
+    const uint32_t c = w < n_words ? (uint32_t)__popcll(bits[w]) : 0u;
+    uint32_t total = 0;
+    block_exclusive_scan(c, scratch, &total);
+    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void k_index_emit_small(const uint64_t* __restrict__ bits, uint32_t n_words,
+                                                             const uint32_t* __restrict__ block_sums,
+                                                             uint32_t* __restrict__ idx, uint32_t k_cap,
+                                                             uint32_t* __restrict__ prefix) {
+    __shared__ uint32_t scratch[kWaves];
+    __shared__ uint32_t s_off;
+    const uint32_t w = blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t word = w < n_words ? bits[w] : 0ull;
+    const uint32_t bs = threadIdx.x < gridDim.x ? block_sums[threadIdx.x] : 0u;
+    uint32_t total = 0;
+    const uint32_t before = block_exclusive_scan(bs, scratch, &total);
+    if (threadIdx.x == blockIdx.x) s_off = before;
+    __syncthreads();
+    const uint32_t pre = s_off + block_exclusive_scan((uint32_t)__popcll(word), scratch, nullptr);
+    if (w < n_words) prefix[w] = pre;
+    if (blockIdx.x == 0 && threadIdx.x == 0) prefix[n_words] = total;
+    uint64_t x = word;
+    uint32_t r = pre;
+    while (x) {
+        if (r < k_cap) idx[r] = w * 64u + (uint32_t)__builtin_ctzll(x);
+        ++r;
+        x &= x - 1;
+    }
+}
+
+hipError_t launch_index_small(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums,
+                              uint32_t* idx, uint32_t k_cap, uint32_t* prefix) {
+    const uint32_t nb = (n_words + kBlock - 1) / kBlock;
+    if (nb == 0 || n_words > kIndexSmallMaxWords) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_index_count_small, dim3(nb), dim3(kBlock), 0, s, bits, n_words, block_sums);
+    hipLaunchKernelGGL(k_index_emit_small, dim3(nb), dim3(kBlock), 0, s, bits, n_words, block_sums, idx, k_cap,
+                       prefix);
+    return hipGetLastError();
+}
+
 // The index without a context: the per-workgroup partial sums live in a
 // file-scope device array instead of a context workspace, for callers that
 // cannot allocate.  Every entry a call reads is written earlier in that call

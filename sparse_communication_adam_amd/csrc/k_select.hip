@@ -48,25 +48,27 @@ namespace scape {
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-// Generic per-layer bucket search over `nbins` bins of `h` (a multiple of
-// kBlock).  Scan order is from the top bin down when `descending`, else from
-// bin 0 up.  Returns (via LDS) the bucket where the running count first
-// reaches `need`, the count before it and the bucket's own count; zeroes the
-// row afterwards.  Each thread owns a contiguous run of bins in scan order:
-// one pass sums it, a workgroup scan places it, and the one thread whose run
-// holds the target walks it again.
+// Generic per-layer bucket search over `nbins` bins of `h` (global or LDS)
+// by a workgroup of kThreads threads.  Scan order is from the top bin down
+// when `descending`, else from bin 0 up.  Returns (via LDS) the bucket where
+// the running count first reaches `need`, the count before it and the
+// bucket's own count; zeroes the row afterwards.  Each thread owns a
+// contiguous run of bins in scan order: one pass sums it, a workgroup scan
+// places it, and the one thread whose run holds the target walks it again.
+template <int kThreads = kBlock>
 __device__ void find_bucket(uint32_t* h, int nbins, bool descending, uint32_t need, uint32_t* s_bucket,
                             uint32_t* s_before, uint32_t* s_count, uint32_t* scan_scratch) {
-    const int per = nbins / kBlock;
+    const int per = (nbins + kThreads - 1) / kThreads;
+    const int e0 = (int)threadIdx.x * per, e1 = min(e0 + per, nbins);  // this thread's run (may be empty)
     auto bin = [&](int o) { return descending ? nbins - 1 - o : o; };
     uint32_t sum = 0;
-    for (int e = 0; e < per; ++e) sum += h[bin(threadIdx.x * per + e)];
+    for (int e = e0; e < e1; ++e) sum += h[bin(e)];
     if (threadIdx.x == 0) *s_bucket = kNone;
-    const uint32_t before = block_exclusive_scan(sum, scan_scratch, nullptr);
+    const uint32_t before = block_exclusive_scan_t<kThreads>(sum, scan_scratch, nullptr);
     if (need > 0 && before < need && before + sum >= need) {
         uint32_t cum = before;
-        for (int e = 0; e < per; ++e) {
-            const int b = bin(threadIdx.x * per + e);
+        for (int e = e0; e < e1; ++e) {
+            const int b = bin(e);
             const uint32_t c = h[b];
             if (cum + c >= need) {
                 *s_bucket = (uint32_t)b;
@@ -78,7 +80,7 @@ __device__ void find_bucket(uint32_t* h, int nbins, bool descending, uint32_t ne
         }
     }
     __syncthreads();
-    for (int e = 0; e < per; ++e) h[bin(threadIdx.x * per + e)] = 0;
+    for (int e = e0; e < e1; ++e) h[bin(e)] = 0;
     __syncthreads();
 }
 
@@ -389,6 +391,29 @@ __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, ui
     }
 }
 
+// The same, with each record's full key fetched first (candidate_keys), so
+// that the records carry all 31 key bits.
+__device__ __forceinline__ void wave_store_full(const uint64_t* stage, uint32_t n, uint32_t first, const SegDesc& G,
+                                                uint64_t* __restrict__ cand, const KeySource& ks, const LayerDesc& L) {
+    const uint32_t lane = lane_id();
+    for (uint32_t i0 = 0; i0 < n; i0 += 64u * kFetch) {
+        uint64_t rec[kFetch];
+        uint32_t sel = 0;
+#pragma unroll
+        for (uint32_t u = 0; u < (uint32_t)kFetch; ++u) {
+            const uint32_t i = i0 + u * 64u + lane;
+            rec[u] = i < n ? stage[i] : 0ull;
+            if (i < n) sel |= 1u << u;
+        }
+        candidate_keys(ks, L, rec, sel);
+#pragma unroll
+        for (uint32_t u = 0; u < (uint32_t)kFetch; ++u) {
+            const uint32_t i = i0 + u * 64u + lane;
+            if (i < n && first + i < G.size) cand[(size_t)G.base + first + i] = rec[u];
+        }
+    }
+}
+
 // Keys of a tile: first digit d >= sel_from -> mask bit; cand_lo <= d <=
 // cand_hi -> record, holding the 16 stored key bits (the low 15 bits zero;
 // the pass over key bits 17..9 fetches the full key of the records it still
@@ -402,24 +427,29 @@ __device__ __forceinline__ void wave_store(const uint64_t* stage, uint32_t n, ui
 // LDS of the key pass: each wave's staged records, and the workgroup's
 // record and bit counts.
 constexpr int kFilterHistBins = 512;  // LDS bins of the records' first digits (wider windows count in global memory)
-struct KeyPassLds {
-    uint64_t rec[kWaves][kWaveStage];
+template <int kNW>
+struct KeyPassLdsT {
+    uint64_t rec[kNW][kWaveStage];
     uint32_t hist[kFilterHistBins];
-    uint32_t n[kWaves], ab[kWaves], base;
+    uint32_t n[kNW], ab[kNW], base;
 };
+using KeyPassLds = KeyPassLdsT<kWaves>;
 
-template <bool kRecords, bool kHist = false>
-__device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
+// With kFullKeys the records are stored with their full keys, from *ks.
+template <bool kRecords, bool kHist = false, int kThreads = kBlock, bool kFullKeys = false>
+__device__ __forceinline__ void key_pass(KeyPassLdsT<kThreads / 64>& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
                                          uint32_t sel_from, uint32_t cand_lo, uint32_t cand_hi,
                                          const uint16_t* __restrict__ key, uint64_t* __restrict__ bits,
                                          uint32_t* __restrict__ seg_fill, uint64_t* __restrict__ cand,
-                                         uint32_t* __restrict__ seg_above, uint32_t* __restrict__ hist_row = nullptr) {
+                                         uint32_t* __restrict__ seg_above, uint32_t* __restrict__ hist_row = nullptr,
+                                         const KeySource* ks = nullptr) {
+    constexpr int kNW = kThreads / 64;
     const uint32_t lend = L.off + L.n;
     // histogram bins of the window's first digits: in LDS when they fit
     const uint32_t width = kHist ? cand_hi - cand_lo + 1u : 0u;
     const bool lds_hist = kHist && width <= (uint32_t)kFilterHistBins;
     if (kHist) {
-        for (uint32_t b = threadIdx.x; b < (lds_hist ? width : 0u); b += kBlock) lds.hist[b] = 0;
+        for (uint32_t b = threadIdx.x; b < (lds_hist ? width : 0u); b += kThreads) lds.hist[b] = 0;
         __syncthreads();
     }
     const uint32_t lane = lane_id();
@@ -432,7 +462,7 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
     const uint32_t k_span = kRecords ? ((cand_hi - cand_lo) << kDigit1FromKey16) | ((1u << kDigit1FromKey16) - 1u) : 0u;
     uint32_t n_st = 0;
     uint32_t above_lane = 0;  // bits set in the mask words this lane wrote
-    constexpr uint32_t kStride = kWaves * kFilterWords;
+    constexpr uint32_t kStride = kNW * kFilterWords;
     // The next trip's keys are loaded before this trip is processed.  Every
     // load is issued, at a word of the tile (a word past its end loads the
     // tile's last word and is skipped), so the count of loads in flight is
@@ -457,7 +487,10 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
                 if (n_st > (uint32_t)(kWaveStage - 64)) {  // no room for a whole word: flush
                     uint32_t first = 0;
                     if (lane == 0) first = atomicAdd(&seg_fill[t.seg], n_st);
-                    wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
+                    if constexpr (kFullKeys)
+                        wave_store_full(stage, n_st, __shfl(first, 0, 64), G, cand, *ks, L);
+                    else
+                        wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
                     n_st = 0;
                 }
                 const bool rec = in_range && (!decltype(partial)::value || lane < left);
@@ -503,10 +536,10 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
         lds.ab[wave] = n_above;
     }
     __syncthreads();
-    if (lds_hist) hist_flush(lds.hist, hist_row + cand_lo, (int)width);
+    if (lds_hist) hist_flush(lds.hist, hist_row + cand_lo, (int)width, kThreads);
     if (threadIdx.x == 0) {
         uint32_t tot = 0, ab = 0;
-        for (int q = 0; q < kWaves; ++q) {
+        for (int q = 0; q < kNW; ++q) {
             tot += lds.n[q];
             ab += lds.ab[q];
         }
@@ -516,7 +549,10 @@ __device__ __forceinline__ void key_pass(KeyPassLds& lds, const TileDesc& t, con
     __syncthreads();
     uint32_t first = lds.base;
     for (uint32_t q = 0; q < wave; ++q) first += lds.n[q];
-    wave_store(stage, n_st, first, G, cand);
+    if constexpr (kFullKeys)
+        wave_store_full(stage, n_st, first, G, cand, *ks, L);
+    else
+        wave_store(stage, n_st, first, G, cand);
 }
 
 __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
@@ -834,24 +870,84 @@ __device__ __forceinline__ uint32_t classify(uint32_t phase, const SelState& S, 
     }
 }
 
-// Passes over the keys of the layers in kModeNoRecords, standing in for the
-// record passes: every element of the layer's exact threshold bucket d1 is
-// classified by the same rule a record of it would be (classify, plus the
-// key test that the record passes leave to compaction), with its full key
-// fetched only where its stored 16 bits equal the threshold prefix
-// (elsewhere those 16 bits decide).  Intermediate phases only histogram the
-// undecided elements; the final pass (kPhaseDone) marks every element the
-// final rule selects (keys above the bucket were set by the exact filter).
-// Run by the record pass's workgroups after their record blocks, walking the
-// tile table; normally no layer needs it (bit 1 of *miss clear).  h is the
-// workgroup's LDS histogram, free on entry; every thread must call it.
+constexpr int kKeyWordGroups = 4;  // groups of kFetch words per wave and trip in key_pass_words
+
+// One phase over the keys of words [w0, w1) of layer L in kModeNoRecords,
+// standing in for a record pass: every element of the layer's exact
+// threshold bucket d1 is classified by the same rule a record of it would be
+// (classify, plus the key test that the record passes leave to compaction),
+// with its full key fetched only where its stored 16 bits equal the
+// threshold prefix (elsewhere those 16 bits decide).  An intermediate phase
+// adds the undecided elements' digits to the LDS histogram h; the final
+// phase (kPhaseDone) marks every element the final rule selects (keys above
+// the bucket were set by the exact filter).  Every thread of the workgroup
+// (kThreads) must call it.  Each wave loads the keys of kKeyWordGroups *
+// kFetch words at once and fetches full keys for kFetch words at a time.
+template <int kThreads>
+__device__ void key_pass_words(uint32_t phase, uint32_t w0, uint32_t w1, const LayerDesc& L, const SelState& S,
+                               const uint16_t* __restrict__ key, const KeySource& ks, uint64_t* __restrict__ bits,
+                               uint32_t* h) {
+    constexpr uint32_t kW = kThreads / 64;
+    constexpr uint32_t kTrip = kKeyWordGroups * kFetch;  // words per wave and trip
+    const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
+    const bool final_pass = phase == kPhaseDone;
+    // top 16 bits of the threshold prefix decided so far
+    const uint32_t p16 = phase == kPhaseKey3   ? S.kprefix
+                         : phase == kPhaseKey4 ? S.kprefix >> kKey3Bits
+                                               : S.T >> kKeyShift;
+    const uint32_t lend = L.off + L.n;
+    for (uint32_t wb = w0 + wave * kTrip; wb < w1; wb += kW * kTrip) {
+        // all of the trip's key loads first (a word past the range or a key
+        // past the layer loads the layer's first key and is skipped)
+        uint32_t kv16[kTrip];
+#pragma unroll
+        for (uint32_t u = 0; u < kTrip; ++u) {
+            const uint32_t j = (wb + u) * 64u + lane;
+            kv16[u] = key[(wb + u < w1 && j < lend) ? j : L.off];
+        }
+#pragma unroll
+        for (uint32_t g = 0; g < kTrip; g += kFetch) {
+            uint64_t rec[kFetch];
+            bool cand[kFetch];
+            uint32_t sel = 0;  // bit u: word g + u needs its full key
+#pragma unroll
+            for (uint32_t u = 0; u < kFetch; ++u) {
+                const uint32_t j = (wb + g + u) * 64u + lane;
+                cand[u] = wb + g + u < w1 && j < lend && (kv16[g + u] >> kDigit1FromKey16) == S.d1;
+                if (cand[u] && phase != kPhaseKey2 && kv16[g + u] == p16) sel |= 1u << u;
+                rec[u] = ((uint64_t)(kv16[g + u] << kKeyShift) << 32) | (uint64_t)(cand[u] ? j - L.off : 0u);
+            }
+            if (wave_ballot(sel != 0u)) candidate_keys(ks, L, rec, sel);
+#pragma unroll
+            for (uint32_t u = 0; u < kFetch; ++u) {
+                const uint32_t j = (wb + g + u) * 64u + lane;
+                const uint32_t kv = (uint32_t)(rec[u] >> 32);
+                uint32_t digit = 0;
+                uint32_t c = cand[u] ? classify(phase, S, kv, j - L.off, &digit) : 0u;
+                // the rules of the later position digits assume the set they
+                // split holds only keys equal to T, as a layer's records do by
+                // then; here every element of the bucket is seen again
+                if ((phase == kPhasePos2 || phase == kPhasePos3) && cand[u] && kv != S.T) c = kv > S.T ? 1u : 0u;
+                if (final_pass) {
+                    if (c == 1u) atomicOr((unsigned long long*)&bits[j >> 6], 1ull << (j & 63u));
+                } else {
+                    if (phase == kPhaseKey3) digit = (kv >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
+                    hist_add_wave(h, digit, c == 2u);
+                }
+            }
+        }
+    }
+}
+
+// The key passes of the layers in kModeNoRecords, run by the record pass's
+// workgroups after their record blocks, walking the tile table; normally no
+// layer needs them (bit 1 of *miss clear).  h is the workgroup's LDS
+// histogram, free on entry; every thread must call it.
 template <int kThreads>
 __device__ void key_passes(uint32_t phase, const TileDesc* __restrict__ tiles, uint32_t n_tiles,
                            const LayerDesc* __restrict__ layers, const SelState* __restrict__ st,
                            const uint16_t* __restrict__ key, const KeySource& ks, uint32_t* __restrict__ hist,
                            uint64_t* __restrict__ bits, uint32_t* h) {
-    constexpr uint32_t kW = kThreads / 64;
-    const uint32_t lane = lane_id();
     const bool final_pass = phase == kPhaseDone;
     const int nb = final_pass ? 0 : phase_bins(phase);
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
@@ -862,33 +958,7 @@ __device__ void key_passes(uint32_t phase, const TileDesc* __restrict__ tiles, u
         const LayerDesc L = layers[t.layer];
         for (int b = threadIdx.x; b < nb; b += kThreads) h[b] = 0;
         __syncthreads();
-        // top 16 bits of the threshold prefix decided so far
-        const uint32_t p16 = phase == kPhaseKey3   ? S.kprefix
-                             : phase == kPhaseKey4 ? S.kprefix >> kKey3Bits
-                                                   : S.T >> kKeyShift;
-        const uint32_t lend = L.off + L.n;
-        for (uint32_t w = t.w0 + threadIdx.x / 64; w < t.w1; w += kW) {
-            const uint32_t j = w * 64u + lane;
-            const bool inl = j < lend;
-            const uint32_t kv16 = key[inl ? j : L.off];
-            const bool cand = inl && (kv16 >> kDigit1FromKey16) == S.d1;
-            const bool need = cand && phase != kPhaseKey2 && kv16 == p16;
-            uint64_t rec[kFetch] = {(uint64_t)(kv16 << kKeyShift) << 32 | (j - L.off), 0, 0, 0};
-            if (wave_ballot(need)) candidate_keys(ks, L, rec, need ? 1u : 0u);
-            const uint32_t kv = (uint32_t)(rec[0] >> 32);
-            uint32_t digit = 0;
-            uint32_t c = cand ? classify(phase, S, kv, j - L.off, &digit) : 0u;
-            // the rules of the later position digits assume the set they split
-            // holds only keys equal to T, as a layer's records do by then;
-            // here every element of the bucket is seen again
-            if ((phase == kPhasePos2 || phase == kPhasePos3) && cand && kv != S.T) c = kv > S.T ? 1u : 0u;
-            if (final_pass) {
-                if (c == 1u) atomicOr((unsigned long long*)&bits[j >> 6], 1ull << (j & 63u));
-            } else {
-                if (phase == kPhaseKey3) digit = (kv >> kKey4Bits) & ((1u << kKey3Bits) - 1u);
-                hist_add_wave(h, digit, c == 2u);
-            }
-        }
+        key_pass_words<kThreads>(phase, t.w0, t.w1, L, S, key, ks, bits, h);
         __syncthreads();
         if (!final_pass) hist_flush(h, hist + (size_t)t.layer * kHistBins, nb, kThreads);
         __syncthreads();
@@ -1045,27 +1115,13 @@ hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb,
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kBlock) void k_select_next(uint32_t phase, int32_t layer0, uint32_t* __restrict__ hist,
-                                                        SelState* __restrict__ st) {
-    __shared__ uint32_t scratch[kWaves];
-    __shared__ uint32_t s_bucket, s_before, s_count;
-    const int l = layer0 + blockIdx.x;
-    SelState S = st[l];
-    if (S.phase != phase) return;  // uniform
-    const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3 || phase == kPhaseKey4;
-    find_bucket(hist + (size_t)l * kHistBins, phase_bins(phase), desc, S.need, &s_bucket, &s_before, &s_count,
-                scratch);
-    if (threadIdx.x != 0) return;
-    if (s_bucket == kNone) {  // inconsistent counts: select no candidate rather than guess
-        S.phase = kPhaseDone;
-        S.T = 0xFFFFFFFFu;
-        S.J = 0;
-        st[l] = S;
-        return;
-    }
-    const uint32_t b = s_bucket;
-    const uint32_t need = S.need - s_before;
-    const bool exact = need == s_count;  // the whole bucket is kept
+// The state of a layer after the bucket search of `phase` found bucket b,
+// with `before` undecided keys ahead of it in scan order and `count` in it:
+// the next digit to resolve, or the final rule once the bucket is taken
+// whole or the last digit is known.
+__device__ __forceinline__ void advance(SelState& S, uint32_t phase, uint32_t b, uint32_t before, uint32_t count) {
+    const uint32_t need = S.need - before;
+    const bool exact = need == count;  // the whole bucket is kept
     S.need = need;
     switch (phase) {
         case kPhaseKey2:
@@ -1098,6 +1154,27 @@ __global__ __launch_bounds__(kBlock) void k_select_next(uint32_t phase, int32_t 
             S.phase = kPhaseDone;
             break;
     }
+}
+
+__global__ __launch_bounds__(kBlock) void k_select_next(uint32_t phase, int32_t layer0, uint32_t* __restrict__ hist,
+                                                        SelState* __restrict__ st) {
+    __shared__ uint32_t scratch[kWaves];
+    __shared__ uint32_t s_bucket, s_before, s_count;
+    const int l = layer0 + blockIdx.x;
+    SelState S = st[l];
+    if (S.phase != phase) return;  // uniform
+    const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3 || phase == kPhaseKey4;
+    find_bucket(hist + (size_t)l * kHistBins, phase_bins(phase), desc, S.need, &s_bucket, &s_before, &s_count,
+                scratch);
+    if (threadIdx.x != 0) return;
+    if (s_bucket == kNone) {  // inconsistent counts: select no candidate rather than guess
+        S.phase = kPhaseDone;
+        S.T = 0xFFFFFFFFu;
+        S.J = 0;
+        st[l] = S;
+        return;
+    }
+    advance(S, phase, s_bucket, s_before, s_count);
     st[l] = S;
 }
 
@@ -1105,6 +1182,380 @@ hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int
                               SelState* st) {
     if (n_layers <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_select_next, dim3(n_layers), dim3(kBlock), 0, s, phase, layer0, hist, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 5. the compact path
+//
+// Where every layer of a range is small, the passes above cost more in
+// launches than in work (a step over one 1024x1024 layer ran some 25 short
+// kernels back to back).  The compact path makes the same mask in two
+// launches, each tile split over `parts` workgroups:
+//  - k_compact_hist histograms the first digit of every key of the range;
+//    the workgroup that finishes a layer last (a ticket per layer, drawn
+//    after a device-scope fence) finds the layer's exact threshold bucket d1
+//    from the full row;
+//  - k_compact_filter turns keys above d1 into mask bits and keys in it into
+//    records, reserved on one counter per layer in the layer's whole record
+//    space; the layer's last workgroup then resolves every remaining digit
+//    alone - LDS histogram, bucket search, compaction in place - and marks
+//    what the final rule selects.  A layer whose bucket did not fit its
+//    record space is resolved the same way from its keys (bit 1 of *miss).
+// Each ticket is put back to zero by the workgroup that draws its last
+// number.
+
+constexpr int kCompactBlock = 1024;  // threads of the filtering and finishing workgroups
+constexpr int kCompactWaves = kCompactBlock / 64;
+constexpr int kFinRecs = 8;          // records per thread per chunk in the finishing workgroup
+
+// Tiles of a layer: its words cut every kTileWords from its first word.
+__device__ __forceinline__ uint32_t layer_tiles(const LayerDesc& L) {
+    return ((L.n + 63u) / 64u + kTileWords - 1u) / kTileWords;
+}
+
+// Part p of `parts` of tile t: words [*w0, *w1) (possibly empty).
+__device__ __forceinline__ void tile_part(const TileDesc& t, uint32_t parts, uint32_t p, uint32_t* w0,
+                                          uint32_t* w1) {
+    const uint32_t span = (t.w1 - t.w0 + parts - 1u) / parts;
+    *w0 = min(t.w0 + p * span, t.w1);
+    *w1 = min(*w0 + span, t.w1);
+}
+
+// Draw this workgroup's ticket for `layer` after its writes; true (in every
+// thread) for the workgroup that completes the layer's `n` tickets, which
+// may then read every other workgroup's writes to global memory.  Each wave
+// first waits for its own stores and atomics, so that the one release (the
+// ticket, drawn by thread 0 after a write-back of its L2) covers the whole
+// workgroup.  In the last workgroup every wave then acquires for itself
+// (invalidating the caches it reads through): an invalidation issued by
+// another wave is not known to be complete when the barrier lets this one
+// load.
+template <int kThreads>
+__device__ __forceinline__ bool last_of_layer(uint32_t* ticket, int layer, uint32_t n, uint32_t* s_flag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&ticket[layer], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == n - 1u;
+        if (last) ticket[layer] = 0u;  // every other ticket is drawn: reset for the next pass
+        *s_flag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0u;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return last;
+}
+
+constexpr int kCompactHistBatch = 4;  // 16-byte key loads in flight per thread
+
+__global__ __launch_bounds__(kCompactBlock) void k_compact_hist(const TileDesc* __restrict__ tiles, uint32_t parts,
+                                                         const LayerDesc* __restrict__ layers,
+                                                         const uint16_t* __restrict__ key,
+                                                         uint32_t* __restrict__ hist, SelState* __restrict__ st,
+                                                         uint32_t* __restrict__ ticket,
+                                                         uint32_t* __restrict__ lrec,
+                                                         uint32_t* __restrict__ labove,
+                                                         uint32_t* __restrict__ miss) {
+    __shared__ __align__(16) uint32_t h[kDigit1Bins];
+    __shared__ uint32_t scratch[kCompactWaves];
+    __shared__ uint32_t s_flag, s_bucket, s_before, s_count;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *miss = 0;
+    const TileDesc t = tiles[blockIdx.x];
+    const LayerDesc L = layers[t.layer];
+    uint32_t w0, w1;
+    tile_part(t, parts, blockIdx.y, &w0, &w1);
+    if (L.k > 0) {  // uniform
+        for (int b = threadIdx.x; b < kDigit1Bins; b += kCompactBlock) h[b] = 0;
+        __syncthreads();
+        const uint32_t lend = L.off + L.n;
+        // 16-byte chunks (8 keys) of the part, kCompactHistBatch per thread in
+        // flight; a chunk past the part or the layer loads the part's first
+        const uint32_t nch = (w1 - w0) * 8u;
+        for (uint32_t c0 = 0; c0 < nch; c0 += kCompactHistBatch * kCompactBlock) {
+            u32x4 v[kCompactHistBatch];
+            uint32_t kc[kCompactHistBatch];
+#pragma unroll
+            for (int i = 0; i < kCompactHistBatch; ++i) {
+                const uint32_t c = c0 + i * kCompactBlock + threadIdx.x;
+                const uint32_t e = w0 * 64u + 8u * c;
+                kc[i] = (c < nch && e < lend) ? min(lend - e, 8u) : 0u;
+                v[i] = *reinterpret_cast<const u32x4*>(key + (kc[i] ? e : w0 * 64u));
+            }
+#pragma unroll
+            for (int i = 0; i < kCompactHistBatch; ++i) hist_add8(h, v[i], kc[i]);
+        }
+        __syncthreads();
+        hist_flush(h, hist + (size_t)t.layer * kHistBins, kDigit1Bins, kCompactBlock);
+    }
+    if (!last_of_layer<kCompactBlock>(ticket, t.layer, layer_tiles(L) * parts, &s_flag)) return;
+    // the exact threshold bucket from the layer's full row, searched in LDS
+    // (the row is left zeroed)
+    {
+        u32x4* row = reinterpret_cast<u32x4*>(hist + (size_t)t.layer * kHistBins);
+        constexpr int kVec = kDigit1Bins / 4 / kCompactBlock;
+        u32x4 v[kVec];
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) v[i] = row[threadIdx.x + i * kCompactBlock];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+            reinterpret_cast<u32x4*>(h)[threadIdx.x + i * kCompactBlock] = v[i];
+            row[threadIdx.x + i * kCompactBlock] = z;
+        }
+        __syncthreads();
+    }
+    find_bucket<kCompactBlock>(h, kDigit1Bins, true, L.k, &s_bucket, &s_before, &s_count, scratch);
+    if (threadIdx.x != 0) return;
+    SelState S{};
+    S.n_lo = 1;
+    S.n_hi = 0;
+    S.mode = kModeReclassify;
+    if (L.k == 0 || s_bucket == kNone) {  // nothing to select (a full row always holds the k-th key)
+        S.none = 1;
+        S.phase = kPhaseDone;
+        S.J = 0xFFFFFFFFu;
+    } else {
+        init_found(S, L.k, s_bucket, s_before, s_count);
+    }
+    st[t.layer] = S;
+    lrec[t.layer] = 0u;
+    labove[t.layer] = 0u;
+}
+
+hipError_t launch_compact_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
+                               const LayerDesc* layers, const uint16_t* key, uint32_t* hist, SelState* st,
+                               uint32_t* ticket, uint32_t* lrec, uint32_t* labove, uint32_t* miss) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_compact_hist, dim3(n_tiles, parts), dim3(kCompactBlock), 0, s, tiles, parts, layers, key, hist, st,
+                       ticket, lrec, labove, miss);
+    return hipGetLastError();
+}
+
+// LDS of the finishing workgroup: its histogram and state, and the records
+// once at most kFinLdsRecs remain.  It shares the key pass's LDS, which is
+// free by then.
+constexpr uint32_t kFinLdsRecs = 3072;
+constexpr int kFinDigitBits = kKey2Bits + kKey3Bits;  // 12: key bits 17..6 in one digit
+constexpr int kFinBins = 1 << kFinDigitBits;
+static_assert(kFinBins >= kPassBins, "the finishing histogram holds every digit");
+struct FinishLds {
+    uint64_t rec[kFinLdsRecs];
+    uint32_t h[kFinBins];
+    uint32_t scratch[kCompactWaves];
+    uint32_t wsum[kCompactWaves];
+    uint32_t bucket, before, count;
+    SelState S;
+};
+union CompactLds {
+    KeyPassLdsT<kCompactWaves> pass;
+    FinishLds fin;
+};
+
+// The bucket search closing `phase` of layer L, finished by one workgroup:
+// the layer's next state in f.S.  With `merged`, the phase of key bits
+// 17..15 took bits 17..6 as one 12-bit digit (records with full keys): its
+// bucket fixes both digits at once, as the two searches would have.  In a
+// layer of at most 2^20 elements every position's bits 30..20 are zero, so
+// that digit's search is skipped (its bucket would be 0, never taken whole).
+__device__ __forceinline__ void finish_select(FinishLds& f, uint32_t phase, const LayerDesc& L, bool merged) {
+    const bool wide = merged && phase == kPhaseKey2;
+    const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3 || phase == kPhaseKey4;
+    find_bucket<kCompactBlock>(f.h, wide ? kFinBins : phase_bins(phase), desc, f.S.need, &f.bucket, &f.before,
+                               &f.count, f.scratch);
+    if (threadIdx.x == 0) {
+        SelState S = f.S;
+        if (f.bucket == kNone) {  // inconsistent counts: select no candidate rather than guess
+            S.phase = kPhaseDone;
+            S.T = 0xFFFFFFFFu;
+            S.J = 0;
+        } else if (wide) {
+            S.need -= f.before;
+            S.kprefix = (S.kprefix << kFinDigitBits) | f.bucket;
+            if (S.need == f.count) {  // the whole bucket is kept
+                S.T = S.kprefix << kKey4Bits;
+                S.J = 0xFFFFFFFFu;
+                S.phase = kPhaseDone;
+            } else {
+                S.phase = kPhaseKey4;
+            }
+        } else {
+            advance(S, phase, f.bucket, f.before, f.count);
+        }
+        if (S.phase == kPhasePos1 && L.n <= (1u << 20)) {
+            S.jprefix = 0;
+            S.phase = kPhasePos2;
+        }
+        f.S = S;
+    }
+    __syncthreads();
+}
+
+// Every remaining digit of layer L from its `cnt` records at grec (the
+// filter's: the layer's exact threshold bucket, with full keys), by one
+// workgroup: each phase classifies the records left by the previous one,
+// marks those its decided prefix selects, histograms and compacts the
+// undecided rest, and fixes its digit; the final rule then marks what
+// remains selected.  The phases and rules are those of the record passes.
+// The first phase keeps every record (all are in the bucket d1), so it only
+// counts.  The records a phase keeps are those of the bucket the previous
+// search chose, whose count that search returned: they go to LDS from the
+// first phase that keeps at most kFinLdsRecs, else they are compacted in
+// place.
+__device__ void finish_records(FinishLds& f, const LayerDesc& L, uint64_t* __restrict__ grec, uint32_t cnt,
+                               uint64_t* __restrict__ bits) {
+    const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
+    bool in_lds = false;
+    uint32_t keep = cnt;  // records the next pass keeps
+    for (;;) {
+        const SelState S = f.S;
+        const uint32_t phase = S.phase;
+        const bool final_pass = phase == kPhaseDone;
+        const bool count_only = phase == kPhaseKey2;
+        // where this phase's kept records go: LDS once they are few enough
+        const bool to_lds = in_lds || keep <= kFinLdsRecs;
+        const uint64_t* src = in_lds ? f.rec : grec;
+        uint64_t* dst = to_lds ? f.rec : grec;
+        uint32_t out = 0;  // records kept so far (uniform)
+        for (uint32_t c0 = 0; c0 < cnt; c0 += kCompactBlock * kFinRecs) {
+            // every load at a slot clamped to the last record, all in flight together
+            uint64_t r[kFinRecs];
+#pragma unroll
+            for (int i = 0; i < kFinRecs; ++i) {
+                const uint32_t p = c0 + threadIdx.x + i * kCompactBlock;
+                r[i] = src[p < cnt ? p : cnt - 1u];
+            }
+            uint32_t und = 0;  // bit i: record i undecided
+#pragma unroll
+            for (int i = 0; i < kFinRecs; ++i) {
+                const uint32_t p = c0 + threadIdx.x + i * kCompactBlock;
+                const uint32_t kv = (uint32_t)(r[i] >> 32), jl = (uint32_t)r[i];
+                uint32_t digit = 0;
+                uint32_t c = p < cnt ? classify(phase, S, kv, jl, &digit) : 0u;
+                // the later position digits' rules assume that only keys equal
+                // to T remain, which the pass over position bits 30..20 leaves;
+                // where that pass was skipped, the key decides the others here
+                if ((phase == kPhasePos2 || phase == kPhasePos3) && p < cnt && kv != S.T) c = kv > S.T ? 1u : 0u;
+                if (c == 1u && jl < L.n) {
+                    const uint32_t jj = L.off + jl;
+                    atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
+                }
+                // the records hold full keys: one digit of key bits 17..6
+                if (phase == kPhaseKey2) digit = (kv >> kKey4Bits) & ((1u << kFinDigitBits) - 1u);
+                if (!final_pass) hist_add_wave(f.h, digit, c == 2u);
+                if (c == 2u) und |= 1u << i;
+            }
+            if (final_pass || count_only) continue;
+            // compaction: the chunk is in registers once the barrier is
+            // passed, and the kept records land below its end (or in LDS)
+            uint32_t ws = 0;
+#pragma unroll
+            for (int i = 0; i < kFinRecs; ++i) ws += (uint32_t)__popcll(wave_ballot((und >> i) & 1u));
+            if (lane == 0) f.wsum[wave] = ws;
+            __syncthreads();
+            uint32_t base = out, total = 0;
+            for (uint32_t q = 0; q < (uint32_t)kCompactWaves; ++q) {
+                if (q < wave) base += f.wsum[q];
+                total += f.wsum[q];
+            }
+#pragma unroll
+            for (int i = 0; i < kFinRecs; ++i) {
+                const bool u = (und >> i) & 1u;
+                const uint64_t bm = wave_ballot(u);
+                const uint32_t slot = base + lanes_below(bm);
+                if (u && (!to_lds || slot < kFinLdsRecs)) dst[slot] = r[i];  // (the count fits by construction)
+                base += (uint32_t)__popcll(bm);
+            }
+            out += total;
+            __syncthreads();
+        }
+        if (final_pass) return;
+        if (!count_only) {
+            cnt = out;
+            in_lds = to_lds;
+        }
+        __syncthreads();  // every wave's counts are in the histogram
+        finish_select(f, phase, L, true);
+        keep = f.count;
+    }
+}
+
+// The same from the layer's keys, for a layer whose threshold bucket did not
+// fit its record space: each phase reads every key of the layer.
+__device__ void finish_keys(FinishLds& f, const LayerDesc& L, const uint16_t* __restrict__ key,
+                            const KeySource& ks, uint64_t* __restrict__ bits) {
+    const uint32_t w0 = L.off / 64u, w1 = (L.off + L.n + 63u) / 64u;
+    for (;;) {
+        const SelState S = f.S;
+        const uint32_t phase = S.phase;
+        key_pass_words<kCompactBlock>(phase, w0, w1, L, S, key, ks, bits, f.h);
+        if (phase == kPhaseDone) return;
+        __syncthreads();
+        finish_select(f, phase, L, false);
+    }
+}
+
+__global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc* __restrict__ tiles, uint32_t parts,
+                                                                  const LayerDesc* __restrict__ layers,
+                                                                  const SegDesc* __restrict__ lspace,
+                                                                  SelState* __restrict__ st,
+                                                                  const uint16_t* __restrict__ key, KeySource ks,
+                                                                  uint64_t* __restrict__ bits,
+                                                                  uint64_t* __restrict__ cand,
+                                                                  uint32_t* __restrict__ ticket,
+                                                                  uint32_t* __restrict__ lrec,
+                                                                  uint32_t* __restrict__ labove,
+                                                                  uint32_t* __restrict__ miss) {
+    __shared__ CompactLds lds;
+    __shared__ uint32_t s_flag;
+    TileDesc t = tiles[blockIdx.x];
+    const int l = t.layer;
+    const LayerDesc L = layers[l];
+    const SegDesc G = lspace[l];
+    const SelState S = st[l];
+    uint32_t w0, w1;
+    tile_part(t, parts, blockIdx.y, &w0, &w1);
+    t.w0 = w0;
+    t.w1 = w1;
+    t.seg = (uint32_t)l;  // the layer's own record counter
+    if (w0 < w1) {        // uniform
+        if (S.none)       // nothing selected: zero words
+            key_pass<false, false, kCompactBlock>(lds.pass, t, L, G, (uint32_t)kDigit1Bins, 1u, 0u, key, bits, lrec,
+                                                  cand, labove);
+        else if (S.all_bucket)  // the threshold bucket and above, no records
+            key_pass<false, false, kCompactBlock>(lds.pass, t, L, G, S.d1, 1u, 0u, key, bits, lrec, cand, labove);
+        else  // above the bucket: bits; in it: records with their full keys
+            key_pass<true, false, kCompactBlock, true>(lds.pass, t, L, G, S.d1 + 1u, S.d1, S.d1, key, bits, lrec,
+                                                       cand, labove, nullptr, &ks);
+    }
+    if (!last_of_layer<kCompactBlock>(ticket, l, layer_tiles(L) * parts, &s_flag)) return;
+    if (S.none || S.phase == kPhaseDone) return;  // the filter wrote the whole mask of the layer
+    FinishLds& f = lds.fin;
+    const uint32_t fill = lrec[l];
+    for (int b = threadIdx.x; b < kFinBins; b += kCompactBlock) f.h[b] = 0;
+    if (threadIdx.x == 0) {
+        f.S = S;
+        if (fill > G.size) {
+            f.S.mode = kModeNoRecords;
+            atomicOr(miss, 2u);
+        }
+    }
+    __syncthreads();
+    if (fill > G.size)
+        finish_keys(f, L, key, ks, bits);
+    else
+        finish_records(f, L, cand + G.base, fill, bits);
+    __syncthreads();
+    if (threadIdx.x == 0) st[l] = f.S;
+}
+
+hipError_t launch_compact_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
+                                 const LayerDesc* layers, const SegDesc* lspace, SelState* st, const uint16_t* key,
+                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, uint32_t* ticket, uint32_t* lrec,
+                                 uint32_t* labove, uint32_t* miss) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_compact_filter, dim3(n_tiles, parts), dim3(kCompactBlock), 0, s, tiles, parts, layers, lspace,
+                       st, key, ks, bits, cand, ticket, lrec, labove, miss);
     return hipGetLastError();
 }
 

@@ -165,6 +165,11 @@ struct scape_ctx {
     uint32_t* d_counts = nullptr;     // per layer: sampled keys
     uint32_t* d_ovf = nullptr;        // per layer: records lost to the record space in the key filter
     float* d_m_stash = nullptr;       // m at the current mask's positions, compacted (k_total)
+    // the compact selection path: per layer its whole record space, and
+    // [ticket | record count | bit count] rows of L counters
+    SegDesc* d_lspace = nullptr;
+    uint32_t* d_lcount = nullptr;
+    int32_t select_path = SCAPE_SELECT_PATH_AUTO;
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -193,6 +198,8 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_hist);
     hipFree(c->d_sel);
     hipFree(c->d_segs);
+    hipFree(c->d_lspace);
+    hipFree(c->d_lcount);
     hipFree(c->d_layer_seg0);
     hipFree(c->d_seg_fill);
     hipFree(c->d_seg_above);
@@ -292,8 +299,45 @@ int prof_begin(scape_ctx* c) {
 // and the source of candidates' full keys, bits into `bits`.
 // `fork`, when given, is recorded on `s` once the key filter is queued (at
 // once if there is nothing to select): the step's update starts there.
+// Whether the layers [la, la + nl) take the compact path: each of them at
+// most kCompactMaxLayer elements, unless the caller chose a path.
+bool compact_range(const scape_ctx* c, int32_t la, int32_t nl) {
+    if (c->select_path != SCAPE_SELECT_PATH_AUTO) return c->select_path == SCAPE_SELECT_PATH_COMPACT;
+    for (int32_t l = la; l < la + nl; ++l)
+        if (c->lay.n[l] > kCompactMaxLayer) return false;
+    return true;
+}
+
+// The compact path: two launches.  The update only waits for the dense pass,
+// so its fork is recorded first.
+int run_select_compact(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
+                       const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork) {
+    (void)la;
+    (void)nl;
+    if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
+    const uint32_t nt = tb - ta;
+    if (nt == 0) return SCAPE_OK;  // only empty layers: no bits to set
+    const TileDesc* tiles = c->d_tiles + ta;
+    const uint32_t L = (uint32_t)c->lay.L;
+    uint32_t* ticket = c->d_lcount;
+    uint32_t* lrec = c->d_lcount + L;
+    uint32_t* labove = c->d_lcount + 2 * (size_t)L;
+    // split the tiles until the launches have about kCompactBlocks workgroups
+    auto parts_for = [&](uint32_t target, uint32_t most) {
+        return std::max<uint32_t>(1u, std::min<uint32_t>(most, (target + nt - 1) / nt));
+    };
+    SCAPE_HIP(launch_compact_hist(s, tiles, nt, parts_for(kCompactHistBlocks, kCompactHistParts), c->d_layers, key,
+                                  c->d_hist, c->d_sel, ticket, lrec, labove, c->d_miss),
+              "compact_hist");
+    SCAPE_HIP(launch_compact_filter(s, tiles, nt, parts_for(kCompactFilterBlocks, kCompactFilterParts), c->d_layers,
+                                    c->d_lspace, c->d_sel, key, ks, bits, c->d_cand, ticket, lrec, labove, c->d_miss),
+              "compact_filter");
+    return SCAPE_OK;
+}
+
 int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
                const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork = nullptr) {
+    if (compact_range(c, la, nl)) return run_select_compact(c, la, nl, ta, tb, key, ks, bits, s, fork);
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
     const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
@@ -348,6 +392,12 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
 }
 
 int run_index(scape_ctx* c, const scape_mask* mk, hipStream_t s) {
+    if (c->n_words > 0 && c->n_words <= kIndexSmallMaxWords) {
+        SCAPE_HIP(launch_index_small(s, mk->bits, c->n_words, c->d_block_sums, mk->idx, (uint32_t)c->lay.k_total,
+                                     mk->block_prefix),
+                  "index_small");
+        return SCAPE_OK;
+    }
     SCAPE_HIP(launch_index_count(s, mk->bits, c->n_words, c->d_block_sums), "index_count");
     SCAPE_HIP(launch_index_scan(s, c->d_block_sums, c->n_index_blocks), "index_scan");
     SCAPE_HIP(launch_index_emit(s, mk->bits, c->n_words, c->d_block_sums, mk->idx, (uint32_t)c->lay.k_total,
@@ -684,6 +734,18 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     }
     c->layer_seg0[c->lay.L] = (uint32_t)c->segs.size();
     const size_t n_segs = c->segs.size();
+    // a layer's segments are consecutive in the record buffer: together they
+    // are its whole record space
+    std::vector<SegDesc> lspace(c->lay.L);
+    for (int32_t l = 0; l < c->lay.L; ++l) {
+        SegDesc g{};
+        g.layer = l;
+        for (uint32_t q = c->layer_seg0[l]; q < c->layer_seg0[l + 1]; ++q) {
+            if (q == c->layer_seg0[l]) g.base = c->segs[q].base;
+            g.size += c->segs[q].size;
+        }
+        lspace[l] = g;
+    }
     c->cand_cap = (uint32_t)rec_total;
     // a segment of s records makes ceil(s / kCandChunk) blocks
     c->vb_cap = (size_t)(rec_total / kCandChunk) + n_segs + 1;
@@ -710,12 +772,16 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(c, &c->d_layer_seg0, L + 1, "layer segment table")) ||
         (rc = dev_alloc(c, &c->d_seg_fill, n_segs, "segment record counters")) ||
         (rc = dev_alloc(c, &c->d_seg_above, n_segs, "segment bit counters")) ||
+        (rc = dev_alloc(c, &c->d_lspace, L, "layer record spaces")) ||
+        (rc = dev_alloc(c, &c->d_lcount, 3 * L, "layer counters")) ||
         (rc = dev_alloc(c, &c->d_vb, c->vb_cap, "record blocks")) ||
         (rc = dev_alloc(c, &c->d_vb_count, c->vb_cap, "record block counts")) ||
         (rc = dev_alloc(c, &c->d_totals, 4, "totals")) || (rc = dev_alloc(c, &c->d_miss, 1, "miss flag")) ||
         (rc = dev_alloc(c, &c->d_cand, (size_t)c->cand_cap, "candidate records")) ||
         (rc = dev_alloc(c, &c->d_key16, (size_t)c->lay.n_pad, "statistic keys")) ||
-        (rc = dev_alloc(c, &c->d_block_sums, (size_t)c->n_index_blocks + 2, "index partial sums")) ||
+        (rc = dev_alloc(c, &c->d_block_sums,
+                        std::max<size_t>((size_t)c->n_index_blocks + 2, ((size_t)c->n_words + kBlock - 1) / kBlock),
+                        "index partial sums")) ||
         (rc = dev_alloc(c, &c->d_word_info, (size_t)c->n_words, "word descriptors")) ||
         (rc = dev_alloc(c, &c->d_counts, L, "per-layer counters")) ||
         (rc = dev_alloc(c, &c->d_ovf, L, "per-layer record overflow flags")) ||
@@ -737,6 +803,8 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         e = hipMemcpy(c->d_tiles, c->tiles.data(), c->tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess && n_segs)
         e = hipMemcpy(c->d_segs, c->segs.data(), n_segs * sizeof(SegDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(c->d_lspace, lspace.data(), L * sizeof(SegDesc), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(c->d_lcount, 0, 3 * L * sizeof(uint32_t));
     if (e == hipSuccess)
         e = hipMemcpy(c->d_layer_seg0, c->layer_seg0.data(), (L + 1) * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess && c->n_words)
@@ -750,6 +818,14 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         return hip_fail(e, "uploading context tables");
     }
     *out = c;
+    return SCAPE_OK;
+}
+
+int scape_set_select_path(scape_ctx* ctx, int32_t path) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (path != SCAPE_SELECT_PATH_AUTO && path != SCAPE_SELECT_PATH_SAMPLED && path != SCAPE_SELECT_PATH_COMPACT)
+        return fail(SCAPE_ERR_INVALID_ARG, "unknown selection path %d", path);
+    ctx->select_path = path;
     return SCAPE_OK;
 }
 

@@ -54,9 +54,11 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// Exclusive scan over a workgroup of kBlock threads.  `scratch` holds kWaves
-// entries of LDS.  Every thread of the block must call it.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+// Exclusive scan over a workgroup of kThreads threads.  `scratch` holds
+// kThreads / 64 entries of LDS.  Every thread of the block must call it.
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_exclusive_scan_t(uint32_t v, uint32_t* scratch, uint32_t* total) {
+    constexpr int kNW = kThreads / 64;
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
     uint32_t inc = wave_inclusive_scan(v);
@@ -64,7 +66,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kNW; ++w) {
         uint32_t s = scratch[w];
         if ((uint32_t)w < wave) off += s;
         tot += s;
@@ -72,6 +74,10 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     __syncthreads();
     if (total) *total = tot;
     return off + inc - v;
+}
+
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+    return block_exclusive_scan_t<kBlock>(v, scratch, total);
 }
 
 // Add one count per active lane with `take` set to lds_hist[bin].  When every

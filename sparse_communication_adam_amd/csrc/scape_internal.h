@@ -33,11 +33,21 @@ constexpr int kKey3Bits = 9;                                // bits 14..6
 constexpr int kKey4Bits = kKeyShift - kKey3Bits;            // 6: bits 5..0
 constexpr int kHistBins = kDigit1Bins;          // histogram row per layer (>= every digit's bins)
 constexpr int kIndexWordsPerBlock = 2048;  // words per workgroup in the index passes
+constexpr uint32_t kIndexSmallMaxWords = (uint32_t)kBlock * kBlock;  // masks indexed in two launches
 // Largest word count of the context-free index (every layout the ABI takes:
 // n_pad < 2^31 elements), and the entries of its static partial-sum array
 // (one per index workgroup, plus the total).
 constexpr int64_t kIndexStaticMaxWords = int64_t(1) << 25;
 constexpr int kIndexScratchEntries = (int)(kIndexStaticMaxWords / kIndexWordsPerBlock) + 2;
+// The compact selection path takes a range whose layers all hold at most
+// kCompactMaxLayer elements (one workgroup finishes each layer); its two
+// launches split tiles until they have about kCompact*Blocks workgroups.
+#ifndef SCAPE_COMPACT_MAX_LAYER
+#define SCAPE_COMPACT_MAX_LAYER (1 << 22)
+#endif
+constexpr int64_t kCompactMaxLayer = SCAPE_COMPACT_MAX_LAYER;
+constexpr uint32_t kCompactHistBlocks = 128, kCompactHistParts = 4;
+constexpr uint32_t kCompactFilterBlocks = 256, kCompactFilterParts = 4;
 constexpr int kCandChunk = 8192;        // candidate records per virtual block
 constexpr int kSegTiles = 16;           // tiles per record segment
 
@@ -202,11 +212,29 @@ hipError_t launch_cand_pass(hipStream_t s, uint32_t phase, const VblockDesc* vb,
 hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int32_t n_layers, uint32_t* hist,
                               SelState* st);
 
+// The compact path (every layer of the range small): tiles split over
+// `parts` workgroups each.  Per layer: lspace[l] its whole record space,
+// ticket[l] the workgroups' ticket counter (zero between launches), lrec[l]
+// and labove[l] its record and bit counters.  k_compact_hist leaves every
+// layer of the range with its exact threshold bucket in st; k_compact_filter
+// writes the layers' mask words and finishes them.
+hipError_t launch_compact_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
+                               const LayerDesc* layers, const uint16_t* key, uint32_t* hist, SelState* st,
+                               uint32_t* ticket, uint32_t* lrec, uint32_t* labove, uint32_t* miss);
+hipError_t launch_compact_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
+                                 const LayerDesc* layers, const SegDesc* lspace, SelState* st, const uint16_t* key,
+                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, uint32_t* ticket, uint32_t* lrec,
+                                 uint32_t* labove, uint32_t* miss);
+
 // bits
 hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);
 hipError_t launch_index_scan(hipStream_t s, uint32_t* block_sums, uint32_t n_blocks);
 hipError_t launch_index_emit(hipStream_t s, const uint64_t* bits, uint32_t n_words, const uint32_t* block_offs,
                              uint32_t* idx, uint32_t k_cap, uint32_t* prefix);
+// Both index launches for a mask of at most kIndexSmallMaxWords words
+// (block_sums: one entry per kBlock words).
+hipError_t launch_index_small(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums,
+                              uint32_t* idx, uint32_t k_cap, uint32_t* prefix);
 // Device address (on the current device) of the index's file-scope
 // partial-sum array, looked up once per device.
 hipError_t index_scratch(uint32_t** out);

@@ -96,6 +96,7 @@ class GpuRun:
     offload: bool = False  # residuals in pinned host memory (scape_step_offload)
     key_out: bool = True  # ask the step for the full statistic keys (else candidates' keys are recomputed)
     interleaved: bool = False  # residuals and gradients in the worker-interleaved layout
+    select_path: Optional[int] = None  # scape_set_select_path (None: the library's default)
     state: object = None
     grads: List[object] = field(default_factory=list)
 
@@ -104,6 +105,9 @@ class GpuRun:
         from sparse_communication_adam_amd.state import ScapeState
         cfg = scape_config(self.wl, self.keep, self.W)
         self.state = ScapeState(cfg, offload=self.offload, interleaved=self.interleaved)
+        if self.select_path is not None:
+            import sparse_communication_adam_amd as sc
+            sc.scape_set_select_path(self.state.ctx, self.select_path)
         self.layout = self.state.layout
         n = self.layout.n_pad
         if not self.x_zero:
@@ -170,7 +174,7 @@ def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int]
 
 def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, keep=None, W=None,
                init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True,
-               offload=False, key_out=True, interleaved=False) -> Dict[str, int]:
+               offload=False, key_out=True, interleaved=False, select_path=None) -> Dict[str, int]:
     """Run `steps` steps on the GPU (all layers) and the oracle (all layers, or
     the sampled ones) and compare every output of every step."""
     import torch
@@ -180,8 +184,9 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
     lay = full if sample is None else oracle.sub_layout(full, tensors)
     log(f"{wl.name}: W={W} L={full.L} n_pad={full.n_pad} k_total={full.k_total} steps={steps} "
         f"oracle layers={len(tensors)} ({lay.n_pad} elements){' residuals on the host' if offload else ''}"
-        f"{'' if key_out else ', candidate keys recomputed'}{', worker-interleaved layout' if interleaved else ''}")
-    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved)
+        f"{'' if key_out else ', candidate keys recomputed'}{', worker-interleaved layout' if interleaved else ''}"
+        f"{'' if select_path is None else f', selection path {select_path}'}")
+    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total
     assert list(glay.layer_offset) == full.off.tolist() and list(glay.layer_k) == full.k.tolist()

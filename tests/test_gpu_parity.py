@@ -31,9 +31,20 @@ def gpu():
     torch.cuda.empty_cache()
 
 
-def _ctx(sizes, W=2, keep=(1, 10)):
+def _ctx(sizes, W=2, keep=(1, 10), path=None):
     import sparse_communication_adam_amd as sc
-    return sc.scape_init(sc.ScapeConfig(layer_numel=list(sizes), workers=W, keep_num=keep[0], keep_den=keep[1]))
+    ctx = sc.scape_init(sc.ScapeConfig(layer_numel=list(sizes), workers=W, keep_num=keep[0], keep_den=keep[1]))
+    if path is not None:
+        sc.scape_set_select_path(ctx, path)
+    return ctx
+
+
+# The two ways of selecting a mask (the sampled multi-pass path and the
+# two-launch compact path, which the library takes by default where every
+# layer of a range has at most 2^22 elements): both must give the oracle's
+# mask, so the tests that build masks run each of them.
+SAMPLED, COMPACT = 1, 2
+PATHS = pytest.mark.parametrize("path", [SAMPLED, COMPACT], ids=["sampled", "compact"])
 
 
 # ----------------------------------------------------------------------------
@@ -120,16 +131,24 @@ def _mtilde_cases():
                                        np.where(rng.random(n) < 0.005, np.float32(np.nan),
                                                 rng.standard_normal(n).astype(np.float32))),
         "narrow": lambda n: (1.0 + rng.integers(0, 3000, n) * 2.0 ** -23).astype(np.float32),
+        # 2% of the keys in one cluster of 50 values inside one run of 64 keys
+        # (each tied some hundred times), the rest far below: at keep 1/100 the
+        # threshold lies in the cluster, so the position digits decide among
+        # records whose keys share all but their lowest 6 bits
+        "cluster": lambda n: np.where(rng.random(n) < 0.02,
+                                      (1.0 + rng.integers(0, 50, n) * 2.0 ** -23).astype(np.float32),
+                                      (rng.standard_normal(n) * 1e-3).astype(np.float32)).astype(np.float32),
     }
 
 
+@PATHS
 @pytest.mark.parametrize("case", list(_mtilde_cases()))
 @pytest.mark.parametrize("keep", [(0, 1), (1, 1000), (1, 100), (1, 10), (1, 2), (1, 1)])
-def test_mask_build_matches_oracle(case, keep):
+def test_mask_build_matches_oracle(case, keep, path):
     import torch
     import sparse_communication_adam_amd as sc
     sizes = [1, 37, 1000, 64, 4097, 70000, 1 << 20, 300001]
-    ctx = _ctx(sizes, W=3, keep=keep)
+    ctx = _ctx(sizes, W=3, keep=keep, path=path)
     lay = oracle.layout(sizes, keep[0], keep[1], 3)
     mt = np.zeros(lay.n_pad, np.float32)
     gen = _mtilde_cases()[case]
@@ -153,16 +172,18 @@ def test_mask_build_matches_oracle(case, keep):
     ctx.destroy()
 
 
-def test_mask_build_heavy_ties_across_many_candidate_blocks():
+@PATHS
+def test_mask_build_heavy_ties_across_many_candidate_blocks(path):
     """One 6M-element layer of 16 levels: the threshold key is tied across
     hundreds of thousands of positions spread over many candidate blocks, so
-    every position-digit pass runs."""
+    every position-digit pass runs (on the compact path, one workgroup
+    resolves those records, or at keep 1/3 the layer's keys)."""
     import torch
     import sparse_communication_adam_amd as sc
     rng = np.random.default_rng(5)
     sizes = [6_000_000, 4096]
     for keep in [(1, 1000), (37, 1000), (1, 3)]:
-        ctx = _ctx(sizes, W=2, keep=keep)
+        ctx = _ctx(sizes, W=2, keep=keep, path=path)
         lay = oracle.layout(sizes, keep[0], keep[1], 2)
         mt = (rng.integers(-8, 8, lay.n_pad) * 2.0 ** -12).astype(np.float32)
         out = sc.alloc_mask(ctx.layout)
@@ -172,22 +193,26 @@ def test_mask_build_heavy_ties_across_many_candidate_blocks():
         ctx.destroy()
 
 
+@PATHS
 @pytest.mark.parametrize("case,keep,want_flags", [
     ("normal", (1, 100), 0),          # records fit: no fallback
     ("levels16", (1, 2), 3),          # window and exact bucket both beyond the record space
     ("all_equal", (1, 10), 3),        # one bucket holds every key
     ("zeros", (37, 1000), 3),
 ])
-def test_mask_build_record_space_overflow(case, keep, want_flags):
+def test_mask_build_record_space_overflow(case, keep, want_flags, path):
     """A record segment holds 1/16 of its elements plus 1024 records.  When a
     layer's window holds more, the layer is redone from an exact histogram;
     when even its exact threshold bucket does not fit, the remaining digits
     are decided by passes over its keys.  The mask is the oracle's either
-    way, and scape_selection_flags reports which path ran."""
+    way, and scape_selection_flags reports which path ran (the compact path
+    has no window: only its exact bucket can overflow)."""
     import torch
     import sparse_communication_adam_amd as sc
+    if path == COMPACT:
+        want_flags &= sc.SELECT_KEY_PASSES
     sizes = [2_000_000, 300_001, 5000]
-    ctx = _ctx(sizes, W=2, keep=keep)
+    ctx = _ctx(sizes, W=2, keep=keep, path=path)
     lay = oracle.layout(sizes, keep[0], keep[1], 2)
     gen = _mtilde_cases()[case]
     mt = np.zeros(lay.n_pad, np.float32)
@@ -204,15 +229,39 @@ def test_mask_build_record_space_overflow(case, keep, want_flags):
     ctx.destroy()
 
 
-def test_mask_build_more_segments_than_lds_map():
-    """Over 4096 record segments (one per tiny layer): the record passes look
-    segments up in global memory instead of their LDS copy."""
+@PATHS
+def test_mask_build_alternating_inputs(path):
+    """Two inputs built in turn, twenty times each, on one context: every
+    build must be its own input's mask, not one made from records or counts
+    the other build left behind (the compact path hands records and counts
+    between workgroups of one launch)."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    rng = np.random.default_rng(13)
+    sizes = [1 << 20, 300_001, 4097]
+    ctx = _ctx(sizes, W=2, keep=(1, 10), path=path)
+    lay = oracle.layout(sizes, 1, 10, 2)
+    ins, exps = [], []
+    for scale in (1e-3, 3e-3):
+        mt = (rng.standard_normal(lay.n_pad) * scale).astype(np.float32)
+        ins.append(torch.from_numpy(mt).cuda())
+        exps.append(oracle.mask_from_keys(lay, oracle.keys_of(mt)))
+    out = sc.alloc_mask(ctx.layout)
+    for it in range(40):
+        sc.scape_mask_build(ctx, ins[it % 2], out)
+        assert np.array_equal(u64(out.bits), exps[it % 2]), f"build {it}"
+    ctx.destroy()
+
+
+@PATHS
+def test_mask_build_more_segments_than_lds_map(path):
+    """Over 4096 record segments (one per tiny layer)."""
     import torch
     import sparse_communication_adam_amd as sc
     rng = np.random.default_rng(11)
     sizes = [int(x) for x in rng.integers(1, 300, 5000)] + [600_000]
     for keep in [(1, 10), (1, 2)]:
-        ctx = _ctx(sizes, W=2, keep=keep)
+        ctx = _ctx(sizes, W=2, keep=keep, path=path)
         lay = oracle.layout(sizes, keep[0], keep[1], 2)
         mt = (rng.standard_normal(lay.n_pad) * 1e-3).astype(np.float32)
         out = sc.alloc_mask(ctx.layout)
@@ -224,14 +273,15 @@ def test_mask_build_more_segments_than_lds_map():
         ctx.destroy()
 
 
-def test_mask_build_empty_layers():
+@PATHS
+def test_mask_build_empty_layers(path):
     """Zero-size layers own no words, tiles or record segments; a shard that
     owns only empty layers writes nothing."""
     import torch
     import sparse_communication_adam_amd as sc
     rng = np.random.default_rng(12)
     sizes = [0, 100, 0, 0, 5000, 0]
-    ctx = _ctx(sizes, W=2, keep=(1, 10))
+    ctx = _ctx(sizes, W=2, keep=(1, 10), path=path)
     lay = oracle.layout(sizes, 1, 10, 2)
     mt = (rng.standard_normal(lay.n_pad) * 1e-3).astype(np.float32)
     d_mt = torch.from_numpy(mt).cuda()
@@ -267,17 +317,19 @@ def _sampled_words(lw0, lwords):
     return np.array(out, np.int64)
 
 
+@PATHS
 @pytest.mark.parametrize("sampled_small", [True, False])
-def test_mask_build_exact_after_a_sampling_miss(sampled_small):
+def test_mask_build_exact_after_a_sampling_miss(sampled_small, path):
     """The sampled words hold values unlike the rest of the layer, so the
     sample's window misses the k-th key: the exact fallback (full first-digit
-    histogram and reclassification) must still give the oracle's mask."""
+    histogram and reclassification) must still give the oracle's mask.  (The
+    compact path samples nothing; the same input checks it too.)"""
     import torch
     import sparse_communication_adam_amd as sc
     rng = np.random.default_rng(41 + sampled_small)
     sizes = [400_000, 5000]
     keep = (1, 10)
-    ctx = _ctx(sizes, W=2, keep=keep)
+    ctx = _ctx(sizes, W=2, keep=keep, path=path)
     lay = oracle.layout(sizes, keep[0], keep[1], 2)
     n0 = sizes[0]
     small = (rng.random(lay.n_pad) * 0.5 + 0.5).astype(np.float32) * np.float32(2.0 ** -10)
@@ -294,6 +346,8 @@ def test_mask_build_exact_after_a_sampling_miss(sampled_small):
     assert np.array_equal(u64(out.bits), exp)
     idx, pre, cnt = oracle.mask_index(exp)
     assert np.array_equal(u32(out.idx)[:cnt], idx) and np.array_equal(u32(out.block_prefix), pre)
+    if path == SAMPLED:
+        assert sc.scape_selection_flags(ctx) & sc.SELECT_EXACT_HISTOGRAM
     ctx.destroy()
 
 
@@ -307,7 +361,7 @@ def test_mask_build_window_wider_than_the_record_histogram():
     rng = np.random.default_rng(43)
     sizes = [600_000]
     keep = (1, 2)
-    ctx = _ctx(sizes, W=2, keep=keep)
+    ctx = _ctx(sizes, W=2, keep=keep, path=SAMPLED)
     lay = oracle.layout(sizes, keep[0], keep[1], 2)
     n = sizes[0]
     mag = np.where(rng.random(n) < 0.5, 2.0 ** 60, 2.0 ** -60) * (1.0 + rng.random(n))
@@ -320,12 +374,13 @@ def test_mask_build_window_wider_than_the_record_histogram():
     ctx.destroy()
 
 
+@PATHS
 @pytest.mark.parametrize("P", [3, 32])
-def test_mask_build_one_shard_at_a_time(P):
+def test_mask_build_one_shard_at_a_time(P, path):
     import torch
     import sparse_communication_adam_amd as sc
     wl = synth.reduced(synth.GPT345M)
-    ctx = _ctx(wl.layer_sizes, W=wl.W, keep=(1, 10))
+    ctx = _ctx(wl.layer_sizes, W=wl.W, keep=(1, 10), path=path)
     lay = oracle.layout(wl.layer_sizes, 1, 10, wl.W)
     rng = np.random.default_rng(P)
     mt = (rng.standard_normal(lay.n_pad) * 1e-3).astype(np.float32)
@@ -385,17 +440,19 @@ def _assert_bitexact(stats):
     assert stats["float_not_bitexact"] == 0, stats
 
 
+@PATHS
 @pytest.mark.parametrize("name", ["single-1024x1024", "gpt-345m", "llama-0.55b", "llama-1.75b", "adversarial-ties"])
-def test_step_parity_oracle_sized(name):
+def test_step_parity_oracle_sized(name, path):
     """Every output of every step, all layers: the single-layer workload at its
     full size, the others with the same tensor kinds at reduced sizes."""
     wl = synth.WORKLOADS[name]
     small = wl if name == "single-1024x1024" else synth.reduced(wl)
-    _assert_bitexact(run_parity(small, wl.steps))
+    _assert_bitexact(run_parity(small, wl.steps, select_path=path))
 
 
-def test_step_parity_ragged_layout():
-    _assert_bitexact(run_parity(synth.ragged(), 5))
+@PATHS
+def test_step_parity_ragged_layout(path):
+    _assert_bitexact(run_parity(synth.ragged(), 5, select_path=path))
 
 
 @pytest.mark.parametrize("W", [1, 2, 4, 5, 16])
@@ -432,10 +489,11 @@ def test_step_single_worker():
     _assert_bitexact(run_parity(synth.reduced(synth.LLAMA055), 3, W=1))
 
 
-def test_step_zero_gradients_tie_everywhere():
+@PATHS
+def test_step_zero_gradients_tie_everywhere(path):
     wl = synth.ragged()
     zero = lambda step, worker, t: np.zeros(wl.tensors[t].numel, np.uint16)  # noqa: E731
-    _assert_bitexact(run_parity(wl, 3, grad_override=zero, x_zero=True))
+    _assert_bitexact(run_parity(wl, 3, grad_override=zero, x_zero=True, select_path=path))
 
 
 # bfloat16 bit patterns of special gradient values: +-Inf, +-0, subnormals
@@ -457,13 +515,14 @@ def _special_grads(wl):
     return grad
 
 
+@PATHS
 @pytest.mark.parametrize("key_out", [True, False])
-def test_step_special_gradient_values(key_out):
+def test_step_special_gradient_values(key_out, path):
     """1% of every worker's gradients are +-Inf, +-0, subnormal, the largest
     finite bfloat16 or NaN: the masks, indices and keys stay bit-exact and
     the state matches (NaN where the oracle has NaN)."""
     wl = synth.ragged()
-    _assert_bitexact(run_parity(wl, 4, grad_override=_special_grads(wl), key_out=key_out))
+    _assert_bitexact(run_parity(wl, 4, grad_override=_special_grads(wl), key_out=key_out, select_path=path))
 
 
 def test_step_is_deterministic():
@@ -607,20 +666,22 @@ def test_step_parity_maximum_size():
 # the configuration bench.py times.
 
 
+@PATHS
 @pytest.mark.parametrize("name", ["single-1024x1024", "gpt-345m", "llama-0.55b", "llama-1.75b", "adversarial-ties"])
-def test_step_recomputed_keys_oracle_sized(name):
+def test_step_recomputed_keys_oracle_sized(name, path):
     wl = synth.WORKLOADS[name]
     small = wl if name == "single-1024x1024" else synth.reduced(wl)
-    _assert_bitexact(run_parity(small, wl.steps, key_out=False))
+    _assert_bitexact(run_parity(small, wl.steps, key_out=False, select_path=path))
 
 
-def test_step_recomputed_keys_edge_cases():
+@PATHS
+def test_step_recomputed_keys_edge_cases(path):
     wl = synth.ragged()
-    _assert_bitexact(run_parity(wl, 5, key_out=False))
-    _assert_bitexact(run_parity(wl, 3, W=1, key_out=False))
-    _assert_bitexact(run_parity(wl, 3, keep=(1, 1), init_mask_all=True, key_out=False))
+    _assert_bitexact(run_parity(wl, 5, key_out=False, select_path=path))
+    _assert_bitexact(run_parity(wl, 3, W=1, key_out=False, select_path=path))
+    _assert_bitexact(run_parity(wl, 3, keep=(1, 1), init_mask_all=True, key_out=False, select_path=path))
     zero = lambda step, worker, tensor: np.zeros(wl.tensors[tensor].numel, np.uint16)  # noqa: E731
-    _assert_bitexact(run_parity(wl, 3, grad_override=zero, key_out=False))
+    _assert_bitexact(run_parity(wl, 3, grad_override=zero, key_out=False, select_path=path))
 
 
 @pytest.mark.parametrize("name", ["llama-1.75b", "adversarial-ties"])
