@@ -84,9 +84,13 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
                                                        uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
-                                                       float* __restrict__ m_stash) {
+                                                       float* __restrict__ m_stash, uint32_t* __restrict__ clear,
+                                                       uint32_t n_clear) {
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     constexpr uint32_t kWords = ef_words<WT>();
+    // the selection's histogram rows, zeroed on the way (spread over every
+    // workgroup; a few KB per layer)
+    for (uint32_t i = blockIdx.x * kEfBlock + threadIdx.x; i < n_clear; i += gridDim.x * kEfBlock) clear[i] = 0u;
     const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
     const uint32_t w0 = (blk * kEfWaves + threadIdx.x / 64) * kWords;
     if (w0 >= n_words) return;
@@ -148,13 +152,13 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, const float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
-                             float* m_stash) {
-    if (n_words == 0) return hipSuccess;
+                             float* m_stash, uint32_t* clear, uint32_t n_clear) {
+    if (n_words == 0) return n_clear ? launch_fill_u32(s, clear, n_clear, 0u) : hipSuccess;
 #define SCAPE_EF_LAUNCH(WV, K)                                                                                 \
     hipLaunchKernelGGL((k_ef_compact<WV, K>),                                                                  \
                        dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())),          \
                        dim3(kEfBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, cur_prefix, k_cap, key16, \
-                       key32, m_stash)
+                       key32, m_stash, clear, n_clear)
 #define SCAPE_EF_CASE(WV)                    \
     case WV:                                 \
         if (key32) SCAPE_EF_LAUNCH(WV, true); \

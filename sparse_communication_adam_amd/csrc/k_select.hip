@@ -1336,12 +1336,13 @@ hipError_t launch_compact_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_
 // once at most kFinLdsRecs remain.  It shares the key pass's LDS, which is
 // free by then.
 constexpr uint32_t kFinLdsRecs = 3072;
+constexpr uint32_t kWaveRecs = 256;  // records one wave finishes faster alone than the workgroup
 constexpr int kFinDigitBits = kKey2Bits + kKey3Bits;  // 12: key bits 17..6 in one digit
 constexpr int kFinBins = 1 << kFinDigitBits;
 static_assert(kFinBins >= kPassBins, "the finishing histogram holds every digit");
 struct FinishLds {
     uint64_t rec[kFinLdsRecs];
-    uint32_t h[kFinBins];
+    alignas(16) uint32_t h[kFinBins];
     uint32_t scratch[kCompactWaves];
     uint32_t wsum[kCompactWaves];
     uint32_t bucket, before, count;
@@ -1391,22 +1392,123 @@ __device__ __forceinline__ void finish_select(FinishLds& f, uint32_t phase, cons
     __syncthreads();
 }
 
+// Bucket search by one wave over `nbins` LDS bins (a multiple of 64), in
+// the order and with the result of find_bucket; zeroes the bins.  False if
+// no bucket reaches `need`.
+__device__ __forceinline__ bool wave_find_bucket(uint32_t* h, int nbins, bool descending, uint32_t need,
+                                                 uint32_t* bucket, uint32_t* before, uint32_t* count) {
+    const uint32_t lane = lane_id();
+    const int per = nbins / 64;
+    auto bin = [&](int o) { return descending ? nbins - 1 - o : o; };
+    uint32_t sum = 0;
+    for (int e = 0; e < per; ++e) sum += h[bin((int)lane * per + e)];
+    const uint32_t inc = wave_inclusive_scan(sum);
+    const bool mine = need > 0 && inc - sum < need && inc >= need;
+    uint32_t b = 0, bef = 0, cnt = 0;
+    if (mine) {
+        uint32_t cum = inc - sum;
+        for (int e = 0; e < per; ++e) {
+            const uint32_t c = h[bin((int)lane * per + e)];
+            if (cum + c >= need) {
+                b = (uint32_t)bin((int)lane * per + e);
+                bef = cum;
+                cnt = c;
+                break;
+            }
+            cum += c;
+        }
+    }
+    for (int e = 0; e < per; ++e) h[bin((int)lane * per + e)] = 0;
+    const uint64_t who = wave_ballot(mine);
+    if (who == 0) return false;
+    const int src = __builtin_ctzll(who);
+    *bucket = __shfl(b, src, 64);
+    *before = __shfl(bef, src, 64);
+    *count = __shfl(cnt, src, 64);
+    return true;
+}
+
+// The remaining phases of a layer by wave 0 alone, once its `cnt` records
+// are in LDS: the same rules, counts and compaction as finish_records, with
+// no workgroup barrier between them.
+__device__ void finish_wave(FinishLds& f, const LayerDesc& L, uint32_t cnt, uint64_t* __restrict__ bits) {
+    const uint32_t lane = lane_id();
+    SelState S = f.S;
+    for (;;) {
+        const uint32_t phase = S.phase;
+        const bool final_pass = phase == kPhaseDone;
+        uint32_t out = 0;
+        for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
+            const uint32_t p = p0 + lane;
+            const uint64_t r = p < cnt ? f.rec[p] : 0ull;
+            const uint32_t kv = (uint32_t)(r >> 32), jl = (uint32_t)r;
+            uint32_t digit = 0;
+            uint32_t c = p < cnt ? classify(phase, S, kv, jl, &digit) : 0u;
+            if ((phase == kPhasePos2 || phase == kPhasePos3) && p < cnt && kv != S.T) c = kv > S.T ? 1u : 0u;
+            if (c == 1u && jl < L.n) {
+                const uint32_t jj = L.off + jl;
+                atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
+            }
+            if (phase == kPhaseKey2) digit = (kv >> kKey4Bits) & ((1u << kFinDigitBits) - 1u);
+            if (final_pass) continue;
+            hist_add_wave(f.h, digit, c == 2u);
+            // compaction in place: every lane has read its record
+            const uint64_t bm = wave_ballot(c == 2u);
+            if (c == 2u) f.rec[out + lanes_below(bm)] = r;
+            out += (uint32_t)__popcll(bm);
+        }
+        if (final_pass) break;
+        cnt = out;
+        const bool wide = phase == kPhaseKey2;
+        const bool desc = phase == kPhaseKey2 || phase == kPhaseKey3 || phase == kPhaseKey4;
+        uint32_t b = 0, bef = 0, count = 0;
+        if (!wave_find_bucket(f.h, wide ? kFinBins : phase_bins(phase), desc, S.need, &b, &bef, &count)) {
+            S.phase = kPhaseDone;  // inconsistent counts: select no candidate rather than guess
+            S.T = 0xFFFFFFFFu;
+            S.J = 0;
+        } else if (wide) {
+            S.need -= bef;
+            S.kprefix = (S.kprefix << kFinDigitBits) | b;
+            if (S.need == count) {
+                S.T = S.kprefix << kKey4Bits;
+                S.J = 0xFFFFFFFFu;
+                S.phase = kPhaseDone;
+            } else {
+                S.phase = kPhaseKey4;
+            }
+        } else {
+            advance(S, phase, b, bef, count);
+        }
+        if (S.phase == kPhasePos1 && L.n <= (1u << 20)) {
+            S.jprefix = 0;
+            S.phase = kPhasePos2;
+        }
+    }
+    if (lane == 0) f.S = S;
+}
+
 // Every remaining digit of layer L from its `cnt` records at grec (the
 // filter's: the layer's exact threshold bucket, with full keys), by one
 // workgroup: each phase classifies the records left by the previous one,
 // marks those its decided prefix selects, histograms and compacts the
-// undecided rest, and fixes its digit; the final rule then marks what
-// remains selected.  The phases and rules are those of the record passes.
-// The first phase keeps every record (all are in the bucket d1), so it only
-// counts.  The records a phase keeps are those of the bucket the previous
-// search chose, whose count that search returned: they go to LDS from the
-// first phase that keeps at most kFinLdsRecs, else they are compacted in
-// place.
+// undecided rest, and fixes its digit; the final rule marks what remains
+// selected.  The phases and rules are those of the record passes, with key
+// bits 17..6 as one digit.  That first phase keeps every record (all are in
+// the bucket d1), so it only counts.  The records a later phase keeps are
+// those of the bucket the previous search chose, whose count that search
+// returned: they go to LDS from the first phase that keeps at most
+// kFinLdsRecs, else they are compacted in place.  Once at most kWaveRecs
+// remain in LDS, wave 0 finishes alone (finish_wave).
 __device__ void finish_records(FinishLds& f, const LayerDesc& L, uint64_t* __restrict__ grec, uint32_t cnt,
                                uint64_t* __restrict__ bits) {
     const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
     bool in_lds = false;
     uint32_t keep = cnt;  // records the next pass keeps
+    if (cnt <= kFinLdsRecs) {  // uniform: few enough to work on in LDS from the start
+        for (uint32_t p = threadIdx.x; p < cnt; p += kCompactBlock) f.rec[p] = grec[p];
+        __syncthreads();
+        in_lds = true;
+    }
     for (;;) {
         const SelState S = f.S;
         const uint32_t phase = S.phase;
@@ -1440,8 +1542,7 @@ __device__ void finish_records(FinishLds& f, const LayerDesc& L, uint64_t* __res
                     const uint32_t jj = L.off + jl;
                     atomicOr((unsigned long long*)&bits[jj >> 6], 1ull << (jj & 63u));
                 }
-                // the records hold full keys: one digit of key bits 17..6
-                if (phase == kPhaseKey2) digit = (kv >> kKey4Bits) & ((1u << kFinDigitBits) - 1u);
+                if (count_only) digit = (kv >> kKey4Bits) & ((1u << kFinDigitBits) - 1u);
                 if (!final_pass) hist_add_wave(f.h, digit, c == 2u);
                 if (c == 2u) und |= 1u << i;
             }
@@ -1477,6 +1578,10 @@ __device__ void finish_records(FinishLds& f, const LayerDesc& L, uint64_t* __res
         __syncthreads();  // every wave's counts are in the histogram
         finish_select(f, phase, L, true);
         keep = f.count;
+        if (in_lds && cnt <= kWaveRecs) {  // uniform: the rest by one wave
+            if (threadIdx.x < 64) finish_wave(f, L, cnt, bits);
+            return;
+        }
     }
 }
 
@@ -1532,7 +1637,6 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
     if (S.none || S.phase == kPhaseDone) return;  // the filter wrote the whole mask of the layer
     FinishLds& f = lds.fin;
     const uint32_t fill = lrec[l];
-    for (int b = threadIdx.x; b < kFinBins; b += kCompactBlock) f.h[b] = 0;
     if (threadIdx.x == 0) {
         f.S = S;
         if (fill > G.size) {
@@ -1540,6 +1644,8 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
             atomicOr(miss, 2u);
         }
     }
+    __syncthreads();
+    for (int b = threadIdx.x; b < kFinBins; b += kCompactBlock) f.h[b] = 0;
     __syncthreads();
     if (fill > G.size)
         finish_keys(f, L, key, ks, bits);

@@ -114,6 +114,7 @@ void owner_map(const HostLayout& h, int32_t P, int32_t* owner) {
 struct ProfSlot {
     hipEvent_t ev[SCAPE_PHASE_COUNT + 1];
     bool pending;
+    bool serial;  // the update ran after the selection on the step's stream
 };
 
 constexpr int kProfSlots = 64;
@@ -275,12 +276,15 @@ void prof_collect(scape_ctx* c, int slot) {
     // points: 0 start, 1 end of the dense pass (where the update and the
     // selection fork), 2 end of the update, 3 end of the selection, 4 end of
     // the index and the join.  The update and the selection run side by side,
-    // so both are measured from point 1.
+    // so both are measured from point 1; in a serial step the update follows
+    // the selection (3 -> 2) and the index follows the update (2 -> 4).
     static const int from[SCAPE_PHASE_COUNT] = {0, 1, 1, 3};
+    static const int from_serial[SCAPE_PHASE_COUNT] = {0, 3, 1, 2};
     static const int to[SCAPE_PHASE_COUNT] = {1, 2, 3, 4};
     for (int i = 0; i < SCAPE_PHASE_COUNT; ++i) {
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, p.ev[from[i]], p.ev[to[i]]) == hipSuccess) c->prof_ms[i] += ms;
+        const int a = p.serial ? from_serial[i] : from[i];
+        if (hipEventElapsedTime(&ms, p.ev[a], p.ev[to[i]]) == hipSuccess) c->prof_ms[i] += ms;
     }
     c->prof_steps += 1;
     p.pending = false;
@@ -292,6 +296,7 @@ int prof_begin(scape_ctx* c) {
     c->prof_next = (c->prof_next + 1) % kProfSlots;
     prof_collect(c, slot);  // the ring wrapped: fold the old record first
     c->prof[slot].pending = true;
+    c->prof[slot].serial = false;
     return slot;
 }
 
@@ -437,8 +442,11 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
             cp.r[i] = stage + (size_t)i * slot_elems;
             cp.g[i] = wp.g[i] + j0;
         }
+        // the first chunk's pass also zeroes the histogram rows
         SCAPE_HIP(launch_ef_compact(s, c->d_word_info + w0, nw, cp, sc, m + j0, cur->bits + w0,
-                                    cur->block_prefix + w0, k_cap, key16 + j0, key32 + j0, c->d_m_stash),
+                                    cur->block_prefix + w0, k_cap, key16 + j0, key32 + j0, c->d_m_stash,
+                                    chunk == 0 ? c->d_hist : nullptr,
+                                    chunk == 0 ? (uint32_t)c->lay.L * kHistBins : 0u),
                   "ef_compact");
         SCAPE_HIP(hipEventRecord(c->ev_k[b], s), "offload event");
         SCAPE_HIP(hipStreamWaitEvent(c->s_out[b], c->ev_k[b], 0), "offload wait");
@@ -564,16 +572,32 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     const int32_t L = ctx->lay.L;
 
     const int slot = prof_begin(ctx);
-    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
+    // the dense pass also zeroes the selection's histogram rows
     if (r_on_host) {
         if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
         SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
-                                    k_cap, ctx->d_key16, key32, ctx->d_m_stash),
+                                    k_cap, ctx->d_key16, key32, ctx->d_m_stash, ctx->d_hist,
+                                    (uint32_t)L * kHistBins),
                   "ef_compact");
     }
     prof_mark(ctx, slot, 1, s);
+    if (compact_range(ctx, 0, L) && !r_on_host) {
+        // The compact selection is two short launches: forking the update
+        // onto its own stream costs more in events than it overlaps, so the
+        // update follows the selection on `stream`.
+        if (slot >= 0) ctx->prof[slot].serial = true;
+        if ((rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s))) return rc;
+        prof_mark(ctx, slot, 3, s);
+        SCAPE_HIP(launch_reduce_update(s, wp, sc, x, m, v, il, cur->idx, cur->block_prefix, ctx->d_m_stash,
+                                       ctx->n_words, (uint32_t)ctx->lay.n_pad, k_cap),
+                  "reduce_update");
+        prof_mark(ctx, slot, 2, s);
+        if ((rc = run_index(ctx, next, s))) return rc;
+        prof_mark(ctx, slot, 4, s);
+        return SCAPE_OK;
+    }
     // The update touches x, v, and m on the mask only; the selection reads
     // the keys, m off the mask, the owner's residual and the sparse buffers.
     // Nothing one writes is read by the other, so the update runs on its own
