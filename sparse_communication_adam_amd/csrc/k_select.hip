@@ -431,13 +431,14 @@ template <int kNW>
 struct KeyPassLdsT {
     uint64_t rec[kNW][kWaveStage];
     uint32_t hist[kFilterHistBins];
-    uint32_t n[kNW], ab[kNW], base;
+    uint32_t n[kNW], ab[kNW], fl[kNW], base, reserved;
 };
 using KeyPassLds = KeyPassLdsT<kWaves>;
 
 // With kFullKeys the records are stored with their full keys, from *ks.
+// Returns (in every thread) the record slots the workgroup reserved.
 template <bool kRecords, bool kHist = false, int kThreads = kBlock, bool kFullKeys = false>
-__device__ __forceinline__ void key_pass(KeyPassLdsT<kThreads / 64>& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
+__device__ __forceinline__ uint32_t key_pass(KeyPassLdsT<kThreads / 64>& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
                                          uint32_t sel_from, uint32_t cand_lo, uint32_t cand_hi,
                                          const uint16_t* __restrict__ key, uint64_t* __restrict__ bits,
                                          uint32_t* __restrict__ seg_fill, uint64_t* __restrict__ cand,
@@ -461,6 +462,7 @@ __device__ __forceinline__ void key_pass(KeyPassLdsT<kThreads / 64>& lds, const 
     const uint32_t k_lo = cand_lo << kDigit1FromKey16;
     const uint32_t k_span = kRecords ? ((cand_hi - cand_lo) << kDigit1FromKey16) | ((1u << kDigit1FromKey16) - 1u) : 0u;
     uint32_t n_st = 0;
+    uint32_t flushed = 0;     // records this wave reserved and stored mid-tile
     uint32_t above_lane = 0;  // bits set in the mask words this lane wrote
     constexpr uint32_t kStride = kNW * kFilterWords;
     // The next trip's keys are loaded before this trip is processed.  Every
@@ -491,6 +493,7 @@ __device__ __forceinline__ void key_pass(KeyPassLdsT<kThreads / 64>& lds, const 
                         wave_store_full(stage, n_st, __shfl(first, 0, 64), G, cand, *ks, L);
                     else
                         wave_store(stage, n_st, __shfl(first, 0, 64), G, cand);
+                    flushed += n_st;
                     n_st = 0;
                 }
                 const bool rec = in_range && (!decltype(partial)::value || lane < left);
@@ -534,25 +537,30 @@ __device__ __forceinline__ void key_pass(KeyPassLdsT<kThreads / 64>& lds, const 
     if (lane == 0) {
         lds.n[wave] = n_st;
         lds.ab[wave] = n_above;
+        lds.fl[wave] = flushed;
     }
     __syncthreads();
     if (lds_hist) hist_flush(lds.hist, hist_row + cand_lo, (int)width, kThreads);
     if (threadIdx.x == 0) {
-        uint32_t tot = 0, ab = 0;
+        uint32_t tot = 0, ab = 0, fl = 0;
         for (int q = 0; q < kNW; ++q) {
             tot += lds.n[q];
             ab += lds.ab[q];
+            fl += lds.fl[q];
         }
         lds.base = tot ? atomicAdd(&seg_fill[t.seg], tot) : 0u;
+        lds.reserved = tot + fl;
         if (ab) atomicAdd(&seg_above[t.seg], ab);
     }
     __syncthreads();
     uint32_t first = lds.base;
+    const uint32_t reserved = lds.reserved;
     for (uint32_t q = 0; q < wave; ++q) first += lds.n[q];
     if constexpr (kFullKeys)
         wave_store_full(stage, n_st, first, G, cand, *ks, L);
     else
         wave_store(stage, n_st, first, G, cand);
+    return reserved;
 }
 
 __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ tiles,
@@ -1247,6 +1255,29 @@ __device__ __forceinline__ bool last_of_layer(uint32_t* ticket, int layer, uint3
     return last;
 }
 
+// The same with a 64-bit ticket word per layer whose low half also sums the
+// workgroups' `count`s: the last workgroup gets the layer's total in *total
+// (the record counter's final value, without reading it back).
+template <int kThreads>
+__device__ __forceinline__ bool last_of_layer_sum(unsigned long long* ticket, int layer, uint32_t n, uint32_t count,
+                                                  uint32_t* s_flag, uint32_t* s_total, uint32_t* total) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long prev = __hip_atomic_fetch_add(&ticket[layer], (1ull << 32) | count, __ATOMIC_RELEASE,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = (uint32_t)(prev >> 32) == n - 1u;
+        if (last) ticket[layer] = 0ull;
+        *s_flag = last ? 1u : 0u;
+        *s_total = (uint32_t)prev + count;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0u;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *total = *s_total;
+    return last;
+}
+
 constexpr int kCompactHistBatch = 4;  // 16-byte key loads in flight per thread
 
 __global__ __launch_bounds__(kCompactBlock) void k_compact_hist(const TileDesc* __restrict__ tiles, uint32_t parts,
@@ -1607,12 +1638,12 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
                                                                   const uint16_t* __restrict__ key, KeySource ks,
                                                                   uint64_t* __restrict__ bits,
                                                                   uint64_t* __restrict__ cand,
-                                                                  uint32_t* __restrict__ ticket,
+                                                                  unsigned long long* __restrict__ ticket,
                                                                   uint32_t* __restrict__ lrec,
                                                                   uint32_t* __restrict__ labove,
                                                                   uint32_t* __restrict__ miss) {
     __shared__ CompactLds lds;
-    __shared__ uint32_t s_flag;
+    __shared__ uint32_t s_flag, s_total;
     TileDesc t = tiles[blockIdx.x];
     const int l = t.layer;
     const LayerDesc L = layers[l];
@@ -1623,6 +1654,7 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
     t.w0 = w0;
     t.w1 = w1;
     t.seg = (uint32_t)l;  // the layer's own record counter
+    uint32_t reserved = 0;
     if (w0 < w1) {        // uniform
         if (S.none)       // nothing selected: zero words
             key_pass<false, false, kCompactBlock>(lds.pass, t, L, G, (uint32_t)kDigit1Bins, 1u, 0u, key, bits, lrec,
@@ -1630,13 +1662,14 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
         else if (S.all_bucket)  // the threshold bucket and above, no records
             key_pass<false, false, kCompactBlock>(lds.pass, t, L, G, S.d1, 1u, 0u, key, bits, lrec, cand, labove);
         else  // above the bucket: bits; in it: records with their full keys
-            key_pass<true, false, kCompactBlock, true>(lds.pass, t, L, G, S.d1 + 1u, S.d1, S.d1, key, bits, lrec,
-                                                       cand, labove, nullptr, &ks);
+            reserved = key_pass<true, false, kCompactBlock, true>(lds.pass, t, L, G, S.d1 + 1u, S.d1, S.d1, key,
+                                                                  bits, lrec, cand, labove, nullptr, &ks);
     }
-    if (!last_of_layer<kCompactBlock>(ticket, l, layer_tiles(L) * parts, &s_flag)) return;
+    uint32_t fill = 0;  // the layer's records (all reservations)
+    if (!last_of_layer_sum<kCompactBlock>(ticket, l, layer_tiles(L) * parts, reserved, &s_flag, &s_total, &fill))
+        return;
     if (S.none || S.phase == kPhaseDone) return;  // the filter wrote the whole mask of the layer
     FinishLds& f = lds.fin;
-    const uint32_t fill = lrec[l];
     if (threadIdx.x == 0) {
         f.S = S;
         if (fill > G.size) {
@@ -1657,8 +1690,8 @@ __global__ __launch_bounds__(kCompactBlock) void k_compact_filter(const TileDesc
 
 hipError_t launch_compact_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
                                  const LayerDesc* layers, const SegDesc* lspace, SelState* st, const uint16_t* key,
-                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, uint32_t* ticket, uint32_t* lrec,
-                                 uint32_t* labove, uint32_t* miss) {
+                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, unsigned long long* ticket,
+                                 uint32_t* lrec, uint32_t* labove, uint32_t* miss) {
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_compact_filter, dim3(n_tiles, parts), dim3(kCompactBlock), 0, s, tiles, parts, layers, lspace,
                        st, key, ks, bits, cand, ticket, lrec, labove, miss);

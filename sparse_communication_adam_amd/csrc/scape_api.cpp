@@ -170,6 +170,7 @@ struct scape_ctx {
     // [ticket | record count | bit count] rows of L counters
     SegDesc* d_lspace = nullptr;
     uint32_t* d_lcount = nullptr;
+    unsigned long long* d_ltick = nullptr;  // the filter's per-layer tickets
     int32_t select_path = SCAPE_SELECT_PATH_AUTO;
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
@@ -201,6 +202,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_segs);
     hipFree(c->d_lspace);
     hipFree(c->d_lcount);
+    hipFree(c->d_ltick);
     hipFree(c->d_layer_seg0);
     hipFree(c->d_seg_fill);
     hipFree(c->d_seg_above);
@@ -335,7 +337,8 @@ int run_select_compact(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32
                                   c->d_hist, c->d_sel, ticket, lrec, labove, c->d_miss),
               "compact_hist");
     SCAPE_HIP(launch_compact_filter(s, tiles, nt, parts_for(kCompactFilterBlocks, kCompactFilterParts), c->d_layers,
-                                    c->d_lspace, c->d_sel, key, ks, bits, c->d_cand, ticket, lrec, labove, c->d_miss),
+                                    c->d_lspace, c->d_sel, key, ks, bits, c->d_cand, c->d_ltick, lrec, labove,
+                                    c->d_miss),
               "compact_filter");
     return SCAPE_OK;
 }
@@ -798,6 +801,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(c, &c->d_seg_above, n_segs, "segment bit counters")) ||
         (rc = dev_alloc(c, &c->d_lspace, L, "layer record spaces")) ||
         (rc = dev_alloc(c, &c->d_lcount, 3 * L, "layer counters")) ||
+        (rc = dev_alloc(c, &c->d_ltick, L, "layer tickets")) ||
         (rc = dev_alloc(c, &c->d_vb, c->vb_cap, "record blocks")) ||
         (rc = dev_alloc(c, &c->d_vb_count, c->vb_cap, "record block counts")) ||
         (rc = dev_alloc(c, &c->d_totals, 4, "totals")) || (rc = dev_alloc(c, &c->d_miss, 1, "miss flag")) ||
@@ -829,6 +833,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         e = hipMemcpy(c->d_segs, c->segs.data(), n_segs * sizeof(SegDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(c->d_lspace, lspace.data(), L * sizeof(SegDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(c->d_lcount, 0, 3 * L * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(c->d_ltick, 0, L * sizeof(unsigned long long));
     if (e == hipSuccess)
         e = hipMemcpy(c->d_layer_seg0, c->layer_seg0.data(), (L + 1) * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess && c->n_words)

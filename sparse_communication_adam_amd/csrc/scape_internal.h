@@ -215,8 +215,9 @@ hipError_t launch_select_next(hipStream_t s, uint32_t phase, int32_t layer0, int
 
 // The compact path (every layer of the range small): tiles split over
 // `parts` workgroups each.  Per layer: lspace[l] its whole record space,
-// ticket[l] the workgroups' ticket counter (zero between launches), lrec[l]
-// and labove[l] its record and bit counters.  k_compact_hist leaves every
+// ticket[l] the workgroups' ticket counter (zero between launches; 64-bit
+// for the filter, whose low half also sums the records), lrec[l] and
+// labove[l] its record and bit counters.  k_compact_hist leaves every
 // layer of the range with its exact threshold bucket in st; k_compact_filter
 // writes the layers' mask words and finishes them.
 hipError_t launch_compact_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
@@ -224,8 +225,8 @@ hipError_t launch_compact_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_
                                uint32_t* ticket, uint32_t* lrec, uint32_t* labove, uint32_t* miss);
 hipError_t launch_compact_filter(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, uint32_t parts,
                                  const LayerDesc* layers, const SegDesc* lspace, SelState* st, const uint16_t* key,
-                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, uint32_t* ticket, uint32_t* lrec,
-                                 uint32_t* labove, uint32_t* miss);
+                                 const KeySource& ks, uint64_t* bits, uint64_t* cand, unsigned long long* ticket,
+                                 uint32_t* lrec, uint32_t* labove, uint32_t* miss);
 
 // bits
 hipError_t launch_index_count(hipStream_t s, const uint64_t* bits, uint32_t n_words, uint32_t* block_sums);
