@@ -63,16 +63,19 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def alg_bytes(N: int, W: int, ksum: int):
+def alg_bytes(N: int, W: int, ksum: int, L: int):
     """Algorithmic bytes of one step and of its dense pass.  Per element the
     dense pass reads W bf16 gradients, W fp32 residuals, m and the mask bit,
     and writes the W residuals and a 16-bit statistic key (10W + 6.125); at
-    each masked element it also writes the W sparse-buffer entries.  The step
-    adds the key's read by the selection and the new mask's bits (10W + 8.25
-    per element), and per masked element the buffers' reads and the
-    idx / m / x reads and x / m / v / next-idx writes (8W + 28)."""
-    dense = N * (10 * W + 6.125) + 4 * W * ksum
-    step = N * (10 * W + 8.25) + ksum * (8 * W + 28)
+    each masked element it also writes the W sparse-buffer entries and the
+    m stash (4W + 4); and it zeroes the selection's histogram rows (8192
+    words per layer).  The step adds the key's read by the selection and the
+    new mask's bits (10W + 8.25 per element), and per masked element the
+    buffers' reads and the idx / m / x reads and x / m / v / next-idx writes
+    (8W + 28)."""
+    rows = 4 * 8192 * L
+    dense = N * (10 * W + 6.125) + (4 * W + 4) * ksum + rows
+    step = N * (10 * W + 8.25) + ksum * (8 * W + 28) + rows
     return dense, step
 
 
@@ -308,7 +311,7 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interle
     state.destroy()
     del state, sets
     torch.cuda.empty_cache()
-    dense_b, step_b = alg_bytes(N, wl.W, ksum)
+    dense_b, step_b = alg_bytes(N, wl.W, ksum, len(wl.tensors))
     ef_ms = phase_ms["ef_compact"] / nrec
     return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}",
             "layout": "worker-interleaved" if interleaved else "per worker", "steps": steps, "warmup": warmup,
@@ -587,7 +590,7 @@ def main() -> int:
         del a, b
         log("calibration copy of 1 GiB done")
 
-    dense_b, step_b = alg_bytes(N, W, ksum)
+    dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors))
     ef_ms = phase_ms["ef_compact"] / nrec
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
     step_gbps = step_b / (ms * 1e-3) / 1e9
