@@ -367,13 +367,17 @@ int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* o
 int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream);
 
 /* Optional per-phase timing of scape_step with HIP events recorded on the
- * step's stream (and on the context's update stream).  On the sampled
- * selection path the W-way reduction and update run on the context's own
- * stream beside the mask selection's record passes (they share no data the
- * other writes), starting once the key filter is done, so those two phases
- * overlap: both are measured from the end of the dense pass.  On the compact
- * path (see scape_set_select_path) the update follows the selection on the
- * step's stream and every phase is measured alone.  Phases: */
+ * step's stream (and on the context's update stream).  Where the mask keeps
+ * at most 1/32 of the elements (and the residuals are on the device), the
+ * dense pass itself finishes the W-way reduction and the update at the mask's
+ * positions (that phase then reads about 0) and the selection follows it.
+ * Otherwise the update is a pass of its own: on the sampled selection path it
+ * runs on the context's own stream beside the selection's record passes
+ * (they share no data the other writes), starting once the key filter is
+ * done, so those two phases overlap and both are measured from the end of the
+ * dense pass; on the compact path (see scape_set_select_path) it follows the
+ * selection on the step's stream and every phase is measured alone.
+ * Phases: */
 #define SCAPE_PHASE_EF_COMPACT 0    /* error feedback, candidates, compaction, statistic */
 #define SCAPE_PHASE_REDUCE_UPDATE 1 /* W-way reduction, reconstruction, v/m/x update     */
 #define SCAPE_PHASE_MASK_SELECT 2   /* per-layer top-k into bits                        */

@@ -78,21 +78,32 @@ constexpr uint32_t ef_words() {
     return WT == 1 ? SCAPE_EF_W1 : 1;
 }
 
-template <int WT, bool K32>
+// With UPD the pass also finishes the step at the current mask's positions:
+// it has every worker's candidate of an element in registers, so the W-way
+// mean of what the workers send, the reconstruction and the m / v / x update
+// (the same fp32 operations in the same order as k_reduce_update) need no
+// second pass over the sparse buffers.  UPD 1: x and v are separate arrays;
+// UPD 2: x holds (x, v) pairs.  The x load of a masked lane is issued as soon
+// as its mask word is known, beside the element loads; every other lane loads
+// `dummy`, which nothing writes.
+template <int WT, bool K32, int UPD>
 __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
-                                                       WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
+                                                       WorkerPtrs wp, StepScalars sc, float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
                                                        uint16_t* __restrict__ key16, uint32_t* __restrict__ key32,
                                                        float* __restrict__ m_stash, uint32_t* __restrict__ clear,
-                                                       uint32_t n_clear) {
+                                                       uint32_t n_clear, float* __restrict__ x, float* __restrict__ v,
+                                                       const float* __restrict__ dummy) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     constexpr uint32_t kWords = ef_words<WT>();
     // the selection's histogram rows, zeroed on the way (spread over every
     // workgroup; a few KB per layer)
     for (uint32_t i = blockIdx.x * kEfBlock + threadIdx.x; i < n_clear; i += gridDim.x * kEfBlock) clear[i] = 0u;
     const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
-    const uint32_t w0 = (blk * kEfWaves + threadIdx.x / 64) * kWords;
+    // wave-uniform, so the descriptors below are scalar loads
+    const uint32_t w0 = (blk * kEfWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64)) * kWords;
     if (w0 >= n_words) return;
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
@@ -115,6 +126,26 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
             gv[e][i] = stream_load(&wp.g[i][jw]);
         }
     }
+    // the parameters of the masked lanes (UPD), loaded once the element loads
+    // are out (the scheduling barrier keeps the wait for the mask word behind
+    // them)
+    float x0[kWords];
+    f32x2* __restrict__ xv = reinterpret_cast<f32x2*>(x);
+    if (UPD) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t e = 0; e < kWords; ++e) {
+            const uint32_t wc = min(w0 + e, n_words - 1u);
+            const uint64_t word = cur_bits[wc];
+            const uint32_t rank = cur_prefix[wc] + lanes_below(word);
+            const bool msk = ((word >> lane) & 1ull) && rank < k_cap && w0 + e < n_words;
+            const size_t j = (size_t)wc * 64u + lane;
+            if (UPD == 2)
+                x0[e] = (msk ? reinterpret_cast<const f32x2*>(&xv[j]) : reinterpret_cast<const f32x2*>(dummy))->x;
+            else
+                x0[e] = *(msk ? &x[j] : dummy);
+        }
+    }
 #pragma unroll
     for (uint32_t e = 0; e < kWords; ++e) {
         const uint32_t w = w0 + e;
@@ -125,44 +156,75 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
         const uint32_t pre = cur_prefix[w];
         const uint32_t count = info & 127u;
         const int owner = (int)((info >> 8) & 63u);
-        if (lane >= count) continue;  // padding lanes of a layer's last word
+        // padding lanes of a layer's last word store nothing (their mask bits
+        // are clear); the test guards the stores only, so that no load waits
+        // for the descriptor
+        const bool live = lane < count;
         const uint32_t rank = pre + lanes_below(word);
         const bool msk = ((word >> lane) & 1ull) && rank < k_cap;
         const float bm = sc.beta1 * mo[e];
         uint32_t kk = 0;
+        float s = 0.0f;  // the sum of what the workers send, in worker order
 #pragma unroll
         for (int i = 0; i < WMAX; ++i) {
             if (i >= W) break;
             const float a = rv[e][i] + bf16_bits_to_f32(gv[e][i]);
             const float mt = bm + sc.c1 * a;
             if (i == owner) kk = magnitude_key(mt);
-            wp.r[i][jw] = msk ? 0.0f : a;
+            if (live) wp.r[i][jw] = msk ? 0.0f : a;
             if (msk) wp.b[i][rank] = mt;
+            if (UPD) s = i == 0 ? mt : s + mt;
         }
         // the selection reads the top 16 bits; candidates get their full key
         // back from the state (or from key32 when it is asked for)
-        key16[j] = (uint16_t)(kk >> kKeyShift);
-        if (K32) key32[j] = kk;
-        // m before the step, compacted like the sparse buffers: the update pass
-        // reads it contiguously instead of gathering one cache line per position
-        if (msk) m_stash[rank] = mo[e];
+        if (live) key16[j] = (uint16_t)(kk >> kKeyShift);
+        if (K32 && live) key32[j] = kk;
+        if (!UPD) {
+            // m before the step, compacted like the sparse buffers: the update
+            // pass reads it contiguously instead of gathering one line per position
+            if (msk) m_stash[rank] = mo[e];
+        } else if (msk) {
+            const float bb = s / (float)W;
+            const float ghat = (bb - bm) / sc.c1;
+            const float vv = sc.beta2 * (mo[e] * mo[e]) + sc.c2 * (ghat * ghat);
+            float upd = bb / (sqrtf(vv) + sc.eps);
+            if (sc.wd != 0.0f) upd = upd + sc.wd * x0[e];
+            __builtin_nontemporal_store(bb, &m[j]);
+            if (UPD == 2) {
+                f32x2 p;
+                p.x = x0[e] - sc.lr * upd;
+                p.y = vv;
+                xv[j] = p;
+            } else {
+                __builtin_nontemporal_store(vv, &v[j]);
+                x[j] = x0[e] - sc.lr * upd;
+            }
+        }
     }
 }
 
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
-                             const StepScalars& sc, const float* m, const uint64_t* cur_bits,
+                             const StepScalars& sc, float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
-                             float* m_stash, uint32_t* clear, uint32_t n_clear) {
+                             float* m_stash, uint32_t* clear, uint32_t n_clear, int upd, float* x, float* v,
+                             const float* dummy) {
     if (n_words == 0) return n_clear ? launch_fill_u32(s, clear, n_clear, 0u) : hipSuccess;
-#define SCAPE_EF_LAUNCH(WV, K)                                                                                 \
-    hipLaunchKernelGGL((k_ef_compact<WV, K>),                                                                  \
-                       dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())),          \
-                       dim3(kEfBlock), 0, s, word_info, n_words, wp, sc, m, cur_bits, cur_prefix, k_cap, key16, \
-                       key32, m_stash, clear, n_clear)
-#define SCAPE_EF_CASE(WV)                    \
-    case WV:                                 \
-        if (key32) SCAPE_EF_LAUNCH(WV, true); \
-        else SCAPE_EF_LAUNCH(WV, false);      \
+    const dim3 block(kEfBlock);
+#define SCAPE_EF_LAUNCH(WV, K, U)                                                                                  \
+    hipLaunchKernelGGL((k_ef_compact<WV, K, U>),                                                                   \
+                       dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())), block, 0, s, \
+                       word_info, n_words, wp, sc, m, cur_bits, cur_prefix, k_cap, key16, key32, m_stash, clear,   \
+                       n_clear, x, v, dummy)
+#define SCAPE_EF_UPD(WV, K)                          \
+    switch (upd) {                                   \
+        case 1: SCAPE_EF_LAUNCH(WV, K, 1); break;    \
+        case 2: SCAPE_EF_LAUNCH(WV, K, 2); break;    \
+        default: SCAPE_EF_LAUNCH(WV, K, 0); break;   \
+    }
+#define SCAPE_EF_CASE(WV)                     \
+    case WV:                                  \
+        if (key32) SCAPE_EF_UPD(WV, true)     \
+        else SCAPE_EF_UPD(WV, false)          \
         break;
     switch (sc.W) {
         SCAPE_EF_CASE(1)
@@ -173,10 +235,11 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
         SCAPE_EF_CASE(16)
         SCAPE_EF_CASE(32)
         default:
-            if (key32) SCAPE_EF_LAUNCH(0, true);
-            else SCAPE_EF_LAUNCH(0, false);
+            if (key32) SCAPE_EF_UPD(0, true)
+            else SCAPE_EF_UPD(0, false)
     }
 #undef SCAPE_EF_LAUNCH
+#undef SCAPE_EF_UPD
 #undef SCAPE_EF_CASE
     return hipGetLastError();
 }

@@ -126,6 +126,9 @@ constexpr int kProfSlots = 64;
 // the 1.75B workload (W = 4) chunks of 2^16, 2^18, 2^19 and 2^21 words took
 // about 1.5, 1.25, 0.97 and 0.94 s per step.  More slots (3 or 4) were not
 // faster.
+// The dense pass finishes the update itself where the mask keeps at most
+// 1 / kFuseMaxDensityInv of the elements.
+constexpr uint64_t kFuseMaxDensityInv = 32;
 constexpr int kOffloadSlots = 2;
 constexpr size_t kOffloadSlotBytes = size_t(512) << 20;
 constexpr uint32_t kOffloadMinChunkWords = 1u << 12;
@@ -171,6 +174,7 @@ struct scape_ctx {
     SegDesc* d_lspace = nullptr;
     uint32_t* d_lcount = nullptr;
     unsigned long long* d_ltick = nullptr;  // the filter's per-layer tickets
+    float* d_dummy = nullptr;               // 16 bytes no kernel writes (a safe load address)
     int32_t select_path = SCAPE_SELECT_PATH_AUTO;
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
@@ -203,6 +207,7 @@ void free_ctx(scape_ctx* c) {
     hipFree(c->d_lspace);
     hipFree(c->d_lcount);
     hipFree(c->d_ltick);
+    hipFree(c->d_dummy);
     hipFree(c->d_layer_seg0);
     hipFree(c->d_seg_fill);
     hipFree(c->d_seg_above);
@@ -446,10 +451,11 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
             cp.g[i] = wp.g[i] + j0;
         }
         // the first chunk's pass also zeroes the histogram rows
-        SCAPE_HIP(launch_ef_compact(s, c->d_word_info + w0, nw, cp, sc, m + j0, cur->bits + w0,
+        SCAPE_HIP(launch_ef_compact(s, c->d_word_info + w0, nw, cp, sc, const_cast<float*>(m) + j0, cur->bits + w0,
                                     cur->block_prefix + w0, k_cap, key16 + j0, key32 + j0, c->d_m_stash,
                                     chunk == 0 ? c->d_hist : nullptr,
-                                    chunk == 0 ? (uint32_t)c->lay.L * kHistBins : 0u),
+                                    chunk == 0 ? (uint32_t)c->lay.L * kHistBins : 0u, 0, nullptr, nullptr,
+                                    c->d_dummy),
                   "ef_compact");
         SCAPE_HIP(hipEventRecord(c->ev_k[b], s), "offload event");
         SCAPE_HIP(hipStreamWaitEvent(c->s_out[b], c->ev_k[b], 0), "offload wait");
@@ -576,16 +582,37 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
 
     const int slot = prof_begin(ctx);
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
-    // the dense pass also zeroes the selection's histogram rows
+    // The dense pass also zeroes the selection's histogram rows.  With the
+    // residuals on the device and a sparse mask it also finishes the update
+    // at the current mask's positions: it holds every worker's candidate of
+    // an element, so the W-way mean needs no second pass over the sparse
+    // buffers, and the update's scattered x / v / m accesses ride on the
+    // streaming pass instead of competing with the selection.  On a denser
+    // mask (several positions per 64-element word) those accesses cost the
+    // streaming pass more than the separate update takes (measured: faster
+    // at a kept fraction of 1/100, slower at 1/10), so the update stays a
+    // pass of its own there.
+    const bool fuse = !r_on_host && (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
     if (r_on_host) {
         if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
         SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
                                     k_cap, ctx->d_key16, key32, ctx->d_m_stash, ctx->d_hist,
-                                    (uint32_t)L * kHistBins),
+                                    (uint32_t)L * kHistBins, fuse ? (il ? 2 : 1) : 0, x, v, ctx->d_dummy),
                   "ef_compact");
     }
     prof_mark(ctx, slot, 1, s);
+    if (fuse) {
+        // The update read and wrote x, v and m on the current mask only; the
+        // selection reads m off it, and follows on `stream`.
+        if (slot >= 0) ctx->prof[slot].serial = true;
+        if ((rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s))) return rc;
+        prof_mark(ctx, slot, 3, s);
+        prof_mark(ctx, slot, 2, s);  // (the update ran inside the dense pass)
+        if ((rc = run_index(ctx, next, s))) return rc;
+        prof_mark(ctx, slot, 4, s);
+        return SCAPE_OK;
+    }
     if (compact_range(ctx, 0, L) && !r_on_host) {
         // The compact selection is two short launches: forking the update
         // onto its own stream costs more in events than it overlaps, so the
@@ -802,6 +829,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
         (rc = dev_alloc(c, &c->d_lspace, L, "layer record spaces")) ||
         (rc = dev_alloc(c, &c->d_lcount, 3 * L, "layer counters")) ||
         (rc = dev_alloc(c, &c->d_ltick, L, "layer tickets")) ||
+        (rc = dev_alloc(c, &c->d_dummy, 4, "load stand-in")) ||
         (rc = dev_alloc(c, &c->d_vb, c->vb_cap, "record blocks")) ||
         (rc = dev_alloc(c, &c->d_vb_count, c->vb_cap, "record block counts")) ||
         (rc = dev_alloc(c, &c->d_totals, 4, "totals")) || (rc = dev_alloc(c, &c->d_miss, 1, "miss flag")) ||
@@ -834,6 +862,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     if (e == hipSuccess) e = hipMemcpy(c->d_lspace, lspace.data(), L * sizeof(SegDesc), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(c->d_lcount, 0, 3 * L * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(c->d_ltick, 0, L * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(c->d_dummy, 0, 4 * sizeof(float));
     if (e == hipSuccess)
         e = hipMemcpy(c->d_layer_seg0, c->layer_seg0.data(), (L + 1) * sizeof(uint32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess && c->n_words)

@@ -160,10 +160,14 @@ struct StepScalars {
 // elementwise: error feedback, candidates, compaction, statistic, digit-1
 // histogram; then reduction + reconstruction + update.
 // clear[0, n_clear) is zeroed on the way (the selection's histogram rows).
+// upd 0: the update is left to launch_reduce_update (m_stash written);
+// upd 1 / 2: the pass also updates m, v, x at the mask's positions (x and v
+// apart / x holding (x, v) pairs); `dummy` is 8 bytes nothing writes.
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
-                             const StepScalars& sc, const float* m, const uint64_t* cur_bits,
+                             const StepScalars& sc, float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
-                             float* m_stash, uint32_t* clear, uint32_t n_clear);
+                             float* m_stash, uint32_t* clear, uint32_t n_clear, int upd, float* x, float* v,
+                             const float* dummy);
 // xv_pairs: x is an array of (x, v) pairs (x at 2j, v at 2j + 1) and v is
 // not used.
 hipError_t launch_reduce_update(hipStream_t s, const WorkerPtrs& wp, const StepScalars& sc, float* x, float* m,
