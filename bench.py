@@ -63,19 +63,29 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def alg_bytes(N: int, W: int, ksum: int, L: int):
+def fused_update(N_pad: int, ksum: int) -> bool:
+    """Whether the dense pass finishes the update itself: the library does so
+    where the mask keeps at most 1/32 of the elements (residuals on the
+    device)."""
+    return ksum * 32 <= N_pad
+
+
+def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
     """Algorithmic bytes of one step and of its dense pass.  Per element the
     dense pass reads W bf16 gradients, W fp32 residuals, m and the mask bit,
-    and writes the W residuals and a 16-bit statistic key (10W + 6.125); at
-    each masked element it also writes the W sparse-buffer entries and the
-    m stash (4W + 4); and it zeroes the selection's histogram rows (8192
-    words per layer).  The step adds the key's read by the selection and the
-    new mask's bits (10W + 8.25 per element), and per masked element the
-    buffers' reads and the idx / m / x reads and x / m / v / next-idx writes
-    (8W + 28)."""
+    and writes the W residuals and a 16-bit statistic key (10W + 6.125); it
+    zeroes the selection's histogram rows (8192 words per layer); at each
+    masked element it writes the W sparse-buffer entries and either the m
+    stash (4W + 4; the update pass then reads the buffers, the stash, idx and
+    x and writes x, m, v: 4W + 20) or, when it finishes the update itself,
+    reads x and writes x, m, v (4W + 16).  The step adds the key's read by the
+    selection and the new mask's bits (2.125 per element) and the next mask's
+    idx (4 per masked element)."""
     rows = 4 * 8192 * L
-    dense = N * (10 * W + 6.125) + (4 * W + 4) * ksum + rows
-    step = N * (10 * W + 8.25) + ksum * (8 * W + 28) + rows
+    per_masked_dense = 4 * W + 16 if fused else 4 * W + 4
+    per_masked_step = 4 * W + 20 if fused else 8 * W + 28
+    dense = N * (10 * W + 6.125) + per_masked_dense * ksum + rows
+    step = N * (10 * W + 8.25) + per_masked_step * ksum + rows
     return dense, step
 
 
@@ -311,7 +321,7 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interle
     state.destroy()
     del state, sets
     torch.cuda.empty_cache()
-    dense_b, step_b = alg_bytes(N, wl.W, ksum, len(wl.tensors))
+    dense_b, step_b = alg_bytes(N, wl.W, ksum, len(wl.tensors), fused_update(lay.n_pad, ksum))
     ef_ms = phase_ms["ef_compact"] / nrec
     return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}",
             "layout": "worker-interleaved" if interleaved else "per worker", "steps": steps, "warmup": warmup,
@@ -590,7 +600,7 @@ def main() -> int:
         del a, b
         log("calibration copy of 1 GiB done")
 
-    dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors))
+    dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors), fused_update(lay.n_pad, ksum))
     ef_ms = phase_ms["ef_compact"] / nrec
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
     step_gbps = step_b / (ms * 1e-3) / 1e9

@@ -18,16 +18,24 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_algorithmic_bytes_per_element():
     import bench
-    N, W, k = 1_000_000, 4, 10_000
-    dense, step = bench.alg_bytes(N, W, k)
+    N, W, k, L = 1_000_000, 4, 10_000, 3
+    rows = L * 8192 * 4  # the histogram rows the dense pass zeroes
     # dense pass: W bf16 gradients and W fp32 residuals read, W residuals
     # written, m read, a 16-bit key written, one mask bit read; W sparse
-    # entries written per masked element
-    assert dense == N * (2 * W + 4 * W + 4 * W + 4 + 2 + 1 / 8) + k * 4 * W
+    # entries and the m stash written per masked element
+    dense, step = bench.alg_bytes(N, W, k, L, fused=False)
+    assert dense == N * (2 * W + 4 * W + 4 * W + 4 + 2 + 1 / 8) + k * (4 * W + 4) + rows
     # the step adds the key's read by the selection and the next mask's bits,
     # and per masked element the buffers' reads, idx / m-stash / x reads and
     # x / m / v / next-idx writes
-    assert step == N * (10 * W + 4 + 2 + 2 + 1 / 8 + 1 / 8) + k * (4 * W + 4 * W + 7 * 4)
+    assert step == N * (10 * W + 4 + 2 + 2 + 1 / 8 + 1 / 8) + k * (4 * W + 4 * W + 7 * 4) + rows
+    # with the update in the dense pass: per masked element the W sparse
+    # entries written, x read and x / m / v written; the step adds the
+    # next mask's idx
+    dense, step = bench.alg_bytes(N, W, k, L, fused=True)
+    assert dense == N * (2 * W + 4 * W + 4 * W + 4 + 2 + 1 / 8) + k * (4 * W + 4 + 3 * 4) + rows
+    assert step == N * (10 * W + 4 + 2 + 2 + 1 / 8 + 1 / 8) + k * (4 * W + 4 + 3 * 4 + 4) + rows
+    assert bench.fused_update(64 * 32, 64) and not bench.fused_update(64 * 32 - 1, 64)
     assert bench.dense_alg_bytes(N, W) == N * (2 * W + 4 + 4 + 4 + 4 + 4)
 
 
