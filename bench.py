@@ -63,11 +63,11 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def fused_update(N_pad: int, ksum: int) -> bool:
-    """Whether the dense pass finishes the update itself: the library does so
-    where the mask keeps at most 1/32 of the elements (residuals on the
-    device)."""
-    return ksum * 32 <= N_pad
+def fused_update(N_pad: int, ksum: int, on: bool = True) -> bool:
+    """Whether the dense pass finishes the update itself: with that switched
+    on (scape_set_update_in_dense_pass) the library does so where the mask
+    keeps at most 1/32 of the elements (residuals on the device)."""
+    return on and ksum * 32 <= N_pad
 
 
 def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
@@ -286,7 +286,8 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
             "union_density": density, "ms_per_worker_added": sum(add_ms[1:]) / max(len(add_ms) - 1, 1)}
 
 
-def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interleaved: bool = True) -> dict:
+def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interleaved: bool = True,
+                   update_in_dense: bool = False) -> dict:
     """The fused step on another workload shape (with `workers` workers instead
     of the workload's own W when given): state and two gradient batches
     resident, `warmup` untimed steps, then `steps` timed ones."""
@@ -302,6 +303,7 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interle
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
     state = ScapeState(cfg, interleaved=interleaved)
+    sc.scape_set_update_in_dense_pass(state.ctx, update_in_dense)
     lay = state.layout
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
     sets = [grad_set(wl, lay.layer_offset, lay.n_pad, s + 1, interleaved) for s in range(2)]
@@ -321,11 +323,12 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interle
     state.destroy()
     del state, sets
     torch.cuda.empty_cache()
-    dense_b, step_b = alg_bytes(N, wl.W, ksum, len(wl.tensors), fused_update(lay.n_pad, ksum))
+    fused = fused_update(lay.n_pad, ksum, update_in_dense)
+    dense_b, step_b = alg_bytes(N, wl.W, ksum, len(wl.tensors), fused)
     ef_ms = phase_ms["ef_compact"] / nrec
     return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}",
-            "layout": "worker-interleaved" if interleaved else "per worker", "steps": steps, "warmup": warmup,
-            "ms_per_step": ms, "params_per_s": N / (ms * 1e-3), "worker_elements_per_s": wl.W * N / (ms * 1e-3),
+            "layout": "worker-interleaved" if interleaved else "per worker", "update_in_dense_pass": fused,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "params_per_s": N / (ms * 1e-3), "worker_elements_per_s": wl.W * N / (ms * 1e-3),
             "step_alg_GBps": step_b / (ms * 1e-3) / 1e9, "step_hbm_frac": step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "dense_pass_ms": ef_ms, "dense_pass_GBps": dense_b / (ef_ms * 1e-3) / 1e9,
             "dense_pass_hbm_frac": dense_b / (ef_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -536,6 +539,9 @@ def main() -> int:
                     help="seconds of plain device copies before anything else (off by default: allocating and "
                          "freeing its buffers just before the state left the state in memory where the dense "
                          "pass ran 15.3 instead of 13.5-14.2 ms)")
+    ap.add_argument("--update-in-dense-pass", action="store_true",
+                    help="let the dense pass finish the update at sparse masks' positions "
+                         "(scape_set_update_in_dense_pass)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -562,6 +568,7 @@ def main() -> int:
     log(f"workload {wl.name}: {len(wl.tensors)} tensors, N={wl.numel}, W={wl.W}, keep={wl.keep_num}/{wl.keep_den}, "
         f"{'worker-interleaved' if il else 'per-worker'} residuals and gradients")
     state = ScapeState(cfg, interleaved=il)
+    sc.scape_set_update_in_dense_pass(state.ctx, args.update_in_dense_pass)
     lay = state.layout
     N, W, ksum = wl.numel, wl.W, lay.k_total
     workspace = sc.scape_workspace_bytes(state.ctx)
@@ -600,7 +607,8 @@ def main() -> int:
         del a, b
         log("calibration copy of 1 GiB done")
 
-    dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors), fused_update(lay.n_pad, ksum))
+    fused = fused_update(lay.n_pad, ksum, args.update_in_dense_pass)
+    dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors), fused)
     ef_ms = phase_ms["ef_compact"] / nrec
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
     step_gbps = step_b / (ms * 1e-3) / 1e9
@@ -618,7 +626,8 @@ def main() -> int:
     torch.cuda.empty_cache()
     other_layout = None
     if not args.no_other_layout:
-        other_layout = other_workload(wl.name, args.steps, args.warmup, interleaved=not il)
+        other_layout = other_workload(wl.name, args.steps, args.warmup, interleaved=not il,
+                                      update_in_dense=args.update_in_dense_pass)
         log(f"{wl.name} with {other_layout['layout']} residuals and gradients: {other_layout['ms_per_step']:.3f} ms/step, "
             f"dense pass {other_layout['dense_pass_ms']:.3f} ms ({other_layout['dense_pass_GBps']:.0f} GB/s)")
     offload = None
@@ -634,7 +643,7 @@ def main() -> int:
         for name in sorted(synth.WORKLOADS):
             if name == wl.name:
                 continue
-            others[name] = other_workload(name, 5, 2, interleaved=il)
+            others[name] = other_workload(name, 5, 2, interleaved=il, update_in_dense=args.update_in_dense_pass)
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
@@ -645,7 +654,8 @@ def main() -> int:
             f"{graphed['graph_ms_per_step']:.3f} ms")
     one_worker = None
     if not args.no_other_workloads:
-        one_worker = other_workload(wl.name, 5, 2, workers=1, interleaved=il)
+        one_worker = other_workload(wl.name, 5, 2, workers=1, interleaved=il,
+                                    update_in_dense=args.update_in_dense_pass)
         log(f"one worker (W = 1) on {wl.name}: {one_worker['ms_per_step']:.3f} ms/step, dense pass "
             f"{one_worker['dense_pass_GBps']:.0f} GB/s")
     pu = None
@@ -669,7 +679,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "params": N, "tensors": len(wl.tensors), "workers": W,
                    "keep": f"{wl.keep_num}/{wl.keep_den}", "kept_total": ksum, "grad_dtype": "bf16",
-                   "gradient_batches": args.grad_sets,
+                   "gradient_batches": args.grad_sets, "update_in_dense_pass": fused,
                    "layout": "worker-interleaved residuals and gradients" if il else "one residual and gradient "
                              "array per worker"},
         "context_workspace_bytes": workspace,

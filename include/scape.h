@@ -149,6 +149,20 @@ int scape_selection_flags(scape_ctx* ctx, uint32_t* flags);
 #define SCAPE_SELECT_PATH_COMPACT 2
 int scape_set_select_path(scape_ctx* ctx, int32_t path);
 
+/* Where scape_step reduces and applies the update (the results are the same
+ * either way).  on = 1: where the residuals are on the device and the mask
+ * keeps at most 1/32 of the elements, the dense pass does it at the mask's
+ * positions, so no separate update pass runs and the selection follows the
+ * dense pass alone; the scattered x / v / m accesses then share the
+ * streaming pass.  That is faster when the streaming pass has bandwidth to
+ * spare and slower when it has none: measured on the 1.75B workload, the
+ * step took 16.2-17.0 ms against 17.3 ms without, in processes whose
+ * buffers landed on fast pages, and 19.1-19.2 ms against 18.0-18.2 ms in a
+ * fresh GPU's first process.  on = 0 (the default): the update is a pass of
+ * its own.  Host only, takes effect from the next call.
+ * Errors: INVALID_ARG. */
+int scape_set_update_in_dense_pass(scape_ctx* ctx, int32_t on);
+
 /*
  * One SCAPE step on W simulated workers, all resident on this GPU.
  *
@@ -367,11 +381,11 @@ int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* o
 int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream);
 
 /* Optional per-phase timing of scape_step with HIP events recorded on the
- * step's stream (and on the context's update stream).  Where the mask keeps
- * at most 1/32 of the elements (and the residuals are on the device), the
- * dense pass itself finishes the W-way reduction and the update at the mask's
- * positions (that phase then reads about 0) and the selection follows it.
- * Otherwise the update is a pass of its own: on the sampled selection path it
+ * step's stream (and on the context's update stream).  Where the dense pass
+ * finishes the W-way reduction and the update itself (see
+ * scape_set_update_in_dense_pass), that phase reads about 0 and the
+ * selection follows the dense pass.  Otherwise the update is a pass of its
+ * own: on the sampled selection path it
  * runs on the context's own stream beside the selection's record passes
  * (they share no data the other writes), starting once the key filter is
  * done, so those two phases overlap and both are measured from the end of the

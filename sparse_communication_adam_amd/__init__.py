@@ -12,7 +12,7 @@ from ._scape import (  # noqa: F401
     scape_copy_probe, scape_profile_enable, scape_profile_read, scape_reduce_sparse, scape_step, scape_step_offload, scape_unpack,
     scape_step_interleaved, scape_dense_step_interleaved, interleaved_view, scape_workspace_bytes,
     scape_mask_index_static, scape_selection_flags, SELECT_EXACT_HISTOGRAM, SELECT_KEY_PASSES,
-    scape_set_select_path, SELECT_PATH_AUTO, SELECT_PATH_SAMPLED, SELECT_PATH_COMPACT,
+    scape_set_select_path, SELECT_PATH_AUTO, SELECT_PATH_SAMPLED, SELECT_PATH_COMPACT, scape_set_update_in_dense_pass,
     scape_version)
 
 

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "scape_workspace_bytes": [vp, vp],
             "scape_selection_flags": [vp, vp],
             "scape_set_select_path": [vp, i32],
+            "scape_set_update_in_dense_pass": [vp, i32],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_interleaved": [vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
@@ -327,6 +328,14 @@ def scape_set_select_path(ctx: Context, path: int) -> None:
     the sampled multi-pass path, the two-launch compact path, or AUTO (compact
     where every layer of the range has at most 2^22 elements)."""
     _check(lib().scape_set_select_path(ctx.handle, int(path)))
+
+
+def scape_set_update_in_dense_pass(ctx: Context, on: bool) -> None:
+    """From the next call on, let the dense pass finish the reduction and the
+    update at the mask's positions where the residuals are on the device and
+    the mask keeps at most 1/32 of the elements (default: off, the update is
+    a pass of its own)."""
+    _check(lib().scape_set_update_in_dense_pass(ctx.handle, int(bool(on))))
 
 
 def scape_step(ctx: Context, x, m, v, r: Sequence, g: Sequence, cur: Mask, next: Mask, sparse_bufs: Sequence,

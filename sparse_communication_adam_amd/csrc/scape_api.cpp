@@ -126,8 +126,8 @@ constexpr int kProfSlots = 64;
 // the 1.75B workload (W = 4) chunks of 2^16, 2^18, 2^19 and 2^21 words took
 // about 1.5, 1.25, 0.97 and 0.94 s per step.  More slots (3 or 4) were not
 // faster.
-// The dense pass finishes the update itself where the mask keeps at most
-// 1 / kFuseMaxDensityInv of the elements.
+// With the update in the dense pass switched on, the dense pass finishes it
+// where the mask keeps at most 1 / kFuseMaxDensityInv of the elements.
 constexpr uint64_t kFuseMaxDensityInv = 32;
 constexpr int kOffloadSlots = 2;
 constexpr size_t kOffloadSlotBytes = size_t(512) << 20;
@@ -176,6 +176,7 @@ struct scape_ctx {
     unsigned long long* d_ltick = nullptr;  // the filter's per-layer tickets
     float* d_dummy = nullptr;               // 16 bytes no kernel writes (a safe load address)
     int32_t select_path = SCAPE_SELECT_PATH_AUTO;
+    bool update_in_dense = false;           // scape_set_update_in_dense_pass
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -582,17 +583,18 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
 
     const int slot = prof_begin(ctx);
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
-    // The dense pass also zeroes the selection's histogram rows.  With the
-    // residuals on the device and a sparse mask it also finishes the update
-    // at the current mask's positions: it holds every worker's candidate of
-    // an element, so the W-way mean needs no second pass over the sparse
-    // buffers, and the update's scattered x / v / m accesses ride on the
-    // streaming pass instead of competing with the selection.  On a denser
-    // mask (several positions per 64-element word) those accesses cost the
-    // streaming pass more than the separate update takes (measured: faster
-    // at a kept fraction of 1/100, slower at 1/10), so the update stays a
-    // pass of its own there.
-    const bool fuse = !r_on_host && (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
+    // The dense pass also zeroes the selection's histogram rows.  Where the
+    // context asks for it, the residuals are on the device and the mask is
+    // sparse, it also finishes the update at the current mask's positions:
+    // it holds every worker's candidate of an element, so the W-way mean
+    // needs no second pass over the sparse buffers, and the update's
+    // scattered x / v / m accesses ride on the streaming pass instead of
+    // competing with the selection.  On a denser mask (several positions per
+    // 64-element word) those accesses cost the streaming pass more than the
+    // separate update takes (measured: faster at a kept fraction of 1/100,
+    // slower at 1/10), so the update stays a pass of its own there.
+    const bool fuse = ctx->update_in_dense && !r_on_host &&
+                      (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
     if (r_on_host) {
         if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
@@ -884,6 +886,13 @@ int scape_set_select_path(scape_ctx* ctx, int32_t path) {
     if (path != SCAPE_SELECT_PATH_AUTO && path != SCAPE_SELECT_PATH_SAMPLED && path != SCAPE_SELECT_PATH_COMPACT)
         return fail(SCAPE_ERR_INVALID_ARG, "unknown selection path %d", path);
     ctx->select_path = path;
+    return SCAPE_OK;
+}
+
+int scape_set_update_in_dense_pass(scape_ctx* ctx, int32_t on) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (on != 0 && on != 1) return fail(SCAPE_ERR_INVALID_ARG, "update_in_dense_pass takes 0 or 1, not %d", on);
+    ctx->update_in_dense = on != 0;
     return SCAPE_OK;
 }
 

@@ -97,6 +97,7 @@ class GpuRun:
     key_out: bool = True  # ask the step for the full statistic keys (else candidates' keys are recomputed)
     interleaved: bool = False  # residuals and gradients in the worker-interleaved layout
     select_path: Optional[int] = None  # scape_set_select_path (None: the library's default)
+    update_in_dense: bool = False  # scape_set_update_in_dense_pass
     state: object = None
     grads: List[object] = field(default_factory=list)
 
@@ -105,9 +106,10 @@ class GpuRun:
         from sparse_communication_adam_amd.state import ScapeState
         cfg = scape_config(self.wl, self.keep, self.W)
         self.state = ScapeState(cfg, offload=self.offload, interleaved=self.interleaved)
+        import sparse_communication_adam_amd as sc
         if self.select_path is not None:
-            import sparse_communication_adam_amd as sc
             sc.scape_set_select_path(self.state.ctx, self.select_path)
+        sc.scape_set_update_in_dense_pass(self.state.ctx, self.update_in_dense)
         self.layout = self.state.layout
         n = self.layout.n_pad
         if not self.x_zero:
@@ -174,7 +176,8 @@ def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int]
 
 def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, keep=None, W=None,
                init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True,
-               offload=False, key_out=True, interleaved=False, select_path=None) -> Dict[str, int]:
+               offload=False, key_out=True, interleaved=False, select_path=None,
+               update_in_dense=False) -> Dict[str, int]:
     """Run `steps` steps on the GPU (all layers) and the oracle (all layers, or
     the sampled ones) and compare every output of every step."""
     import torch
@@ -185,8 +188,10 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
     log(f"{wl.name}: W={W} L={full.L} n_pad={full.n_pad} k_total={full.k_total} steps={steps} "
         f"oracle layers={len(tensors)} ({lay.n_pad} elements){' residuals on the host' if offload else ''}"
         f"{'' if key_out else ', candidate keys recomputed'}{', worker-interleaved layout' if interleaved else ''}"
-        f"{'' if select_path is None else f', selection path {select_path}'}")
-    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path)
+        f"{'' if select_path is None else f', selection path {select_path}'}"
+        f"{', update in the dense pass' if update_in_dense else ''}")
+    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path,
+                 update_in_dense)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total
     assert list(glay.layer_offset) == full.off.tolist() and list(glay.layer_k) == full.k.tolist()

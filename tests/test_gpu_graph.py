@@ -20,13 +20,14 @@ def gpu():
     yield
 
 
-def _state(wl, interleaved=False):
+def _state(wl, interleaved=False, update_in_dense=False):
     import sparse_communication_adam_amd as sc
     from sparse_communication_adam_amd.state import ScapeState
     cfg = sc.ScapeConfig(layer_numel=wl.layer_sizes, workers=wl.W, keep_num=wl.keep_num, keep_den=wl.keep_den,
                          owner_shards=wl.P, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, eps=wl.eps,
                          weight_decay=wl.weight_decay)
     st = ScapeState(cfg, interleaved=interleaved)
+    sc.scape_set_update_in_dense_pass(st.ctx, update_in_dense)
     synth.params_flat_gpu(wl, st.layout.layer_offset, st.x)
     return st
 
@@ -45,13 +46,14 @@ def _arrays(st):
     return {k: v.view(-1).cpu().numpy().view(np.uint8) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("name,interleaved", [("ragged", False), ("single-1024x1024", False),
-                                             ("ragged", True), ("single-1024x1024", True)])
-def test_graph_replays_match_eager_steps(name, interleaved):
+@pytest.mark.parametrize("name,interleaved,update_in_dense", [
+    ("ragged", False, False), ("single-1024x1024", False, False), ("ragged", True, False),
+    ("single-1024x1024", True, False), ("ragged", False, True), ("ragged", True, True)])
+def test_graph_replays_match_eager_steps(name, interleaved, update_in_dense):
     import torch
     import sparse_communication_adam_amd as sc
     wl = synth.ragged() if name == "ragged" else synth.WORKLOADS[name]
-    eager, graphed = _state(wl, interleaved), _state(wl, interleaved)
+    eager, graphed = _state(wl, interleaved, update_in_dense), _state(wl, interleaved, update_in_dense)
     lay = eager.layout
     bufs = [torch.zeros(lay.n_pad, dtype=torch.int16, device="cuda") for _ in range(wl.W)]
     g_il = torch.zeros(lay.n_pad * wl.W, dtype=torch.int16, device="cuda")

@@ -688,3 +688,75 @@ def test_step_recomputed_keys_edge_cases(path):
 def test_step_recomputed_keys_full_size_sampled_layers(name):
     wl = synth.WORKLOADS[name]
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name], key_out=False))
+
+
+# The update inside the dense pass (scape_set_update_in_dense_pass): where
+# the mask keeps at most 1/32 of the elements the dense pass itself reduces
+# the W candidates and updates x, v and m at the mask's positions, in both
+# residual layouts; denser masks keep the separate update, so the cases at
+# keep 1/10 and 1/1 check that the switch leaves them alone.
+LAYOUTS = pytest.mark.parametrize("interleaved", [False, True], ids=["per-worker", "interleaved"])
+
+
+@LAYOUTS
+@pytest.mark.parametrize("name", ["single-1024x1024", "gpt-345m", "llama-0.55b", "llama-1.75b", "adversarial-ties"])
+def test_step_update_in_dense_pass_oracle_sized(name, interleaved):
+    wl = synth.WORKLOADS[name]
+    small = wl if name == "single-1024x1024" else synth.reduced(wl)
+    _assert_bitexact(run_parity(small, wl.steps, key_out=False, interleaved=interleaved, update_in_dense=True))
+
+
+@LAYOUTS
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 16, 32])
+def test_step_update_in_dense_pass_ragged_worker_counts(W, interleaved):
+    """Every worker count with its own kernel instance, and 3 and 5 without;
+    the ragged layout's last workgroup lies partly past the end."""
+    _assert_bitexact(run_parity(synth.ragged(), 4, W=W, key_out=False, interleaved=interleaved,
+                                update_in_dense=True))
+
+
+@LAYOUTS
+def test_step_update_in_dense_pass_edge_cases(interleaved):
+    """Weight decay at worker counts whose mean rounds, from an empty and a
+    full first mask; special gradient values; zero gradients tied
+    everywhere; keys kept in full; a kept fraction of 1/100."""
+    wl = synth.ragged()
+    kw = dict(interleaved=interleaved, update_in_dense=True)
+    wd = dataclasses.replace(wl, weight_decay=0.1)
+    for W in (3, 5):
+        _assert_bitexact(run_parity(wd, 4, W=W, key_out=False, **kw))
+        _assert_bitexact(run_parity(wd, 3, W=W, key_out=False, keep=(1, 1), init_mask_all=True, **kw))
+    _assert_bitexact(run_parity(wl, 4, grad_override=_special_grads(wl), key_out=False, **kw))
+    zero = lambda step, worker, t: np.zeros(wl.tensors[t].numel, np.uint16)  # noqa: E731
+    _assert_bitexact(run_parity(wl, 3, grad_override=zero, x_zero=True, key_out=False, **kw))
+    _assert_bitexact(run_parity(wl, 4, key_out=True, **kw))
+    _assert_bitexact(run_parity(wl, 4, keep=(1, 100), key_out=False, **kw))
+
+
+@pytest.mark.timeout(900)
+def test_step_update_in_dense_pass_full_size():
+    """The 1.75B shape at full size, worker-interleaved: every output of its
+    largest layers and of sampled small ones against the oracle."""
+    wl = synth.WORKLOADS["llama-1.75b"]
+    _assert_bitexact(run_parity(wl, 3, sample=FULL_LARGEST[wl.name], key_out=False, interleaved=True,
+                                update_in_dense=True))
+    _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[wl.name], key_out=False, interleaved=True,
+                                update_in_dense=True))
+
+
+def test_step_update_in_dense_pass_matches_separate_update():
+    """Both settings give the same bytes for every output, step after step."""
+    import torch
+    wl = synth.reduced(synth.LLAMA175)
+    outs = []
+    for on in (False, True):
+        run = GpuRun(wl, interleaved=True, key_out=False, update_in_dense=on)
+        for t in range(1, 5):
+            run.step(t)
+        torch.cuda.synchronize()
+        st = run.state
+        outs.append([to_np(a).copy() for a in [st.xv, st.m, st.r_il, st.cur_mask.bits, st.cur_mask.idx]
+                     + st.sparse])
+        release(run)
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
