@@ -311,10 +311,13 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 // ---------------------------------------------------------------------------
 // 2. the pass over every key
 
-#ifndef SCAPE_FILTER_WORDS
-#define SCAPE_FILTER_WORDS 8
-#endif
-constexpr int kFilterWords = SCAPE_FILTER_WORDS;  // words per wave per trip
+// Words per wave per trip of a key pass: each is one 2-byte load per lane,
+// and the next trip's loads are in flight while a trip is processed.  The
+// hot key filter takes 16 (measured on 1.75G keys: 4 words 1.24 ms, 8 0.91,
+// 16 0.82, 24 0.91, 32 0.95: more in flight until the registers cut the
+// waves per SIMD); the other passes keep 8.
+constexpr int kFilterWords = 8;
+constexpr int kFilterWordsHot = 16;
 constexpr int kWaveStage = 256;                 // staged records per wave (2 KB): 8 KB per workgroup
 
 // Full keys of up to kFetch records of layer L (the bits of `sel` say
@@ -437,7 +440,7 @@ using KeyPassLds = KeyPassLdsT<kWaves>;
 
 // With kFullKeys the records are stored with their full keys, from *ks.
 // Returns (in every thread) the record slots the workgroup reserved.
-template <bool kRecords, bool kHist = false, int kThreads = kBlock, bool kFullKeys = false>
+template <bool kRecords, bool kHist = false, int kThreads = kBlock, bool kFullKeys = false, int kWords = kFilterWords>
 __device__ __forceinline__ uint32_t key_pass(KeyPassLdsT<kThreads / 64>& lds, const TileDesc& t, const LayerDesc& L, const SegDesc& G,
                                          uint32_t sel_from, uint32_t cand_lo, uint32_t cand_hi,
                                          const uint16_t* __restrict__ key, uint64_t* __restrict__ bits,
@@ -457,34 +460,43 @@ __device__ __forceinline__ uint32_t key_pass(KeyPassLdsT<kThreads / 64>& lds, co
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     uint64_t* stage = lds.rec[wave];
     // the digit tests on the stored 16-bit key (digit = key >> 3): above is
-    // key >= k_above, a record key - k_lo <= k_span (unsigned)
-    const uint32_t k_above = sel_from << kDigit1FromKey16;
+    // key >= k_above; with records the window ends where the bits begin
+    // (every caller passes sel_from = cand_hi + 1), so a record is a key >=
+    // k_lo that is not above
+    const uint32_t k_above = (kRecords ? cand_hi + 1u : sel_from) << kDigit1FromKey16;
     const uint32_t k_lo = cand_lo << kDigit1FromKey16;
-    const uint32_t k_span = kRecords ? ((cand_hi - cand_lo) << kDigit1FromKey16) | ((1u << kDigit1FromKey16) - 1u) : 0u;
     uint32_t n_st = 0;
     uint32_t flushed = 0;     // records this wave reserved and stored mid-tile
     uint32_t above_lane = 0;  // bits set in the mask words this lane wrote
-    constexpr uint32_t kStride = kNW * kFilterWords;
+    constexpr uint32_t kStride = kNW * kWords;
     // The next trip's keys are loaded before this trip is processed.  Every
     // load is issued, at a word of the tile (a word past its end loads the
     // tile's last word and is skipped), so the count of loads in flight is
     // the same on every path and the next trip's loads stay in flight while
     // this one is processed.
-    uint32_t nxt[kFilterWords];
+    uint32_t nxt[kWords];
     auto load_keys = [&](uint32_t w0, uint32_t* kv) {
+        if (w0 + kWords <= t.w1) {  // one base address, the words at immediate offsets
+            const uint16_t* p = key + (size_t)w0 * 64u + lane;
 #pragma unroll
-        for (int e = 0; e < kFilterWords; ++e) kv[e] = key[(size_t)min(w0 + e, t.w1 - 1u) * 64u + lane];
+            for (int e = 0; e < kWords; ++e) kv[e] = p[e * 64];
+        } else {
+#pragma unroll
+            for (int e = 0; e < kWords; ++e) kv[e] = key[(size_t)min(w0 + e, t.w1 - 1u) * 64u + lane];
+        }
     };
     // One word: its mask word (kept by lane e) and its records.  `left` is
     // the number of its keys inside the layer (64 for every word but a
     // layer's last).
     auto one_word = [&](auto partial, uint32_t w, uint32_t kw, int e, uint32_t left, uint64_t lmask,
-                        uint64_t& mine) {
-        const uint64_t word = wave_ballot(kw >= k_above) & lmask;
-        if (lane == (uint32_t)e) mine = word;
+                        uint32_t& mine_lo, uint32_t& mine_hi) {
+        const uint64_t above = wave_ballot(kw >= k_above);
+        const uint64_t word = above & lmask;
+        // lane e keeps the word: two lane writes, no per-lane select
+        write_lane(mine_lo, (uint32_t)word, e);
+        write_lane(mine_hi, (uint32_t)(word >> 32), e);
         if (kRecords) {
-            const bool in_range = kw - k_lo <= k_span;
-            const uint64_t cb = wave_ballot(in_range) & lmask;
+            const uint64_t cb = wave_ballot(kw >= k_lo) & ~above & lmask;
             if (cb) {
                 if (n_st > (uint32_t)(kWaveStage - 64)) {  // no room for a whole word: flush
                     uint32_t first = 0;
@@ -496,7 +508,7 @@ __device__ __forceinline__ uint32_t key_pass(KeyPassLdsT<kThreads / 64>& lds, co
                     flushed += n_st;
                     n_st = 0;
                 }
-                const bool rec = in_range && (!decltype(partial)::value || lane < left);
+                const bool rec = (cb >> lane) & 1u;
                 if (rec)
                     stage[n_st + lanes_below(cb)] = ((uint64_t)(kw << kKeyShift) << 32) | (uint64_t)(w * 64u + lane - L.off);
                 n_st += (uint32_t)__popcll(cb);
@@ -508,27 +520,30 @@ __device__ __forceinline__ uint32_t key_pass(KeyPassLdsT<kThreads / 64>& lds, co
             }
         }
     };
-    load_keys(t.w0 + wave * kFilterWords, nxt);
-    for (uint32_t w0 = t.w0 + wave * kFilterWords; w0 < t.w1; w0 += kStride) {
-        uint32_t kv[kFilterWords];
+    load_keys(t.w0 + wave * kWords, nxt);
+    for (uint32_t w0 = t.w0 + wave * kWords; w0 < t.w1; w0 += kStride) {
+        uint32_t kv[kWords];
 #pragma unroll
-        for (int e = 0; e < kFilterWords; ++e) kv[e] = nxt[e];
+        for (int e = 0; e < kWords; ++e) kv[e] = nxt[e];
         load_keys(w0 + kStride, nxt);
-        uint64_t mine = 0;  // lane e: the mask word of word w0 + e
-        if (w0 + kFilterWords <= t.w1 && (w0 + kFilterWords) * 64u <= lend) {
+        uint32_t mine_lo = 0, mine_hi = 0;  // lane e: the mask word of word w0 + e
+        if (w0 + kWords <= t.w1 && (w0 + kWords) * 64u <= lend) {
             // every word of the trip is in the tile and wholly in the layer
 #pragma unroll
-            for (int e = 0; e < kFilterWords; ++e) one_word(std::false_type{}, w0 + e, kv[e], e, 64u, ~0ull, mine);
+            for (int e = 0; e < kWords; ++e)
+                one_word(std::false_type{}, w0 + e, kv[e], e, 64u, ~0ull, mine_lo, mine_hi);
         } else {
 #pragma unroll
-            for (int e = 0; e < kFilterWords; ++e) {
+            for (int e = 0; e < kWords; ++e) {
                 const uint32_t w = w0 + e;
                 if (w >= t.w1) break;
                 const uint32_t left = lend - w * 64u;  // >= 1 for a word of the tile
-                one_word(std::true_type{}, w, kv[e], e, left, left >= 64u ? ~0ull : (1ull << left) - 1ull, mine);
+                one_word(std::true_type{}, w, kv[e], e, left, left >= 64u ? ~0ull : (1ull << left) - 1ull, mine_lo,
+                         mine_hi);
             }
         }
-        if (lane < (uint32_t)kFilterWords && w0 + lane < t.w1) {
+        const uint64_t mine = ((uint64_t)mine_hi << 32) | mine_lo;
+        if (lane < (uint32_t)kWords && w0 + lane < t.w1) {
             bits[w0 + lane] = mine;
             above_lane += (uint32_t)__popcll(mine);
         }
@@ -578,7 +593,8 @@ __global__ __launch_bounds__(kBlock) void k_filter(const TileDesc* __restrict__ 
     __shared__ KeyPassLds lds;
     // no window (nothing to select, or an empty sample): no bits, no records
     if (win)
-        key_pass<true, true>(lds, t, L, G, S.n_hi + 1, S.n_lo, S.n_hi, key, bits, seg_fill, cand, seg_above,
+        key_pass<true, true, kBlock, false, kFilterWordsHot>(lds, t, L, G, S.n_hi + 1, S.n_lo, S.n_hi, key, bits,
+                                                             seg_fill, cand, seg_above,
                              hist + (size_t)t.layer * kHistBins);
     else  // no window (nothing to select, or an empty sample): no bits, no records
         key_pass<false>(lds, t, L, G, (uint32_t)kDigit1Bins, 1u, 0u, key, bits, seg_fill, cand, seg_above);

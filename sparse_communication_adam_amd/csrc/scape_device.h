@@ -15,6 +15,18 @@ __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 // an integer and compares it again, two more vector instructions per use.
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// The compiler's lane-write intrinsic (v_writelane_b32), which this clang
+// does not expose as a builtin.  Called through the intrinsic rather than
+// written as inline assembly, so that the compiler sees the operands and
+// inserts the wait states a lane write needs after a vector instruction
+// that wrote its scalar source (a comparison's result, for one).
+__device__ int scape_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Lane `lane` (a constant) of v takes the wave-uniform value u.
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t u, int lane) {
+    v = (uint32_t)scape_writelane_i32((int)u, lane, (int)v);
+}
+
 // Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8),
 // each with its own L2 and translation caches.  xcd_block(b, n) renumbers the
 // n workgroups so that each XCD's share is one contiguous run of [0, n), in
