@@ -872,6 +872,7 @@ int scape_init(const scape_config* cfg, scape_ctx** out) {
     if (e == hipSuccess) e = hipMemset(c->d_hist, 0, L * kHistBins * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(c->d_sel, 0, L * sizeof(SelState));
     if (e == hipSuccess) e = hipMemset(c->d_totals, 0, 4 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(c->d_miss, 0, sizeof(uint32_t));  // no flags before the first selection
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         free_ctx(c);
