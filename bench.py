@@ -460,6 +460,31 @@ def graph_step(name: str, steps: int = 20, warmup: int = 2) -> dict:
     return out
 
 
+def shaped_probe(state, g_il, W: int, reps: int = 5):
+    """scape_stream_probe with the dense pass's traffic over the step's own
+    buffers (same pages): read the W workers' residuals (4W bytes per
+    element) and bf16 gradients (2W) and m (4), write the residuals back in
+    place (4W) and a 2-byte key.  None where a width would pass 16 bytes
+    (W > 4).  The step's state is garbage afterwards."""
+    import torch
+    import sparse_communication_adam_amd as sc
+    if 4 * W > 16:
+        return None
+    n_words = state.layout.n_pad // 64
+    srcs, sw = [state.r_il, g_il, state.m], [4 * W, 2 * W, 4]
+    dsts, dw = [state.r_il, state.key], [4 * W, 2]
+    sc.scape_stream_probe(srcs, sw, dsts, dw, n_words)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        sc.scape_stream_probe(srcs, sw, dsts, dw, n_words)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    nbytes = n_words * 64 * (sum(sw) + sum(dw))
+    return {"ms": ms, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes_per_element": sum(sw) + sum(dw)}
+
+
 def spin_up(seconds: float) -> None:
     """Plain device-to-device copies for `seconds`: an idle GPU takes a while
     to reach its steady memory and fabric clocks."""
@@ -611,6 +636,10 @@ def main() -> int:
     dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors), fused)
     ef_ms = phase_ms["ef_compact"] / nrec
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
+    shaped = shaped_probe(state, sets[0], W) if il else None
+    if shaped:
+        log(f"a pass of the dense pass's shape over the same buffers: {shaped['ms']:.3f} ms, "
+            f"{shaped['GBps']:.0f} GB/s (the dense pass: {ef_gbps / shaped['GBps']:.3f} of it)")
     step_gbps = step_b / (ms * 1e-3) / 1e9
     traffic = counter_traffic(wl.name)
     offsets, n_pad = list(lay.layer_offset), lay.n_pad
@@ -691,7 +720,9 @@ def main() -> int:
         "roofline": {"kernel": "scape_k_ef_compact (dense pass)", "bound": "hbm", "achieved": ef_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
-                     "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps},
+                     "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps,
+                     "shaped_probe": shaped,
+                     "frac_of_shaped_probe": ef_gbps / shaped["GBps"] if shaped else None},
     }
     if other_layout is not None:
         result["other_layout_step"] = other_layout

@@ -380,6 +380,23 @@ int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* o
  * with.  bytes = 0 enqueues nothing.  Errors: INVALID_ARG, ALIGN, SHAPE, HIP. */
 int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream);
 
+/* Measurement helper, not a step of the method: a pass with a chosen
+ * traffic shape and no other work, to compare a kernel with the rate the
+ * memory system gives that shape.  It reads n_src device arrays and writes
+ * n_dst device arrays (each 0..4, not both 0; host arrays of pointers and
+ * widths) over n_words 64-element words: element e of array i spans
+ * width[i] bytes (2, 4, 8 or 16) at byte e * width[i], so a word of it is
+ * 64 * width[i] bytes.  Each lane reads its element of every source, all
+ * loads issued before any is used, and writes to every destination the XOR
+ * of the 32-bit parts it read (a 2-byte element zero-extended), repeated to
+ * the destination's width (low half for width 2).  A destination may be a
+ * source (read, then written in place).  The same one-shot, XCD-aware order
+ * and non-temporal accesses as the dense pass.  n_words = 0 enqueues
+ * nothing.  Errors: INVALID_ARG, ALIGN (an array not aligned to its width),
+ * SHAPE, HIP. */
+int scape_stream_probe(const void* const* src, const uint32_t* src_width, int32_t n_src, void* const* dst,
+                       const uint32_t* dst_width, int32_t n_dst, uint64_t n_words, void* stream);
+
 /* Optional per-phase timing of scape_step with HIP events recorded on the
  * step's stream (and on the context's update stream).  Where the dense pass
  * finishes the W-way reduction and the update itself (see

@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "scape_profile_enable": [vp, i32],
             "scape_profile_read": [vp, vp, vp],
             "scape_copy_probe": [vp, vp, ctypes.c_uint64, vp],
+            "scape_stream_probe": [vp, vp, i32, vp, vp, i32, ctypes.c_uint64, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -492,6 +493,25 @@ def scape_copy_probe(src, dst, nbytes: Optional[int] = None, stream=None) -> Non
         if t.numel() * t.element_size() < nbytes:
             raise ValueError(f"{name} is smaller than {nbytes} bytes")
     _check(lib().scape_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)))
+
+
+def scape_stream_probe(srcs: Sequence, src_widths: Sequence[int], dsts: Sequence, dst_widths: Sequence[int],
+                       n_words: int, stream=None) -> None:
+    """A pass that reads every tensor of srcs and writes every tensor of dsts
+    over n_words 64-element words, width bytes per element (2, 4, 8 or 16)
+    each, with no other work (scape_stream_probe in include/scape.h)."""
+    import torch
+    for t, w in list(zip(srcs, src_widths)) + list(zip(dsts, dst_widths)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("arrays must be contiguous device tensors")
+        if t.numel() * t.element_size() < int(n_words) * 64 * int(w):
+            raise ValueError(f"an array of {t.numel() * t.element_size()} bytes is smaller than "
+                             f"{n_words} words of width {w}")
+    sw = (ctypes.c_uint32 * max(len(srcs), 1))(*[int(w) for w in src_widths])
+    dw = (ctypes.c_uint32 * max(len(dsts), 1))(*[int(w) for w in dst_widths])
+    _check(lib().scape_stream_probe(_ptr_array([t.data_ptr() for t in srcs]), sw, len(srcs),
+                                    _ptr_array([t.data_ptr() for t in dsts]), dw, len(dsts), int(n_words),
+                                    _stream(stream)))
 
 
 def scape_profile_enable(ctx: Context, enable: bool = True) -> None:

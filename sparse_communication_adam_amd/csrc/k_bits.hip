@@ -346,4 +346,63 @@ hipError_t launch_copy_probe(hipStream_t s, const void* src, void* dst, uint64_t
     return hipGetLastError();
 }
 
+// Stream probe: a pass of a given traffic shape and nothing else.  A wave
+// per 64-element word reads its lanes' chunk of each source (width bytes
+// per lane: 2, 4, 8 or 16), all loads issued before any is used, and
+// writes to each destination the XOR of every 32-bit part it read,
+// repeated to the destination's width.  Non-temporal loads and stores,
+// one-shot workgroups in the dense pass's XCD-aware order.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 probe_load(const uint8_t* base, uint32_t width, size_t e) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    const uint8_t* p = base + e * width;
+    switch (width) {
+        case 2: v.x = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)); break;
+        case 4: v.x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); break;
+        case 8: {
+            const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            v.x = t.x;
+            v.y = t.y;
+            break;
+        }
+        default: v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); break;
+    }
+    return v;
+}
+
+__device__ __forceinline__ void probe_store(uint8_t* base, uint32_t width, size_t e, uint32_t x) {
+    uint8_t* p = base + e * width;
+    switch (width) {
+        case 2: __builtin_nontemporal_store((uint16_t)x, reinterpret_cast<uint16_t*>(p)); break;
+        case 4: __builtin_nontemporal_store(x, reinterpret_cast<uint32_t*>(p)); break;
+        case 8: __builtin_nontemporal_store(u32x2{x, x}, reinterpret_cast<u32x2*>(p)); break;
+        default: __builtin_nontemporal_store(u32x4{x, x, x, x}, reinterpret_cast<u32x4*>(p)); break;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_stream_probe(StreamProbe a, uint32_t n_words) {
+    const uint32_t w = xcd_block(blockIdx.x, gridDim.x) * kWaves + threadIdx.x / 64;
+    if (w >= n_words) return;
+    const size_t e = (size_t)w * 64 + (threadIdx.x & 63);
+    u32x4 v[kStreamProbeMax];
+#pragma unroll
+    for (int i = 0; i < kStreamProbeMax; ++i)
+        if (i < a.n_src) v[i] = probe_load(a.src[i], a.src_width[i], e);
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < kStreamProbeMax; ++i)
+        if (i < a.n_src) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+#pragma unroll
+    for (int i = 0; i < kStreamProbeMax; ++i)
+        if (i < a.n_dst) probe_store(a.dst[i], a.dst_width[i], e, x);
+}
+
+hipError_t launch_stream_probe(hipStream_t s, const StreamProbe& a, uint32_t n_words) {
+    if (n_words == 0) return hipSuccess;
+    const uint32_t blocks = (n_words + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(k_stream_probe, dim3(blocks), dim3(kBlock), 0, s, a, n_words);
+    return hipGetLastError();
+}
+
 }  // namespace scape

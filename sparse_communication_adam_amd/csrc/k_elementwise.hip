@@ -41,9 +41,14 @@ namespace scape {
 // 16-bit descriptor gives the owner worker (bits 8..13) and the number of
 // elements of the word inside its layer (bits 0..6, 1..64; 0 = padding).
 // Every worker's loads are issued before any store.
-// The dense pass loads its streamed arrays non-temporally: that keeps the
-// sparse buffers and the m stash, which the update pass reads next, in the
-// caches (measured faster; non-temporal stores here made the update slower).
+// The dense pass loads and stores its streamed arrays (gradients,
+// residuals, m, keys) non-temporally, and writes the sparse buffers and the
+// m stash, which the update pass reads next, through the caches.  The
+// streamed stores matter most: with plain residual and key stores the pass
+// ran at 0.87 of a pass that only moves the same bytes over the same buffers
+// in a fresh GPU's first process, with non-temporal ones at 0.96-1.0
+// (1.75B shape: 14.5 against 13.0 ms); non-temporal stores to the sparse
+// buffers made the update slower.
 template <typename T>
 __device__ __forceinline__ T stream_load(const T* p) {
     return __builtin_nontemporal_load(p);
@@ -171,13 +176,13 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
             const float a = rv[e][i] + bf16_bits_to_f32(gv[e][i]);
             const float mt = bm + sc.c1 * a;
             if (i == owner) kk = magnitude_key(mt);
-            if (live) wp.r[i][jw] = msk ? 0.0f : a;
+            if (live) __builtin_nontemporal_store(msk ? 0.0f : a, &wp.r[i][jw]);
             if (msk) wp.b[i][rank] = mt;
             if (UPD) s = i == 0 ? mt : s + mt;
         }
         // the selection reads the top 16 bits; candidates get their full key
         // back from the state (or from key32 when it is asked for)
-        if (live) key16[j] = (uint16_t)(kk >> kKeyShift);
+        if (live) __builtin_nontemporal_store((uint16_t)(kk >> kKeyShift), &key16[j]);
         if (K32 && live) key32[j] = kk;
         if (!UPD) {
             // m before the step, compacted like the sparse buffers: the update
@@ -203,6 +208,89 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
     }
 }
 
+// Worker lanes (worker-interleaved arrays, W = 4, no update in the pass, no
+// full keys asked for): a wave's lanes split into W groups of 64 / W, a
+// group per worker, and each lane takes W consecutive elements of its
+// worker's part of the word, which in the interleaved layout are the lane's
+// own 4W (residuals) or 2W (gradients) bytes of the word.  (At W = 8 the
+// same mapping was much slower on the 0.35B and 0.55B shapes: every lane
+// then reads 32 bytes of m that seven other groups read too.)  Every array then moves as one access per lane of 4W bytes
+// (residuals; m, whose same elements every group reads), 2W (gradients)
+// or 2W (keys, stored by the owner's group) instead of W accesses of 4 or
+// 2 bytes: the same bytes in a quarter of the memory instructions.  The
+// arithmetic and its order per element and worker are those above.
+#ifndef SCAPE_EF_WL
+#define SCAPE_EF_WL 1
+#endif
+template <int W>
+__global__ __launch_bounds__(kEfBlock) void k_ef_wl(const uint16_t* __restrict__ word_info, uint32_t n_words,
+                                                  WorkerPtrs wp, StepScalars sc, const float* __restrict__ m,
+                                                  const uint64_t* __restrict__ cur_bits,
+                                                  const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
+                                                  uint16_t* __restrict__ key16, float* __restrict__ m_stash,
+                                                  uint32_t* __restrict__ clear, uint32_t n_clear) {
+    typedef float fvec __attribute__((ext_vector_type(W)));
+    typedef uint16_t hvec __attribute__((ext_vector_type(W)));
+    constexpr uint32_t kLanesPerWorker = 64 / W;
+    for (uint32_t i = blockIdx.x * kEfBlock + threadIdx.x; i < n_clear; i += gridDim.x * kEfBlock) clear[i] = 0u;
+    const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t w = blk * kEfWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    if (w >= n_words) return;
+    const uint32_t lane = lane_id();
+    const uint32_t wi = lane / kLanesPerWorker, q = lane % kLanesPerWorker;
+    // worker wi's q-th group of W elements of word w: in the interleaved
+    // layout (word stride 64 W, worker i at 64 i) that is element w * 64 W +
+    // lane * W of the array worker 0's pointer starts
+    float* rp = wp.r[0] + (size_t)w * (64u * W) + lane * W;
+    const uint16_t* gp = wp.g[0] + (size_t)w * (64u * W) + lane * W;
+    const fvec rv = stream_load(reinterpret_cast<const fvec*>(rp));
+    const hvec gv = stream_load(reinterpret_cast<const hvec*>(gp));
+    // the group's sparse buffer, chosen among the workers' pointers held in
+    // scalar registers (the empty statements keep the compiler from turning
+    // the choice into a per-lane load of the argument block)
+    float* bp;
+    {
+        float* bs[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            bs[i] = wp.b[i];
+            asm volatile("" : "+s"(bs[i]));
+        }
+        bp = bs[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) bp = wi == (uint32_t)i ? bs[i] : bp;
+    }
+    const fvec mv = stream_load(reinterpret_cast<const fvec*>(m + (size_t)w * 64u + q * W));
+    const uint32_t info = word_info[w];
+    const uint64_t word = cur_bits[w];
+    const uint32_t pre = cur_prefix[w];
+    const uint32_t count = info & 127u;
+    const uint32_t owner = (info >> 8) & 63u;
+    // the lane's W mask bits, and the set bits of the word before them
+    const uint32_t p0 = q * W;
+    const uint32_t slice = (uint32_t)(word >> p0) & ((1u << W) - 1u);
+    const uint32_t below = pre + (uint32_t)__popcll(word & ((1ull << p0) - 1ull));
+    fvec out;
+    hvec kout;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        const bool live = p0 + e < count;  // padding elements keep their residual
+        const uint32_t rank = below + (uint32_t)__popc(slice & ((1u << e) - 1u));
+        const bool msk = ((slice >> e) & 1u) && rank < k_cap;
+        const float bm = sc.beta1 * mv[e];
+        const float a = rv[e] + bf16_bits_to_f32(gv[e]);
+        const float mt = bm + sc.c1 * a;
+        out[e] = live ? (msk ? 0.0f : a) : rv[e];
+        kout[e] = live ? (uint16_t)(magnitude_key(mt) >> kKeyShift) : (uint16_t)0;
+        if (msk) {
+            bp[rank] = mt;
+            if (wi == 0) m_stash[rank] = mv[e];
+        }
+    }
+    __builtin_nontemporal_store(out, reinterpret_cast<fvec*>(rp));
+    if (wi == owner) __builtin_nontemporal_store(kout, reinterpret_cast<hvec*>(key16 + (size_t)w * 64u + q * W));
+}
+
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
@@ -210,6 +298,11 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
                              const float* dummy) {
     if (n_words == 0) return n_clear ? launch_fill_u32(s, clear, n_clear, 0u) : hipSuccess;
     const dim3 block(kEfBlock);
+    if (SCAPE_EF_WL && upd == 0 && !key32 && sc.W == 4 && wp.ws == 64u * 4u) {
+        hipLaunchKernelGGL(k_ef_wl<4>, dim3((n_words + kEfWaves - 1) / kEfWaves), block, 0, s, word_info, n_words, wp,
+                           sc, m, cur_bits, cur_prefix, k_cap, key16, m_stash, clear, n_clear);
+        return hipGetLastError();
+    }
 #define SCAPE_EF_LAUNCH(WV, K, U)                                                                                  \
     hipLaunchKernelGGL((k_ef_compact<WV, K, U>),                                                                   \
                        dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())), block, 0, s, \

@@ -1077,6 +1077,35 @@ int scape_copy_probe(const void* src, void* dst, uint64_t bytes, void* stream) {
     return SCAPE_OK;
 }
 
+int scape_stream_probe(const void* const* src, const uint32_t* src_width, int32_t n_src, void* const* dst,
+                       const uint32_t* dst_width, int32_t n_dst, uint64_t n_words, void* stream) {
+    if (n_src < 0 || n_src > kStreamProbeMax || n_dst < 0 || n_dst > kStreamProbeMax || n_src + n_dst == 0)
+        return fail(SCAPE_ERR_INVALID_ARG, "n_src and n_dst must be 0..%d, not both 0", kStreamProbeMax);
+    if ((n_src && (!src || !src_width)) || (n_dst && (!dst || !dst_width)))
+        return fail(SCAPE_ERR_INVALID_ARG, "array lists must not be NULL");
+    if (n_words > 0xFFFFFFFFull - kWaves) return fail(SCAPE_ERR_SHAPE, "n_words too large");
+    StreamProbe a{};
+    a.n_src = n_src;
+    a.n_dst = n_dst;
+    auto ok_width = [](uint32_t w) { return w == 2 || w == 4 || w == 8 || w == 16; };
+    for (int i = 0; i < n_src; ++i) {
+        if (!src[i]) return fail(SCAPE_ERR_INVALID_ARG, "src[%d] is NULL", i);
+        if (!ok_width(src_width[i])) return fail(SCAPE_ERR_INVALID_ARG, "src_width[%d] must be 2, 4, 8 or 16", i);
+        if (!aligned(src[i], src_width[i])) return fail(SCAPE_ERR_ALIGN, "src[%d] must be aligned to its width", i);
+        a.src[i] = static_cast<const uint8_t*>(src[i]);
+        a.src_width[i] = src_width[i];
+    }
+    for (int i = 0; i < n_dst; ++i) {
+        if (!dst[i]) return fail(SCAPE_ERR_INVALID_ARG, "dst[%d] is NULL", i);
+        if (!ok_width(dst_width[i])) return fail(SCAPE_ERR_INVALID_ARG, "dst_width[%d] must be 2, 4, 8 or 16", i);
+        if (!aligned(dst[i], dst_width[i])) return fail(SCAPE_ERR_ALIGN, "dst[%d] must be aligned to its width", i);
+        a.dst[i] = static_cast<uint8_t*>(dst[i]);
+        a.dst_width[i] = dst_width[i];
+    }
+    SCAPE_HIP(launch_stream_probe((hipStream_t)stream, a, (uint32_t)n_words), "stream_probe");
+    return SCAPE_OK;
+}
+
 int scape_reduce_sparse(const float* const* bufs, int32_t W, int64_t k, float* out, void* stream) {
     if (W < 1 || W > SCAPE_MAX_WORKERS) return fail(SCAPE_ERR_INVALID_ARG, "W must be in 1..%d", SCAPE_MAX_WORKERS);
     if (k < 0) return fail(SCAPE_ERR_INVALID_ARG, "k must be >= 0");

@@ -248,5 +248,15 @@ hipError_t launch_or_words(hipStream_t s, const uint64_t* src, uint64_t* acc, ui
 hipError_t launch_pack(hipStream_t s, const uint8_t* pred, int64_t n, uint64_t* bits);
 hipError_t launch_unpack(hipStream_t s, const uint64_t* bits, int64_t n, uint8_t* pred);
 hipError_t launch_copy_probe(hipStream_t s, const void* src, void* dst, uint64_t n16);
+// A pass that reads n_src arrays and writes n_dst arrays word by word,
+// width bytes per lane each (2, 4, 8 or 16), and does nothing else.
+constexpr int kStreamProbeMax = 4;
+struct StreamProbe {
+    const uint8_t* src[kStreamProbeMax];
+    uint8_t* dst[kStreamProbeMax];
+    uint32_t src_width[kStreamProbeMax], dst_width[kStreamProbeMax];
+    int32_t n_src, n_dst;
+};
+hipError_t launch_stream_probe(hipStream_t s, const StreamProbe& a, uint32_t n_words);
 
 }  // namespace scape

@@ -126,6 +126,14 @@ def test_null_arguments_rejected_before_any_launch(sc):
     assert lib.scape_copy_probe(ctypes.c_void_p(16), ctypes.c_void_p(8), 16, None) == -3  # dst misaligned
     assert lib.scape_copy_probe(ctypes.c_void_p(16), ctypes.c_void_p(32), 24, None) == -2  # not whole 16-byte units
     assert lib.scape_init(None, None) == -1
+    assert lib.scape_stream_probe(None, None, 0, None, None, 0, 4, None) == -1  # no arrays
+    assert lib.scape_stream_probe(None, None, 5, None, None, 0, 4, None) == -1  # too many
+    w3 = (ctypes.c_uint32 * 1)(3)
+    one = (ctypes.c_void_p * 1)(16)
+    assert lib.scape_stream_probe(one, w3, 1, None, None, 0, 4, None) == -1  # width 3
+    w8 = (ctypes.c_uint32 * 1)(8)
+    odd = (ctypes.c_void_p * 1)(4)
+    assert lib.scape_stream_probe(odd, w8, 1, None, None, 0, 4, None) == -3  # not aligned to its width
 
 
 def test_init_without_gpu_reports_hip_error(sc):
