@@ -717,7 +717,7 @@ def main() -> int:
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
         "device_copy_GBps": copy_gbps, "stream_copy_GBps": stream_gbps,
-        "roofline": {"kernel": "scape_k_ef_compact (dense pass)", "bound": "hbm", "achieved": ef_gbps,
+        "roofline": {"kernel": "dense pass (k_ef_wl<4> at W = 4 in the interleaved layout, else k_ef_compact)", "bound": "hbm", "achieved": ef_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
                      "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps,
