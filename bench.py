@@ -89,9 +89,20 @@ def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
     return dense, step
 
 
+def dense_kernel_name(W: int, interleaved: bool, fused: bool) -> str:
+    """The dense-pass kernel the library launches for this configuration
+    (residuals on the device, keys not asked for)."""
+    if fused:
+        return f"k_ef_compact<{W if W in (1, 2, 3, 4, 8, 16, 32) else 0}, false, {2 if interleaved else 1}> (with the update)"
+    if interleaved and W == 4:
+        return "k_ef_wl<4>"
+    return f"k_ef_compact<{W if W in (1, 2, 3, 4, 8, 16, 32) else 0}, false, 0>"
+
+
 def kernel_source_hash() -> str:
-    """Hash of what the dense pass is compiled from: its kernel and launcher,
-    the device helpers, and the constants and argument structs it uses."""
+    """Hash of what the dense pass is compiled from: its kernels and launcher,
+    the device helpers, and the constants and argument structs it uses, with
+    comments left out."""
     csrc = os.path.join(ROOT, "sparse_communication_adam_amd", "csrc")
     el = open(os.path.join(csrc, "k_elementwise.hip")).read()
     a = el.index("// Dense pass, one-shot layout")   # the dense pass's section: helpers, knobs, kernel
@@ -101,19 +112,30 @@ def kernel_source_hash() -> str:
     for pat in (r"constexpr int kBlock = .*?;", r"constexpr int kWaves = .*?;", r"struct WorkerPtrs \{.*?\};",
                 r"struct StepScalars \{.*?\};"):
         parts.append(re.search(pat, hdr, re.S).group(0))
-    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
+    # comments and blank lines do not change the compiled kernel
+    code = []
+    for part in parts:
+        for line in part.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
+def counter_traffic(workload: str, fused: bool):
     """HBM bytes per dense-pass launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+    summary, if it was taken on the current kernel source and on the same
+    kind of pass (with or without the update in it)."""
     path = os.path.join(ROOT, "profiles", f"ef_compact_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"kernel source hash:\s*`?([0-9a-f]+)", text)
     val = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
+    kind = re.search(r"update in the dense pass:\s*(yes|no)", text)
+    if not src or not val or not kind or src.group(1) != kernel_source_hash():
+        return None
+    if (kind.group(1) == "yes") != fused:
         return None
     return float(val.group(1))
 
@@ -287,7 +309,7 @@ def fill_in(wl, cfg, layer_offset, n_pad: int) -> dict:
 
 
 def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interleaved: bool = True,
-                   update_in_dense: bool = False) -> dict:
+                   update_in_dense: bool = True) -> dict:
     """The fused step on another workload shape (with `workers` workers instead
     of the workload's own W when given): state and two gradient batches
     resident, `warmup` untimed steps, then `steps` timed ones."""
@@ -564,9 +586,9 @@ def main() -> int:
                     help="seconds of plain device copies before anything else (off by default: allocating and "
                          "freeing its buffers just before the state left the state in memory where the dense "
                          "pass ran 15.3 instead of 13.5-14.2 ms)")
-    ap.add_argument("--update-in-dense-pass", action="store_true",
-                    help="let the dense pass finish the update at sparse masks' positions "
-                         "(scape_set_update_in_dense_pass)")
+    ap.add_argument("--separate-update", action="store_true",
+                    help="make the update a pass of its own instead of finishing it in the dense pass "
+                         "(scape_set_update_in_dense_pass(0))")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -593,7 +615,7 @@ def main() -> int:
     log(f"workload {wl.name}: {len(wl.tensors)} tensors, N={wl.numel}, W={wl.W}, keep={wl.keep_num}/{wl.keep_den}, "
         f"{'worker-interleaved' if il else 'per-worker'} residuals and gradients")
     state = ScapeState(cfg, interleaved=il)
-    sc.scape_set_update_in_dense_pass(state.ctx, args.update_in_dense_pass)
+    sc.scape_set_update_in_dense_pass(state.ctx, not args.separate_update)
     lay = state.layout
     N, W, ksum = wl.numel, wl.W, lay.k_total
     workspace = sc.scape_workspace_bytes(state.ctx)
@@ -632,7 +654,7 @@ def main() -> int:
         del a, b
         log("calibration copy of 1 GiB done")
 
-    fused = fused_update(lay.n_pad, ksum, args.update_in_dense_pass)
+    fused = fused_update(lay.n_pad, ksum, not args.separate_update)
     dense_b, step_b = alg_bytes(N, W, ksum, len(wl.tensors), fused)
     ef_ms = phase_ms["ef_compact"] / nrec
     ef_gbps = dense_b / (ef_ms * 1e-3) / 1e9
@@ -641,7 +663,7 @@ def main() -> int:
         log(f"a pass of the dense pass's shape over the same buffers: {shaped['ms']:.3f} ms, "
             f"{shaped['GBps']:.0f} GB/s (the dense pass: {ef_gbps / shaped['GBps']:.3f} of it)")
     step_gbps = step_b / (ms * 1e-3) / 1e9
-    traffic = counter_traffic(wl.name)
+    traffic = counter_traffic(wl.name, fused)
     offsets, n_pad = list(lay.layer_offset), lay.n_pad
     state.destroy()
     del state
@@ -656,7 +678,7 @@ def main() -> int:
     other_layout = None
     if not args.no_other_layout:
         other_layout = other_workload(wl.name, args.steps, args.warmup, interleaved=not il,
-                                      update_in_dense=args.update_in_dense_pass)
+                                      update_in_dense=not args.separate_update)
         log(f"{wl.name} with {other_layout['layout']} residuals and gradients: {other_layout['ms_per_step']:.3f} ms/step, "
             f"dense pass {other_layout['dense_pass_ms']:.3f} ms ({other_layout['dense_pass_GBps']:.0f} GB/s)")
     offload = None
@@ -672,7 +694,7 @@ def main() -> int:
         for name in sorted(synth.WORKLOADS):
             if name == wl.name:
                 continue
-            others[name] = other_workload(name, 5, 2, interleaved=il, update_in_dense=args.update_in_dense_pass)
+            others[name] = other_workload(name, 5, 2, interleaved=il, update_in_dense=not args.separate_update)
             o = others[name]
             log(f"workload {name}: {o['ms_per_step']:.3f} ms/step, {o['params_per_s'] / 1e9:.1f}G params/s, "
                 f"dense pass {o['dense_pass_GBps']:.0f} GB/s")
@@ -684,7 +706,7 @@ def main() -> int:
     one_worker = None
     if not args.no_other_workloads:
         one_worker = other_workload(wl.name, 5, 2, workers=1, interleaved=il,
-                                    update_in_dense=args.update_in_dense_pass)
+                                    update_in_dense=not args.separate_update)
         log(f"one worker (W = 1) on {wl.name}: {one_worker['ms_per_step']:.3f} ms/step, dense pass "
             f"{one_worker['dense_pass_GBps']:.0f} GB/s")
     pu = None
@@ -717,7 +739,7 @@ def main() -> int:
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
         "device_copy_GBps": copy_gbps, "stream_copy_GBps": stream_gbps,
-        "roofline": {"kernel": "dense pass (k_ef_wl<4> at W = 4 in the interleaved layout, else k_ef_compact)", "bound": "hbm", "achieved": ef_gbps,
+        "roofline": {"kernel": dense_kernel_name(W, il, fused), "bound": "hbm", "achieved": ef_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
                      "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps,

@@ -150,17 +150,14 @@ int scape_selection_flags(scape_ctx* ctx, uint32_t* flags);
 int scape_set_select_path(scape_ctx* ctx, int32_t path);
 
 /* Where scape_step reduces and applies the update (the results are the same
- * either way).  on = 1: where the residuals are on the device and the mask
- * keeps at most 1/32 of the elements, the dense pass does it at the mask's
- * positions, so no separate update pass runs and the selection follows the
- * dense pass alone; the scattered x / v / m accesses then share the
- * streaming pass.  That is faster when the streaming pass has bandwidth to
- * spare and slower when it has none: measured on the 1.75B workload, the
- * step took 16.2-17.0 ms against 17.3 ms without, in processes whose
- * buffers landed on fast pages, and 19.1-19.2 ms against 18.0-18.2 ms in a
- * fresh GPU's first process.  on = 0 (the default): the update is a pass of
- * its own.  Host only, takes effect from the next call.
- * Errors: INVALID_ARG. */
+ * either way).  on = 1 (the default): where the residuals are on the device
+ * and the mask keeps at most 1/32 of the elements, the dense pass does it at
+ * the mask's positions (it holds every worker's candidate of an element), so
+ * no separate update pass runs and the selection follows the dense pass
+ * alone.  Measured on the 1.75B workload in a fresh GPU's first process: a
+ * step of 15.75-15.78 ms against 16.22-16.25 ms with the update as a pass of
+ * its own.  on = 0: the update is a pass of its own, beside the selection.
+ * Host only, takes effect from the next call.  Errors: INVALID_ARG. */
 int scape_set_update_in_dense_pass(scape_ctx* ctx, int32_t on);
 
 /*

@@ -212,13 +212,16 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
 // full keys asked for): a wave's lanes split into W groups of 64 / W, a
 // group per worker, and each lane takes W consecutive elements of its
 // worker's part of the word, which in the interleaved layout are the lane's
-// own 4W (residuals) or 2W (gradients) bytes of the word.  (At W = 8 the
-// same mapping was much slower on the 0.35B and 0.55B shapes: every lane
-// then reads 32 bytes of m that seven other groups read too.)  Every array then moves as one access per lane of 4W bytes
-// (residuals; m, whose same elements every group reads), 2W (gradients)
-// or 2W (keys, stored by the owner's group) instead of W accesses of 4 or
-// 2 bytes: the same bytes in a quarter of the memory instructions.  The
-// arithmetic and its order per element and worker are those above.
+// own 4W (residuals) or 2W (gradients) bytes of the word.  Every array then
+// moves as one access per lane of 4W bytes (residuals; m, whose same
+// elements every group reads), 2W (gradients) or 2W (keys, stored by the
+// owner's group) instead of W accesses of 4 or 2 bytes: the same bytes in a
+// quarter of the memory instructions.  The arithmetic and its order per
+// element and worker are those above.  (At W = 8 the same mapping was much
+// slower on the 0.35B and 0.55B shapes: every lane then reads 32 bytes of m
+// that seven other groups read too.  With the update in the pass it was no
+// faster than the mapping above, whether the workers' candidates met through
+// lane shuffles or through LDS.)
 #ifndef SCAPE_EF_WL
 #define SCAPE_EF_WL 1
 #endif

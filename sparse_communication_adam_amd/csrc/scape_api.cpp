@@ -176,7 +176,7 @@ struct scape_ctx {
     unsigned long long* d_ltick = nullptr;  // the filter's per-layer tickets
     float* d_dummy = nullptr;               // 16 bytes no kernel writes (a safe load address)
     int32_t select_path = SCAPE_SELECT_PATH_AUTO;
-    bool update_in_dense = false;           // scape_set_update_in_dense_pass
+    bool update_in_dense = true;            // scape_set_update_in_dense_pass
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
