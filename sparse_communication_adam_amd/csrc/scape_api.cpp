@@ -128,7 +128,10 @@ constexpr int kProfSlots = 64;
 // faster.
 // With the update in the dense pass switched on, the dense pass finishes it
 // where the mask keeps at most 1 / kFuseMaxDensityInv of the elements.
-constexpr uint64_t kFuseMaxDensityInv = 32;
+#ifndef SCAPE_FUSE_MAX_DENSITY_INV
+#define SCAPE_FUSE_MAX_DENSITY_INV 32
+#endif
+constexpr uint64_t kFuseMaxDensityInv = SCAPE_FUSE_MAX_DENSITY_INV;
 constexpr int kOffloadSlots = 2;
 constexpr size_t kOffloadSlotBytes = size_t(512) << 20;
 constexpr uint32_t kOffloadMinChunkWords = 1u << 12;
