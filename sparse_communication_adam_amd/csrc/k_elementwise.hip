@@ -87,10 +87,15 @@ constexpr uint32_t ef_words() {
 // it has every worker's candidate of an element in registers, so the W-way
 // mean of what the workers send, the reconstruction and the m / v / x update
 // (the same fp32 operations in the same order as k_reduce_update) need no
-// second pass over the sparse buffers.  UPD 1: x and v are separate arrays;
-// UPD 2: x holds (x, v) pairs.  The x load of a masked lane is issued as soon
-// as its mask word is known, beside the element loads; every other lane loads
-// `dummy`, which nothing writes.
+// second pass over the sparse buffers.  UPD 1 and 3: x and v are separate
+// arrays; UPD 2 and 4: x holds (x, v) pairs.  UPD 1 and 2 (sparse masks):
+// only masked lanes touch x, v and m; the x load of a masked lane is issued
+// as soon as its mask word is known, beside the element loads, and every
+// other lane loads `dummy`, which nothing writes.  UPD 3 and 4 (denser
+// masks, where most lines of x, v and m hold a masked element anyway): every
+// lane streams its x and v in with the element loads and writes x, v and m
+// back, the old values where it is not masked, so those arrays move as whole
+// lines instead of scattered partial ones.
 template <int WT, bool K32, int UPD>
 __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
                                                        WorkerPtrs wp, StepScalars sc, float* __restrict__ m,
@@ -119,6 +124,10 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
     float mo[kWords];
     float rv[kWords][WMAX];
     uint16_t gv[kWords][WMAX];
+    constexpr bool kPairs = UPD == 2 || UPD == 4;  // x holds (x, v) pairs
+    constexpr bool kFull = UPD >= 3;                // every lane stores x, v and m
+    float x0[kWords], v0[kWords];
+    f32x2* __restrict__ xv = reinterpret_cast<f32x2*>(x);
 #pragma unroll
     for (uint32_t e = 0; e < kWords; ++e) {
         const size_t wc = min(w0 + e, n_words - 1u);
@@ -130,13 +139,19 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
             rv[e][i] = stream_load(&wp.r[i][jw]);
             gv[e][i] = stream_load(&wp.g[i][jw]);
         }
+        if (kFull && kPairs) {
+            const f32x2 p = stream_load(&xv[j]);
+            x0[e] = p.x;
+            v0[e] = p.y;
+        } else if (kFull) {
+            x0[e] = stream_load(&x[j]);
+            v0[e] = stream_load(&v[j]);
+        }
     }
-    // the parameters of the masked lanes (UPD), loaded once the element loads
-    // are out (the scheduling barrier keeps the wait for the mask word behind
-    // them)
-    float x0[kWords];
-    f32x2* __restrict__ xv = reinterpret_cast<f32x2*>(x);
-    if (UPD) {
+    // the parameters of the masked lanes (UPD 1, 2), loaded once the element
+    // loads are out (the scheduling barrier keeps the wait for the mask word
+    // behind them)
+    if (UPD && !kFull) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t e = 0; e < kWords; ++e) {
@@ -188,6 +203,26 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
             // m before the step, compacted like the sparse buffers: the update
             // pass reads it contiguously instead of gathering one line per position
             if (msk) m_stash[rank] = mo[e];
+        } else if (kFull) {
+            // every lane computes; the unmasked ones store what they loaded
+            const float bb = s / (float)W;
+            const float ghat = (bb - bm) / sc.c1;
+            const float vv = sc.beta2 * (mo[e] * mo[e]) + sc.c2 * (ghat * ghat);
+            float upd = bb / (sqrtf(vv) + sc.eps);
+            if (sc.wd != 0.0f) upd = upd + sc.wd * x0[e];
+            const float xn = x0[e] - sc.lr * upd;
+            if (live) {
+                __builtin_nontemporal_store(msk ? bb : mo[e], &m[j]);
+                if (kPairs) {
+                    f32x2 p;
+                    p.x = msk ? xn : x0[e];
+                    p.y = msk ? vv : v0[e];
+                    __builtin_nontemporal_store(p, &xv[j]);
+                } else {
+                    __builtin_nontemporal_store(msk ? xn : x0[e], &x[j]);
+                    __builtin_nontemporal_store(msk ? vv : v0[e], &v[j]);
+                }
+            }
         } else if (msk) {
             const float bb = s / (float)W;
             const float ghat = (bb - bm) / sc.c1;
@@ -315,6 +350,8 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
     switch (upd) {                                   \
         case 1: SCAPE_EF_LAUNCH(WV, K, 1); break;    \
         case 2: SCAPE_EF_LAUNCH(WV, K, 2); break;    \
+        case 3: SCAPE_EF_LAUNCH(WV, K, 3); break;    \
+        case 4: SCAPE_EF_LAUNCH(WV, K, 4); break;    \
         default: SCAPE_EF_LAUNCH(WV, K, 0); break;   \
     }
 #define SCAPE_EF_CASE(WV)                     \

@@ -126,10 +126,15 @@ constexpr int kProfSlots = 64;
 // the 1.75B workload (W = 4) chunks of 2^16, 2^18, 2^19 and 2^21 words took
 // about 1.5, 1.25, 0.97 and 0.94 s per step.  More slots (3 or 4) were not
 // faster.
-// With the update in the dense pass switched on, the dense pass finishes it
-// where the mask keeps at most 1 / kFuseMaxDensityInv of the elements.
+// With the update in the dense pass switched on, the dense pass touches x,
+// v and m at the masked elements only where the mask keeps at most
+// 1 / kFuseMaxDensityInv of the elements, and streams them whole on denser
+// masks (SCAPE_FUSE_DENSE 0: denser masks keep the separate update).
 #ifndef SCAPE_FUSE_MAX_DENSITY_INV
 #define SCAPE_FUSE_MAX_DENSITY_INV 32
+#endif
+#ifndef SCAPE_FUSE_DENSE
+#define SCAPE_FUSE_DENSE 1
 #endif
 constexpr uint64_t kFuseMaxDensityInv = SCAPE_FUSE_MAX_DENSITY_INV;
 constexpr int kOffloadSlots = 2;
@@ -587,28 +592,30 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     const int slot = prof_begin(ctx);
     prof_mark(ctx, slot, 0, s);  // the first phase brackets the dense pass alone
     // The dense pass also zeroes the selection's histogram rows.  Where the
-    // context asks for it, the residuals are on the device and the mask is
-    // sparse, it also finishes the update at the current mask's positions:
-    // it holds every worker's candidate of an element, so the W-way mean
-    // needs no second pass over the sparse buffers, and the update's
-    // scattered x / v / m accesses ride on the streaming pass instead of
-    // competing with the selection.  On a denser mask (several positions per
-    // 64-element word) those accesses cost the streaming pass more than the
-    // separate update takes (measured: faster at a kept fraction of 1/100,
-    // slower at 1/10), so the update stays a pass of its own there.
-    const bool fuse = ctx->update_in_dense && !r_on_host &&
-                      (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
+    // context asks for it and the residuals are on the device, it also
+    // finishes the update at the current mask's positions: it holds every
+    // worker's candidate of an element, so the W-way mean needs no second
+    // pass over the sparse buffers, and the update's x / v / m accesses ride
+    // on the streaming pass instead of competing with the selection.  On a
+    // sparse mask only the masked elements' x, v and m are touched; on a
+    // denser one (several positions per 64-element word) scattered accesses
+    // to them cost the pass more than the separate update takes (measured
+    // at a kept fraction of 1/10), so there the pass streams x, v and m
+    // whole and writes back the unmasked elements' old values.
+    const bool sparse_mask = (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
+    const bool fuse = ctx->update_in_dense && !r_on_host && (sparse_mask || SCAPE_FUSE_DENSE);
+    const int upd = !fuse ? 0 : sparse_mask ? (il ? 2 : 1) : (il ? 4 : 3);
     if (r_on_host) {
         if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
         SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
                                     k_cap, ctx->d_key16, key32, ctx->d_m_stash, ctx->d_hist,
-                                    (uint32_t)L * kHistBins, fuse ? (il ? 2 : 1) : 0, x, v, ctx->d_dummy),
+                                    (uint32_t)L * kHistBins, upd, x, v, ctx->d_dummy),
                   "ef_compact");
     }
     prof_mark(ctx, slot, 1, s);
     if (fuse) {
-        // The update read and wrote x, v and m on the current mask only; the
+        // The update changed x, v and m on the current mask only; the
         // selection reads m off it, and follows on `stream`.
         if (slot >= 0) ctx->prof[slot].serial = true;
         if ((rc = run_select(ctx, 0, L, 0, n_tiles, ctx->d_key16, ks, next->bits, s))) return rc;
