@@ -65,9 +65,16 @@ def log(msg: str) -> None:
 
 def fused_update(N_pad: int, ksum: int, on: bool = True) -> bool:
     """Whether the dense pass finishes the update itself: with that switched
-    on (scape_set_update_in_dense_pass) the library does so where the mask
-    keeps at most 1/32 of the elements (residuals on the device)."""
-    return on and ksum * 32 <= N_pad
+    on (scape_set_update_in_dense_pass) the library does so at every mask
+    density (residuals on the device)."""
+    return on
+
+
+def streams_whole(N_pad: int, ksum: int) -> bool:
+    """Whether the update inside the dense pass streams x, v and m whole
+    (masks keeping more than 1/32 of the elements) rather than touching the
+    masked elements only."""
+    return ksum * 32 > N_pad
 
 
 def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
@@ -78,7 +85,8 @@ def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
     masked element it writes the W sparse-buffer entries and either the m
     stash (4W + 4; the update pass then reads the buffers, the stash, idx and
     x and writes x, m, v: 4W + 20) or, when it finishes the update itself,
-    reads x and writes x, m, v (4W + 16).  The step adds the key's read by the
+    reads x and writes x, m, v (4W + 16; on dense masks the kernel moves x, v
+    and m whole, by choice, but only the masked elements' bytes count).  The step adds the key's read by the
     selection and the new mask's bits (2.125 per element) and the next mask's
     idx (4 per masked element)."""
     rows = 4 * 8192 * L
@@ -89,11 +97,12 @@ def alg_bytes(N: int, W: int, ksum: int, L: int, fused: bool):
     return dense, step
 
 
-def dense_kernel_name(W: int, interleaved: bool, fused: bool) -> str:
+def dense_kernel_name(W: int, interleaved: bool, fused: bool, whole: bool = False) -> str:
     """The dense-pass kernel the library launches for this configuration
     (residuals on the device, keys not asked for)."""
     if fused:
-        return f"k_ef_compact<{W if W in (1, 2, 3, 4, 8, 16, 32) else 0}, false, {2 if interleaved else 1}> (with the update)"
+        upd = (4 if interleaved else 3) if whole else (2 if interleaved else 1)
+        return f"k_ef_compact<{W if W in (1, 2, 3, 4, 8, 16, 32) else 0}, false, {upd}> (with the update)"
     if interleaved and W == 4:
         return "k_ef_wl<4>"
     return f"k_ef_compact<{W if W in (1, 2, 3, 4, 8, 16, 32) else 0}, false, 0>"
@@ -350,6 +359,7 @@ def other_workload(name: str, steps: int, warmup: int, workers: int = 0, interle
     ef_ms = phase_ms["ef_compact"] / nrec
     return {"params": N, "workers": wl.W, "keep": f"{wl.keep_num}/{wl.keep_den}",
             "layout": "worker-interleaved" if interleaved else "per worker", "update_in_dense_pass": fused,
+            "dense_pass_kernel": dense_kernel_name(wl.W, interleaved, fused, streams_whole(lay.n_pad, ksum)),
             "steps": steps, "warmup": warmup, "ms_per_step": ms, "params_per_s": N / (ms * 1e-3), "worker_elements_per_s": wl.W * N / (ms * 1e-3),
             "step_alg_GBps": step_b / (ms * 1e-3) / 1e9, "step_hbm_frac": step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "dense_pass_ms": ef_ms, "dense_pass_GBps": dense_b / (ef_ms * 1e-3) / 1e9,
@@ -739,7 +749,7 @@ def main() -> int:
         "step_alg_GBps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "phase_ms": {k: v / nrec for k, v in phase_ms.items()},
         "device_copy_GBps": copy_gbps, "stream_copy_GBps": stream_gbps,
-        "roofline": {"kernel": dense_kernel_name(W, il, fused), "bound": "hbm", "achieved": ef_gbps,
+        "roofline": {"kernel": dense_kernel_name(W, il, fused, streams_whole(lay.n_pad, ksum)), "bound": "hbm", "achieved": ef_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ef_gbps / HBM_PEAK_GBPS,
                      "alg_bytes_per_launch": dense_b, "mean_launch_ms": ef_ms, "traffic": traffic,
                      "stream_copy_GBps": stream_gbps, "frac_of_stream_copy": ef_gbps / stream_gbps,

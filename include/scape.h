@@ -150,14 +150,17 @@ int scape_selection_flags(scape_ctx* ctx, uint32_t* flags);
 int scape_set_select_path(scape_ctx* ctx, int32_t path);
 
 /* Where scape_step reduces and applies the update (the results are the same
- * either way).  on = 1 (the default): where the residuals are on the device
- * and the mask keeps at most 1/32 of the elements, the dense pass does it at
- * the mask's positions (it holds every worker's candidate of an element), so
- * no separate update pass runs and the selection follows the dense pass
- * alone.  Measured on the 1.75B workload in a fresh GPU's first process: a
- * step of 15.75-15.78 ms against 16.22-16.25 ms with the update as a pass of
- * its own.  on = 0: the update is a pass of its own, beside the selection.
- * Host only, takes effect from the next call.  Errors: INVALID_ARG. */
+ * either way).  on = 1 (the default): where the residuals are on the device,
+ * the dense pass does it at the mask's positions (it holds every worker's
+ * candidate of an element), so no separate update pass runs and the
+ * selection follows the dense pass alone.  Where the mask keeps at most 1/32
+ * of the elements the pass touches x, v and m at the masked elements only;
+ * on denser masks it streams them whole and stores the other elements' old
+ * values back.  Measured in a fresh GPU's first process: the 1.75B workload
+ * (keep 1/100) 15.75-15.78 ms against 16.22-16.25 ms with the update as a
+ * pass of its own, the GPT-345M-shaped one (keep 1/10) 7.58 against 7.92 ms.
+ * on = 0: the update is a pass of its own, beside the selection.  Host only,
+ * takes effect from the next call.  Errors: INVALID_ARG. */
 int scape_set_update_in_dense_pass(scape_ctx* ctx, int32_t on);
 
 /*

@@ -35,7 +35,10 @@ def test_algorithmic_bytes_per_element():
     dense, step = bench.alg_bytes(N, W, k, L, fused=True)
     assert dense == N * (2 * W + 4 * W + 4 * W + 4 + 2 + 1 / 8) + k * (4 * W + 4 + 3 * 4) + rows
     assert step == N * (10 * W + 4 + 2 + 2 + 1 / 8 + 1 / 8) + k * (4 * W + 4 + 3 * 4 + 4) + rows
-    assert bench.fused_update(64 * 32, 64) and not bench.fused_update(64 * 32 - 1, 64)
+    assert bench.fused_update(64 * 32, 64) and bench.fused_update(64 * 32 - 1, 64)
+    assert not bench.fused_update(64 * 32, 64, on=False)
+    assert not bench.streams_whole(64 * 32, 64) and bench.streams_whole(64 * 32 - 1, 64)
+    assert bench.dense_kernel_name(8, True, True, True) == "k_ef_compact<8, false, 4> (with the update)"
     assert bench.dense_alg_bytes(N, W) == N * (2 * W + 4 + 4 + 4 + 4 + 4)
 
 
