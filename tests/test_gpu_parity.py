@@ -690,11 +690,12 @@ def test_step_recomputed_keys_full_size_sampled_layers(name):
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[name], key_out=False))
 
 
-# The update inside the dense pass (scape_set_update_in_dense_pass): where
-# the mask keeps at most 1/32 of the elements the dense pass itself reduces
-# the W candidates and updates x, v and m at the mask's positions, in both
-# residual layouts; denser masks keep the separate update, so the cases at
-# keep 1/10 and 1/1 check that the switch leaves them alone.
+# The update inside the dense pass (scape_set_update_in_dense_pass): the
+# dense pass itself reduces the W candidates and updates x, v and m at the
+# mask's positions, in both residual layouts.  Where the mask keeps at most
+# 1/32 of the elements it touches x, v and m at those positions only (the
+# cases at keep 1/100 and 1/1000); on denser masks it streams them whole and
+# stores the old values back elsewhere (keep 1/10 and 1/1).
 LAYOUTS = pytest.mark.parametrize("interleaved", [False, True], ids=["per-worker", "interleaved"])
 
 
@@ -734,10 +735,13 @@ def test_step_update_in_dense_pass_edge_cases(interleaved):
 
 
 @pytest.mark.timeout(900)
-def test_step_update_in_dense_pass_full_size():
-    """The 1.75B shape at full size, worker-interleaved: every output of its
+@pytest.mark.parametrize("name", ["llama-1.75b", "gpt-345m"])
+def test_step_update_in_dense_pass_full_size(name):
+    """At full size, worker-interleaved, as bench.py times them: the 1.75B
+    shape (keep 1/100: x, v and m touched at the masked elements only) and
+    the GPT-345M shape (keep 1/10: streamed whole); every output of the
     largest layers and of sampled small ones against the oracle."""
-    wl = synth.WORKLOADS["llama-1.75b"]
+    wl = synth.WORKLOADS[name]
     _assert_bitexact(run_parity(wl, 3, sample=FULL_LARGEST[wl.name], key_out=False, interleaved=True,
                                 update_in_dense=True))
     _assert_bitexact(run_parity(wl, wl.steps, sample=FULL_SAMPLES[wl.name], key_out=False, interleaved=True,
