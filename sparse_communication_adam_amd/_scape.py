@@ -333,9 +333,8 @@ def scape_set_select_path(ctx: Context, path: int) -> None:
 
 def scape_set_update_in_dense_pass(ctx: Context, on: bool) -> None:
     """From the next call on, let the dense pass finish the reduction and the
-    update at the mask's positions where the residuals are on the device and
-    the mask keeps at most 1/32 of the elements (the default), or make the
-    update a pass of its own (on = False)."""
+    update at the mask's positions where the residuals are on the device (the
+    default), or make the update a pass of its own (on = False)."""
     _check(lib().scape_set_update_in_dense_pass(ctx.handle, int(bool(on))))
 
 
