@@ -83,6 +83,21 @@ constexpr uint32_t ef_words() {
     return WT == 1 ? SCAPE_EF_W1 : 1;
 }
 
+// Threads per workgroup.  At W = 8 one-wave workgroups are faster, measured
+// build against build on one state: 64, 128 and 256 threads took 7.94, 8.08
+// and 8.18 ms on the 0.55B shape (update inside), 6.59, 6.66 and 6.69-6.70
+// on the GPT-345M shape (x, v and m streamed whole) and 5.23, 5.31 and 5.35
+// there without the update.  At W = 32 256 threads were the fastest (64:
+// 20.99, 128: 20.63, 256: 20.44 ms on the adversarial shard); at W = 4 the
+// three were within 0.4%.
+#ifndef SCAPE_EF_BLOCK_W8
+#define SCAPE_EF_BLOCK_W8 64
+#endif
+template <int WT>
+constexpr int ef_block() {
+    return WT == 8 ? SCAPE_EF_BLOCK_W8 : kEfBlock;
+}
+
 // With UPD the pass also finishes the step at the current mask's positions:
 // it has every worker's candidate of an element in registers, so the W-way
 // mean of what the workers send, the reconstruction and the m / v / x update
@@ -97,7 +112,7 @@ constexpr uint32_t ef_words() {
 // back, the old values where it is not masked, so those arrays move as whole
 // lines instead of scattered partial ones.
 template <int WT, bool K32, int UPD>
-__global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
+__global__ __launch_bounds__(ef_block<WT>()) void k_ef_compact(const uint16_t* __restrict__ word_info, uint32_t n_words,
                                                        WorkerPtrs wp, StepScalars sc, float* __restrict__ m,
                                                        const uint64_t* __restrict__ cur_bits,
                                                        const uint32_t* __restrict__ cur_prefix, uint32_t k_cap,
@@ -108,12 +123,13 @@ __global__ __launch_bounds__(kEfBlock) void k_ef_compact(const uint16_t* __restr
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int WMAX = WT > 0 ? WT : SCAPE_MAX_WORKERS;
     constexpr uint32_t kWords = ef_words<WT>();
+    constexpr int kB = ef_block<WT>(), kNW = kB / 64;
     // the selection's histogram rows, zeroed on the way (spread over every
     // workgroup; a few KB per layer)
-    for (uint32_t i = blockIdx.x * kEfBlock + threadIdx.x; i < n_clear; i += gridDim.x * kEfBlock) clear[i] = 0u;
+    for (uint32_t i = blockIdx.x * kB + threadIdx.x; i < n_clear; i += gridDim.x * kB) clear[i] = 0u;
     const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
     // wave-uniform, so the descriptors below are scalar loads
-    const uint32_t w0 = (blk * kEfWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64)) * kWords;
+    const uint32_t w0 = (blk * kNW + __builtin_amdgcn_readfirstlane(threadIdx.x / 64)) * kWords;
     if (w0 >= n_words) return;
     const uint32_t lane = lane_id();
     const int W = WT > 0 ? WT : sc.W;
@@ -343,7 +359,9 @@ hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t 
     }
 #define SCAPE_EF_LAUNCH(WV, K, U)                                                                                  \
     hipLaunchKernelGGL((k_ef_compact<WV, K, U>),                                                                   \
-                       dim3((n_words + kEfWaves * ef_words<WV>() - 1) / (kEfWaves * ef_words<WV>())), block, 0, s, \
+                       dim3((n_words + ef_block<WV>() / 64 * ef_words<WV>() - 1) /                                  \
+                            (ef_block<WV>() / 64 * ef_words<WV>())),                                                \
+                       dim3(ef_block<WV>()), 0, s,                                                                  \
                        word_info, n_words, wp, sc, m, cur_bits, cur_prefix, k_cap, key16, key32, m_stash, clear,   \
                        n_clear, x, v, dummy)
 #define SCAPE_EF_UPD(WV, K)                          \
