@@ -88,8 +88,8 @@ constexpr uint32_t ef_words() {
 // and 8.18 ms on the 0.55B shape (update inside), 6.59, 6.66 and 6.69-6.70
 // on the GPT-345M shape (x, v and m streamed whole) and 5.23, 5.31 and 5.35
 // there without the update.  At W = 32 256 threads were the fastest (64:
-// 20.99, 128: 20.63, 256: 20.44 ms on the adversarial shard); at W = 4 the
-// three were within 0.4%.
+// 20.99, 128: 20.63, 256: 20.44 ms on the adversarial shard); at W = 4 and
+// W = 1 (1.75B shape) the three were within 0.5%.
 #ifndef SCAPE_EF_BLOCK_W8
 #define SCAPE_EF_BLOCK_W8 64
 #endif
