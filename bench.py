@@ -19,7 +19,9 @@ gradient batches, with HIP events on its stream.  `fill_in` measures the
 alternative the pages' partitioned masks avoid: the union of per-worker masks
 over every layer, its density as workers are added, and the time to add one
 worker's mask.  `offload` times the step with the W residuals in pinned host
-memory (scape_step_offload), whose rate is bound by the PCIe copies.
+memory (scape_step_offload), whose rate is bound by PCIe: with the dense pass
+reading and writing them in host memory, and (`staged`) with copies through
+the GPU.
 `workloads` times the same step on every other workload shape (a few steps
 each, after everything above), with the same byte accounting.
 `shard_mask_build` times the mask build one worker runs on its own
@@ -251,13 +253,16 @@ def dense_adams(wl, layer_offset, n_pad: int, sets, steps: int, warmup: int, int
             "alg_bytes_per_step": dense_alg_bytes(N, wl.W), "alg_GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
-def offload_step(cfg, wl, steps: int, warmup: int) -> dict:
-    """The step with the residuals in pinned host memory: W*N*4 bytes copied
-    in and out over PCIe per step (one gradient batch, per-worker arrays)."""
+def offload_step(cfg, wl, steps: int, warmup: int, staged: bool = False) -> dict:
+    """The step with the residuals in pinned host memory: W*N*4 bytes read
+    and written over PCIe per step (one gradient batch, per-worker arrays),
+    by the dense pass itself, or through the staging slots (staged)."""
     import torch
     import synth
+    import sparse_communication_adam_amd as sc
     from sparse_communication_adam_amd.state import ScapeState
     state = ScapeState(cfg, offload=True)
+    sc.scape_set_offload_path(state.ctx, sc.OFFLOAD_PATH_STAGED if staged else sc.OFFLOAD_PATH_AUTO)
     lay = state.layout
     synth.params_flat_gpu(wl, lay.layer_offset, state.x)
     sets = [grad_set(wl, lay.layer_offset, lay.n_pad, 1, False)]
@@ -694,7 +699,12 @@ def main() -> int:
     offload = None
     if not args.no_offload:
         offload = offload_step(cfg, wl, 3, 2)
+        offload["path"] = "dense pass reads and writes the pinned residuals"
         log(f"offloaded-residual step: {offload['ms_per_step']:.1f} ms ({offload['pcie_GBps']:.1f} GB/s over PCIe)")
+        staged = offload_step(cfg, wl, 3, 2, staged=True)
+        offload["staged"] = {k: staged[k] for k in ("ms_per_step", "params_per_s", "pcie_GBps")}
+        log(f"offloaded-residual step, staged copies: {staged['ms_per_step']:.1f} ms "
+            f"({staged['pcie_GBps']:.1f} GB/s over PCIe)")
     fill = None
     if not args.no_fill_in:
         fill = fill_in(wl, cfg, offsets, n_pad)

@@ -163,6 +163,17 @@ int scape_set_select_path(scape_ctx* ctx, int32_t path);
  * takes effect from the next call.  Errors: INVALID_ARG. */
 int scape_set_update_in_dense_pass(scape_ctx* ctx, int32_t on);
 
+/* How scape_step_offload moves the residuals (the results are the same
+ * either way).  SCAPE_OFFLOAD_PATH_AUTO (the default): where every r_host[i]
+ * lies in pinned host memory mapped for the GPU (hipHostMalloc, a pinned
+ * torch tensor), the dense pass reads and writes them over PCIe itself, its
+ * reads and writes in flight together; otherwise through the staging slots.
+ * SCAPE_OFFLOAD_PATH_STAGED: always through the staging slots.  Host only,
+ * takes effect from the next call.  Errors: INVALID_ARG. */
+#define SCAPE_OFFLOAD_PATH_AUTO 0
+#define SCAPE_OFFLOAD_PATH_STAGED 1
+int scape_set_offload_path(scape_ctx* ctx, int32_t path);
+
 /*
  * One SCAPE step on W simulated workers, all resident on this GPU.
  *
@@ -250,22 +261,25 @@ int scape_step_interleaved(scape_ctx* ctx, float* xv, float* m, float* r_il, con
 /*
  * scape_step with the W residuals in pinned host memory: CPU offloading of
  * the residual buffers with double buffering ([TS-2] Memory Optimization).
- * Same computation and results as scape_step, bit for bit.  The residuals
- * move through the GPU in chunks of 2^27 / W elements per worker (512 MB of
- * residuals per chunk, the whole n_pad if smaller): host -> one of two device
- * staging slots on that slot's copy-in stream, the dense pass on `stream`,
- * staging -> host on the slot's copy-out stream, the two slots alternating so
- * the PCIe copies of one chunk overlap the dense pass and copies of the
- * other.  The rest of the step does not touch the residuals, so the last
- * copies back overlap it.
+ * Same computation and results as scape_step, bit for bit.  Where the GPU
+ * can address every residual array (pinned, mapped host memory; see
+ * scape_set_offload_path), the dense pass reads and writes the residuals in
+ * host memory itself, so PCIe carries both directions at once.  Otherwise
+ * the residuals move through the GPU in chunks of 2^27 / W elements per
+ * worker (512 MB of residuals per chunk, the whole n_pad if smaller): host ->
+ * one of two device staging slots on that slot's copy-in stream, the dense
+ * pass on `stream`, staging -> host on the slot's copy-out stream, the two
+ * slots alternating so the PCIe copies of one chunk overlap the dense pass
+ * and copies of the other.  The rest of the step does not touch the
+ * residuals, so the last copies back overlap it.
  * The step is complete on `stream` only once every residual chunk is back.
  * Arguments as scape_step, except r_host: a host array of W pointers to
  * pinned host memory (hipHostMalloc, or a pinned torch tensor), n_pad fp32
  * each, 16-byte aligned; pageable memory also works but copies synchronously.
  * The host must not touch r_host while a step is in flight.  The first call
  * on a context allocates what only this entry point uses, kept until
- * scape_destroy: a full-key array (n_pad x 4 bytes; the selection cannot
- * recompute candidates' keys without the residuals on the device), the
+ * scape_destroy: a full-key array (n_pad x 4 bytes; the selection does not
+ * read candidates' residuals in host memory), and for the staged path the
  * staging slots (2 x 512 MB at most) and four copy streams (default
  * priority); that call may block like hipMalloc.
  * Errors: as scape_step, and OOM.

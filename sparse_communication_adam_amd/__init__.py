@@ -13,6 +13,7 @@ from ._scape import (  # noqa: F401
     scape_step_interleaved, scape_dense_step_interleaved, interleaved_view, scape_workspace_bytes,
     scape_mask_index_static, scape_selection_flags, SELECT_EXACT_HISTOGRAM, SELECT_KEY_PASSES,
     scape_set_select_path, SELECT_PATH_AUTO, SELECT_PATH_SAMPLED, SELECT_PATH_COMPACT, scape_set_update_in_dense_pass,
+    scape_set_offload_path, OFFLOAD_PATH_AUTO, OFFLOAD_PATH_STAGED,
     scape_version)
 
 

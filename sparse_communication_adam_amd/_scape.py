@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "scape_selection_flags": [vp, vp],
             "scape_set_select_path": [vp, i32],
             "scape_set_update_in_dense_pass": [vp, i32],
+            "scape_set_offload_path": [vp, i32],
             "scape_step": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_offload": [vp, vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
             "scape_step_interleaved": [vp, vp, vp, vp, vp, maskp, maskp, vp, vp, vp],
@@ -329,6 +330,18 @@ def scape_set_select_path(ctx: Context, path: int) -> None:
     the sampled multi-pass path, the two-launch compact path, or AUTO (compact
     where every layer of the range has at most 2^22 elements)."""
     _check(lib().scape_set_select_path(ctx.handle, int(path)))
+
+
+OFFLOAD_PATH_AUTO = 0
+OFFLOAD_PATH_STAGED = 1
+
+
+def scape_set_offload_path(ctx: Context, path: int) -> None:
+    """From the next call on, move scape_step_offload's residuals by the
+    dense pass itself over PCIe where they are pinned, mapped host memory
+    (OFFLOAD_PATH_AUTO, the default), or always through the staging
+    slots (OFFLOAD_PATH_STAGED)."""
+    _check(lib().scape_set_offload_path(ctx.handle, int(path)))
 
 
 def scape_set_update_in_dense_pass(ctx: Context, on: bool) -> None:

@@ -185,6 +185,7 @@ struct scape_ctx {
     float* d_dummy = nullptr;               // 16 bytes no kernel writes (a safe load address)
     int32_t select_path = SCAPE_SELECT_PATH_AUTO;
     bool update_in_dense = true;            // scape_set_update_in_dense_pass
+    int32_t offload_path = SCAPE_OFFLOAD_PATH_AUTO;  // scape_set_offload_path
     // the update runs on its own stream beside the mask selection
     hipStream_t s_upd = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -482,10 +483,13 @@ int ef_offload(scape_ctx* c, const WorkerPtrs& wp, float* const* r_host, const S
 // recompute candidates' keys), the staging slots, and each slot's copy
 // streams and events (default priority; the events only order work).
 // Whatever a failed attempt made is kept and freed with the context.
-int ensure_offload(scape_ctx* c) {
-    if (c->offload_ready || c->n_words == 0) return SCAPE_OK;
+// What the offloaded step needs: the full-key array always, the staging
+// slots and copy streams only for the staged path.
+int ensure_offload(scape_ctx* c, bool staging) {
+    if (c->n_words == 0) return SCAPE_OK;
     int rc;
     if (!c->d_key32 && (rc = dev_alloc(c, &c->d_key32, (size_t)c->lay.n_pad, "full statistic keys"))) return rc;
+    if (c->offload_ready || !staging) return SCAPE_OK;
     c->chunk_words = std::min<uint32_t>(
         c->n_words, std::max<uint32_t>(kOffloadMinChunkWords, (uint32_t)(kOffloadSlotBytes / ((size_t)c->cfg.workers *
                                                                                              64 * sizeof(float)))));
@@ -506,6 +510,19 @@ int ensure_offload(scape_ctx* c) {
     if (e != hipSuccess) return hip_fail(e, "creating offload streams and events");
     c->offload_ready = true;
     return SCAPE_OK;
+}
+
+// The address the GPU reaches host memory at p by, if p lies in pinned host
+// memory mapped for the device (with unified addressing, p itself).  A
+// failed query leaves no error behind for the next launch check.
+bool host_device_pointer(float* p, float** dev) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || d == nullptr) {
+        (void)hipGetLastError();
+        return false;
+    }
+    *dev = static_cast<float*>(d);
+    return true;
 }
 
 // Where the W residuals and gradients are: one device array per worker, one
@@ -548,13 +565,23 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     if (cur->bits == next->bits || cur->idx == next->idx || cur->block_prefix == next->block_prefix)
         return fail(SCAPE_ERR_STATE, "next must not alias cur (the mask built now is used at the next step)");
     if ((rc = check_device(ctx))) return rc;
-    if (r_on_host && (rc = ensure_offload(ctx))) return rc;
+    // Residuals in host memory the GPU can address (pinned by hipHostMalloc
+    // or a pinned torch tensor) are read and written by the dense pass itself
+    // over PCIe, reads and writes in flight together; otherwise they move
+    // through the staging slots.
+    float* r_dev[SCAPE_MAX_WORKERS] = {};
+    bool direct = false;
+    if (r_on_host && ctx->offload_path == SCAPE_OFFLOAD_PATH_AUTO && ctx->n_words > 0) {
+        direct = true;
+        for (int i = 0; i < W && direct; ++i) direct = host_device_pointer(r[i], &r_dev[i]);
+    }
+    if (r_on_host && (rc = ensure_offload(ctx, !direct))) return rc;
 
     hipStream_t s = (hipStream_t)stream;
     WorkerPtrs wp{};
     wp.ws = il ? 64u * (uint32_t)W : 64u;
     for (int i = 0; i < W; ++i) {
-        wp.r[i] = r_on_host ? nullptr : il ? r[0] + 64 * i : r[i];
+        wp.r[i] = r_on_host ? r_dev[i] : il ? r[0] + 64 * i : r[i];
         wp.g[i] = il ? g[0] + 64 * i : g[i];
         wp.b[i] = ctx->lay.k_total > 0 ? sparse_bufs[i] : nullptr;
     }
@@ -605,7 +632,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     const bool sparse_mask = (uint64_t)k_cap * kFuseMaxDensityInv <= (uint64_t)ctx->lay.n_pad;
     const bool fuse = ctx->update_in_dense && !r_on_host && (sparse_mask || SCAPE_FUSE_DENSE);
     const int upd = !fuse ? 0 : sparse_mask ? (il ? 2 : 1) : (il ? 4 : 3);
-    if (r_on_host) {
+    if (r_on_host && !direct) {
         if ((rc = ef_offload(ctx, wp, r, sc, m, cur, k_cap, ctx->d_key16, key32, s))) return rc;
     } else {
         SCAPE_HIP(launch_ef_compact(s, ctx->d_word_info, ctx->n_words, wp, sc, m, cur->bits, cur->block_prefix,
@@ -666,7 +693,7 @@ int step_common(scape_ctx* ctx, float* x, float* m, float* v, float* const* r, c
     // join even after a failed launch
     SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_join, 0), "join");
     if (rc) return rc;
-    if (r_on_host && ctx->n_words > 0) {
+    if (r_on_host && !direct && ctx->n_words > 0) {
         // the step completes on `stream` only once every residual chunk is home
         for (int b = 0; b < kOffloadSlots; ++b) SCAPE_HIP(hipStreamWaitEvent(s, ctx->ev_out[b], 0), "offload wait");
     }
@@ -897,6 +924,14 @@ int scape_set_select_path(scape_ctx* ctx, int32_t path) {
     if (path != SCAPE_SELECT_PATH_AUTO && path != SCAPE_SELECT_PATH_SAMPLED && path != SCAPE_SELECT_PATH_COMPACT)
         return fail(SCAPE_ERR_INVALID_ARG, "unknown selection path %d", path);
     ctx->select_path = path;
+    return SCAPE_OK;
+}
+
+int scape_set_offload_path(scape_ctx* ctx, int32_t path) {
+    if (!ctx) return fail(SCAPE_ERR_INVALID_ARG, "ctx is NULL");
+    if (path != SCAPE_OFFLOAD_PATH_AUTO && path != SCAPE_OFFLOAD_PATH_STAGED)
+        return fail(SCAPE_ERR_INVALID_ARG, "unknown offload path %d", path);
+    ctx->offload_path = path;
     return SCAPE_OK;
 }
 

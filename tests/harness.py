@@ -98,6 +98,7 @@ class GpuRun:
     interleaved: bool = False  # residuals and gradients in the worker-interleaved layout
     select_path: Optional[int] = None  # scape_set_select_path (None: the library's default)
     update_in_dense: bool = False  # scape_set_update_in_dense_pass
+    offload_path: Optional[int] = None  # scape_set_offload_path (None: the library's default)
     state: object = None
     grads: List[object] = field(default_factory=list)
 
@@ -110,6 +111,8 @@ class GpuRun:
         if self.select_path is not None:
             sc.scape_set_select_path(self.state.ctx, self.select_path)
         sc.scape_set_update_in_dense_pass(self.state.ctx, self.update_in_dense)
+        if self.offload_path is not None:
+            sc.scape_set_offload_path(self.state.ctx, self.offload_path)
         self.layout = self.state.layout
         n = self.layout.n_pad
         if not self.x_zero:
@@ -177,7 +180,7 @@ def oracle_inputs(wl: synth.Workload, lay: oracle.Layout, tensors: Sequence[int]
 def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] = None, keep=None, W=None,
                init_mask_all=False, x_zero=False, grad_override=None, check_buffers=True,
                offload=False, key_out=True, interleaved=False, select_path=None,
-               update_in_dense=False) -> Dict[str, int]:
+               update_in_dense=False, offload_path=None) -> Dict[str, int]:
     """Run `steps` steps on the GPU (all layers) and the oracle (all layers, or
     the sampled ones) and compare every output of every step."""
     import torch
@@ -189,9 +192,10 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
         f"oracle layers={len(tensors)} ({lay.n_pad} elements){' residuals on the host' if offload else ''}"
         f"{'' if key_out else ', candidate keys recomputed'}{', worker-interleaved layout' if interleaved else ''}"
         f"{'' if select_path is None else f', selection path {select_path}'}"
-        f"{', update in the dense pass' if update_in_dense else ''}")
+        f"{', update in the dense pass' if update_in_dense else ''}"
+        f"{'' if offload_path is None else f', offload path {offload_path}'}")
     run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path,
-                 update_in_dense)
+                 update_in_dense, offload_path)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total
     assert list(glay.layer_offset) == full.off.tolist() and list(glay.layer_k) == full.k.tolist()

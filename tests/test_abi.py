@@ -121,6 +121,7 @@ def test_null_arguments_rejected_before_any_launch(sc):
     assert lib.scape_profile_enable(None, 1) == -1
     assert lib.scape_set_select_path(None, 0) == -1
     assert lib.scape_set_update_in_dense_pass(None, 1) == -1
+    assert lib.scape_set_offload_path(None, 0) == -1
     assert lib.scape_copy_probe(None, None, 0, None) == 0  # nothing to copy
     assert lib.scape_copy_probe(None, None, 16, None) == -1
     assert lib.scape_copy_probe(ctypes.c_void_p(16), ctypes.c_void_p(8), 16, None) == -3  # dst misaligned

@@ -1,9 +1,11 @@
 """Parity of the step with the residuals in pinned host memory
 (scape_step_offload: CPU offloading with double buffering, Memory
 Optimization in the gist.science Technical Summary, s.2) with the oracle, on
-a GPU.  The offloaded step runs the same kernels as scape_step over chunks of
-512 MB of residuals (2^27 / W elements), so every output is expected
-bit-exact.
+a GPU, on both of its paths: the dense pass reading and writing the pinned
+residuals over PCIe itself (the default for pinned memory), and the staged
+path, which runs the same kernels as scape_step over chunks of 512 MB of
+residuals (2^27 / W elements) copied through the GPU.  Every output is
+expected bit-exact.
 """
 import gc
 
@@ -34,15 +36,25 @@ def _assert_bitexact(stats):
     assert stats["float_not_bitexact"] == 0, stats
 
 
-def test_offload_step_ragged_single_chunk():
-    _assert_bitexact(run_parity(synth.ragged(), 5, offload=True))
+PATHS = pytest.mark.parametrize("path", ["direct", "staged"])
+
+
+def _path(name):
+    import sparse_communication_adam_amd as sc
+    return sc.OFFLOAD_PATH_AUTO if name == "direct" else sc.OFFLOAD_PATH_STAGED
+
+
+@PATHS
+def test_offload_step_ragged_single_chunk(path):
+    _assert_bitexact(run_parity(synth.ragged(), 5, offload=True, offload_path=_path(path)))
 
 
 def _pad64(n):
     return (n + 63) // 64 * 64
 
 
-def test_offload_step_three_chunks_with_boundaries_inside_layers():
+@PATHS
+def test_offload_step_three_chunks_with_boundaries_inside_layers(path):
     """About 87M elements at W = 4 (33,554,432 elements per chunk, the
     library's 512 MB staging slot): three residual chunks, staging slot 0
     reused, and the two chunk boundaries falling inside small layers, which
@@ -58,8 +70,9 @@ def test_offload_step_three_chunks_with_boundaries_inside_layers():
     assert off[1] < chunk < off[1] + ts[1].numel and off[3] < 2 * chunk < off[3] + ts[3].numel
     assert 2 * chunk < n_pad <= 3 * chunk
     wl = synth.ragged().with_tensors(ts, name="offload-chunks")
-    _assert_bitexact(run_parity(wl, 4, sample=[1, 3, 5], W=W, offload=True))
+    _assert_bitexact(run_parity(wl, 4, sample=[1, 3, 5], W=W, offload=True, offload_path=_path(path)))
 
 
-def test_offload_step_reduced_llama():
-    _assert_bitexact(run_parity(synth.reduced(synth.LLAMA175), 3, offload=True))
+@PATHS
+def test_offload_step_reduced_llama(path):
+    _assert_bitexact(run_parity(synth.reduced(synth.LLAMA175), 3, offload=True, offload_path=_path(path)))
