@@ -715,4 +715,21 @@ hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t valu
     return hipGetLastError();
 }
 
+// Several ranges zeroed by one launch: row y of the grid takes range y.
+__global__ __launch_bounds__(kBlock) void k_zero_ranges(ZeroRanges zr) {
+    uint32_t* __restrict__ p = zr.p[blockIdx.y];
+    const uint64_t n = zr.n[blockIdx.y];
+    for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kBlock) p[i] = 0u;
+}
+
+hipError_t launch_zero_ranges(hipStream_t s, const ZeroRanges& zr) {
+    uint64_t most = 0;
+    for (int i = 0; i < zr.count; ++i) most = zr.n[i] > most ? zr.n[i] : most;
+    if (most == 0) return hipSuccess;
+    uint64_t blocks = (most + kBlock - 1) / kBlock;
+    if (blocks > 8192u) blocks = 8192u;
+    hipLaunchKernelGGL(k_zero_ranges, dim3((uint32_t)blocks, (uint32_t)zr.count), dim3(kBlock), 0, s, zr);
+    return hipGetLastError();
+}
+
 }  // namespace scape

@@ -358,21 +358,30 @@ int run_select_compact(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32
     return SCAPE_OK;
 }
 
+// `zero`: ranges the caller needs zeroed before the selection (the mask
+// build's histogram rows); the sampled path zeroes them with its own counters
+// in one launch.
 int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, const uint16_t* key,
-               const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork = nullptr) {
-    if (compact_range(c, la, nl)) return run_select_compact(c, la, nl, ta, tb, key, ks, bits, s, fork);
+               const KeySource& ks, uint64_t* bits, hipStream_t s, hipEvent_t fork = nullptr,
+               ZeroRanges zero = ZeroRanges{}) {
+    if (compact_range(c, la, nl)) {
+        SCAPE_HIP(launch_zero_ranges(s, zero), "zero");
+        return run_select_compact(c, la, nl, ta, tb, key, ks, bits, s, fork);
+    }
     const TileDesc* tiles = c->d_tiles + ta;
     const uint32_t nt = tb - ta;
     const uint32_t sa = c->layer_seg0[la], ns = c->layer_seg0[la + nl] - sa;
     if (ns == 0) {  // every layer in the range is empty: no bits to set
+        SCAPE_HIP(launch_zero_ranges(s, zero), "zero");
         if (fork) SCAPE_HIP(hipEventRecord(fork, s), "fork");
         return SCAPE_OK;
     }
     uint32_t* sample_count = c->d_counts;
-    SCAPE_HIP(launch_fill_u32(s, c->d_seg_fill + sa, (uint64_t)ns, 0u), "fill");
-    SCAPE_HIP(launch_fill_u32(s, c->d_seg_above + sa, (uint64_t)ns, 0u), "fill");
-    SCAPE_HIP(launch_fill_u32(s, sample_count + la, (uint64_t)nl, 0u), "fill");
-    SCAPE_HIP(launch_fill_u32(s, c->d_ovf + la, (uint64_t)nl, 0u), "fill");
+    zero.add(c->d_seg_fill + sa, (uint64_t)ns);
+    zero.add(c->d_seg_above + sa, (uint64_t)ns);
+    zero.add(sample_count + la, (uint64_t)nl);
+    zero.add(c->d_ovf + la, (uint64_t)nl);
+    SCAPE_HIP(launch_zero_ranges(s, zero), "zero");
     SCAPE_HIP(launch_sample_hist(s, tiles, nt, c->d_layers, key, c->d_hist, sample_count), "sample_hist");
     SCAPE_HIP(launch_estimate(s, la, nl, c->d_layers, c->d_hist, sample_count, c->d_sel, c->d_miss), "estimate");
     SCAPE_HIP(launch_filter(s, tiles, nt, c->d_layers, c->d_segs, c->d_sel, key, bits, c->d_seg_fill, c->d_cand,
@@ -1026,14 +1035,15 @@ int scape_mask_build(scape_ctx* ctx, const float* mtilde, int32_t num_shards, in
         if (la >= lb) return SCAPE_OK;  // the shard owns no layer
     }
     const uint32_t ta = ctx->layer_tile0[la], tb = ctx->layer_tile0[lb];
-    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist + (size_t)la * kHistBins, (uint64_t)(lb - la) * kHistBins, 0u), "fill");
     const uint32_t wa = (uint32_t)(ctx->lay.off[la] / 64), wb = ctx->layer_tile0[lb] > ctx->layer_tile0[la]
                                                                  ? ctx->tiles[ctx->layer_tile0[lb] - 1].w1
                                                                  : wa;
     SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, wa, wb, mtilde, ctx->d_key16), "keys");
     KeySource ks{};
     ks.mtilde = mtilde;
-    if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key16, ks, out->bits, s))) return rc;
+    ZeroRanges rows{};  // the range's histogram rows (the step's dense pass clears them on its way)
+    rows.add(ctx->d_hist + (size_t)la * kHistBins, (uint64_t)(lb - la) * kHistBins);
+    if ((rc = run_select(ctx, la, lb - la, ta, tb, ctx->d_key16, ks, out->bits, s, nullptr, rows))) return rc;
     if (all && (rc = run_index(ctx, out, s))) return rc;
     return SCAPE_OK;
 }
@@ -1048,11 +1058,13 @@ int scape_mask_union_add(scape_ctx* ctx, const float* mtilde, uint64_t* acc_bits
     hipStream_t s = (hipStream_t)stream;
     const int32_t L = ctx->lay.L;
     if (L == 0 || ctx->tiles.empty()) return SCAPE_OK;
-    SCAPE_HIP(launch_fill_u32(s, ctx->d_hist, (uint64_t)L * kHistBins, 0u), "fill");
     SCAPE_HIP(launch_keys_from_mtilde(s, ctx->d_word_info, 0, ctx->n_words, mtilde, ctx->d_key16), "keys");
     KeySource ks{};
     ks.mtilde = mtilde;
-    if ((rc = run_select(ctx, 0, L, 0, (uint32_t)ctx->tiles.size(), ctx->d_key16, ks, ctx->d_union_bits, s)))
+    ZeroRanges rows{};
+    rows.add(ctx->d_hist, (uint64_t)L * kHistBins);
+    if ((rc = run_select(ctx, 0, L, 0, (uint32_t)ctx->tiles.size(), ctx->d_key16, ks, ctx->d_union_bits, s, nullptr,
+                         rows)))
         return rc;
     SCAPE_HIP(launch_or_words(s, ctx->d_union_bits, acc_bits, ctx->n_words), "or_words");
     return SCAPE_OK;

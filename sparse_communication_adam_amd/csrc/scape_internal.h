@@ -181,6 +181,20 @@ hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uin
                                    const float* mtilde, uint16_t* key16);
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t value);
+// Up to kZeroRangesMax arrays of 32-bit words zeroed by one launch (ranges of
+// n = 0 are allowed; nothing is launched if every range is empty).
+constexpr int kZeroRangesMax = 6;
+struct ZeroRanges {
+    uint32_t* p[kZeroRangesMax];
+    uint64_t n[kZeroRangesMax];
+    int32_t count;
+    void add(uint32_t* ptr, uint64_t words) {
+        p[count] = ptr;
+        n[count] = words;
+        ++count;
+    }
+};
+hipError_t launch_zero_ranges(hipStream_t s, const ZeroRanges& zr);
 
 // selection
 hipError_t launch_sample_hist(hipStream_t s, const TileDesc* tiles, uint32_t n_tiles, const LayerDesc* layers,
