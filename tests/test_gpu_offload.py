@@ -76,3 +76,13 @@ def test_offload_step_three_chunks_with_boundaries_inside_layers(path):
 @PATHS
 def test_offload_step_reduced_llama(path):
     _assert_bitexact(run_parity(synth.reduced(synth.LLAMA175), 3, offload=True, offload_path=_path(path)))
+
+
+@pytest.mark.timeout(900)
+def test_offload_step_full_size_direct():
+    """The 1.75B shape at full size with its 28 GB of residuals in pinned
+    host memory, read and written by the dense pass over PCIe: every output
+    of sampled layers (norms, an attention output, the last layers) against
+    the oracle for three steps."""
+    wl = synth.WORKLOADS["llama-1.75b"]
+    _assert_bitexact(run_parity(wl, 3, sample=[1, 3, 4, 190, 193], offload=True, offload_path=_path("direct")))
