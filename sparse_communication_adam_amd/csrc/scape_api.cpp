@@ -377,6 +377,7 @@ int run_select(scape_ctx* c, int32_t la, int32_t nl, uint32_t ta, uint32_t tb, c
         return SCAPE_OK;
     }
     uint32_t* sample_count = c->d_counts;
+    if (zero.count > kZeroRangesMax - 4) return fail(SCAPE_ERR_STATE, "too many ranges to zero");
     zero.add(c->d_seg_fill + sa, (uint64_t)ns);
     zero.add(c->d_seg_above + sa, (uint64_t)ns);
     zero.add(sample_count + la, (uint64_t)nl);

@@ -182,7 +182,9 @@ hipError_t launch_keys_from_mtilde(hipStream_t s, const uint16_t* word_info, uin
 hipError_t launch_reduce_sparse(hipStream_t s, const float* const* bufs, int32_t W, int64_t k, float* out);
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, uint64_t n, uint32_t value);
 // Up to kZeroRangesMax arrays of 32-bit words zeroed by one launch (ranges of
-// n = 0 are allowed; nothing is launched if every range is empty).
+// n = 0 are allowed; nothing is launched if every range is empty).  add()
+// does not check the count: the selection adds four ranges to at most two
+// of its caller's.
 constexpr int kZeroRangesMax = 6;
 struct ZeroRanges {
     uint32_t* p[kZeroRangesMax];
