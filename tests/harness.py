@@ -85,7 +85,7 @@ def first_mask_diff(lay: oracle.Layout, got_bits: np.ndarray, exp_bits: np.ndarr
 
 
 @dataclass
-class GpuRun:
+class GpuSession:
     """A ScapeState driven with GPU-generated inputs for one workload."""
     wl: synth.Workload
     keep: Optional[tuple] = None
@@ -194,7 +194,7 @@ def run_parity(wl: synth.Workload, steps: int, sample: Optional[Sequence[int]] =
         f"{'' if select_path is None else f', selection path {select_path}'}"
         f"{', update in the dense pass' if update_in_dense else ''}"
         f"{'' if offload_path is None else f', offload path {offload_path}'}")
-    run = GpuRun(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path,
+    run = GpuSession(wl, keep, W, init_mask_all, x_zero, grad_override, offload, key_out, interleaved, select_path,
                  update_in_dense, offload_path)
     glay = run.layout
     assert glay.n_pad == full.n_pad and glay.k_total == full.k_total

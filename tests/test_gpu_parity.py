@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from harness import GpuRun, log, release, run_parity, scape_config, to_np, u32, u64
+from harness import GpuSession, log, release, run_parity, scape_config, to_np, u32, u64
 
 pytestmark = pytest.mark.gpu
 
@@ -530,7 +530,7 @@ def test_step_is_deterministic():
     wl = synth.reduced(synth.ADVERSARIAL)
     outs = []
     for _ in range(2):
-        run = GpuRun(wl)
+        run = GpuSession(wl)
         for t in range(1, 4):
             run.step(t)
         torch.cuda.synchronize()
@@ -754,7 +754,7 @@ def test_step_update_in_dense_pass_matches_separate_update():
     wl = synth.reduced(synth.LLAMA175)
     outs = []
     for on in (False, True):
-        run = GpuRun(wl, interleaved=True, key_out=False, update_in_dense=on)
+        run = GpuSession(wl, interleaved=True, key_out=False, update_in_dense=on)
         for t in range(1, 5):
             run.step(t)
         torch.cuda.synchronize()
