@@ -163,8 +163,9 @@ struct StepScalars {
 // upd 0: the update is left to launch_reduce_update (m_stash written);
 // upd 1 / 2: the pass also updates m, v, x at the mask's positions (x and v
 // apart / x holding (x, v) pairs), touching them there only; `dummy` is 8
-// bytes nothing writes.  upd 3 / 4: the same, streaming x, v and m whole and
-// storing the unmasked elements' old values back.
+// bytes nothing writes.  upd 3 / 4: the same, streaming x, v and m whole
+// (upd 4: the (x, v) pairs of lines that hold a masked element) and storing
+// the unmasked elements' old values back.
 hipError_t launch_ef_compact(hipStream_t s, const uint16_t* word_info, uint32_t n_words, const WorkerPtrs& wp,
                              const StepScalars& sc, float* m, const uint64_t* cur_bits,
                              const uint32_t* cur_prefix, uint32_t k_cap, uint16_t* key16, uint32_t* key32,
