@@ -315,7 +315,8 @@ hipError_t launch_estimate(hipStream_t s, int32_t layer0, int32_t n_layers, cons
 // and the next trip's loads are in flight while a trip is processed.  The
 // hot key filter takes 16 (measured on 1.75G keys: 4 words 1.24 ms, 8 0.91,
 // 16 0.82, 24 0.91, 32 0.95: more in flight until the registers cut the
-// waves per SIMD); the other passes keep 8.
+// waves per SIMD; on the GPT-345M shape at keep 1/10, with records in most
+// words, 8, 16 and 24 took 287, 276 and 326 us); the other passes keep 8.
 constexpr int kFilterWords = 8;
 constexpr int kFilterWordsHot = 16;
 constexpr int kWaveStage = 256;                 // staged records per wave (2 KB): 8 KB per workgroup
