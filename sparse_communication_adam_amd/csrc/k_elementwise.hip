@@ -66,6 +66,16 @@ constexpr int kEfWaves = kEfBlock / 64;
 #define SCAPE_EF_XCD 1
 #endif
 constexpr bool kEfXcd = SCAPE_EF_XCD != 0;
+// The exception: at W = 4 in the interleaved layout with the update inside,
+// measured build against build on one state, the pass without the
+// renumbering took 14.02-14.04 against 14.21-14.24 ms in a fresh GPU's first
+// process (where a training job's process runs) and 13.75 against 13.52 in
+// the process after it; at W = 8 and 32 the renumbering was 4-13% faster in
+// either.
+template <int WT, int UPD>
+constexpr bool ef_xcd() {
+    return kEfXcd && !(WT == 4 && UPD == 2);
+}
 
 // Consecutive words per wave.  Measured on the 1.75B shape in both
 // residual/gradient layouts: at W = 4 one word per wave took 15.3 ms (one
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(ef_block<WT>()) void k_ef_compact(const uint16_t* _
     // the selection's histogram rows, zeroed on the way (spread over every
     // workgroup; a few KB per layer)
     for (uint32_t i = blockIdx.x * kB + threadIdx.x; i < n_clear; i += gridDim.x * kB) clear[i] = 0u;
-    const uint32_t blk = kEfXcd ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t blk = ef_xcd<WT, UPD>() ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
     // wave-uniform, so the descriptors below are scalar loads
     const uint32_t w0 = (blk * kNW + __builtin_amdgcn_readfirstlane(threadIdx.x / 64)) * kWords;
     if (w0 >= n_words) return;
